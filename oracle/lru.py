@@ -1,0 +1,123 @@
+"""Fixed-size HBM page cache over a host-resident KV tier -- TEST INFRASTRUCTURE ONLY.
+
+Oracle of the in-graph cache resolver described on [P2] "HiSparse: Scaling
+Sparse Attention Decoding with Hierarchical KV Cache" (abstract, sentence on the
+fused resolver: hit detection, LRU replacement and host-to-device fetch inside
+the decode graph; and the sentence stating that only placement changes, so
+outputs are unchanged).  The pages give no slot or tie rules; the ones below
+are this library's reading, stated once here:
+
+* A cache unit is one (logical page, KV head) of one request: its K tile and V
+  tile.  unit id = h * max_pages + p.
+* Per request and step, the requested set R is the union of that request's
+  per-KV-head page lists.  Units of R already resident are hits; they get the
+  step number as their stamp.
+* Misses, in ascending unit id, take slots in ascending slot index from the
+  available set.  If the free slots suffice, the available set is the lowest
+  free slots; otherwise it is every free slot plus the r least recently used
+  resident units outside R, ordered by (stamp ascending, unit id ascending),
+  r = |misses| - |free|.  (This is exact LRU eviction with ties broken by the
+  lower unit id; which slot a miss lands in is placement only.)
+* If fewer slots can be made available than there are misses, the step sets
+  the overflow flag, the misses that got no slot keep slot -1, and the step's
+  outputs are not meaningful.
+"""
+
+from collections import OrderedDict
+
+import numpy as np
+
+
+class LRUState:
+    """Cache state of one request: capacity slots, their unit tags and stamps."""
+
+    def __init__(self, capacity, n_units):
+        self.capacity = int(capacity)
+        self.tag = np.full(self.capacity, -1, dtype=np.int64)
+        self.stamp = np.full(self.capacity, -1, dtype=np.int64)
+        self.slot_of = np.full(int(n_units), -1, dtype=np.int64)
+
+    def copy(self):
+        c = LRUState(self.capacity, self.slot_of.shape[0])
+        c.tag[:] = self.tag
+        c.stamp[:] = self.stamp
+        c.slot_of[:] = self.slot_of
+        return c
+
+
+def resolve_step(state, requested_units, step):
+    """Apply one step to ``state`` in place.
+
+    requested_units: iterable of unit ids (duplicates allowed).  Returns a dict
+    with 'hits', 'misses', 'evictions', 'overflow' and 'placed' (list of
+    (unit, slot) for the misses, ascending unit id; slot -1 if unplaced).
+    """
+    R = np.unique(np.asarray(list(requested_units), dtype=np.int64))
+    resident = state.slot_of[R] >= 0
+    hits = R[resident]
+    misses = R[~resident]
+    state.stamp[state.slot_of[hits]] = step
+
+    free = np.nonzero(state.tag < 0)[0]
+    if misses.size <= free.size:
+        avail = free[:misses.size]
+    else:
+        r = misses.size - free.size
+        inR = np.zeros(state.slot_of.shape[0], dtype=bool)
+        inR[R] = True
+        cand = np.nonzero((state.tag >= 0) & ~inR[np.maximum(state.tag, 0)])[0]
+        order = np.lexsort((state.tag[cand], state.stamp[cand]))
+        victims = cand[order[:r]]
+        avail = np.sort(np.concatenate([free, victims]))
+
+    evictions = 0
+    placed = []
+    for i, u in enumerate(misses):
+        if i >= avail.size:
+            placed.append((int(u), -1))
+            continue
+        s = int(avail[i])
+        old = state.tag[s]
+        if old >= 0:
+            state.slot_of[old] = -1
+            evictions += 1
+        state.tag[s] = u
+        state.stamp[s] = step
+        state.slot_of[u] = s
+        placed.append((int(u), s))
+    overflow = int(misses.size > avail.size)
+    return {"hits": int(hits.size), "misses": int(misses.size),
+            "evictions": evictions, "overflow": overflow, "placed": placed}
+
+
+def textbook_lru_trace(capacity, steps_units):
+    """Plain LRU over an OrderedDict, one step at a time.
+
+    Within a step every requested unit counts as used at that step; units used
+    at the same step are ordered by ascending unit id.  Eviction only happens
+    when the cache is full and takes the least recently used unit that the
+    step does not request.  Returns per step (hits, misses, evictions,
+    resident set).
+    """
+    lru = OrderedDict()
+    out = []
+    for units in steps_units:
+        R = sorted(set(int(u) for u in units))
+        Rset = set(R)
+        hits = [u for u in R if u in lru]
+        misses = [u for u in R if u not in lru]
+        ev = 0
+        for u in misses:
+            if len(lru) >= capacity:
+                victim = next((k for k in lru if k not in Rset), None)
+                if victim is None:
+                    raise OverflowError("more distinct units in one step than slots")
+                del lru[victim]
+                ev += 1
+            lru[u] = True
+        for u in R:            # re-insert the step's units in ascending id
+            del lru[u]
+        for u in R:
+            lru[u] = True
+        out.append((len(hits), len(misses), ev, frozenset(lru.keys())))
+    return out
