@@ -1,0 +1,251 @@
+// Self-planning split-K decode attention over variable-length page lists
+// ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
+// Hierarchy", MOIRA abstract, sentence on self-planning attention: each block
+// derives its share of the work from the list lengths, with no host-side
+// plan, so the step stays inside the graph).
+//
+// The grid is fixed (one workgroup per possible chunk).  Workgroup c finds its
+// unit by a wave-parallel search over the device-written chunk prefix sums,
+// then its 4 waves split the chunk's pages; each wave runs an online softmax
+// for the unit's G query heads on the bf16 matrix cores:
+//   QK:  S^T[t][g] = K[t][:] . q[g][:]   v_mfma_f32_16x16x32_bf16, 4 k-slices
+//        (A = K tile rows = tokens, read straight from HBM in 16-byte runs;
+//         B = q of the group, columns = heads)
+//   PV:  O^T[d][g] += V^T[d][t] P^T[t][g]  v_mfma_f32_16x16x16bf16_1k, 8 tiles
+//        (A = the channel-major V tile, 8-byte token runs; B = P, which the
+//         QK result layout already holds in the right lanes).  P is split
+//        into a bf16 high part and a bf16 residual, two products, so the
+//        weights keep ~16 significant bits.
+// The 4 waves' (max, sum, O) are merged in LDS into one normalised partial
+// and its log-sum-exp per head.
+
+#include "common.h"
+
+namespace sp {
+
+constexpr int kAttnWaves = 4;
+
+// Largest u in [0, U) with offs[u] <= c (offs non-decreasing, offs[0] = 0 <= c).
+__device__ __forceinline__ int find_unit(const int32_t* __restrict__ offs, int U, int c) {
+  const int lane = lane_id();
+  int lo = 0, n = U;
+  while (n > 64) {
+    const int step = (n + 63) / 64;
+    const bool ok = (lane * step < n) && offs[lo + lane * step] <= c;
+    const unsigned long long mask = __ballot(ok);
+    const int last = 63 - __clzll(mask);
+    lo += last * step;
+    n = min(step, n - last * step);
+  }
+  const bool ok = (lane < n) && offs[lo + lane] <= c;
+  const unsigned long long mask = __ballot(ok);
+  return lo + (63 - __clzll(mask));
+}
+
+struct PageFrag {
+  u32x4 k[4];   // K tile: token (lane & 15), channels 32 s + 8 (lane >> 4) .. +7
+  u32x2 v[8];   // V^T tile m: channel 16 m + (lane & 15), tokens 4 (lane >> 4) .. +3
+  int valid;    // valid tokens (0 = skip page)
+};
+
+__device__ __forceinline__ void load_page(PageFrag& f, const uint16_t* __restrict__ kv,
+                                          int64_t stride_page, int64_t stride_head,
+                                          int64_t pool_pages, int h, int L,
+                                          const int32_t* __restrict__ lp,
+                                          const int32_t* __restrict__ lx, int i) {
+  const int lane = lane_id(), row = lane & 15, j = lane >> 4;
+  const int p = lp[i];
+  const int x = lx[i];
+  int nv = min(kP, L - kP * p);
+  if (x < 0 || x >= pool_pages || p < 0) nv = 0;
+  f.valid = max(nv, 0);
+  if (f.valid == 0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.k[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) f.v[m] = u32x2{0u, 0u};
+    return;
+  }
+  const uint16_t* kt = kv + (int64_t)x * stride_page + (int64_t)h * stride_head;
+  const uint16_t* vt = kt + kTile;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    f.k[s] = *reinterpret_cast<const u32x4*>(kt + row * kD + 32 * s + 8 * j);
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    f.v[m] = *reinterpret_cast<const u32x2*>(vt + (16 * m + row) * kP + 4 * j);
+}
+
+__global__ __launch_bounds__(256) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
+    int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ chunk_offsets,
+    const int32_t* __restrict__ sel_pages, const int32_t* __restrict__ sel_phys,
+    float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int U,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
+  const int c = blockIdx.x;
+  const int total = chunk_offsets[U];
+  if (c >= total) return;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
+  const int u = find_unit(chunk_offsets, U, c);
+  const int b = u / hkv, h = u - (u / hkv) * hkv;
+  const int L = min(max(ctx_lens[b], 0), max_pages * kP);
+  const int cnt = min(sel_counts[u], max_pages);
+  const int i0 = (c - chunk_offsets[u]) * chunk_pages;
+  const int i1 = min(i0 + chunk_pages, cnt);
+  const int32_t* lp = sel_pages + (int64_t)u * max_pages;
+  const int32_t* lx = sel_phys + (int64_t)u * max_pages;
+
+  // B operand of QK: q of head g = row (zero for padding columns).
+  const int g = row;
+  const bool gok = g < group;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (gok)
+      w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hkv * group + h * group + g) * kD +
+                                          32 * s + 8 * j);
+    qf[s] = as_bf16x8(w);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 o[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  int i = i0 + wv;
+  PageFrag cur;
+  if (i < i1) load_page(cur, kv, stride_page, stride_head, pool_pages, h, L, lp, lx, i);
+  for (; i < i1; i += kAttnWaves) {
+    PageFrag nxt;
+    const bool more = i + kAttnWaves < i1;
+    if (more) load_page(nxt, kv, stride_page, stride_head, pool_pages, h, L, lp, lx, i + kAttnWaves);
+    if (cur.valid > 0) {
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[s]), qf[s], sacc, 0, 0, 0);
+      // lane (g, j): logits of tokens 4j + e, in log2 units
+      float xs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[e] = (gok && 4 * j + e < cur.valid) ? sacc[e] * scale_log2 : -INFINITY;
+      float pm = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+      const float m_new = gok ? fmaxf(m_run, pm) : 0.f;
+      const float alpha = gok ? exp2f(m_run - m_new) : 1.f;
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = gok ? exp2f(xs[e] - m_new) : 0.f;
+      l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+      m_run = gok ? m_new : m_run;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o[m] *= alpha;
+      if (cur.valid < kP) {
+        // zero V of tokens past the end of the context (they may hold anything)
+        const int t0 = 4 * j;
+        const uint32_t k0 = (t0 + 0 < cur.valid ? 0x0000FFFFu : 0u) | (t0 + 1 < cur.valid ? 0xFFFF0000u : 0u);
+        const uint32_t k1 = (t0 + 2 < cur.valid ? 0x0000FFFFu : 0u) | (t0 + 3 < cur.valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          cur.v[m][0] &= k0;
+          cur.v[m][1] &= k1;
+        }
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = f32_to_bf16_rne(pv[e]);
+        lo[e] = f32_to_bf16_rne(pv[e] - __uint_as_float(hi[e] << 16));
+      }
+      const short4v phi = as_short4(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+      const short4v plo = as_short4(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(cur.v[m]), phi, o[m], 0, 0, 0);
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(cur.v[m]), plo, o[m], 0, 0, 0);
+      }
+    }
+    if (more) cur = nxt;
+  }
+
+  // ---- merge the waves of the workgroup ------------------------------------
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  float* so = smem;                                   // [kAttnWaves][group][kD]
+  float* sm = smem + kAttnWaves * group * kD;         // [kAttnWaves][group]
+  float* sl = sm + kAttnWaves * group;
+  if (gok) {
+    float* dst = so + (wv * group + g) * kD;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      *reinterpret_cast<floatx4*>(dst + 16 * m + 4 * j) = o[m];
+    if (j == 0) {
+      sm[wv * group + g] = m_run;
+      sl[wv * group + g] = l_run;
+    }
+  }
+  __syncthreads();
+  const float ln2 = 0.6931471805599453f;
+  for (int idx = threadIdx.x; idx < group * kD; idx += 256) {
+    const int gg = idx / kD, d = idx - (idx / kD) * kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm[w * group + gg]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = sm[w * group + gg];
+        if (mw == -INFINITY) continue;
+        const float a = exp2f(mw - M);
+        num += a * so[(w * group + gg) * kD + d];
+        den += a * sl[w * group + gg];
+      }
+    }
+    const int64_t slot = (int64_t)c * group + gg;
+    part_o[slot * kD + d] = (den > 0.f) ? num / den : 0.f;
+    if (d == 0) part_lse[slot] = (den > 0.f) ? (M + log2f(den)) * ln2 : -INFINITY;
+  }
+}
+
+}  // namespace sp
+
+extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages) {
+  if (sp::check_dims(dims) != SPARSE_OK || chunk_pages < 1) return -1;
+  const int64_t U = (int64_t)dims->batch * dims->num_kv_heads;
+  return U * ((dims->max_pages + chunk_pages - 1) / chunk_pages);
+}
+
+extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q,
+                                            const uint16_t* kv, int64_t stride_page,
+                                            int64_t stride_head, int64_t pool_pages,
+                                            const int32_t* ctx_lens, const int32_t* sel_counts,
+                                            const int32_t* chunk_offsets,
+                                            const int32_t* sel_pages, const int32_t* sel_phys,
+                                            float scale, int32_t chunk_pages, float* part_o,
+                                            float* part_lse, int64_t max_parts, void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if ((st = sp::check_pool(kv, stride_page, stride_head, pool_pages)) != SPARSE_OK) return st;
+  if (!q || !ctx_lens || !sel_counts || !chunk_offsets || !sel_pages || !sel_phys || !part_o ||
+      !part_lse)
+    return SPARSE_ERR_INVALID;
+  if (!sp::aligned(q, 16) || !sp::aligned(part_o, 16) || !isfinite(scale))
+    return SPARSE_ERR_INVALID;
+  if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
+  if (max_parts != sparse_decode_max_parts(dims, chunk_pages)) return SPARSE_ERR_INVALID;
+  if (max_parts > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  const size_t lds = sizeof(float) * (size_t)sp::kAttnWaves * group * (sp::kD + 2);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)max_parts), dim3(256), lds,
+                     (hipStream_t)stream, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
+                     sel_counts, chunk_offsets, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
+                     group, dims->max_pages, U, part_o, part_lse);
+  return sp::launch_status();
+}

@@ -1,0 +1,119 @@
+// Internal helpers of the gfx950 sparse paged decode library (kernels + C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sparse_paged.h"
+
+namespace sp {
+
+constexpr int kD = 128;            // head_dim
+constexpr int kP = 16;             // tokens per page
+constexpr int kTile = kP * kD;     // elements of one K (or V) tile
+constexpr int kMaxGroup = 16;      // query heads per KV head
+constexpr int kMaxPages = 32768;   // page-table row length limit
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short short4v;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ short4v as_short4(u32x2 v) { return __builtin_bit_cast(short4v, v); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- wave (64-lane) reductions / scans -------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64,
+// at most 4096).  `scratch` holds NT/64 elements.  Returns the exclusive
+// prefix of `v`; `total` receives the block total.  Contains barriers: every
+// thread of the block must call it.
+template <typename T, int NT>
+__device__ __forceinline__ T block_excl_scan(T v, T* scratch, T& total) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  T incl = wave_incl_scan(v);
+  if (lane == 63) scratch[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    T s = (lane < NW) ? scratch[lane] : T(0);
+    s = wave_incl_scan(s);
+    if (lane < NW) scratch[lane] = s;
+  }
+  __syncthreads();
+  T base = (w > 0) ? scratch[w - 1] : T(0);
+  total = scratch[NW - 1];
+  __syncthreads();
+  return base + incl - v;
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+  T total;
+  block_excl_scan<T, NT>(v, scratch, total);
+  return total;
+}
+
+// ---- host-side argument checks ----------------------------------------------
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline sparse_status check_dims(const sparse_dims* d) {
+  if (!d) return SPARSE_ERR_INVALID;
+  if (d->batch < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1 || d->max_pages < 1)
+    return SPARSE_ERR_INVALID;
+  if (d->num_q_heads % d->num_kv_heads != 0) return SPARSE_ERR_INVALID;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->head_dim != kD || d->page_size != kP || G > kMaxGroup || d->max_pages > kMaxPages)
+    return SPARSE_ERR_UNSUPPORTED;
+  return SPARSE_OK;
+}
+
+inline sparse_status check_pool(const void* kv, int64_t stride_page, int64_t stride_head,
+                                int64_t pool_pages) {
+  if (!kv || pool_pages < 1 || stride_page < 0 || stride_head < 0) return SPARSE_ERR_INVALID;
+  if (!aligned(kv, 16) || (stride_page % 8) != 0 || (stride_head % 8) != 0)
+    return SPARSE_ERR_INVALID;
+  return SPARSE_OK;
+}
+
+inline sparse_status launch_status() {
+  return hipGetLastError() == hipSuccess ? SPARSE_OK : SPARSE_ERR_HIP;
+}
+
+}  // namespace sp

@@ -1,0 +1,126 @@
+// Page scoring: the estimated attention logit of every page, per query head.
+//
+// u = sum_d max(q_d kmin_d, q_d kmax_d) is the Quest-style bound on q.k_t
+// over the page's tokens.  Since max(q a, q b) = q+ b + q- a for a <= b
+// (q+ = max(q,0), q- = min(q,0)), u is the dot product of the 256-element
+// summary row [kmin | kmax] with [q- | q+]: a 16-page x 256 x G contraction
+// per tile, which runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
+// with exact bf16 products and fp32 accumulation.  logit = scale*u +
+// ln(valid tokens), the log of an upper bound of the page's unnormalised
+// attention mass -- the estimate the coverage rule cuts on ("Adaptive
+// DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", MOIRA
+// abstract, coverage-rule sentence; the estimator itself is not given there).
+
+#include "common.h"
+
+namespace sp {
+
+constexpr int kScoreTilesPerWave = 2;   // 16-page tiles per wave
+constexpr int kScoreWaves = 4;          // waves per workgroup
+constexpr int kScorePagesPerBlock = 16 * kScoreTilesPerWave * kScoreWaves;
+
+// MFMA 16x16x32 bf16 operand layout (wave64): lane l supplies row (l & 15) of
+// A and column (l & 15) of B, k-elements 8*(l >> 4) .. +7 of the 32-wide
+// k-slice; the fp32 result in lane l is column (l & 15), rows 4*(l >> 4) + i.
+// Here rows = pages of the tile, columns = query heads of the group, and
+// k-slice s covers summary elements [32 s, 32 s + 32) (s < 4: kmin channels,
+// s >= 4: kmax channels).
+__global__ __launch_bounds__(256) void score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ summ, int64_t pool_pages,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ ctx_lens, float scale,
+    float* __restrict__ logits, int hkv, int group, int max_pages) {
+  const int u = blockIdx.y;
+  const int b = u / hkv, h = u - (u / hkv) * hkv;
+  const int L = min(max(ctx_lens[b], 0), max_pages * kP);
+  const int n = (L + kP - 1) / kP;
+  const int wave = blockIdx.x * kScoreWaves + (threadIdx.x >> 6);
+  const int p_begin = wave * kScoreTilesPerWave * 16;
+  if (p_begin >= n) return;
+  const int lane = lane_id(), row = lane & 15, j = lane >> 4;
+
+  // B operands: q- for the kmin half, q+ for the kmax half (bf16 bit masks).
+  bf16x8 qneg[4], qpos[4];
+  {
+    const int g = row;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (g < group) {
+        const int hq = h * group + g;
+        w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hkv * group + hq) * kD + 32 * s +
+                                            8 * j);
+      }
+      u32x4 neg, pos;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // per 16-bit half: all-ones where the sign bit is set
+        const uint32_t sgn = (w[e] >> 15) & 0x00010001u;
+        const uint32_t m = sgn * 0xFFFFu;
+        neg[e] = w[e] & m;
+        pos[e] = w[e] & ~m;
+      }
+      qneg[s] = as_bf16x8(neg);
+      qpos[s] = as_bf16x8(pos);
+    }
+  }
+
+  const float ln16 = 2.772588722239781f;
+  float* out = logits + (int64_t)u * group * max_pages;
+  const int32_t* pt = page_table + (int64_t)b * max_pages;
+
+#pragma unroll
+  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
+    const int p0 = p_begin + tile * 16;
+    if (p0 >= n) break;
+    const int p = p0 + row;
+    int x = -1;
+    if (p < n) x = pt[p];
+    const bool ok = (x >= 0) && (x < pool_pages);
+    u32x4 a[8];
+    const uint16_t* src = summ + ((int64_t)(ok ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      a[s] = ok ? *reinterpret_cast<const u32x4*>(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+    }
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]), qneg[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[4 + s]), qpos[s], acc, 0, 0, 0);
+    // lane (g = row, j) now holds u for pages p0 + 4j + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pi = p0 + 4 * j + i;
+      const bool oki = __shfl(ok ? 1 : 0, 4 * j + i, 64) != 0;
+      if (row < group && pi < n) {
+        const int nv = min(kP, L - kP * pi);
+        const float lnv = (nv == kP) ? ln16 : logf((float)nv);
+        out[(int64_t)row * max_pages + pi] = oki ? fmaf(scale, acc[i], lnv) : -INFINITY;
+      }
+    }
+  }
+}
+
+}  // namespace sp
+
+extern "C" sparse_status sparse_score_pages(const sparse_dims* dims, const uint16_t* q,
+                                            const uint16_t* summ, int64_t pool_pages,
+                                            const int32_t* page_table, const int32_t* ctx_lens,
+                                            float scale, float* logits, void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if (!q || !summ || !page_table || !ctx_lens || !logits || pool_pages < 1)
+    return SPARSE_ERR_INVALID;
+  if (!sp::aligned(q, 16) || !sp::aligned(summ, 16) || !isfinite(scale))
+    return SPARSE_ERR_INVALID;
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  dim3 grid((dims->max_pages + sp::kScorePagesPerBlock - 1) / sp::kScorePagesPerBlock, U);
+  if (grid.y > 65535) return SPARSE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(sp::score_kernel, grid, dim3(256), 0, (hipStream_t)stream, q, summ,
+                     pool_pages, page_table, ctx_lens, scale, logits, hkv, group,
+                     dims->max_pages);
+  return sp::launch_status();
+}

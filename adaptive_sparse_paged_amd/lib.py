@@ -1,0 +1,169 @@
+"""Python binding of the C ABI in include/sparse_paged.h (ctypes).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libsparse_paged.so.  torch supplies device memory and the stream.
+The library is looked for next to this file; when it is missing, ``load()``
+raises -- there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_paged.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+
+EXPORTS = (
+    "sparse_version",
+    "sparse_status_string",
+    "sparse_build_page_summaries",
+    "sparse_score_pages",
+    "sparse_select_workspace_bytes",
+    "sparse_select_coverage",
+    "sparse_decode_max_parts",
+    "sparse_decode_attn",
+    "sparse_merge_splits",
+)
+
+
+class SparseError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} returned {code} ({msg})")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+    ]
+
+
+def make_dims(batch, q_heads, kv_heads, max_pages, head_dim=128, page_size=16):
+    return Dims(batch, q_heads, kv_heads, head_dim, page_size, max_pages)
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_D = ctypes.POINTER(Dims)
+
+_SIGS = {
+    "sparse_version": (ctypes.c_char_p, []),
+    "sparse_status_string": (ctypes.c_char_p, [_I32]),
+    "sparse_build_page_summaries": (_I32, [_D, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P]),
+    "sparse_score_pages": (_I32, [_D, _P, _P, _I64, _P, _P, _F, _P, _P]),
+    "sparse_select_workspace_bytes": (ctypes.c_size_t, [_D]),
+    "sparse_select_coverage": (_I32, [_D, _P, _P, _P, _F, _I32, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "sparse_decode_max_parts": (_I64, [_D, _I32]),
+    "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _F, _I32,
+                                  _P, _P, _I64, _P]),
+    "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libsparse_paged.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m adaptive_sparse_paged_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, code):
+    if code != OK:
+        msg = load().sparse_status_string(code).decode()
+        raise SparseError(fn, code, msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def version():
+    return load().sparse_version().decode()
+
+
+def build_page_summaries(dims, kv, stride_page, stride_head, pool_pages, pages, valid, summ,
+                         stream=None):
+    _dev(kv, pages, valid, summ)
+    n = pages.numel()
+    _check("sparse_build_page_summaries", load().sparse_build_page_summaries(
+        ctypes.byref(dims), _ptr(kv), stride_page, stride_head, pool_pages, _ptr(pages),
+        _ptr(valid), n, _ptr(summ), _stream(stream)))
+
+
+def score_pages(dims, q, summ, pool_pages, page_table, ctx_lens, scale, logits, stream=None):
+    _dev(q, summ, page_table, ctx_lens, logits)
+    _check("sparse_score_pages", load().sparse_score_pages(
+        ctypes.byref(dims), _ptr(q), _ptr(summ), pool_pages, _ptr(page_table), _ptr(ctx_lens),
+        scale, _ptr(logits), _stream(stream)))
+
+
+def select_workspace_bytes(dims):
+    return int(load().sparse_select_workspace_bytes(ctypes.byref(dims)))
+
+
+def select_coverage(dims, logits, ctx_lens, page_table, gamma, chunk_pages, sel_counts,
+                    sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
+    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
+         sel_phys, ws)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("sparse_select_coverage", load().sparse_select_coverage(
+        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), gamma, chunk_pages,
+        _ptr(sel_counts), _ptr(sel_offsets), _ptr(chunk_offsets), _ptr(sel_pages),
+        _ptr(sel_phys), _ptr(ws), nbytes, _stream(stream)))
+
+
+def decode_max_parts(dims, chunk_pages):
+    return int(load().sparse_decode_max_parts(ctypes.byref(dims), chunk_pages))
+
+
+def decode_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
+                chunk_offsets, sel_pages, sel_phys, scale, chunk_pages, part_o, part_lse,
+                max_parts, stream=None):
+    _dev(q, kv, ctx_lens, sel_counts, chunk_offsets, sel_pages, sel_phys, part_o, part_lse)
+    _check("sparse_decode_attn", load().sparse_decode_attn(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
+        _ptr(ctx_lens), _ptr(sel_counts), _ptr(chunk_offsets), _ptr(sel_pages), _ptr(sel_phys),
+        scale, chunk_pages, _ptr(part_o), _ptr(part_lse), max_parts, _stream(stream)))
+
+
+def merge_splits(dims, part_o, part_lse, sel_counts, chunk_offsets, chunk_pages, out, out_lse,
+                 stream=None):
+    _dev(part_o, part_lse, sel_counts, chunk_offsets, out, out_lse)
+    _check("sparse_merge_splits", load().sparse_merge_splits(
+        ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), _ptr(chunk_offsets),
+        chunk_pages, _ptr(out), _ptr(out_lse), _stream(stream)))

@@ -1,0 +1,116 @@
+"""One sparse decode step (score -> select -> attention -> merge) on caller-owned
+buffers, and its capture into a single HIP graph.
+
+Buffers are torch tensors (device memory only); every operation is a call into
+the HIP library.  The step is captured whole: nothing in it waits on the host,
+and the page lists, their lengths and the chunk plan live on the device, so a
+captured graph replays correctly after the queries, context lengths or page
+tables change in place.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+from . import lib
+
+PAGE = 16
+HEAD_DIM = 128
+
+
+@dataclass
+class StepBuffers:
+    logits: torch.Tensor        # fp32 [B][Hkv][G][max_pages]
+    sel_counts: torch.Tensor    # int32 [U]
+    sel_offsets: torch.Tensor   # int32 [U+1]
+    chunk_offsets: torch.Tensor  # int32 [U+1]
+    sel_pages: torch.Tensor     # int32 [U][max_pages]
+    sel_phys: torch.Tensor      # int32 [U][max_pages]
+    ws: torch.Tensor            # uint8 workspace (zero-filled once)
+    part_o: torch.Tensor        # fp32 [max_parts][G][D]
+    part_lse: torch.Tensor      # fp32 [max_parts][G]
+    out: torch.Tensor           # fp32 [B][Hq][D]
+    out_lse: torch.Tensor       # fp32 [B][Hq]
+
+
+class SparseDecodeStep:
+    """Fixed-shape decode step for one layer shape.
+
+    dims: lib.Dims; gamma in (0, 1]; chunk_pages: pages per attention
+    workgroup.  Intermediate buffers are shared by every layer run through
+    this object on one stream; outputs can be given per call.
+    """
+
+    def __init__(self, dims, gamma, chunk_pages=32, scale=None, device="cuda"):
+        self.dims = dims
+        self.gamma = float(gamma)
+        self.chunk_pages = int(min(chunk_pages, dims.max_pages))
+        self.scale = float(scale if scale is not None else HEAD_DIM ** -0.5)
+        B, Hq, Hkv, MP = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.max_pages
+        G = Hq // Hkv
+        U = B * Hkv
+        self.max_parts = lib.decode_max_parts(dims, self.chunk_pages)
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.buf = StepBuffers(
+            logits=torch.empty((B, Hkv, G, MP), **f32),
+            sel_counts=torch.zeros(U, **i32),
+            sel_offsets=torch.zeros(U + 1, **i32),
+            chunk_offsets=torch.zeros(U + 1, **i32),
+            sel_pages=torch.zeros((U, MP), **i32),
+            sel_phys=torch.zeros((U, MP), **i32),
+            ws=torch.zeros(lib.select_workspace_bytes(dims), dtype=torch.uint8, device=device),
+            part_o=torch.empty((self.max_parts, G, HEAD_DIM), **f32),
+            part_lse=torch.empty((self.max_parts, G), **f32),
+            out=torch.empty((B, Hq, HEAD_DIM), **f32),
+            out_lse=torch.empty((B, Hq), **f32),
+        )
+
+    def score_select(self, q, summ, pool_pages, page_table, ctx_lens, stream=None):
+        d, b = self.dims, self.buf
+        lib.score_pages(d, q, summ, pool_pages, page_table, ctx_lens, self.scale, b.logits, stream)
+        lib.select_coverage(d, b.logits, ctx_lens, page_table, self.gamma, self.chunk_pages,
+                            b.sel_counts, b.sel_offsets, b.chunk_offsets, b.sel_pages, b.sel_phys,
+                            b.ws, stream)
+
+    def attend(self, q, kv, stride_page, stride_head, pool_pages, ctx_lens, out=None,
+               out_lse=None, stream=None, sel_pages=None, sel_phys=None):
+        d, b = self.dims, self.buf
+        out = b.out if out is None else out
+        out_lse = b.out_lse if out_lse is None else out_lse
+        sp = b.sel_pages if sel_pages is None else sel_pages
+        sx = b.sel_phys if sel_phys is None else sel_phys
+        lib.decode_attn(d, q, kv, stride_page, stride_head, pool_pages, ctx_lens, b.sel_counts,
+                        b.chunk_offsets, sp, sx, self.scale, self.chunk_pages, b.part_o,
+                        b.part_lse, self.max_parts, stream)
+        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, b.chunk_offsets,
+                         self.chunk_pages, out, out_lse, stream)
+        return out, out_lse
+
+    def run(self, q, summ, kv, stride_page, stride_head, pool_pages, page_table, ctx_lens,
+            out=None, out_lse=None, stream=None):
+        """Enqueue the whole step for one layer."""
+        self.score_select(q, summ, pool_pages, page_table, ctx_lens, stream)
+        return self.attend(q, kv, stride_page, stride_head, pool_pages, ctx_lens, out, out_lse,
+                           stream)
+
+
+def canonical_strides(kv_heads):
+    """(stride_page, stride_head) in elements of the pool [Ppool][Hkv][2][P*D]."""
+    return kv_heads * 2 * PAGE * HEAD_DIM, 2 * PAGE * HEAD_DIM
+
+
+def capture(fn, warmup=1):
+    """Capture everything ``fn`` enqueues on a side stream into one graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g

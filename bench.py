@@ -1,0 +1,267 @@
+"""Benchmark of the sparse paged decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload long_128k] [--gamma 0.99]
+
+A step is one pass of the whole hot path -- for every layer: page scoring,
+coverage selection, self-planning split-K attention and the split merge --
+over one batch of synthetic, HBM-resident inputs, captured as one HIP graph.
+Default workload: 4 requests of 131072 tokens, Llama-3-8B layer shape (32 query
+heads / 8 KV heads, head_dim 128, 16-token pages), 32 independent seeded
+layers, gamma 0.99.
+
+Prints ONE JSON line.  `value` is the achieved HBM throughput in GB/s on the
+bytes the step must move (page summaries, logits, page lists, the selected K/V
+tokens, split partials, queries and outputs -- counted from the device's own
+page counts); `us_per_layer` is the step time divided by the layers.
+`roofline` covers the attention kernel (the dominant one), timed with HIP
+events on its own stream; `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PAGE, D = 16, 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_128k")
+    ap.add_argument("--gamma", type=float, default=0.99)
+    ap.add_argument("--chunk", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def counted_bytes(n, k, tsel, G, Hkv, chunk):
+    """Algorithmic bytes of one unit: n pages, k kept, tsel kept valid tokens."""
+    return (512 * n                 # page summaries (kmin|kmax bf16)
+            + 2 * 4 * G * n         # fp32 logits written and read
+            + 4 * n / Hkv           # the request's page-table row, shared by its KV heads
+            + 512 * tsel            # kept K and V tokens (bf16)
+            + 16 * k                # kept logical/physical ids written and read
+            + 2 * math.ceil(k / chunk) * G * (D + 1) * 4   # split partials written and read
+            + 2 * G * D * 2 + G * D * 4 + G * 4)           # q read twice, out, lse
+
+
+def attn_bytes(k, tsel, G, chunk):
+    """Algorithmic bytes of the attention kernel alone for one unit."""
+    return 512 * tsel + 8 * k + G * D * 2 + math.ceil(k / chunk) * G * (D + 1) * 4
+
+
+def kept_tokens(counts, pages, lens, Hkv, max_pages):
+    U = counts.shape[0]
+    tsel = np.zeros(U, dtype=np.int64)
+    for u in range(U):
+        b = u // Hkv
+        k = int(counts[u])
+        p = pages[u, :k].astype(np.int64)
+        tsel[u] = np.minimum(PAGE, lens[b] - PAGE * p).clip(min=0).sum()
+    return tsel
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, lens, gamma, budget_s):
+    """Time the fp64 oracle (score, masses, cut, attention) unit by unit on the
+    host until about budget_s seconds have passed; scale to one layer."""
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:                      # pragma: no cover
+        limiter = None
+    import oracle as O
+    from adaptive_sparse_paged_amd import inputs as I
+    spent, units = 0.0, 0
+    t_total = time.time()
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            L = int(lens[b])
+            k, v, q, nv = I.unit_host(w, 0, b, h, L)
+            lo, hi = O.summaries(k, nv)        # prefill-time, not timed
+            Kf, Vf = O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v)
+            t0 = time.perf_counter()
+            sel = O.select_unit(q, lo, hi, nv, w.scale, gamma)
+            O.attend_pages(O.bf16_bits_to_f64(q), Kf, Vf, nv, sel["list"], w.scale)
+            spent += time.perf_counter() - t0
+            units += 1
+            if spent >= budget_s or time.time() - t_total > 4 * budget_s:
+                break
+        if spent >= budget_s or time.time() - t_total > 4 * budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    per_unit = spent / units
+    us_layer = per_unit * w.batch * w.kv_heads * 1e6
+    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{units} of {w.batch * w.kv_heads} (request, KV head) units of layer 0, "
+                      f"{spent:.1f} s of fp64 NumPy on one host thread, scaled to one layer"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode path here is single-GPU "
+              "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from adaptive_sparse_paged_amd import inputs as I
+    from adaptive_sparse_paged_amd import lib
+    from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides, capture
+
+    lib.load()
+    w = I.WORKLOADS[args.workload]
+    layers = args.layers or w.layers
+    lens = I.context_lengths(w)
+    dev = "cuda"
+    t_gen = time.time()
+    L_in, summs = [], []
+    for layer in range(layers):
+        li = I.build_layer(w, layer, dev, lens=lens)
+        dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, li.max_pages)
+        sp_, sh_ = canonical_strides(w.kv_heads)
+        summ = torch.empty((li.pool_pages, w.kv_heads, 2, D), dtype=torch.int16, device=dev)
+        lib.build_page_summaries(dims, li.kv_pool, sp_, sh_, li.pool_pages,
+                                 torch.arange(li.pool_pages, dtype=torch.int32, device=dev),
+                                 li.page_valid, summ)
+        L_in.append(li)
+        summs.append(summ)
+        if layer % 8 == 7:
+            print(f"# generated {layer + 1}/{layers} layers ({time.time() - t_gen:.0f} s)",
+                  file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    stride_page, stride_head = canonical_strides(w.kv_heads)
+    max_pages = L_in[0].max_pages
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
+    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev)
+    outs = [torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev) for _ in range(layers)]
+    lses = [torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev) for _ in range(layers)]
+    counts = [torch.empty_like(st.buf.sel_counts) for _ in range(layers)]
+
+    def step_fn():
+        for l, li in enumerate(L_in):
+            st.run(li.q, summs[l], li.kv_pool, stride_page, stride_head, li.pool_pages,
+                   li.page_table, li.ctx_lens, outs[l], lses[l])
+
+    # one eager pass to record the per-layer selections (for byte accounting)
+    sel_stats = []
+    for l, li in enumerate(L_in):
+        st.run(li.q, summs[l], li.kv_pool, stride_page, stride_head, li.pool_pages,
+               li.page_table, li.ctx_lens, outs[l], lses[l])
+        torch.cuda.synchronize()
+        c = st.buf.sel_counts.cpu().numpy()
+        pg = st.buf.sel_pages.cpu().numpy()
+        sel_stats.append((c, kept_tokens(c, pg, lens, w.kv_heads, max_pages)))
+    graph = capture(step_fn)
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # bytes moved per step
+    G, Hkv = w.group, w.kv_heads
+    npages = np.array([I.pages_of(L) for L in lens])
+    total_bytes, attn_total, kept, pages_all = 0.0, 0.0, 0, 0
+    for c, tsel in sel_stats:
+        for u in range(c.shape[0]):
+            n = int(npages[u // Hkv])
+            total_bytes += counted_bytes(n, int(c[u]), int(tsel[u]), G, Hkv, st.chunk_pages)
+            attn_total += attn_bytes(int(c[u]), int(tsel[u]), G, st.chunk_pages)
+            kept += int(c[u])
+            pages_all += n
+    gbs = total_bytes / (ms_step * 1e-3) / 1e9
+
+    # attention kernel alone: eager passes over every layer with HIP events
+    # around each attention launch, on the stream the launches run on
+    stream = torch.cuda.current_stream()
+    marks = []
+    for _ in range(args.steps):
+        for l, li in enumerate(L_in):
+            st.score_select(li.q, summs[l], li.pool_pages, li.page_table, li.ctx_lens)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            lib.decode_attn(dims, li.q, li.kv_pool, stride_page, stride_head, li.pool_pages,
+                            li.ctx_lens, st.buf.sel_counts, st.buf.chunk_offsets,
+                            st.buf.sel_pages, st.buf.sel_phys, st.scale, st.chunk_pages,
+                            st.buf.part_o, st.buf.part_lse, st.max_parts)
+            a1.record(stream)
+            lib.merge_splits(dims, st.buf.part_o, st.buf.part_lse, st.buf.sel_counts,
+                             st.buf.chunk_offsets, st.chunk_pages, outs[l], lses[l])
+            marks.append((a0, a1))
+    torch.cuda.synchronize()
+    attn_us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / len(marks)
+    attn_launch_bytes = 0.0
+    for c, tsel in sel_stats:
+        attn_launch_bytes += sum(attn_bytes(int(c[u]), int(tsel[u]), G, st.chunk_pages)
+                                 for u in range(c.shape[0]))
+    attn_launch_bytes /= layers
+    attn_gbs = attn_launch_bytes / (attn_us * 1e-6) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
+    if os.path.exists(tfile):
+        rec = json.load(open(tfile))
+        src = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc", "attn.hip")
+        if rec.get("source_sha256_16") == source_hash(src) and rec.get("workload") == w.name:
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": "sparse decode step us/layer + achieved HBM GB/s vs peak at 128k ctx, gamma=0.99",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "us_per_layer": round(ms_step * 1e3 / layers, 2),
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "ctx": int(lens.max()),
+                   "layers": layers, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": D, "page_size": PAGE, "gamma": args.gamma,
+                   "chunk_pages": st.chunk_pages},
+        "selected_fraction": round(kept / pages_all, 4),
+        "bytes_per_step": int(total_bytes),
+        "roofline": {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(attn_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(attn_us, 2),
+                     "bytes_per_launch": int(attn_launch_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lens, args.gamma, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * sparse_paged.h -- C ABI of the MI355X (gfx950) sparse paged decode step.
+ *
+ * One decode step, per (request, KV head) "unit": score every KV page of the
+ * request with a cheap upper bound of its attention mass, keep the smallest
+ * page set whose estimated mass reaches a fraction gamma, then run exact
+ * attention for the unit's GQA group over that variable-length page list,
+ * split into fixed-size chunks that each workgroup finds for itself from the
+ * prefix-summed list lengths, and merge the chunk partials.
+ *
+ * Pages cited:
+ *   [P1] "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
+ *        Hierarchy" (thelatestinai.com/papers/2610.13708), MOIRA abstract.
+ *   [P2] "HiSparse: Scaling Sparse Attention Decoding with Hierarchical KV
+ *        Cache" (scholarbro.com/p/47450), abstract.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *   buffer; the library never allocates, frees or synchronises, and every
+ *   call only enqueues kernels on `stream` (a hipStream_t, or NULL for the
+ *   default stream).  Any sequence of calls can therefore be captured into
+ *   one HIP graph.
+ * - Errors: a nonzero sparse_status comes only from synchronous host-side
+ *   argument checks (or a failed launch).  On a nonzero return nothing was
+ *   enqueued and no output was touched.  Device-resident values (context
+ *   lengths, page ids) cannot be checked on the host; page ids outside
+ *   [0, pool_pages) are treated as empty pages by every kernel (never read).
+ * - Supported shapes: head_dim D = 128, page_size P = 16, GQA group
+ *   G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, max_pages <= 32768.
+ *   Other shapes return SPARSE_ERR_UNSUPPORTED.
+ * - bf16 values are passed as uint16_t bit patterns.
+ * - Query head j = h * G + g belongs to KV head h.  Unit u = b * Hkv + h.
+ * - Request b has ctx_lens[b] = L_b tokens in n_b = ceil(L_b / 16) logical
+ *   pages; logical page p holds tokens [16p, min(16p + 16, L_b)).
+ *   page_table[b][p] is the physical page id of logical page p.
+ *
+ * KV pool layout (one layer)
+ * --------------------------
+ * The K tile of (physical page x, KV head h) starts at element
+ *   kv + x * stride_page + h * stride_head
+ * and is token-major [16][128] bf16 (4 KiB).  The V tile follows it
+ * immediately (element offset +2048) and is CHANNEL-major [128][16] bf16
+ * (V transposed within the page), so that the products over tokens read
+ * contiguous token runs.  The canonical pool is [Ppool][Hkv][2][2048] with
+ * stride_head = 4096 and stride_page = Hkv * 4096.
+ */
+#ifndef SPARSE_PAGED_H
+#define SPARSE_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARSE_OK = 0,
+  SPARSE_ERR_INVALID = 1,     /* null pointer, bad size, gamma outside (0,1] */
+  SPARSE_ERR_UNSUPPORTED = 2, /* shape outside the supported set above */
+  SPARSE_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  SPARSE_ERR_HIP = 4          /* a kernel launch failed */
+} sparse_status;
+
+typedef struct {
+  int32_t batch;        /* B: requests */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv; Hq must be a multiple of it */
+  int32_t head_dim;     /* D: 128 */
+  int32_t page_size;    /* P: 16 */
+  int32_t max_pages;    /* row length of page_table and of the page lists */
+} sparse_dims;
+
+/* Library version string (host, static storage). */
+const char* sparse_version(void);
+
+/* Human-readable name of a status code (host, static storage). */
+const char* sparse_status_string(int32_t status);
+
+/*
+ * sparse_build_page_summaries -- per-page, per-channel key summaries.
+ *
+ * For i < n, page x = pages[i] and every KV head h, writes
+ *   summ[x][h][0][d] = min over the first valid[i] tokens t of K[t][d]
+ *   summ[x][h][1][d] = max over the same tokens
+ * (bf16, bit-exact; -0 orders below +0; NaN inputs are unsupported).
+ * This is the Quest-style page summary ([P2], abstract, the evaluated
+ * sparse-attention families include Quest); [P1] names no estimator.
+ * valid[i] is clamped to [0, 16]; pages with 0 valid tokens are skipped.
+ * Runs at prefill / append time, outside the decode step.
+ *
+ *   kv        bf16 KV pool (layout above), read only
+ *   pages     int32 [n] physical page ids, each in [0, pool_pages)
+ *   valid     int32 [n] valid tokens of each listed page
+ *   summ      bf16 [pool_pages][Hkv][2][128], written for the listed pages
+ */
+sparse_status sparse_build_page_summaries(const sparse_dims* dims, const uint16_t* kv,
+                                          int64_t stride_page, int64_t stride_head,
+                                          int64_t pool_pages, const int32_t* pages,
+                                          const int32_t* valid, int32_t n, uint16_t* summ,
+                                          void* stream);
+
+/*
+ * sparse_score_pages -- estimated attention logit of every page, per query head.
+ *
+ * For every unit (b, h), query head g of its group and logical page
+ * p < n_b, with x = page_table[b][p]:
+ *   u = sum_d max(q[b][hG+g][d] * kmin[x][h][d], q[b][hG+g][d] * kmax[x][h][d])
+ *   logits[b][h][g][p] = scale * u + ln(valid tokens of page p)
+ * n_valid * exp(scale * u) bounds the page's unnormalised attention mass;
+ * this is the estimate behind the coverage rule ([P1], abstract, sentence on
+ * the coverage rule; the pages leave the estimator open).  Entries with
+ * p >= n_b are not written.  fp32 accumulation.
+ *
+ *   q          bf16 [B][Hq][128]
+ *   summ       bf16 [pool_pages][Hkv][2][128] (from sparse_build_page_summaries)
+ *   page_table int32 [B][max_pages]
+ *   ctx_lens   int32 [B], 0 <= L_b <= 16 * max_pages
+ *   logits     fp32 [B][Hkv][G][max_pages]
+ */
+sparse_status sparse_score_pages(const sparse_dims* dims, const uint16_t* q, const uint16_t* summ,
+                                 int64_t pool_pages, const int32_t* page_table,
+                                 const int32_t* ctx_lens, float scale, float* logits,
+                                 void* stream);
+
+/* Bytes of workspace sparse_select_coverage needs (host). */
+size_t sparse_select_workspace_bytes(const sparse_dims* dims);
+
+/*
+ * sparse_select_coverage -- the coverage rule, per unit ([P1], abstract,
+ * coverage-rule sentence: keep the smallest page set whose estimated mass
+ * reaches gamma).
+ *
+ * Per unit: pi_g = softmax over pages of logits[b][h][g][:n_b]; page mass
+ * m = mean_g pi_g; the kept set is the first k* pages in (m descending, page
+ * ascending) order, k* = min{k >= 1 : sum of the first k masses >= gamma * sum
+ * of all masses}; gamma = 1 keeps every page.  Masses are fp32, the cut's sums
+ * are exact 64-bit fixed point (weight = floor(m * 2^52)), found by a
+ * mass-weighted radix select over the fp32 bit patterns with ties at the cut
+ * filled by ascending page index.
+ *
+ * Outputs (unit u = b * Hkv + h; lists use a fixed stride of max_pages):
+ *   sel_counts    int32 [U]            k* of each unit (0 when L_b = 0)
+ *   sel_pages     int32 [U][max_pages] kept logical pages, ascending, first k* valid
+ *   sel_phys      int32 [U][max_pages] page_table[b][sel_pages[..]]
+ *   sel_offsets   int32 [U + 1]        exclusive prefix sum of sel_counts
+ *   chunk_offsets int32 [U + 1]        exclusive prefix sum of ceil(k* / chunk_pages)
+ * The prefix sums are written by whichever workgroup finishes last (a
+ * device-side ticket in the workspace), so no host plan is involved.
+ *
+ *   ws / ws_bytes  device workspace of at least sparse_select_workspace_bytes();
+ *                  it must be zero-filled ONCE before its first use and is
+ *                  left zero-filled by every call.  Calls sharing one
+ *                  workspace must not overlap in time.
+ *   gamma          in (0, 1]; chunk_pages in [1, max_pages]
+ */
+sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
+                                     const int32_t* ctx_lens, const int32_t* page_table,
+                                     float gamma, int32_t chunk_pages, int32_t* sel_counts,
+                                     int32_t* sel_offsets, int32_t* chunk_offsets,
+                                     int32_t* sel_pages, int32_t* sel_phys, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* Upper bound on the number of chunks (= partial slots) of one step (host):
+ * U * ceil(max_pages / chunk_pages). */
+int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
+
+/*
+ * sparse_decode_attn -- self-planning split-K attention over the page lists
+ * ([P1], abstract, sentence on self-planning attention: each block derives
+ * its own share of the work from the list lengths, so no host-side plan is
+ * needed and the step stays inside the graph).
+ *
+ * The grid has max_parts workgroups, fixed at enqueue time.  Workgroup c
+ * finds the unit u with chunk_offsets[u] <= c < chunk_offsets[u+1] by a
+ * search over the prefix sums, takes list entries
+ * [(c - chunk_offsets[u]) * chunk_pages, +chunk_pages) of that unit, and
+ * computes exact attention of the unit's G query heads over the valid
+ * tokens of those pages; workgroups past chunk_offsets[U] exit.
+ * Writes, for each chunk c and head g:
+ *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the chunk)
+ *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
+ * K/V are read from the pool at sel_phys (physical ids or cache slots).
+ *
+ *   part_o   fp32 [max_parts][G][128];  part_lse fp32 [max_parts][G]
+ *   max_parts must equal sparse_decode_max_parts(dims, chunk_pages)
+ */
+sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
+                                 int64_t stride_page, int64_t stride_head, int64_t pool_pages,
+                                 const int32_t* ctx_lens, const int32_t* sel_counts,
+                                 const int32_t* chunk_offsets, const int32_t* sel_pages,
+                                 const int32_t* sel_phys, float scale, int32_t chunk_pages,
+                                 float* part_o, float* part_lse, int64_t max_parts,
+                                 void* stream);
+
+/*
+ * sparse_merge_splits -- log-sum-exp merge of the chunk partials of each unit:
+ *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) * o_c
+ * (the identity that makes the split over chunks exact).
+ *   out      fp32 [B][Hq][128];  out_lse fp32 [B][Hq]
+ * A unit with no kept page gets o = 0 and lse = -inf.
+ */
+sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
+                                  const float* part_lse, const int32_t* sel_counts,
+                                  const int32_t* chunk_offsets, int32_t chunk_pages, float* out,
+                                  float* out_lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_PAGED_H */

@@ -1,0 +1,133 @@
+"""Shared driver of the GPU parity tests: build a layer on the GPU from the
+seeded generator, run the library's step, and compare against the fp64
+oracle on units regenerated on the host."""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from adaptive_sparse_paged_amd import inputs as I
+from adaptive_sparse_paged_amd import lib
+from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides
+
+ATTN_TOL = 1e-2      # max-abs on outputs (bf16 K/V, fp32 accumulation)
+LIST_EPS = 1e-5      # relative mass perturbation under which a list is accepted
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dims_of(w, max_pages):
+    return lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
+
+
+class GpuLayer:
+    """One layer's inputs on the GPU plus its summaries."""
+
+    def __init__(self, w, layer=0, lens=None, seed=0):
+        self.w, self.layer, self.seed = w, layer, seed
+        self.li = I.build_layer(w, layer, "cuda", seed=seed, lens=lens)
+        self.lens = self.li.ctx_lens.cpu().numpy()
+        self.dims = dims_of(w, self.li.max_pages)
+        self.stride_page, self.stride_head = canonical_strides(w.kv_heads)
+        P = self.li.pool_pages
+        self.summ = torch.zeros((P, w.kv_heads, 2, 128), dtype=torch.int16, device="cuda")
+        pages = torch.arange(P, dtype=torch.int32, device="cuda")
+        lib.build_page_summaries(self.dims, self.li.kv_pool, self.stride_page, self.stride_head,
+                                 P, pages, self.li.page_valid, self.summ)
+
+    def step(self, gamma, chunk_pages):
+        st = SparseDecodeStep(self.dims, gamma, chunk_pages, scale=self.w.scale)
+        return st
+
+    def run(self, st):
+        li = self.li
+        st.run(li.q, self.summ, li.kv_pool, self.stride_page, self.stride_head, li.pool_pages,
+               li.page_table, li.ctx_lens)
+        torch.cuda.synchronize()
+
+    def unit_oracle(self, b, h):
+        """Host regeneration of unit (b, h) and its oracle selection inputs."""
+        w = self.w
+        L = int(self.lens[b])
+        k, v, q, nv = I.unit_host(w, self.layer, b, h, L, self.seed)
+        kmin, kmax = O.summaries(k, nv)
+        return dict(k=k, v=v, q=q, nv=nv, kmin=kmin, kmax=kmax, L=L, n=I.pages_of(L))
+
+
+def check_unit(layer, st, b, h, gamma, full=True, attn_on_oracle=None):
+    """Compare one unit of a finished step against the oracle.  Returns a dict
+    of measured errors; asserts the acceptance bars."""
+    w = layer.w
+    G = w.group
+    U = layer.oracle_cache.get((b, h)) if hasattr(layer, "oracle_cache") else None
+    un = layer.unit_oracle(b, h) if U is None else U
+    n = un["n"]
+    u = b * w.kv_heads + h
+    res = {}
+    # summaries: bit-exact
+    phys = layer.li.page_table[b, :n].long().cpu()
+    gs = layer.summ[phys.cuda(), h].cpu().numpy().astype(np.int64) & 0xFFFF
+    assert np.array_equal(gs[:, 0], un["kmin"].astype(np.int64)), "kmin mismatch"
+    assert np.array_equal(gs[:, 1], un["kmax"].astype(np.int64)), "kmax mismatch"
+    # scores
+    sel = O.select_unit(un["q"], un["kmin"], un["kmax"], un["nv"], w.scale, gamma)
+    x_gpu = st.buf.logits[b, h, :, :n].double().cpu().numpy()
+    qf = O.bf16_bits_to_f64(un["q"])
+    mag = np.abs(qf)[:, None, :] * np.maximum(np.abs(O.bf16_bits_to_f64(un["kmin"])),
+                                              np.abs(O.bf16_bits_to_f64(un["kmax"])))[None]
+    tol = w.scale * 300 * 2.0 ** -24 * mag.sum(-1) + 1e-6
+    err = np.abs(x_gpu - sel["x"])
+    res["score_err"] = float(err.max())
+    assert np.all(err <= tol), f"score error {err.max()} above bound"
+    # list
+    cnt = int(st.buf.sel_counts[u].item())
+    lst = st.buf.sel_pages[u, :cnt].cpu().numpy()
+    phys_l = st.buf.sel_phys[u, :cnt].cpu().numpy()
+    ok, why = O.list_accepted(lst, sel["m"], gamma, LIST_EPS)
+    assert ok, f"unit {(b, h)} list rejected: {why} (gpu {cnt}, oracle {sel['count']})"
+    assert np.array_equal(phys_l, layer.li.page_table[b, lst].cpu().numpy())
+    res["exact"] = bool(cnt == sel["count"] and np.array_equal(lst, sel["list"]))
+    res["frac"] = cnt / n
+    # attention on the GPU's own list
+    if full:
+        Kf = O.bf16_bits_to_f64(un["k"])
+        Vf = O.bf16_bits_to_f64(un["v"])
+        o_ref, lse_ref = O.attend_pages(qf, Kf, Vf, un["nv"], lst, w.scale)
+        o_gpu = st.buf.out[b, h * G:(h + 1) * G].double().cpu().numpy()
+        lse_gpu = st.buf.out_lse[b, h * G:(h + 1) * G].double().cpu().numpy()
+        res["attn_err"] = float(np.abs(o_gpu - o_ref).max())
+        res["lse_err"] = float(np.abs(lse_gpu - lse_ref).max())
+        assert res["attn_err"] <= ATTN_TOL
+        res["oracle_list"] = sel["list"]
+    return res
+
+
+def feed_lists(st, layer, lists):
+    """Write host page lists {u: logical pages} into the step's buffers and the
+    chunk plan they imply (exclusive prefix sums of ceil(count/chunk))."""
+    w = layer.w
+    U = w.batch * w.kv_heads
+    MP = layer.dims.max_pages
+    pages = np.zeros((U, MP), dtype=np.int32)
+    phys = np.zeros((U, MP), dtype=np.int32)
+    counts = np.zeros(U, dtype=np.int64)
+    table = layer.li.page_table.cpu().numpy()
+    for u, lst in lists.items():
+        b = u // w.kv_heads
+        counts[u] = len(lst)
+        pages[u, :len(lst)] = lst
+        phys[u, :len(lst)] = table[b, lst]
+    chunks = -(-counts // st.chunk_pages)
+    offs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    soff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    st.buf.sel_pages.copy_(torch.from_numpy(pages))
+    st.buf.sel_phys.copy_(torch.from_numpy(phys))
+    st.buf.sel_counts.copy_(torch.from_numpy(counts.astype(np.int32)))
+    st.buf.chunk_offsets.copy_(torch.from_numpy(offs))
+    st.buf.sel_offsets.copy_(torch.from_numpy(soff))

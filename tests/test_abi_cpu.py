@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-side argument checks reject bad calls before
+any HIP call is made."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from adaptive_sparse_paged_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_paged.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        from adaptive_sparse_paged_amd import build
+        build.build(verbose=False)
+    return lib.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib.EXPORTS)
+    out = os.popen(f"nm -D --defined-only {lib.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in lib.version()
+    assert L.sparse_status_string(0) == b"ok"
+    assert L.sparse_status_string(3).startswith(b"workspace")
+
+
+def _dims(**kw):
+    d = dict(batch=2, q_heads=8, kv_heads=2, max_pages=64)
+    d.update(kw)
+    return lib.make_dims(d["batch"], d["q_heads"], d["kv_heads"], d["max_pages"],
+                         d.get("head_dim", 128), d.get("page_size", 16))
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def test_max_parts_and_workspace(L):
+    d = _dims()
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 4
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 5) == 4 * 13
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 0) == -1
+    assert L.sparse_select_workspace_bytes(ctypes.byref(d)) >= 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), lib.ERR_UNSUPPORTED),
+    (dict(page_size=32), lib.ERR_UNSUPPORTED),
+    (dict(q_heads=7), lib.ERR_INVALID),
+    (dict(q_heads=64, kv_heads=2), lib.ERR_UNSUPPORTED),
+    (dict(max_pages=40000), lib.ERR_UNSUPPORTED),
+    (dict(batch=0), lib.ERR_INVALID),
+])
+def test_dims_rejected(L, kw, code):
+    d = _dims(**kw)
+    r = L.sparse_score_pages(ctypes.byref(d), FAKE, FAKE, 10, FAKE, FAKE, 0.1, FAKE, None)
+    assert r == code
+
+
+def test_null_and_value_checks(L):
+    d = _dims()
+    assert L.sparse_score_pages(None, FAKE, FAKE, 10, FAKE, FAKE, 0.1, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_score_pages(ctypes.byref(d), None, FAKE, 10, FAKE, FAKE, 0.1, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_score_pages(ctypes.byref(d), FAKE, FAKE, 10, FAKE, FAKE, float("nan"), FAKE, None) == lib.ERR_INVALID
+    sel = lambda gamma, chunk, ws, wsb: L.sparse_select_coverage(
+        ctypes.byref(d), FAKE, FAKE, FAKE, gamma, chunk, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert sel(0.0, 8, FAKE, 256) == lib.ERR_INVALID
+    assert sel(1.5, 8, FAKE, 256) == lib.ERR_INVALID
+    assert sel(float("nan"), 8, FAKE, 256) == lib.ERR_INVALID
+    assert sel(0.99, 0, FAKE, 256) == lib.ERR_INVALID
+    assert sel(0.99, 65, FAKE, 256) == lib.ERR_INVALID
+    assert sel(0.99, 8, None, 256) == lib.ERR_WORKSPACE
+    assert sel(0.99, 8, FAKE, 1) == lib.ERR_WORKSPACE
+    attn = lambda kvp, sp_, sh, mp: L.sparse_decode_attn(
+        ctypes.byref(d), FAKE, kvp, sp_, sh, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 16, FAKE,
+        FAKE, mp, None)
+    assert attn(FAKE, 8192, 4096, 15) == lib.ERR_INVALID          # wrong max_parts
+    assert attn(ctypes.c_void_p(0x10002), 8192, 4096, 16) == lib.ERR_INVALID  # misaligned pool
+    assert attn(FAKE, 8191, 4096, 16) == lib.ERR_INVALID          # stride not 16-byte
+    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        lib.load.__wrapped__ if hasattr(lib.load, "__wrapped__") else None
+        saved = lib._lib
+        try:
+            lib._lib = None
+            lib.load(str(tmp_path / "nope.so"))
+        finally:
+            lib._lib = saved
