@@ -189,7 +189,8 @@ def valid_tokens(L):
     """Valid tokens of each logical page of a context of L tokens."""
     n = pages_of(L)
     v = np.full(n, PAGE, dtype=np.int64)
-    v[-1] = int(L) - PAGE * (n - 1)
+    if n:
+        v[-1] = int(L) - PAGE * (n - 1)
     return v
 
 
@@ -207,7 +208,8 @@ def unit_params(w, layer, b, h, n_pages, seed=0):
         alpha = float(math.exp(r.uniform(math.log(a[1]), math.log(a[2]))))
     t = w.targets
     nt = int(t[1]) if t[0] == "fixed" else int(r.integers(t[1], t[2] + 1))
-    nt = max(1, min(nt, n_pages))
+    nt = max(1, nt) if n_pages > 0 else 0
+    nt = min(nt, n_pages)
     targets = np.sort(r.choice(n_pages, size=nt, replace=False))
     return alpha, targets
 
@@ -233,10 +235,13 @@ def unit_query_bits(w, layer, b, h, L, seed=0):
     Returns int16 [G][D]."""
     n = pages_of(L)
     alpha, targets = unit_params(w, layer, b, h, n, seed)
-    kt = bf16_bits_to_float(unit_kv_bits(w, layer, b, h, n, 0, pages=targets, seed=seed)).double()
-    nv = valid_tokens(L)[targets]
-    rows = torch.cat([kt[i, :int(nv[i])] for i in range(len(targets))], 0)
-    mu = rows.mean(0)
+    if len(targets):
+        kt = bf16_bits_to_float(unit_kv_bits(w, layer, b, h, n, 0, pages=targets, seed=seed)).double()
+        nv = valid_tokens(L)[targets]
+        rows = torch.cat([kt[i, :int(nv[i])] for i in range(len(targets))], 0)
+        mu = rows.mean(0)
+    else:                                   # empty context: noise only
+        mu = torch.zeros(HEAD_DIM, dtype=torch.float64)
     noise = torch.from_numpy(_rng(w, 2, layer, b, h, seed=seed).standard_normal((w.group, HEAD_DIM)))
     return float_to_bf16_bits(alpha * mu[None, :] + noise)
 
@@ -283,12 +288,14 @@ def build_layer(w, layer, device, seed=0, lens=None):
         phys = torch.from_numpy(table[b, :n].astype(np.int64)).to(device)
         page_valid[table[b, :n]] = valid_tokens(lens[b])
         for h in range(H):
+            q[b, h * w.group:(h + 1) * w.group] = unit_query_bits(w, layer, b, h, lens[b], seed)
+            if n == 0:
+                continue
             k = unit_kv_bits(w, layer, b, h, n, 0, device=device, seed=seed)
             v = unit_kv_bits(w, layer, b, h, n, 1, device=device, seed=seed)
             pool[phys, h, 0] = k.reshape(n, PAGE * HEAD_DIM)
             pool[phys, h, 1] = v.transpose(1, 2).reshape(n, PAGE * HEAD_DIM)
             del k, v
-            q[b, h * w.group:(h + 1) * w.group] = unit_query_bits(w, layer, b, h, lens[b], seed)
     return LayerInputs(
         kv_pool=pool,
         page_table=torch.from_numpy(table).to(device),
