@@ -48,14 +48,13 @@ struct PageFrag {
   int valid;    // valid tokens (0 = skip page)
 };
 
+// Issue the loads of one page's K and V fragments.  p is the logical page,
+// x its physical page (or cache slot); both are wave-uniform.  K/V are read
+// once per step, so the loads are non-temporal (streaming).
 __device__ __forceinline__ void load_page(PageFrag& f, const uint16_t* __restrict__ kv,
                                           int64_t stride_page, int64_t stride_head,
-                                          int64_t pool_pages, int h, int L,
-                                          const int32_t* __restrict__ lp,
-                                          const int32_t* __restrict__ lx, int i) {
+                                          int64_t pool_pages, int h, int L, int p, int x) {
   const int lane = lane_id(), row = lane & 15, j = lane >> 4;
-  const int p = lp[i];
-  const int x = lx[i];
   int nv = min(kP, L - kP * p);
   if (x < 0 || x >= pool_pages || p < 0) nv = 0;
   f.valid = max(nv, 0);
@@ -70,13 +69,66 @@ __device__ __forceinline__ void load_page(PageFrag& f, const uint16_t* __restric
   const uint16_t* vt = kt + kTile;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    f.k[s] = *reinterpret_cast<const u32x4*>(kt + row * kD + 32 * s + 8 * j);
+    f.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + row * kD + 32 * s + 8 * j));
 #pragma unroll
   for (int m = 0; m < 8; ++m)
-    f.v[m] = *reinterpret_cast<const u32x2*>(vt + (16 * m + row) * kP + 4 * j);
+    f.v[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vt + (16 * m + row) * kP + 4 * j));
 }
 
-__global__ __launch_bounds__(256) void attn_kernel(
+// One page of the online softmax: QK on the matrix cores, running max/sum
+// update, PV with P split into bf16 high and residual parts.
+__device__ __forceinline__ void attend_page(PageFrag& f, const bf16x8* qf, bool gok, int j,
+                                            float scale_log2, float& m_run, float& l_run,
+                                            floatx4* o) {
+  if (f.valid == 0) return;
+  floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[s]), qf[s], sacc, 0, 0, 0);
+  // lane (g, j): logits of tokens 4j + e, in log2 units
+  float xs[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    xs[e] = (gok && 4 * j + e < f.valid) ? sacc[e] * scale_log2 : -INFINITY;
+  float pm = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+  pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+  pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+  const float m_new = gok ? fmaxf(m_run, pm) : 0.f;
+  const float alpha = gok ? exp2f(m_run - m_new) : 1.f;
+  float pv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pv[e] = gok ? exp2f(xs[e] - m_new) : 0.f;
+  l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+  m_run = gok ? m_new : m_run;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] *= alpha;
+  if (f.valid < kP) {
+    // zero V of tokens past the end of the context (they may hold anything)
+    const int t0 = 4 * j;
+    const uint32_t k0 = (t0 + 0 < f.valid ? 0x0000FFFFu : 0u) | (t0 + 1 < f.valid ? 0xFFFF0000u : 0u);
+    const uint32_t k1 = (t0 + 2 < f.valid ? 0x0000FFFFu : 0u) | (t0 + 3 < f.valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      f.v[m][0] &= k0;
+      f.v[m][1] &= k1;
+    }
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = f32_to_bf16_rne(pv[e]);
+    lo[e] = f32_to_bf16_rne(pv[e] - __uint_as_float(hi[e] << 16));
+  }
+  const short4v phi = as_short4(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+  const short4v plo = as_short4(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(f.v[m]), phi, o[m], 0, 0, 0);
+    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(f.v[m]), plo, o[m], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
     int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ chunk_offsets,
@@ -115,61 +167,26 @@ __global__ __launch_bounds__(256) void attn_kernel(
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  int i = i0 + wv;
-  PageFrag cur;
-  if (i < i1) load_page(cur, kv, stride_page, stride_head, pool_pages, h, L, lp, lx, i);
-  for (; i < i1; i += kAttnWaves) {
-    PageFrag nxt;
-    const bool more = i + kAttnWaves < i1;
-    if (more) load_page(nxt, kv, stride_page, stride_head, pool_pages, h, L, lp, lx, i + kAttnWaves);
-    if (cur.valid > 0) {
-      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[s]), qf[s], sacc, 0, 0, 0);
-      // lane (g, j): logits of tokens 4j + e, in log2 units
-      float xs[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        xs[e] = (gok && 4 * j + e < cur.valid) ? sacc[e] * scale_log2 : -INFINITY;
-      float pm = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-      const float m_new = gok ? fmaxf(m_run, pm) : 0.f;
-      const float alpha = gok ? exp2f(m_run - m_new) : 1.f;
-      float pv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[e] = gok ? exp2f(xs[e] - m_new) : 0.f;
-      l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
-      m_run = gok ? m_new : m_run;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] *= alpha;
-      if (cur.valid < kP) {
-        // zero V of tokens past the end of the context (they may hold anything)
-        const int t0 = 4 * j;
-        const uint32_t k0 = (t0 + 0 < cur.valid ? 0x0000FFFFu : 0u) | (t0 + 1 < cur.valid ? 0xFFFF0000u : 0u);
-        const uint32_t k1 = (t0 + 2 < cur.valid ? 0x0000FFFFu : 0u) | (t0 + 3 < cur.valid ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          cur.v[m][0] &= k0;
-          cur.v[m][1] &= k1;
-        }
-      }
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = f32_to_bf16_rne(pv[e]);
-        lo[e] = f32_to_bf16_rne(pv[e] - __uint_as_float(hi[e] << 16));
-      }
-      const short4v phi = as_short4(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
-      const short4v plo = as_short4(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(cur.v[m]), phi, o[m], 0, 0, 0);
-        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(cur.v[m]), plo, o[m], 0, 0, 0);
-      }
+  // This wave's pages are list entries i0 + wv + 4k.  Their logical and
+  // physical ids are read once per 64 pages into lanes k and broadcast with
+  // readlane, so no KV load waits on a list load.
+  const int nk = (i1 - i0 - wv + kAttnWaves - 1) / kAttnWaves;
+  for (int base = 0; base < nk; base += 64) {
+    const int cnt_k = min(64, nk - base);
+    const int ie = i0 + wv + kAttnWaves * (base + lane);
+    const int pl = (lane < cnt_k) ? lp[ie] : -1;
+    const int xl = (lane < cnt_k) ? lx[ie] : -1;
+    PageFrag cur, nxt;
+    load_page(cur, kv, stride_page, stride_head, pool_pages, h, L,
+              __builtin_amdgcn_readlane(pl, 0), __builtin_amdgcn_readlane(xl, 0));
+    for (int k = 0; k < cnt_k; ++k) {
+      const bool more = k + 1 < cnt_k;
+      if (more)
+        load_page(nxt, kv, stride_page, stride_head, pool_pages, h, L,
+                  __builtin_amdgcn_readlane(pl, k + 1), __builtin_amdgcn_readlane(xl, k + 1));
+      attend_page(cur, qf, gok, j, scale_log2, m_run, l_run, o);
+      if (more) cur = nxt;
     }
-    if (more) cur = nxt;
   }
 
   // ---- merge the waves of the workgroup ------------------------------------

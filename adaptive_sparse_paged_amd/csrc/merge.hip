@@ -6,48 +6,68 @@
 
 namespace sp {
 
-// One 256-thread workgroup per unit.  Wave w computes (max, sum of exp) of the
-// chunk lse values of heads g = w, w + 4, ...; then every thread accumulates
-// its (head, channel) outputs over the unit's chunks.
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_lse,
-                                                    const int32_t* __restrict__ chunk_offsets,
-                                                    int hkv, int group, float* __restrict__ out,
-                                                    float* __restrict__ out_lse) {
-  __shared__ float s_max[kMaxGroup], s_inv[kMaxGroup];
-  const int u = blockIdx.x;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
+
+// One 1024-thread workgroup per (unit, query head).  Thread t reads channel
+// quad t % 32 of chunks c0 + t / 32, c0 + t / 32 + 32, ... (each chunk's 128
+// floats are one coalesced 512-byte read by 32 threads), keeping an online
+// (max, sum, weighted sum); the 32 slots are then combined through LDS.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ chunk_offsets, int hkv, int group, float* __restrict__ out,
+    float* __restrict__ out_lse) {
+  __shared__ floatx4 s_acc[kMergeSlots][32];
+  __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
+  const int u = blockIdx.x, g = blockIdx.y;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   const int c0 = chunk_offsets[u], c1 = chunk_offsets[u + 1];
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  for (int g = wv; g < group; g += 4) {
-    float mx = -INFINITY;
-    for (int c = c0 + lane; c < c1; c += 64) mx = fmaxf(mx, part_lse[(int64_t)c * group + g]);
-    mx = wave_max(mx);
-    float s = 0.f;
-    if (mx != -INFINITY)
-      for (int c = c0 + lane; c < c1; c += 64) {
-        const float l = part_lse[(int64_t)c * group + g];
-        if (l != -INFINITY) s += __expf(l - mx);
-      }
-    s = wave_sum(s);
-    if (lane == 0) {
-      s_max[g] = mx;
-      s_inv[g] = (s > 0.f) ? 1.f / s : 0.f;
-      out_lse[(int64_t)b * hkv * group + h * group + g] = (s > 0.f) ? mx + __logf(s) : -INFINITY;
-    }
+  const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
+
+  float m = -INFINITY, s = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = c0 + slot; c < c1; c += 2 * kMergeSlots) {
+    const bool two = c + kMergeSlots < c1;
+    const int64_t r0 = (int64_t)c * group + g;
+    const int64_t r1 = (int64_t)(two ? c + kMergeSlots : c) * group + g;
+    const float l0 = part_lse[r0];
+    const float l1 = two ? part_lse[r1] : -INFINITY;
+    const floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
+    const floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
+    const float mn = fmaxf(m, fmaxf(l0, l1));
+    if (mn == -INFINITY) continue;
+    const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
+    const float w0 = (l0 == -INFINITY) ? 0.f : __expf(l0 - mn);
+    const float w1 = (l1 == -INFINITY) ? 0.f : __expf(l1 - mn);
+    acc = acc * a + o0 * w0 + o1 * w1;
+    s = s * a + w0 + w1;
+    m = mn;
+  }
+  s_acc[slot][quad] = acc;
+  if (quad == 0) {
+    s_m[slot] = m;
+    s_s[slot] = s;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < group * kD; idx += 256) {
-    const int g = idx / kD, d = idx - (idx / kD) * kD;
-    const float mx = s_max[g], inv = s_inv[g];
-    float acc = 0.f;
-    if (mx != -INFINITY)
-      for (int c = c0; c < c1; ++c) {
-        const float l = part_lse[(int64_t)c * group + g];
-        if (l != -INFINITY) acc += __expf(l - mx) * part_o[((int64_t)c * group + g) * kD + d];
-      }
-    out[((int64_t)b * hkv * group + h * group + g) * kD + d] = acc * inv;
+  if (slot != 0) return;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int k = 0; k < kMergeSlots; ++k) M = fmaxf(M, s_m[k]);
+  floatx4 tot = {0.f, 0.f, 0.f, 0.f};
+  float S = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 8
+    for (int k = 0; k < kMergeSlots; ++k) {
+      if (s_m[k] == -INFINITY) continue;
+      const float a = __expf(s_m[k] - M);
+      tot += s_acc[k][quad] * a;
+      S += s_s[k] * a;
+    }
   }
+  const int64_t row = (int64_t)b * hkv * group + h * group + g;
+  const float inv = (S > 0.f) ? 1.f / S : 0.f;
+  *reinterpret_cast<floatx4*>(out + row * kD + 4 * quad) = tot * inv;
+  if (quad == 0) out_lse[row] = (S > 0.f) ? M + __logf(S) : -INFINITY;
 }
 
 }  // namespace sp
@@ -60,10 +80,12 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
   if (st != SPARSE_OK) return st;
   if (!part_o || !part_lse || !sel_counts || !chunk_offsets || !out || !out_lse)
     return SPARSE_ERR_INVALID;
+  if (!sp::aligned(part_o, 16) || !sp::aligned(out, 16)) return SPARSE_ERR_INVALID;
   if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  hipLaunchKernelGGL(sp::merge_kernel, dim3(U), dim3(256), 0, (hipStream_t)stream, part_o,
-                     part_lse, chunk_offsets, hkv, group, out, out_lse);
+  hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
+                     (hipStream_t)stream, part_o, part_lse, chunk_offsets, hkv, group, out,
+                     out_lse);
   return sp::launch_status();
 }

@@ -68,32 +68,43 @@ __global__ __launch_bounds__(256) void score_kernel(
   float* out = logits + (int64_t)u * group * max_pages;
   const int32_t* pt = page_table + (int64_t)b * max_pages;
 
+  // Page ids of every tile first, then every summary load, then the math:
+  // two memory round trips per wave in all.
+  int xs[kScoreTilesPerWave];
+  bool oks[kScoreTilesPerWave];
+#pragma unroll
+  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
+    const int p = p_begin + tile * 16 + row;
+    xs[tile] = (p < n) ? pt[p] : -1;
+  }
+  u32x4 a[kScoreTilesPerWave][8];
+#pragma unroll
+  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
+    const int x = xs[tile];
+    oks[tile] = (x >= 0) && (x < pool_pages);
+    const uint16_t* src = summ + ((int64_t)(oks[tile] ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      a[tile][s] = oks[tile]
+                       ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 32 * s))
+                       : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
     const int p0 = p_begin + tile * 16;
     if (p0 >= n) break;
-    const int p = p0 + row;
-    int x = -1;
-    if (p < n) x = pt[p];
-    const bool ok = (x >= 0) && (x < pool_pages);
-    u32x4 a[8];
-    const uint16_t* src = summ + ((int64_t)(ok ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      a[s] = ok ? *reinterpret_cast<const u32x4*>(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-    }
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]), qneg[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[tile][s]), qneg[s], acc, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[4 + s]), qpos[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[tile][4 + s]), qpos[s], acc, 0, 0, 0);
     // lane (g = row, j) now holds u for pages p0 + 4j + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pi = p0 + 4 * j + i;
-      const bool oki = __shfl(ok ? 1 : 0, 4 * j + i, 64) != 0;
+      const bool oki = __shfl(oks[tile] ? 1 : 0, 4 * j + i, 64) != 0;
       if (row < group && pi < n) {
         const int nv = min(kP, L - kP * pi);
         const float lnv = (nv == kP) ? ln16 : logf((float)nv);

@@ -5,17 +5,20 @@
 //
 // One 1024-thread workgroup per unit; thread t owns pages [t*NPT, t*NPT+NPT)
 // in registers.  Steps:
-//   1. per query head g: (max, sum of exp) over the unit's pages by one
-//      block reduction, then m[p] += exp(x_g[p] - max_g) / sum_g;  m /= G.
+//   1. per query head g: (max, sum of exp) over the unit's pages (block
+//      reduction of all heads at once), then m[p] += exp(x_g[p] - max_g) /
+//      sum_g;  m /= G.
 //   2. weights w[p] = floor(m[p] * 2^52) (exact 64-bit fixed point, so the
 //      cut's sums are exact and order independent) and keys = fp32 bits of
 //      m[p] (monotone for m >= 0).
 //   3. target T = ceil(gamma * sum w); a mass-weighted radix select over the
-//      key bits (11 + 11 + 9 bits, LDS histograms of counts and weights,
-//      suffix scans) finds the key tau with W(key > tau) < T <= W(key >= tau).
+//      key bits below the highest bit in which the unit's keys differ (up to
+//      11 bits per pass; LDS histograms of counts and weights; one wave scans
+//      the bins from the top) finds the key tau with
+//      W(key > tau) < T <= W(key >= tau).
 //   4. keep every page with key > tau plus the r lowest-index pages with key
 //      == tau, r = ceil((T - W(key > tau)) / w_tau); compact in ascending page
-//      order by a block prefix sum.
+//      order by one block prefix sum of packed (above, tie) counts.
 //   5. the last workgroup to finish (device ticket) writes the prefix sums of
 //      the counts and of the chunk counts over all units, then re-arms the
 //      ticket -- the plan the attention kernel reads, made on the device.
@@ -30,6 +33,11 @@ constexpr int kSelWaves = kSelThreads / 64;
 struct PairMS {
   float m, s;
 };
+
+// fixed-point weight of a page from its fp32 mass bits: floor(m * 2^52)
+__device__ __forceinline__ unsigned long long weight_of(uint32_t key) {
+  return (unsigned long long)(__uint_as_float(key) * 4503599627370496.0f);
+}
 
 __device__ __forceinline__ PairMS combine(PairMS a, PairMS b) {
   const float M = fmaxf(a.m, b.m);
@@ -46,13 +54,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int max_pages, int U, int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_offsets,
     int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
-  __shared__ uint32_t hcnt[2048];
-  __shared__ unsigned long long hw[2048];
-  __shared__ float red_m[kSelWaves], red_s[kSelWaves];
-  __shared__ unsigned long long scan64[kSelWaves];
+  // two histogram buffers, used by alternate radix passes
+  __shared__ uint32_t hcnt[2][2048];
+  __shared__ unsigned long long hw[2][2048];
+  __shared__ float red_m[kMaxGroup][kSelWaves], red_s[kMaxGroup][kSelWaves];
+  __shared__ unsigned long long red_z[kSelWaves];
+  __shared__ uint32_t red_lo[kSelWaves], red_hi[kSelWaves];
   __shared__ uint32_t scan32[kSelWaves];
-  __shared__ int s_bin;
-  __shared__ unsigned long long s_wgt;
+  __shared__ unsigned long long scan64[kSelWaves];
+  __shared__ int s_bin[2];
+  __shared__ unsigned long long s_wgt[2];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
@@ -65,171 +76,252 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   if (n > 0) {
     const float* X = logits + (int64_t)u * group * max_pages;
+    const int32_t* pt = page_table + (int64_t)b * max_pages;
+    // physical ids, read early to overlap the logits (when registers allow)
+    constexpr bool kPrefetchPhys = NPT <= 16;
+    int32_t phys[kPrefetchPhys ? NPT : 1];
+    if constexpr (kPrefetchPhys) {
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) phys[i] = (pbase + i < n) ? pt[pbase + i] : -1;
+    }
     float m[NPT];
 #pragma unroll
     for (int i = 0; i < NPT; ++i) m[i] = 0.f;
 
     // ---- 1. per-head softmax normalisers, group mass --------------------
-    for (int g = 0; g < group; ++g) {
-      float xv[NPT];
-      const float* Xg = X + (int64_t)g * max_pages;
+    // Logits are read HPR heads at a time with every load issued before the
+    // first use (one memory round trip per round).  (max, sum of exp) per
+    // head: thread-local, wave shuffles, then one lane per head combines the
+    // wave partials.  When all heads fit one round the values stay in
+    // registers for the mass; otherwise they are read again (L2 hits).
+    constexpr int HPR = (NPT >= 32) ? 1 : 32 / NPT;
+    const bool one_round = group <= HPR;
+    float xv[HPR][NPT];
+    for (int g0 = 0; g0 < group; g0 += HPR) {
 #pragma unroll
-      for (int i = 0; i < NPT; ++i) xv[i] = (pbase + i < n) ? Xg[pbase + i] : -INFINITY;
-      float mx = -INFINITY;
+      for (int hh = 0; hh < HPR; ++hh) {
+        const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
 #pragma unroll
-      for (int i = 0; i < NPT; ++i) mx = fmaxf(mx, xv[i]);
-      float se = 0.f;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) se += __expf(xv[i] - mx);
+        for (int i = 0; i < NPT; ++i)
+          xv[hh][i] = (g0 + hh < group && pbase + i < n) ? Xg[pbase + i] : -INFINITY;
       }
-      PairMS pr = {mx, se};
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        PairMS other = {__shfl_xor(pr.m, o, 64), __shfl_xor(pr.s, o, 64)};
-        pr = combine(pr, other);
+      for (int hh = 0; hh < HPR; ++hh) {
+        if (g0 + hh >= group) break;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) mx = fmaxf(mx, xv[hh][i]);
+        float se = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < NPT; ++i) se += __expf(xv[hh][i] - mx);
+        }
+        PairMS pr = {mx, se};
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          PairMS other = {__shfl_xor(pr.m, o, 64), __shfl_xor(pr.s, o, 64)};
+          pr = combine(pr, other);
+        }
+        if (lane == 0) {
+          red_m[g0 + hh][wv] = pr.m;
+          red_s[g0 + hh][wv] = pr.s;
+        }
       }
-      if (lane == 0) {
-        red_m[wv] = pr.m;
-        red_s[wv] = pr.s;
-      }
-      __syncthreads();
-      PairMS tot = {red_m[0], red_s[0]};
-#pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) tot = combine(tot, PairMS{red_m[w], red_s[w]});
-      __syncthreads();
-      const float inv = 1.f / tot.s;
-#pragma unroll
-      for (int i = 0; i < NPT; ++i)
-        if (pbase + i < n) m[i] += __expf(xv[i] - tot.m) * inv;
     }
+    __syncthreads();
+    if (tid < group) {
+      PairMS tot = {red_m[tid][0], red_s[tid][0]};
+      for (int w = 1; w < kSelWaves; ++w) tot = combine(tot, PairMS{red_m[tid][w], red_s[tid][w]});
+      red_m[tid][0] = tot.m;
+      red_s[tid][0] = 1.f / tot.s;
+    }
+    __syncthreads();
+    for (int g0 = 0; g0 < group; g0 += HPR) {
+      if (!one_round) {
+#pragma unroll
+        for (int hh = 0; hh < HPR; ++hh) {
+          const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
+#pragma unroll
+          for (int i = 0; i < NPT; ++i)
+            xv[hh][i] = (g0 + hh < group && pbase + i < n) ? Xg[pbase + i] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < HPR; ++hh) {
+        if (g0 + hh >= group) break;
+        const float M = red_m[g0 + hh][0], inv = red_s[g0 + hh][0];
+#pragma unroll
+        for (int i = 0; i < NPT; ++i)
+          if (pbase + i < n) m[i] += __expf(xv[hh][i] - M) * inv;
+      }
+    }
+
+    // ---- 2. keys, fixed-point weights, total and key range ----------------
     const float invg = 1.f / (float)group;
     uint32_t key[NPT];
-    unsigned long long wsum_local = 0ull;
+    unsigned long long zl = 0ull;
+    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const float mi = m[i] * invg;
-      key[i] = (pbase + i < n) ? __float_as_uint(mi) : 0u;
-      wsum_local += (unsigned long long)(__uint_as_float(key[i]) * 4503599627370496.0f);  // 2^52
+      key[i] = (pbase + i < n) ? __float_as_uint(m[i] * invg) : 0u;
+      if (pbase + i < n) {
+        zl += weight_of(key[i]);
+        klo = min(klo, key[i]);
+        khi = max(khi, key[i]);
+      }
     }
-    const unsigned long long Z = block_sum<unsigned long long, kSelThreads>(wsum_local, scan64);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      zl += __shfl_xor(zl, o, 64);
+      klo = min(klo, (uint32_t)__shfl_xor((int)klo, o, 64));
+      khi = max(khi, (uint32_t)__shfl_xor((int)khi, o, 64));
+    }
+    if (lane == 0) {
+      red_z[wv] = zl;
+      red_lo[wv] = klo;
+      red_hi[wv] = khi;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      unsigned long long z = (lane < kSelWaves) ? red_z[lane] : 0ull;
+      uint32_t lo2 = (lane < kSelWaves) ? red_lo[lane] : 0xFFFFFFFFu;
+      uint32_t hi2 = (lane < kSelWaves) ? red_hi[lane] : 0u;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        z += __shfl_xor(z, o, 64);
+        lo2 = min(lo2, (uint32_t)__shfl_xor((int)lo2, o, 64));
+        hi2 = max(hi2, (uint32_t)__shfl_xor((int)hi2, o, 64));
+      }
+      if (lane == 0) {
+        red_z[0] = z;
+        red_lo[0] = lo2;
+        red_hi[0] = hi2;
+      }
+    }
+    __syncthreads();
+    const unsigned long long Z = red_z[0];
+    const uint32_t KLO = red_lo[0], KHI = red_hi[0];
 
-    // ---- 2-4. the cut ---------------------------------------------------
-    uint32_t tau = 0u;
-    unsigned long long need = 0ull, w_tau = 1ull;
+    // ---- 3. the cut: key tau and the number of ties at tau to keep -------
     const bool all = !(gamma < 1.0f);
+    uint32_t tau = 0u;
+    unsigned long long need = 0ull;
     if (!all) {
       unsigned long long T = (unsigned long long)ceil((double)gamma * (double)Z);
       if (T > Z) T = Z;
       if (T < 1ull) T = 1ull;
-      uint32_t prefix = 0u, hi_mask = 0u;
-      const int shifts[3] = {20, 9, 0};
-      const int widths[3] = {11, 11, 9};
-#pragma unroll
-      for (int pass = 0; pass < 3; ++pass) {
-        const int sh = shifts[pass], nb = 1 << widths[pass];
-        for (int k = tid; k < nb; k += kSelThreads) {
-          hcnt[k] = 0u;
-          hw[k] = 0ull;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) {
-          if (pbase + i < n && (key[i] & hi_mask) == prefix) {
-            const int bin = (key[i] >> sh) & (nb - 1);
-            atomicAdd(&hcnt[bin], 1u);
-            atomicAdd(&hw[bin], (unsigned long long)(__uint_as_float(key[i]) * 4503599627370496.0f));
+      unsigned long long w_tau = weight_of(KHI);
+      if (KLO == KHI) {
+        tau = KHI;                          // every page has the same mass
+      } else {
+        // radix passes over the bits below the highest bit where keys differ
+        const int top = 31 - __clz(KLO ^ KHI);
+        uint32_t hi_mask = ~((2u << top) - 1u);
+        uint32_t prefix = KHI & hi_mask;
+        int lo = top + 1, buf = 0;
+        while (lo > 0) {
+          const int width = min(11, lo);
+          const int sh = lo - width, nb = 1 << width;
+          uint32_t* cnt = hcnt[buf];
+          unsigned long long* wgt = hw[buf];
+          for (int k = tid; k < nb; k += kSelThreads) {
+            cnt[k] = 0u;
+            wgt[k] = 0ull;
           }
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < NPT; ++i) {
+            if (pbase + i < n && (key[i] & hi_mask) == prefix) {
+              const int bin = (key[i] >> sh) & (nb - 1);
+              atomicAdd(&cnt[bin], 1u);
+              atomicAdd(&wgt[bin], weight_of(key[i]));
+            }
+          }
+          __syncthreads();
+          {
+            // thread t owns bins 2t, 2t+1; the weight of all bins above a
+            // thread's comes from one block prefix sum
+            const int b0 = 2 * tid, b1 = 2 * tid + 1;
+            const unsigned long long w0 = (b0 < nb) ? wgt[b0] : 0ull;
+            const unsigned long long w1 = (b1 < nb) ? wgt[b1] : 0ull;
+            unsigned long long total;
+            const unsigned long long ex =
+                block_excl_scan<unsigned long long, kSelThreads>(w0 + w1, scan64, total);
+            const unsigned long long gt1 = total - (ex + w0 + w1);  // weight above bin b1
+            const unsigned long long gt0 = gt1 + w1;                // weight above bin b0
+            if (b1 < nb && gt1 < T && T <= gt1 + w1) {
+              s_bin[buf] = b1;
+              s_wgt[buf] = gt1;
+            }
+            if (b0 < nb && gt0 < T && T <= gt0 + w0) {
+              s_bin[buf] = b0;
+              s_wgt[buf] = gt0;
+            }
+          }
+          __syncthreads();
+          const int bin = s_bin[buf];
+          T -= s_wgt[buf];
+          prefix |= (uint32_t)bin << sh;
+          hi_mask |= (uint32_t)(nb - 1) << sh;
+          if (sh == 0) {
+            const unsigned long long c = cnt[bin];
+            w_tau = c ? wgt[bin] / c : 1ull;   // every page with key tau has one weight
+          }
+          lo = sh;
+          buf ^= 1;
         }
-        __syncthreads();
-        // thread t owns bins 2t, 2t+1; find the bin where the running weight
-        // from the top crosses T.
-        const int b0 = 2 * tid, b1 = 2 * tid + 1;
-        const unsigned long long w0 = (b0 < nb) ? hw[b0] : 0ull;
-        const unsigned long long w1 = (b1 < nb) ? hw[b1] : 0ull;
-        unsigned long long total;
-        const unsigned long long ex = block_excl_scan<unsigned long long, kSelThreads>(w0 + w1, scan64, total);
-        const unsigned long long gt1 = total - (ex + w0 + w1);  // weight of bins > b1
-        const unsigned long long gt0 = gt1 + w1;                // weight of bins > b0
-        if (b1 < nb && gt1 < T && T <= gt1 + w1) {
-          s_bin = b1;
-          s_wgt = gt1;
-        }
-        if (b0 < nb && gt0 < T && T <= gt0 + w0) {
-          s_bin = b0;
-          s_wgt = gt0;
-        }
-        __syncthreads();
-        const int bin = s_bin;
-        T -= s_wgt;
-        prefix |= (uint32_t)bin << sh;
-        hi_mask |= (uint32_t)(nb - 1) << sh;
-        if (pass == 2) {
-          // every page with key tau has the same weight
-          const unsigned long long cnt = hcnt[bin];
-          w_tau = cnt ? hw[bin] / cnt : 1ull;
-          if (w_tau == 0ull) w_tau = 1ull;
-        }
-        __syncthreads();
+        tau = prefix;
       }
-      tau = prefix;
-      need = (T + w_tau - 1ull) / w_tau;  // ties at tau to keep, >= 1
+      if (w_tau == 0ull) w_tau = 1ull;
+      need = (T + w_tau - 1ull) / w_tau;    // pages at tau to keep (>= 1)
     }
 
-    // ---- rank ties, compact in ascending page order ---------------------
-    uint32_t ties_local = 0u;
-    if (!all) {
-#pragma unroll
-      for (int i = 0; i < NPT; ++i) ties_local += (pbase + i < n && key[i] == tau) ? 1u : 0u;
-    }
-    uint32_t ties_total;
-    const uint32_t tie_rank0 = block_excl_scan<uint32_t, kSelThreads>(ties_local, scan32, ties_total);
-    uint32_t keep_mask = 0u, keep_local = 0u, tr = tie_rank0;
+    // ---- 4. compact in ascending page order: one scan of packed counts ----
+    // high half: pages above tau (all pages when gamma = 1); low half: ties
+    uint32_t packed = 0u;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      bool keep = false;
       if (pbase + i < n) {
-        if (all) {
-          keep = true;
-        } else if (key[i] > tau) {
-          keep = true;
-        } else if (key[i] == tau) {
-          keep = (unsigned long long)tr < need;
-          ++tr;
-        }
-      }
-      if (keep) {
-        keep_mask |= 1u << i;
-        ++keep_local;
+        if (all || key[i] > tau) packed += 0x10000u;
+        else if (key[i] == tau) packed += 1u;
       }
     }
-    uint32_t kept_total;
-    uint32_t pos = block_excl_scan<uint32_t, kSelThreads>(keep_local, scan32, kept_total);
+    uint32_t tot_packed;
+    const uint32_t ex = block_excl_scan<uint32_t, kSelThreads>(packed, scan32, tot_packed);
+    uint32_t gtb = ex >> 16, tb = ex & 0xFFFFu;
     int32_t* lp = sel_pages + (int64_t)u * max_pages;
     int32_t* lx = sel_phys + (int64_t)u * max_pages;
-    const int32_t* pt = page_table + (int64_t)b * max_pages;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      if (keep_mask & (1u << i)) {
+      if (pbase + i >= n) continue;
+      int pos = -1;
+      if (all || key[i] > tau) {
+        pos = (int)(gtb + (uint32_t)min((unsigned long long)tb, need));
+        ++gtb;
+      } else if (key[i] == tau) {
+        if ((unsigned long long)tb < need) pos = (int)(gtb + tb);
+        ++tb;
+      }
+      if (pos >= 0) {
         lp[pos] = pbase + i;
-        lx[pos] = pt[pbase + i];
-        ++pos;
+        if constexpr (kPrefetchPhys) lx[pos] = phys[i];
+        else lx[pos] = pt[pbase + i];
       }
     }
-    count = (int)kept_total;
+    count = (int)((tot_packed >> 16) + min((unsigned long long)(tot_packed & 0xFFFFu), need));
   }
 
   // ---- 5. last workgroup: prefix sums over units --------------------------
-  if (tid == 0) sel_counts[u] = count;
-  __threadfence();
-  __syncthreads();
+  __syncthreads();   // every thread's list writes are issued before the ticket
   if (tid == 0) {
+    sel_counts[u] = count;
+    __threadfence();   // release this unit's list and count device-wide
     const uint32_t t = atomicAdd(ticket, 1u);
     s_last = (t == (uint32_t)(U - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __threadfence();     // acquire every unit's count
   uint32_t run = 0u, runc = 0u;
   for (int base = 0; base < U; base += kSelThreads) {
     const int v = base + tid;
