@@ -85,9 +85,8 @@ __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* src = summ + ((int64_t)(oks[tile] ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      a[tile][s] = oks[tile]
-                       ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 32 * s))
-                       : u32x4{0u, 0u, 0u, 0u};
+      a[tile][s] = oks[tile] ? *reinterpret_cast<const u32x4*>(src + 32 * s)
+                             : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {

@@ -3,8 +3,9 @@
 // DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", MOIRA
 // abstract, coverage-rule sentence).
 //
-// One 1024-thread workgroup per unit; thread t owns pages [t*NPT, t*NPT+NPT)
-// in registers.  Steps:
+// One 1024-thread workgroup per unit.  Logits are read coalesced (thread t:
+// pages t, t + 1024, ...); the page keys then pass through LDS so that for the
+// cut thread t owns the blocked run [t*NPT, t*NPT + NPT).  Steps:
 //   1. per query head g: (max, sum of exp) over the unit's pages (block
 //      reduction of all heads at once), then m[p] += exp(x_g[p] - max_g) /
 //      sum_g;  m /= G.
@@ -54,9 +55,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int max_pages, int U, int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_offsets,
     int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
-  // two histogram buffers, used by alternate radix passes
-  __shared__ uint32_t hcnt[2][2048];
-  __shared__ unsigned long long hw[2][2048];
+  // Page keys, staged so that loads are coalesced (thread t reads pages
+  // t, t + 1024, ...) while the cut works on blocked runs (thread t owns
+  // pages t*NPT .. t*NPT + NPT-1); later reused for the kept page list.
+  __shared__ uint32_t keys_lds[NPT * kSelThreads];
+  // radix histograms: two buffers (alternate passes) while LDS allows
+  constexpr int kHistBufs = (NPT <= 16) ? 2 : 1;
+  __shared__ uint32_t hcnt[kHistBufs][2048];
+  __shared__ unsigned long long hw[kHistBufs][2048];
   __shared__ float red_m[kMaxGroup][kSelWaves], red_s[kMaxGroup][kSelWaves];
   __shared__ unsigned long long red_z[kSelWaves];
   __shared__ uint32_t red_lo[kSelWaves], red_hi[kSelWaves];
@@ -71,29 +77,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int b = u / hkv;
   const int L = min(max(ctx_lens[b], 0), max_pages * kP);
   const int n = (L + kP - 1) / kP;
-  const int pbase = tid * NPT;
   int count = 0;
 
   if (n > 0) {
     const float* X = logits + (int64_t)u * group * max_pages;
-    const int32_t* pt = page_table + (int64_t)b * max_pages;
-    // physical ids, read early to overlap the logits (when registers allow)
-    constexpr bool kPrefetchPhys = NPT <= 16;
-    int32_t phys[kPrefetchPhys ? NPT : 1];
-    if constexpr (kPrefetchPhys) {
-#pragma unroll
-      for (int i = 0; i < NPT; ++i) phys[i] = (pbase + i < n) ? pt[pbase + i] : -1;
-    }
-    float m[NPT];
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) m[i] = 0.f;
 
-    // ---- 1. per-head softmax normalisers, group mass --------------------
-    // Logits are read HPR heads at a time with every load issued before the
-    // first use (one memory round trip per round).  (max, sum of exp) per
-    // head: thread-local, wave shuffles, then one lane per head combines the
-    // wave partials.  When all heads fit one round the values stay in
-    // registers for the mass; otherwise they are read again (L2 hits).
+    // ---- 1. per-head softmax normalisers -----------------------------------
+    // Logits of HPR heads at a time, every load issued before the first use.
+    // (max, sum of exp) per head: thread-local, wave shuffles, then one lane
+    // per head combines the wave partials.  When all heads fit one round the
+    // values stay in registers for step 2; otherwise they are read again.
     constexpr int HPR = (NPT >= 32) ? 1 : 32 / NPT;
     const bool one_round = group <= HPR;
     float xv[HPR][NPT];
@@ -102,19 +95,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int hh = 0; hh < HPR; ++hh) {
         const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
 #pragma unroll
-        for (int i = 0; i < NPT; ++i)
-          xv[hh][i] = (g0 + hh < group && pbase + i < n) ? Xg[pbase + i] : -INFINITY;
+        for (int k = 0; k < NPT; ++k) {
+          const int p = k * kSelThreads + tid;
+          xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) mx = fmaxf(mx, xv[hh][i]);
+        for (int k = 0; k < NPT; ++k) mx = fmaxf(mx, xv[hh][k]);
         float se = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
-          for (int i = 0; i < NPT; ++i) se += __expf(xv[hh][i] - mx);
+          for (int k = 0; k < NPT; ++k) se += __expf(xv[hh][k] - mx);
         }
         PairMS pr = {mx, se};
 #pragma unroll
@@ -136,14 +131,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       red_s[tid][0] = 1.f / tot.s;
     }
     __syncthreads();
+
+    // ---- 2. group mass, keys, fixed-point weights, total and key range ----
+    float m[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) m[k] = 0.f;
     for (int g0 = 0; g0 < group; g0 += HPR) {
       if (!one_round) {
 #pragma unroll
         for (int hh = 0; hh < HPR; ++hh) {
           const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
 #pragma unroll
-          for (int i = 0; i < NPT; ++i)
-            xv[hh][i] = (g0 + hh < group && pbase + i < n) ? Xg[pbase + i] : -INFINITY;
+          for (int k = 0; k < NPT; ++k) {
+            const int p = k * kSelThreads + tid;
+            xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
+          }
         }
       }
 #pragma unroll
@@ -151,23 +153,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (g0 + hh >= group) break;
         const float M = red_m[g0 + hh][0], inv = red_s[g0 + hh][0];
 #pragma unroll
-        for (int i = 0; i < NPT; ++i)
-          if (pbase + i < n) m[i] += __expf(xv[hh][i] - M) * inv;
+        for (int k = 0; k < NPT; ++k) m[k] += __expf(xv[hh][k] - M) * inv;
       }
     }
-
-    // ---- 2. keys, fixed-point weights, total and key range ----------------
     const float invg = 1.f / (float)group;
-    uint32_t key[NPT];
     unsigned long long zl = 0ull;
     uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      key[i] = (pbase + i < n) ? __float_as_uint(m[i] * invg) : 0u;
-      if (pbase + i < n) {
-        zl += weight_of(key[i]);
-        klo = min(klo, key[i]);
-        khi = max(khi, key[i]);
+    for (int k = 0; k < NPT; ++k) {
+      const int p = k * kSelThreads + tid;
+      if (p < n) {
+        const uint32_t key = __float_as_uint(m[k] * invg);
+        keys_lds[p] = key;
+        zl += weight_of(key);
+        klo = min(klo, key);
+        khi = max(khi, key);
       }
     }
 #pragma unroll
@@ -201,6 +201,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     const unsigned long long Z = red_z[0];
     const uint32_t KLO = red_lo[0], KHI = red_hi[0];
+    // this thread's blocked run of keys
+    const int pbase = tid * NPT;
+    uint32_t key[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) key[i] = (pbase + i < n) ? keys_lds[pbase + i] : 0u;
 
     // ---- 3. the cut: key tau and the number of ties at tau to keep -------
     const bool all = !(gamma < 1.0f);
@@ -250,17 +255,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const unsigned long long gt1 = total - (ex + w0 + w1);  // weight above bin b1
             const unsigned long long gt0 = gt1 + w1;                // weight above bin b0
             if (b1 < nb && gt1 < T && T <= gt1 + w1) {
-              s_bin[buf] = b1;
-              s_wgt[buf] = gt1;
+              s_bin[buf & 1] = b1;
+              s_wgt[buf & 1] = gt1;
             }
             if (b0 < nb && gt0 < T && T <= gt0 + w0) {
-              s_bin[buf] = b0;
-              s_wgt[buf] = gt0;
+              s_bin[buf & 1] = b0;
+              s_wgt[buf & 1] = gt0;
             }
           }
           __syncthreads();
-          const int bin = s_bin[buf];
-          T -= s_wgt[buf];
+          const int bin = s_bin[buf & 1];
+          T -= s_wgt[buf & 1];
           prefix |= (uint32_t)bin << sh;
           hi_mask |= (uint32_t)(nb - 1) << sh;
           if (sh == 0) {
@@ -268,7 +273,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             w_tau = c ? wgt[bin] / c : 1ull;   // every page with key tau has one weight
           }
           lo = sh;
-          buf ^= 1;
+          if constexpr (kHistBufs == 2) {
+            buf ^= 1;
+          } else {
+            __syncthreads();                  // single buffer: wait before it is cleared
+          }
         }
         tau = prefix;
       }
@@ -288,9 +297,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     uint32_t tot_packed;
     const uint32_t ex = block_excl_scan<uint32_t, kSelThreads>(packed, scan32, tot_packed);
+    // every thread has its keys in registers by now: reuse keys_lds for the list
     uint32_t gtb = ex >> 16, tb = ex & 0xFFFFu;
-    int32_t* lp = sel_pages + (int64_t)u * max_pages;
-    int32_t* lx = sel_phys + (int64_t)u * max_pages;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       if (pbase + i >= n) continue;
@@ -302,13 +310,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if ((unsigned long long)tb < need) pos = (int)(gtb + tb);
         ++tb;
       }
-      if (pos >= 0) {
-        lp[pos] = pbase + i;
-        if constexpr (kPrefetchPhys) lx[pos] = phys[i];
-        else lx[pos] = pt[pbase + i];
-      }
+      if (pos >= 0) keys_lds[pos] = (uint32_t)(pbase + i);
     }
     count = (int)((tot_packed >> 16) + min((unsigned long long)(tot_packed & 0xFFFFu), need));
+    __syncthreads();
+    int32_t* lp = sel_pages + (int64_t)u * max_pages;
+    int32_t* lx = sel_phys + (int64_t)u * max_pages;
+    const int32_t* pt = page_table + (int64_t)b * max_pages;
+    for (int i = tid; i < count; i += kSelThreads) {
+      const int p = (int)keys_lds[i];
+      lp[i] = p;
+      lx[i] = pt[p];
+    }
   }
 
   // ---- 5. last workgroup: prefix sums over units --------------------------
