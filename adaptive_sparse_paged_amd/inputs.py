@@ -316,3 +316,55 @@ def unit_host(w, layer, b, h, L, seed=0):
     v = unit_kv_bits(w, layer, b, h, n, 1, seed=seed).numpy()
     q = unit_query_bits(w, layer, b, h, L, seed).numpy()
     return k, v, q, valid_tokens(L)
+
+
+# ----------------------------------------------------------------------------
+# Host-resident KV tier: host pool and drifting page lists
+# ----------------------------------------------------------------------------
+
+def drift_lists(w, n_pages, list_pages, steps, drift, seed=0):
+    """Synthetic page lists for the host-tier workload: per (request, KV head)
+    a list of `list_pages` distinct logical pages; each step replaces
+    round(drift * list_pages) of them, chosen uniformly, with pages drawn
+    uniformly from those not in the list.  Returns int32
+    [steps][B][Hkv][list_pages], each list ascending."""
+    B, H = w.batch, w.kv_heads
+    out = np.empty((steps, B, H, list_pages), dtype=np.int32)
+    k = int(round(drift * list_pages))
+    for b in range(B):
+        for h in range(H):
+            r = _rng(w, 5, b, h, seed=seed)
+            cur = r.choice(n_pages, size=list_pages, replace=False)
+            for t in range(steps):
+                out[t, b, h] = np.sort(cur)
+                drop = r.choice(list_pages, size=k, replace=False)
+                keep = np.delete(cur, drop)
+                pool = np.setdiff1d(np.arange(n_pages), cur)
+                cur = np.concatenate([keep, r.choice(pool, size=k, replace=False)])
+    return out
+
+
+def build_host_pool(w, layer=0, seed=0, lens=None, device="cuda"):
+    """The full KV history in pinned host memory, layout
+    [B][max_pages][Hkv][2][P*D] (K tile token-major, then V tile
+    channel-major), generated on `device` one request at a time."""
+    if lens is None:
+        lens = context_lengths(w, seed)
+    max_pages = int(max(pages_of(L) for L in lens))
+    H = w.kv_heads
+    host = torch.empty((w.batch, max_pages, H, 2, PAGE * HEAD_DIM), dtype=torch.int16,
+                       pin_memory=True)
+    for b in range(w.batch):
+        n = pages_of(lens[b])
+        dev = torch.zeros((max_pages, H, 2, PAGE * HEAD_DIM), dtype=torch.int16, device=device)
+        for h in range(H):
+            if n == 0:
+                continue
+            k = unit_kv_bits(w, layer, b, h, n, 0, device=device, seed=seed)
+            v = unit_kv_bits(w, layer, b, h, n, 1, device=device, seed=seed)
+            dev[:n, h, 0] = k.reshape(n, PAGE * HEAD_DIM)
+            dev[:n, h, 1] = v.transpose(1, 2).reshape(n, PAGE * HEAD_DIM)
+            del k, v
+        host[b].copy_(dev)
+        del dev
+    return host, max_pages

@@ -26,6 +26,8 @@ EXPORTS = (
     "sparse_decode_max_parts",
     "sparse_decode_attn",
     "sparse_merge_splits",
+    "sparse_cache_workspace_bytes",
+    "sparse_hbm_cache_resolve",
 )
 
 
@@ -68,6 +70,9 @@ _SIGS = {
     "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _F, _I32,
                                   _P, _P, _I64, _P]),
     "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
+    "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -167,3 +172,20 @@ def merge_splits(dims, part_o, part_lse, sel_counts, chunk_offsets, chunk_pages,
     _check("sparse_merge_splits", load().sparse_merge_splits(
         ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), _ptr(chunk_offsets),
         chunk_pages, _ptr(out), _ptr(out_lse), _stream(stream)))
+
+
+def cache_workspace_bytes(dims, capacity):
+    return int(load().sparse_cache_workspace_bytes(ctypes.byref(dims), capacity))
+
+
+def hbm_cache_resolve(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity, slot_tag,
+                      slot_stamp, unit_slot, step, sel_phys, stats, ws, stream=None):
+    """host_kv must be pinned host memory (torch pin_memory) addressable by the GPU."""
+    _dev(sel_counts, sel_pages, cache_kv, slot_tag, slot_stamp, unit_slot, sel_phys, stats, ws)
+    if not host_kv.is_pinned():
+        raise ValueError("host_kv must be pinned host memory")
+    nbytes = ws.numel() * ws.element_size()
+    _check("sparse_hbm_cache_resolve", load().sparse_hbm_cache_resolve(
+        ctypes.byref(dims), _ptr(sel_counts), _ptr(sel_pages), _ptr(host_kv), _ptr(cache_kv),
+        capacity, _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), step, _ptr(sel_phys),
+        _ptr(stats), _ptr(ws), nbytes, _stream(stream)))

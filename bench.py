@@ -116,12 +116,139 @@ def cpu_baseline(w, lens, gamma, budget_s):
                       f"{spent:.1f} s of fp64 NumPy on one host thread, scaled to one layer"}
 
 
+def host_tier_bench(args):
+    """Host-resident KV tier: 16 requests x 524288 tokens of bf16 KV in pinned
+    host memory (32 GiB), a 4096-slot HBM cache per request, page lists of 448
+    pages per (request, KV head) drifting 10% per step over 64 steps.  Per step:
+    resolve (hits, LRU, device-initiated fetch of misses) + attention + merge,
+    each step timed with HIP events.  Also: the same step with every access a
+    hit (no host IO) against attention + merge alone, and the pinned
+    host-to-device copy rate of the link for reference."""
+    import torch
+    from adaptive_sparse_paged_amd import inputs as I
+    from adaptive_sparse_paged_amd import lib
+    from adaptive_sparse_paged_amd.host_tier import HbmPageCache
+    from adaptive_sparse_paged_amd.step import SparseDecodeStep
+
+    lib.load()
+    w = I.WORKLOADS["host_tier_512k"]
+    ex = w.extra
+    lens = I.context_lengths(w)
+    t0 = time.time()
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    print(f"# host pool {host.numel() * 2 / 2**30:.0f} GiB pinned ({time.time() - t0:.0f} s)",
+          file=sys.stderr, flush=True)
+    steps, LP, C = ex["steps"], ex["list_pages"], ex["capacity"]
+    lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"])
+    B, H = w.batch, w.kv_heads
+    U = B * H
+    dims = lib.make_dims(B, w.q_heads, H, MP)
+    cache = HbmPageCache(dims, host, C)
+    chunk = min(args.chunk, LP)
+    st = SparseDecodeStep(dims, args.gamma, chunk, scale=w.scale)
+    q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
+    for b in range(B):
+        for h in range(H):
+            q[b, h * w.group:(h + 1) * w.group] = I.unit_query_bits(w, 0, b, h, int(lens[b]))
+    q = q.cuda()
+    ctx = torch.from_numpy(lens.astype(np.int32)).cuda()
+    lists_dev = torch.from_numpy(lists.reshape(steps, U, LP)).cuda()
+    st.buf.sel_counts.fill_(LP)
+    nch = -(-LP // chunk)
+    st.buf.chunk_offsets.copy_(torch.arange(U + 1, dtype=torch.int32) * nch)
+    st.buf.sel_offsets.copy_(torch.arange(U + 1, dtype=torch.int32) * LP)
+    kv, s_page, s_head, ppages = cache.pool_args()
+
+    def run_step(t, marks=None):
+        st.buf.sel_pages[:, :LP].copy_(lists_dev[t])
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, t, st.buf.sel_phys)
+        e[1].record()
+        st.attend(q, kv, s_page, s_head, ppages, ctx)
+        e[2].record()
+        if marks is not None:
+            marks.append(e)
+
+    marks, stats = [], []
+    for t in range(steps):
+        run_step(t, marks)
+        stats.append(cache.stats.clone())
+    torch.cuda.synchronize()
+    res_us = np.array([m[0].elapsed_time(m[1]) * 1e3 for m in marks])
+    att_us = np.array([m[1].elapsed_time(m[2]) * 1e3 for m in marks])
+    st_np = np.stack([s.cpu().numpy() for s in stats])          # [steps][B][4]
+    hits, misses = st_np[:, :, 0].sum(1), st_np[:, :, 1].sum(1)
+    overflow = int(st_np[:, :, 3].max())
+    unit_bytes = 2 * 16 * 128 * 2
+    h2d = misses[1:] * unit_bytes / (res_us[1:] * 1e-6) / 1e9
+    # all-hit step (no host IO): the last list again, after it is resident
+    t_last = steps - 1
+    allhit = []
+    for k in range(args.steps):
+        m = []
+        run_step(t_last, m)
+        allhit.append(m[0])
+    torch.cuda.synchronize()
+    allhit_res = np.array([m[0].elapsed_time(m[1]) * 1e3 for m in allhit])
+    allhit_att = np.array([m[1].elapsed_time(m[2]) * 1e3 for m in allhit])
+    assert int(cache.stats[:, 1].sum().item()) == 0
+    # the link: pinned host -> device copy of 1 GiB
+    src = host.view(-1)[: 512 * 1024 * 1024]
+    dst = torch.empty(src.shape, dtype=src.dtype, device="cuda")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    dst.copy_(src, non_blocking=True)
+    c1.record()
+    torch.cuda.synchronize()
+    link = src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    step_us = res_us[1:] + att_us[1:]
+    kept_bytes = U * LP * unit_bytes
+    result = {
+        "metric": "host-tier sparse decode step us (resolve + attention + merge), 4096-slot HBM cache",
+        "value": round(float(np.median(step_us)), 1),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps - 1,
+        "warmup": 1,
+        "ms_per_step": round(float(np.median(step_us)) / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "ctx": int(lens.max()), "kv_heads": H,
+                   "q_heads": w.q_heads, "capacity_slots": C, "list_pages": LP,
+                   "drift": ex["drift"], "chunk_pages": chunk},
+        "cold_step_us": round(float(res_us[0] + att_us[0]), 1),
+        "resolve_fetch_us_median": round(float(np.median(res_us[1:])), 1),
+        "attention_merge_us_median": round(float(np.median(att_us[1:])), 1),
+        "hit_rate_steady": round(float(hits[1:].sum() / (hits[1:].sum() + misses[1:].sum())), 4),
+        "misses_per_step_median": int(np.median(misses[1:])),
+        "h2d_gbs_median": round(float(np.median(h2d)), 1),
+        "pinned_copy_gbs": round(link, 1),
+        "h2d_frac_of_link": round(float(np.median(h2d)) / link, 3),
+        "attention_hbm_gbs": round(kept_bytes / (float(np.median(att_us[1:])) * 1e-6) / 1e9, 1),
+        "overflow": overflow,
+        "no_io": {"resolve_us": round(float(np.median(allhit_res)), 1),
+                  "attention_merge_us": round(float(np.median(allhit_att)), 1),
+                  "resolve_share": round(float(np.median(allhit_res) /
+                                               (np.median(allhit_res) + np.median(allhit_att))), 4)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "host_tier_512k":
+        host_tier_bench(args)
+        return
     import torch
     from adaptive_sparse_paged_amd import inputs as I
     from adaptive_sparse_paged_amd import lib

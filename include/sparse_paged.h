@@ -206,6 +206,55 @@ sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                   const int32_t* chunk_offsets, int32_t chunk_pages, float* out,
                                   float* out_lse, void* stream);
 
+/* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
+ * list of placed misses handed from the resolve kernel to the fetch kernel. */
+size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
+
+/*
+ * sparse_hbm_cache_resolve -- host-resident KV tier behind a fixed-size HBM
+ * page cache, resolved on the device inside the step ([P2], abstract: full KV
+ * history in host memory, a small fixed-size GPU cache per request, and one
+ * in-graph resolver doing hit detection, LRU replacement and host-to-device
+ * fetch; only placement changes, so attention outputs are unchanged).
+ *
+ * Cache unit = (logical page p, KV head h) of request b, unit id
+ * v = h * max_pages + p.  Per request, the requested set R is the union of the
+ * request's KV-head lists (sel_pages / sel_counts, as written by
+ * sparse_select_coverage or supplied by the caller).  Units of R already
+ * resident are hits (their stamp becomes `step`).  Misses, in ascending unit
+ * id, take slots in ascending slot index from the available set: the lowest
+ * free slots if they suffice, else every free slot plus the
+ * r = misses - free least recently used resident units outside R, ordered by
+ * (stamp, unit id) -- exact LRU with ties to the lower unit id.  Each placed
+ * miss is copied (8 KiB: K tile then channel-major V tile) from host_kv into
+ * its slot by device-initiated reads of pinned host memory.  Misses that find
+ * no slot get sel_phys = -1 and set the overflow flag (attention treats them
+ * as empty pages; the step's outputs are then not meaningful).
+ *
+ *   host_kv    bf16 [B][max_pages][Hkv][2][2048], pinned host memory the
+ *              device can address (hipHostMalloc / torch pin_memory)
+ *   cache_kv   bf16 [B * capacity][2][2048] device; attend it with
+ *              sparse_decode_attn(kv = cache_kv, stride_page = 4096,
+ *              stride_head = 0, pool_pages = B * capacity, sel_phys)
+ *   slot_tag   int32 [B][capacity]  unit id held by each slot, -1 = free
+ *   slot_stamp int32 [B][capacity]  step of last use (-1 when free)
+ *   unit_slot  int32 [B][Hkv * max_pages]  slot of each unit, -1 = not resident
+ *              (the caller initialises tags/stamps/unit_slot to -1 once; the
+ *              library keeps them consistent afterwards)
+ *   step       >= 0, increasing from call to call
+ *   sel_phys   int32 [U][max_pages] out: global slot id b * capacity + slot
+ *   stats      int32 [B][4] out: hits, misses, evictions, overflow flag
+ *   capacity   slots per request, 1..8192; num_kv_heads <= 64
+ * Enqueues two kernels (resolve: one workgroup per request; fetch).  Calls
+ * sharing cache state or a workspace must not overlap in time.
+ */
+sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* sel_counts,
+                                       const int32_t* sel_pages, const uint16_t* host_kv,
+                                       uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
+                                       int32_t* slot_stamp, int32_t* unit_slot, int32_t step,
+                                       int32_t* sel_phys, int32_t* stats, void* ws,
+                                       size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

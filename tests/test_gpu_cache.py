@@ -1,0 +1,128 @@
+"""GPU parity of the host-tier cache resolver against the oracle's LRU model:
+slot tags, stamps, unit map, statistics and slot ids exact at every step;
+every resident slot holds its unit's bytes exactly; attention read through the
+cache is bit-identical to attention over the HBM pool (placement only)."""
+
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from adaptive_sparse_paged_amd import inputs as I
+from adaptive_sparse_paged_amd import lib
+from adaptive_sparse_paged_amd.host_tier import HbmPageCache
+from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides
+
+from _gpu_case import feed_lists, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=None):
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    assert MP == li.max_pages
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
+    cache = HbmPageCache(dims, host, C)
+    n_pages = min(I.pages_of(L) for L in lens)
+    if lists is None:
+        lists = I.drift_lists(w, n_pages, list_pages, steps, drift)
+    B, H = w.batch, w.kv_heads
+    states = [O.LRUState(C, H * MP) for _ in range(B)]
+    st = SparseDecodeStep(dims, 0.99, chunk, scale=w.scale)
+    layer = types.SimpleNamespace(w=w, dims=dims, li=li)
+    sp_, sh_ = canonical_strides(H)
+    out_stats = []
+    for t in range(lists.shape[0]):
+        feed_lists(st, layer, {b * H + h: lists[t, b, h] for b in range(B) for h in range(H)})
+        phys_hbm = st.buf.sel_phys.clone()
+        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, t, st.buf.sel_phys)
+        torch.cuda.synchronize()
+        tags = cache.slot_tag.cpu().numpy()
+        stamps = cache.slot_stamp.cpu().numpy()
+        umap = cache.unit_slot.cpu().numpy()
+        stats = cache.stats.cpu().numpy()
+        phys = st.buf.sel_phys.cpu().numpy()
+        for b in range(B):
+            units = [h * MP + int(p) for h in range(H) for p in lists[t, b, h]]
+            r = O.resolve_step(states[b], units, t)
+            assert np.array_equal(tags[b], states[b].tag), (t, b, "tags")
+            assert np.array_equal(stamps[b], states[b].stamp), (t, b, "stamps")
+            assert np.array_equal(umap[b], states[b].slot_of), (t, b, "unit map")
+            assert stats[b].tolist() == [r["hits"], r["misses"], r["evictions"], r["overflow"]], (t, b)
+            for h in range(H):
+                u = b * H + h
+                k = len(lists[t, b, h])
+                want = [states[b].slot_of[h * MP + int(p)] for p in lists[t, b, h]]
+                want = [b * C + s if s >= 0 else -1 for s in want]
+                assert phys[u, :k].tolist() == want, (t, b, h, "slot ids")
+            out_stats.append(r)
+        # resident slots hold their units' bytes
+        cache_kv = cache.cache_kv.view(B, C, -1)
+        for b in range(B):
+            res = np.nonzero(tags[b] >= 0)[0]
+            if not check_all_slots:
+                res = res[:: max(1, len(res) // 64)]
+            v = tags[b][res]
+            h, p = v // MP, v % MP
+            want = host[b, torch.from_numpy(p), torch.from_numpy(h)].reshape(len(res), -1)
+            got = cache_kv[b, torch.from_numpy(res).cuda()].cpu()
+            assert torch.equal(got, want), (t, b, "slot contents")
+        # attention through the cache is bit-identical to attention over HBM
+        if not any(r["overflow"] for r in out_stats[-B:]):
+            kv, s_page, s_head, ppages = cache.pool_args()
+            oc, lc = st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)
+            oc, lc = oc.clone(), lc.clone()
+            oh, lh = st.attend(li.q, li.kv_pool, sp_, sh_, li.pool_pages, li.ctx_lens,
+                               sel_phys=phys_hbm)
+            torch.cuda.synchronize()
+            assert torch.equal(oc, oh) and torch.equal(lc, lh), (t, "attention differs")
+    return out_stats
+
+
+def test_cache_resolver_small_drift(gpu_lib):
+    w = I.custom_workload("cache_small", 2, 8, 2, ("fixed", 3200), index=120)
+    say("[cache] small: B=2 Hkv=2 200 pages, 48 slots, lists of 20, drift 20%, 14 steps")
+    stats = _case(w, C=48, list_pages=20, steps=14, drift=0.2)
+    assert sum(r["evictions"] for r in stats) > 0
+    assert sum(r["hits"] for r in stats) > 0
+
+
+def test_cache_resolver_random_lists_and_ties(gpu_lib):
+    """Lists of varying length that jump around, so LRU ties at equal stamps
+    are broken by unit id, and some steps leave slots free."""
+    w = I.custom_workload("cache_jump", 3, 12, 3, ("fixed", 1600), index=121)
+    rng = np.random.default_rng(3)
+    steps, H, n = 10, 3, 100
+    L = 12
+    lists = np.zeros((steps, 3, H, L), dtype=np.int32)
+    for t in range(steps):
+        for b in range(3):
+            for h in range(H):
+                lists[t, b, h] = np.sort(rng.choice(n if t % 3 else 30, size=L, replace=False))
+    say("[cache] jumping lists, 3 requests x 3 KV heads, 40 slots")
+    stats = _case(w, C=40, list_pages=L, steps=steps, drift=0.0, chunk=5, lists=lists)
+    assert sum(r["evictions"] for r in stats) > 0
+
+
+def test_cache_overflow_flagged(gpu_lib):
+    w = I.custom_workload("cache_ovf", 2, 8, 2, ("fixed", 1600), index=122)
+    say("[cache] overflow: 2 heads x 20 pages into 30 slots")
+    stats = _case(w, C=30, list_pages=20, steps=2, drift=0.1, chunk=4)
+    assert all(r["overflow"] == 1 for r in stats)
+
+
+@pytest.mark.timeout(300)
+def test_cache_resolver_host_tier_shape(gpu_lib):
+    """The host-tier workload's shape (524288-token contexts, 8 KV heads,
+    4096 slots, lists of 448 pages drifting 10%) for 2 requests and 4 steps."""
+    base = I.WORKLOADS["host_tier_512k"]
+    w = I.custom_workload("host_tier_2req", 2, 32, 8, base.ctx, alpha=base.alpha, index=4)
+    ex = base.extra
+    say("[cache] host-tier shape: 2 x 524288 tokens, 4096 slots, 448-page lists")
+    stats = _case(w, C=ex["capacity"], list_pages=ex["list_pages"], steps=4, drift=ex["drift"],
+                  chunk=128, check_all_slots=False)
+    assert stats[-1]["misses"] > 0 and stats[-1]["hits"] > 0
