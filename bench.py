@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only launch what the hardware-counter runs measure")
     return ap.parse_args()
 
 
@@ -240,12 +242,55 @@ def host_tier_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def pmc_probe(args):
+    """Launches for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE, then
+    WRITE_SIZE): a plain device copy of 1 GiB (known bytes, the calibration)
+    and the attention kernel on layer 0 of the workload, three times each."""
+    import torch
+    from adaptive_sparse_paged_amd import inputs as I
+    from adaptive_sparse_paged_amd import lib
+    from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides
+
+    lib.load()
+    w = I.WORKLOADS[args.workload]
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, li.max_pages)
+    sp_, sh_ = canonical_strides(w.kv_heads)
+    summ = torch.empty((li.pool_pages, w.kv_heads, 2, D), dtype=torch.int16, device="cuda")
+    lib.build_page_summaries(dims, li.kv_pool, sp_, sh_, li.pool_pages,
+                             torch.arange(li.pool_pages, dtype=torch.int32, device="cuda"),
+                             li.page_valid, summ)
+    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale)
+    st.score_select(li.q, summ, li.pool_pages, li.page_table, li.ctx_lens)
+    torch.cuda.synchronize()
+    c = st.buf.sel_counts.cpu().numpy()
+    tsel = kept_tokens(c, st.buf.sel_pages.cpu().numpy(), lens, w.kv_heads, li.max_pages)
+    ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, st.chunk_pages) for u in range(len(c)))
+    for _ in range(3):
+        lib.decode_attn(dims, li.q, li.kv_pool, sp_, sh_, li.pool_pages, li.ctx_lens,
+                        st.buf.sel_counts, st.buf.chunk_offsets, st.buf.sel_pages,
+                        st.buf.sel_phys, st.scale, st.chunk_pages, st.buf.part_o,
+                        st.buf.part_lse, st.max_parts)
+    src = torch.empty(512 * 1024 * 1024, dtype=torch.int16, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"attn_algorithmic_bytes_per_launch": int(ab),
+                      "calibration_copy_bytes_each_way": src.numel() * 2}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_probe:
+        pmc_probe(args)
+        return
     if args.workload == "host_tier_512k":
         host_tier_bench(args)
         return
