@@ -71,6 +71,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ int s_bin[2];
   __shared__ unsigned long long s_wgt[2];
   __shared__ int s_last;
+  __shared__ uint32_t s_ncand, s_tau, s_need;
+  __shared__ uint32_t cand_key[64], cand_page[64];
 
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const int u = blockIdx.x;
@@ -124,11 +126,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       }
     }
     __syncthreads();
-    if (tid < group) {
-      PairMS tot = {red_m[tid][0], red_s[tid][0]};
-      for (int w = 1; w < kSelWaves; ++w) tot = combine(tot, PairMS{red_m[tid][w], red_s[tid][w]});
-      red_m[tid][0] = tot.m;
-      red_s[tid][0] = 1.f / tot.s;
+    if (wv == 0) {
+      // lane l combines wave partial (l & 15) of head g0 + (l >> 4)
+      for (int g0 = 0; g0 < group; g0 += 4) {
+        const int g = g0 + (lane >> 4), w = lane & 15;
+        PairMS pr = (g < group) ? PairMS{red_m[g][w], red_s[g][w]} : PairMS{-INFINITY, 0.f};
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          PairMS other = {__shfl_xor(pr.m, o, 64), __shfl_xor(pr.s, o, 64)};
+          pr = combine(pr, other);
+        }
+        if (w == 0 && g < group) {
+          red_m[g][0] = pr.m;
+          red_s[g][0] = 1.f / pr.s;
+        }
+      }
     }
     __syncthreads();
 
@@ -224,6 +236,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         uint32_t hi_mask = ~((2u << top) - 1u);
         uint32_t prefix = KHI & hi_mask;
         int lo = top + 1, buf = 0;
+        bool resolved = false;
         while (lo > 0) {
           const int width = min(11, lo);
           const int sh = lo - width, nb = 1 << width;
@@ -233,6 +246,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             cnt[k] = 0u;
             wgt[k] = 0ull;
           }
+          if (tid == 0) s_ncand = 0u;
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
@@ -273,16 +287,68 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             w_tau = c ? wgt[bin] / c : 1ull;   // every page with key tau has one weight
           }
           lo = sh;
+          if (sh > 0 && cnt[bin] <= 64u) {
+            // Few pages share the resolved high bits: one wave sorts them by
+            // (key descending, page ascending) and walks their weights.
+            for (int i = 0; i < NPT; ++i) {
+              if (pbase + i < n && (key[i] & hi_mask) == prefix) {
+                const uint32_t at = atomicAdd(&s_ncand, 1u);
+                if (at < 64u) {
+                  cand_key[at] = key[i];
+                  cand_page[at] = (uint32_t)(pbase + i);
+                }
+              }
+            }
+            __syncthreads();
+            if (wv == 0) {
+              const uint32_t nc = s_ncand;
+              const bool ok = (uint32_t)lane < nc;
+              unsigned long long c =
+                  ok ? (((unsigned long long)(~cand_key[lane]) << 32) | cand_page[lane]) : ~0ull;
+#pragma unroll
+              for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+                for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                  const unsigned long long o =
+                      (unsigned long long)__shfl_xor((long long)c, jj, 64);
+                  const bool up = (lane & k) == 0, low = (lane & jj) == 0;
+                  c = (low == up) ? min(c, o) : max(c, o);
+                }
+              }
+              const uint32_t kk = ~(uint32_t)(c >> 32);
+              const unsigned long long wk = ok ? weight_of(kk) : 0ull;
+              const unsigned long long cum = wave_incl_scan(wk);
+              const unsigned long long reach = __ballot(ok && cum >= T);
+              const int at = __ffsll((long long)reach) - 1;     // first lane reaching T
+              const uint32_t t_key = (uint32_t)__shfl((int)kk, at, 64);
+              const unsigned long long eq = __ballot(ok && kk == t_key);
+              const int first_eq = __ffsll((long long)eq) - 1;
+              if (lane == 0) {
+                s_tau = t_key;
+                s_need = (uint32_t)(at - first_eq + 1);
+              }
+            }
+            __syncthreads();
+            resolved = true;
+            break;
+          }
           if constexpr (kHistBufs == 2) {
             buf ^= 1;
           } else {
             __syncthreads();                  // single buffer: wait before it is cleared
           }
         }
-        tau = prefix;
+        if (resolved) {
+          tau = s_tau;
+          need = s_need;
+        } else {
+          tau = prefix;
+        }
       }
-      if (w_tau == 0ull) w_tau = 1ull;
-      need = (T + w_tau - 1ull) / w_tau;    // pages at tau to keep (>= 1)
+      if (need == 0ull) {
+        if (w_tau == 0ull) w_tau = 1ull;
+        need = (T + w_tau - 1ull) / w_tau;  // pages at tau to keep (>= 1)
+      }
     }
 
     // ---- 4. compact in ascending page order: one scan of packed counts ----
@@ -341,15 +407,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t c = 0u;
     if (v < U) c = (uint32_t)__hip_atomic_load(sel_counts + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t ch = (c + (uint32_t)chunk_pages - 1u) / (uint32_t)chunk_pages;
-    uint32_t t1, t2;
-    const uint32_t e1 = block_excl_scan<uint32_t, kSelThreads>(c, scan32, t1);
-    const uint32_t e2 = block_excl_scan<uint32_t, kSelThreads>(ch, scan32, t2);
+    // both prefix sums in one scan: count in the high word, chunks in the low
+    unsigned long long tot;
+    const unsigned long long ex = block_excl_scan<unsigned long long, kSelThreads>(
+        ((unsigned long long)c << 32) | ch, scan64, tot);
     if (v < U) {
-      sel_offsets[v] = (int32_t)(run + e1);
-      chunk_offsets[v] = (int32_t)(runc + e2);
+      sel_offsets[v] = (int32_t)(run + (uint32_t)(ex >> 32));
+      chunk_offsets[v] = (int32_t)(runc + (uint32_t)ex);
     }
-    run += t1;
-    runc += t2;
+    run += (uint32_t)(tot >> 32);
+    runc += (uint32_t)tot;
   }
   if (tid == 0) {
     sel_offsets[U] = (int32_t)run;

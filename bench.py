@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--gamma", type=float, default=0.99)
     ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--groups", type=int, default=1,
+                    help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -323,7 +325,8 @@ def main():
     stride_page, stride_head = canonical_strides(w.kv_heads)
     max_pages = L_in[0].max_pages
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
-    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev)
+    groups = max(1, min(args.groups, w.batch))
+    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev, groups=groups)
     outs = [torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     lses = [torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev) for _ in range(layers)]
     counts = [torch.empty_like(st.buf.sel_counts) for _ in range(layers)]
@@ -421,7 +424,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": int(lens.max()),
                    "layers": layers, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": D, "page_size": PAGE, "gamma": args.gamma,
-                   "chunk_pages": st.chunk_pages},
+                   "chunk_pages": st.chunk_pages, "stream_groups": groups},
         "selected_fraction": round(kept / pages_all, 4),
         "bytes_per_step": int(total_bytes),
         "roofline": {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(attn_gbs, 1),

@@ -201,3 +201,32 @@ def test_deterministic(gpu_lib):
     layer.run(st)
     assert torch.equal(a[0], st.buf.out) and torch.equal(a[1], st.buf.sel_pages)
     assert torch.equal(a[2], st.buf.logits)
+
+
+def test_grouped_streams_match_single_stream(gpu_lib):
+    """Request groups on separate streams (selection of one group under the
+    attention of another) give bitwise the same lists and outputs, eagerly and
+    replayed from a captured graph."""
+    w = I.custom_workload("groups", 5, 8, 2, ("uniform", 300, 9000), alpha=("uniform", 1, 6),
+                          index=111)
+    say("[groups] 5 requests in 3 stream groups")
+    layer = GpuLayer(w)
+    li = layer.li
+    ref = layer.step(0.97, 16)
+    layer.run(ref)
+    grp = SparseDecodeStep(layer.dims, 0.97, 16, scale=w.scale, groups=3)
+    args = (li.q, layer.summ, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages,
+            li.page_table, li.ctx_lens)
+    grp.run(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(grp.buf.sel_counts, ref.buf.sel_counts)
+    for u in range(w.batch * w.kv_heads):
+        k = int(ref.buf.sel_counts[u])
+        assert torch.equal(grp.buf.sel_pages[u, :k], ref.buf.sel_pages[u, :k])
+    assert torch.equal(grp.buf.out, ref.buf.out) and torch.equal(grp.buf.out_lse, ref.buf.out_lse)
+    g = capture(lambda: grp.run(*args))
+    for _ in range(3):
+        grp.buf.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(grp.buf.out, ref.buf.out)
