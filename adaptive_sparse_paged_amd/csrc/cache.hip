@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scan32[kResThreads / 64];
+  __shared__ unsigned long long scan64[kResThreads / 64];
   __shared__ int32_t head_off[kMaxKvHeads + 1];
   __shared__ int s_bin;
   __shared__ uint32_t s_below;
@@ -67,36 +68,64 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   const int E = head_off[hkv];
 
   // ---- pass 1: hits (stamp, mark, slot id) and the number of misses ------
+  // Elements e = tid + 1024 k, up to 8 per thread per batch, loads issued
+  // together; only the totals are needed here (ranks come in pass 2).
   uint32_t M = 0u, H = 0u;
-  for (int base = 0; base < E; base += kResThreads) {
-    const int e = base + tid;
-    uint32_t miss = 0u, hit = 0u;
-    if (e < E) {
-      int h = 0;
-      while (e >= head_off[h + 1]) ++h;
-      const int i = e - head_off[h];
-      const int64_t li = (int64_t)(b * hkv + h) * max_pages + i;
-      const int p = sel_pages[li];
-      const int v = h * max_pages + p;
-      int s = (p >= 0 && p < max_pages) ? umap[v] : -2;
-      if (s >= C) s = -2;                  // corrupt state: never index past the cache
-      if (s >= 0) {
-        hit = 1u;
-        req[s] = 1;
-        stamps[s] = step;
-        sel_phys[li] = b * C + s;
-      } else if (s == -1) {
-        miss = 1u;
-      } else {
-        sel_phys[li] = -1;   // page id out of range: treated as an empty page
+  {
+    constexpr int kBatch = 8;
+    uint32_t m_local = 0u, h_local = 0u;
+    for (int base = 0; base < E; base += kBatch * kResThreads) {
+      int64_t li[kBatch];
+      int v[kBatch], s[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e = base + k * kResThreads + tid;
+        li[k] = -1;
+        v[k] = -1;
+        if (e < E) {
+          int h = 0;
+          while (e >= head_off[h + 1]) ++h;
+          li[k] = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
+          const int p = sel_pages[li[k]];
+          if (p >= 0 && p < max_pages) v[k] = h * max_pages + p;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) s[k] = (v[k] >= 0) ? umap[v[k]] : -2;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (li[k] < 0) continue;
+        int sk = s[k];
+        if (sk >= C) sk = -2;                // corrupt state: never index past the cache
+        if (sk >= 0) {
+          ++h_local;
+          req[sk] = 1;
+          stamps[sk] = step;
+          sel_phys[li[k]] = b * C + sk;
+        } else if (sk == -1) {
+          ++m_local;
+        } else {
+          sel_phys[li[k]] = -1;              // page id out of range: an empty page
+        }
       }
     }
-    uint32_t tot;
-    block_excl_scan<uint32_t, kResThreads>(miss | (hit << 16), scan32, tot);
-    M += tot & 0xFFFFu;
-    H += tot >> 16;
+    unsigned long long tot;
+    block_excl_scan<unsigned long long, kResThreads>(
+        ((unsigned long long)h_local << 32) | m_local, scan64, tot);
+    M = (uint32_t)tot;
+    H = (uint32_t)(tot >> 32);
   }
   // (block_excl_scan ends with a barrier: every req mark is visible here)
+  if (M == 0u) {                 // every requested unit is resident: nothing to place
+    if (tid == 0) {
+      stats[b * 4 + 0] = (int32_t)H;
+      stats[b * 4 + 1] = 0;
+      stats[b * 4 + 2] = 0;
+      stats[b * 4 + 3] = 0;
+      miss_count[b] = 0;
+    }
+    return;
+  }
 
   // ---- free slots and victim candidates ----------------------------------
   constexpr int kSPT = kMaxSlots / kResThreads;   // slots per thread, strided
