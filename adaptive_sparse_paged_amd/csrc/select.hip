@@ -26,6 +26,8 @@
 
 #include "common.h"
 
+extern "C" size_t sparse_select_workspace_bytes(const sparse_dims* dims);
+
 namespace sp {
 
 constexpr int kSelThreads = 1024;
@@ -40,6 +42,12 @@ __device__ __forceinline__ unsigned long long weight_of(uint32_t key) {
   return (unsigned long long)(__uint_as_float(key) * 4503599627370496.0f);
 }
 
+template <bool COUNT>
+__device__ __forceinline__ unsigned long long wgt_of(uint32_t key) {
+  if constexpr (COUNT) return 1ull;
+  else return weight_of(key);
+}
+
 __device__ __forceinline__ PairMS combine(PairMS a, PairMS b) {
   const float M = fmaxf(a.m, b.m);
   if (M == -INFINITY) return {M, 0.f};
@@ -48,10 +56,14 @@ __device__ __forceinline__ PairMS combine(PairMS a, PairMS b) {
   return {M, sa + sb};
 }
 
-template <int NPT>
+// COUNT = false: the coverage cut (page weight = its fixed-point mass, target
+// ceil(gamma * total)).  COUNT = true: the fixed-budget variant (page weight 1,
+// target min(k_pages, n)) -- the k highest-mass pages, ties to lower index.
+template <int NPT, bool COUNT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ page_table, float gamma, int chunk_pages, int hkv, int group,
+    const int32_t* __restrict__ page_table, float gamma, int k_pages, int chunk_pages, int hkv,
+    int group,
     int max_pages, int U, int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_offsets,
     int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       if (p < n) {
         const uint32_t key = __float_as_uint(m[k] * invg);
         keys_lds[p] = key;
-        zl += weight_of(key);
+        zl += wgt_of<COUNT>(key);
         klo = min(klo, key);
         khi = max(khi, key);
       }
@@ -220,14 +232,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int i = 0; i < NPT; ++i) key[i] = (pbase + i < n) ? keys_lds[pbase + i] : 0u;
 
     // ---- 3. the cut: key tau and the number of ties at tau to keep -------
-    const bool all = !(gamma < 1.0f);
+    const bool all = COUNT ? (k_pages >= n) : !(gamma < 1.0f);
     uint32_t tau = 0u;
     unsigned long long need = 0ull;
     if (!all) {
-      unsigned long long T = (unsigned long long)ceil((double)gamma * (double)Z);
+      unsigned long long T = COUNT ? (unsigned long long)k_pages
+                                   : (unsigned long long)ceil((double)gamma * (double)Z);
       if (T > Z) T = Z;
       if (T < 1ull) T = 1ull;
-      unsigned long long w_tau = weight_of(KHI);
+      unsigned long long w_tau = wgt_of<COUNT>(KHI);
       if (KLO == KHI) {
         tau = KHI;                          // every page has the same mass
       } else {
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             if (pbase + i < n && (key[i] & hi_mask) == prefix) {
               const int bin = (key[i] >> sh) & (nb - 1);
               atomicAdd(&cnt[bin], 1u);
-              atomicAdd(&wgt[bin], weight_of(key[i]));
+              atomicAdd(&wgt[bin], wgt_of<COUNT>(key[i]));
             }
           }
           __syncthreads();
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 }
               }
               const uint32_t kk = ~(uint32_t)(c >> 32);
-              const unsigned long long wk = ok ? weight_of(kk) : 0ull;
+              const unsigned long long wk = ok ? wgt_of<COUNT>(kk) : 0ull;
               const unsigned long long cum = wave_incl_scan(wk);
               const unsigned long long reach = __ballot(ok && cum >= T);
               const int at = __ffsll((long long)reach) - 1;     // first lane reaching T
@@ -425,16 +438,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
-template <int NPT>
+template <int NPT, bool COUNT>
 static void launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
-                          const int32_t* page_table, float gamma, int chunk_pages, int hkv,
-                          int group, int max_pages, int32_t* sel_counts, int32_t* sel_offsets,
-                          int32_t* chunk_offsets, int32_t* sel_pages, int32_t* sel_phys,
-                          uint32_t* ticket) {
-  hipLaunchKernelGGL(select_kernel<NPT>, dim3(U), dim3(kSelThreads), 0, st, logits, ctx_lens,
-                     page_table, gamma, chunk_pages, hkv, group, max_pages, U, sel_counts,
-                     sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket);
+                          const int32_t* page_table, float gamma, int k_pages, int chunk_pages,
+                          int hkv, int group, int max_pages, int32_t* sel_counts,
+                          int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
+                          int32_t* sel_phys, uint32_t* ticket) {
+  hipLaunchKernelGGL((select_kernel<NPT, COUNT>), dim3(U), dim3(kSelThreads), 0, st, logits,
+                     ctx_lens, page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, U,
+                     sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket);
 }
+
+template <bool COUNT>
+static sparse_status select_entry(const sparse_dims* dims, const float* logits,
+                                  const int32_t* ctx_lens, const int32_t* page_table, float gamma,
+                                  int k_pages, int32_t chunk_pages, int32_t* sel_counts,
+                                  int32_t* sel_offsets, int32_t* chunk_offsets,
+                                  int32_t* sel_pages, int32_t* sel_phys, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 }  // namespace sp
 
@@ -443,31 +464,32 @@ extern "C" size_t sparse_select_workspace_bytes(const sparse_dims* dims) {
   return 256;  // the finishing ticket (one 32-bit counter), padded
 }
 
-extern "C" sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
-                                                const int32_t* ctx_lens, const int32_t* page_table,
-                                                float gamma, int32_t chunk_pages,
-                                                int32_t* sel_counts, int32_t* sel_offsets,
-                                                int32_t* chunk_offsets, int32_t* sel_pages,
-                                                int32_t* sel_phys, void* ws, size_t ws_bytes,
-                                                void* stream) {
-  sparse_status st = sp::check_dims(dims);
+namespace sp {
+
+template <bool COUNT>
+static sparse_status select_entry(const sparse_dims* dims, const float* logits,
+                                  const int32_t* ctx_lens, const int32_t* page_table, float gamma,
+                                  int k_pages, int32_t chunk_pages, int32_t* sel_counts,
+                                  int32_t* sel_offsets, int32_t* chunk_offsets,
+                                  int32_t* sel_pages, int32_t* sel_phys, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  sparse_status st = check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!logits || !ctx_lens || !page_table || !sel_counts || !sel_offsets || !chunk_offsets ||
       !sel_pages || !sel_phys)
     return SPARSE_ERR_INVALID;
-  if (!(gamma > 0.0f && gamma <= 1.0f)) return SPARSE_ERR_INVALID;
   if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
-  if (!ws || ws_bytes < sparse_select_workspace_bytes(dims) || !sp::aligned(ws, 4))
+  if (!ws || ws_bytes < sparse_select_workspace_bytes(dims) || !aligned(ws, 4))
     return SPARSE_ERR_WORKSPACE;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  const int npt = (dims->max_pages + sp::kSelThreads - 1) / sp::kSelThreads;
+  const int npt = (dims->max_pages + kSelThreads - 1) / kSelThreads;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* ticket = static_cast<uint32_t*>(ws);
-#define SP_SEL(N)                                                                             \
-  sp::launch_select<N>(s, U, logits, ctx_lens, page_table, gamma, chunk_pages, hkv, group,   \
-                       dims->max_pages, sel_counts, sel_offsets, chunk_offsets, sel_pages,   \
-                       sel_phys, ticket)
+#define SP_SEL(N)                                                                           \
+  launch_select<N, COUNT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages, \
+                          hkv, group, dims->max_pages, sel_counts, sel_offsets,           \
+                          chunk_offsets, sel_pages, sel_phys, ticket)
   if (npt <= 1) SP_SEL(1);
   else if (npt <= 2) SP_SEL(2);
   else if (npt <= 4) SP_SEL(4);
@@ -475,5 +497,33 @@ extern "C" sparse_status sparse_select_coverage(const sparse_dims* dims, const f
   else if (npt <= 16) SP_SEL(16);
   else SP_SEL(32);
 #undef SP_SEL
-  return sp::launch_status();
+  return launch_status();
+}
+
+}  // namespace sp
+
+extern "C" sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
+                                                const int32_t* ctx_lens, const int32_t* page_table,
+                                                float gamma, int32_t chunk_pages,
+                                                int32_t* sel_counts, int32_t* sel_offsets,
+                                                int32_t* chunk_offsets, int32_t* sel_pages,
+                                                int32_t* sel_phys, void* ws, size_t ws_bytes,
+                                                void* stream) {
+  if (!(gamma > 0.0f && gamma <= 1.0f)) return SPARSE_ERR_INVALID;
+  return sp::select_entry<false>(dims, logits, ctx_lens, page_table, gamma, 0, chunk_pages,
+                                 sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ws,
+                                 ws_bytes, stream);
+}
+
+extern "C" sparse_status sparse_select_topk(const sparse_dims* dims, const float* logits,
+                                            const int32_t* ctx_lens, const int32_t* page_table,
+                                            int32_t k_pages, int32_t chunk_pages,
+                                            int32_t* sel_counts, int32_t* sel_offsets,
+                                            int32_t* chunk_offsets, int32_t* sel_pages,
+                                            int32_t* sel_phys, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  if (k_pages < 1) return SPARSE_ERR_INVALID;
+  return sp::select_entry<true>(dims, logits, ctx_lens, page_table, 1.0f, k_pages, chunk_pages,
+                                sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ws,
+                                ws_bytes, stream);
 }

@@ -28,6 +28,8 @@ EXPORTS = (
     "sparse_merge_splits",
     "sparse_cache_workspace_bytes",
     "sparse_hbm_cache_resolve",
+    "sparse_select_topk",
+    "sparse_append_tokens",
 )
 
 
@@ -71,6 +73,9 @@ _SIGS = {
                                   _P, _P, _I64, _P]),
     "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
+    "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+    "sparse_append_tokens": (_I32, [_D, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
 }
@@ -189,3 +194,22 @@ def hbm_cache_resolve(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity, 
         ctypes.byref(dims), _ptr(sel_counts), _ptr(sel_pages), _ptr(host_kv), _ptr(cache_kv),
         capacity, _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), step, _ptr(sel_phys),
         _ptr(stats), _ptr(ws), nbytes, _stream(stream)))
+
+
+def select_topk(dims, logits, ctx_lens, page_table, k_pages, chunk_pages, sel_counts,
+                sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
+    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
+         sel_phys, ws)
+    nbytes = ws.numel() * ws.element_size()
+    _check("sparse_select_topk", load().sparse_select_topk(
+        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), k_pages, chunk_pages,
+        _ptr(sel_counts), _ptr(sel_offsets), _ptr(chunk_offsets), _ptr(sel_pages),
+        _ptr(sel_phys), _ptr(ws), nbytes, _stream(stream)))
+
+
+def append_tokens(dims, k_new, v_new, kv, stride_page, stride_head, pool_pages, page_table,
+                  ctx_lens, summ, stream=None):
+    _dev(k_new, v_new, kv, page_table, ctx_lens, summ)
+    _check("sparse_append_tokens", load().sparse_append_tokens(
+        ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(kv), stride_page, stride_head,
+        pool_pages, _ptr(page_table), _ptr(ctx_lens), _ptr(summ), _stream(stream)))

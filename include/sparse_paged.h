@@ -162,6 +162,39 @@ sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logit
                                      int32_t* sel_pages, int32_t* sel_phys, void* ws,
                                      size_t ws_bytes, void* stream);
 
+/*
+ * sparse_select_topk -- the fixed-budget selection the coverage rule is
+ * argued against ([P1], abstract, sentence on fixed budgets): per unit keep
+ * the min(k_pages, n_b) pages of highest group mass m (m as in
+ * sparse_select_coverage), ties to the lower page index.  Same outputs,
+ * workspace and prefix sums as sparse_select_coverage.  k_pages >= 1.
+ */
+sparse_status sparse_select_topk(const sparse_dims* dims, const float* logits,
+                                 const int32_t* ctx_lens, const int32_t* page_table,
+                                 int32_t k_pages, int32_t chunk_pages, int32_t* sel_counts,
+                                 int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
+                                 int32_t* sel_phys, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_append_tokens -- decode-time append of each request's new token,
+ * with the refresh of its page's summary (so the step's own token is scored
+ * like every other).  For request b with L_b = ctx_lens[b] tokens, the token
+ * goes to logical page p = L_b / 16, slot t = L_b % 16, of physical page
+ * x = page_table[b][p] (allocated by the caller): row t of the K tile and
+ * column t of the channel-major V tile, for every KV head.  The summary of
+ * (x, h) becomes k itself when t = 0, else its per-channel min / max with k
+ * (the total order of sparse_build_page_summaries: bit-exact with a rebuild
+ * over the first t + 1 tokens).  ctx_lens[b] then advances by one.  A request
+ * whose page is missing (p >= max_pages or x outside [0, pool_pages)) is left
+ * untouched and its length is not advanced.
+ *   k_new, v_new  bf16 [B][Hkv][128]
+ */
+sparse_status sparse_append_tokens(const sparse_dims* dims, const uint16_t* k_new,
+                                   const uint16_t* v_new, uint16_t* kv, int64_t stride_page,
+                                   int64_t stride_head, int64_t pool_pages,
+                                   const int32_t* page_table, int32_t* ctx_lens, uint16_t* summ,
+                                   void* stream);
+
 /* Upper bound on the number of chunks (= partial slots) of one step (host):
  * U * ceil(max_pages / chunk_pages). */
 int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);

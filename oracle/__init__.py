@@ -29,6 +29,7 @@ from .sparse_oracle import (  # noqa: F401
     head_mass,
     group_mass,
     coverage_cut,
+    topk_cut,
     select_unit,
     attend_tokens,
     attend_pages,

@@ -191,6 +191,18 @@ def coverage_cut(m, gamma):
     return np.sort(order[:k]), k, order, S
 
 
+def topk_cut(m, k):
+    """Fixed-budget selection (the baseline the coverage rule replaces,
+    [P1, abstract, sentence on fixed budgets]): the min(k, n) pages of highest
+    mass, ties to the lower page index, emitted ascending."""
+    m = np.asarray(m, dtype=np.float64)
+    n = m.shape[0]
+    if k < 1:
+        raise ValueError("k >= 1")
+    order = np.lexsort((np.arange(n), -m))
+    return np.sort(order[:min(k, n)])
+
+
 def select_unit(q_bits, kmin_bits, kmax_bits, n_valid, scale, gamma):
     """Score, mass and cut for one (request, KV head) unit.
 

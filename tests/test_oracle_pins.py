@@ -360,3 +360,18 @@ def test_lru_overflow_flagged():
     assert sum(1 for _, s in r["placed"] if s < 0) == 4
     with pytest.raises(OverflowError):
         O.textbook_lru_trace(8, [range(12)])
+
+
+def test_topk_brute_force_and_agrees_with_coverage():
+    for n in (1, 4, 9):
+        m = RNG.dirichlet(np.ones(n))
+        if n > 2:
+            m[0] = m[2]                      # a tie: lower index first
+        for k in range(1, n + 2):
+            got = O.topk_cut(m, k).tolist()
+            best = sorted(range(n), key=lambda p: (-m[p], p))[:min(k, n)]
+            assert got == sorted(best)
+    m = RNG.dirichlet(np.full(500, 0.3))
+    for gamma in (0.5, 0.9, 0.99):
+        lst, k, _, _ = O.coverage_cut(m, gamma)
+        assert O.topk_cut(m, k).tolist() == lst.tolist()
