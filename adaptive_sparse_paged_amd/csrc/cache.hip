@@ -36,7 +36,7 @@ struct MissRec {
 
 __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
-    int max_pages, int C, int step, int32_t* __restrict__ slot_tag,
+    int max_pages, int C, const int32_t* __restrict__ step_counter, int32_t* __restrict__ slot_tag,
     int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
     int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats, MissRec* __restrict__ misses,
     int32_t* __restrict__ miss_count) {
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  const int step = *step_counter;
   int32_t* tags = slot_tag + (int64_t)b * C;
   int32_t* stamps = slot_stamp + (int64_t)b * C;
   int32_t* umap = unit_slot + (int64_t)b * hkv * max_pages;
@@ -309,8 +310,12 @@ __global__ __launch_bounds__(256) void fetch_kernel(const uint16_t* __restrict__
                                                     int max_pages, int C,
                                                     const MissRec* __restrict__ misses,
                                                     const int32_t* __restrict__ miss_count,
-                                                    int waves_per_req) {
+                                                    int waves_per_req,
+                                                    int32_t* __restrict__ step_counter) {
   const int b = blockIdx.y;
+  // every resolve workgroup has read the step (the resolve kernel ran first on
+  // this stream): advance it for the next call
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *step_counter += 1;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   const int cnt = miss_count[b];
@@ -338,14 +343,14 @@ extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t 
 extern "C" sparse_status sparse_hbm_cache_resolve(
     const sparse_dims* dims, const int32_t* sel_counts, const int32_t* sel_pages,
     const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
-    int32_t* slot_stamp, int32_t* unit_slot, int32_t step, int32_t* sel_phys, int32_t* stats,
-    void* ws, size_t ws_bytes, void* stream) {
+    int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter, int32_t* sel_phys,
+    int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!sel_counts || !sel_pages || !host_kv || !cache_kv || !slot_tag || !slot_stamp ||
-      !unit_slot || !sel_phys || !stats)
+      !unit_slot || !step_counter || !sel_phys || !stats)
     return SPARSE_ERR_INVALID;
-  if (capacity < 1 || step < 0) return SPARSE_ERR_INVALID;
+  if (capacity < 1) return SPARSE_ERR_INVALID;
   if (capacity > sp::kMaxSlots || dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
   if (!sp::aligned(host_kv, 16) || !sp::aligned(cache_kv, 16)) return SPARSE_ERR_INVALID;
   if (!ws || ws_bytes < sparse_cache_workspace_bytes(dims, capacity) || !sp::aligned(ws, 8))
@@ -355,12 +360,12 @@ extern "C" sparse_status sparse_hbm_cache_resolve(
   int32_t* miss_count = reinterpret_cast<int32_t*>(misses + (size_t)B * capacity);
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(sp::resolve_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
-                     sel_pages, hkv, dims->max_pages, capacity, step, slot_tag, slot_stamp,
+                     sel_pages, hkv, dims->max_pages, capacity, step_counter, slot_tag, slot_stamp,
                      unit_slot, sel_phys, stats, misses, miss_count);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   const int waves_per_req = 256;   // 64 workgroups of 4 waves per request
   hipLaunchKernelGGL(sp::fetch_kernel, dim3(waves_per_req / 4, B), dim3(256), 0, s, host_kv,
                      cache_kv, hkv, dims->max_pages, capacity, misses, miss_count,
-                     waves_per_req);
+                     waves_per_req, step_counter);
   return sp::launch_status();
 }

@@ -45,13 +45,16 @@ class HbmPageCache:
         self.slot_stamp = torch.full((B, capacity), -1, **i32)
         self.unit_slot = torch.full((B, H * MP), -1, **i32)
         self.stats = torch.zeros((B, 4), **i32)
+        self.step_counter = torch.zeros(1, **i32)
         self.ws = torch.zeros(lib.cache_workspace_bytes(dims, capacity), dtype=torch.uint8,
                               device=device)
 
-    def resolve(self, sel_counts, sel_pages, step, sel_phys, stream=None):
+    def resolve(self, sel_counts, sel_pages, sel_phys, stream=None):
+        """Resolve one step's lists; the step number comes from (and advances)
+        the device counter, so this can be captured and replayed."""
         lib.hbm_cache_resolve(self.dims, sel_counts, sel_pages, self.host_kv, self.cache_kv,
                               self.capacity, self.slot_tag, self.slot_stamp, self.unit_slot,
-                              int(step), sel_phys, self.stats, self.ws, stream)
+                              self.step_counter, sel_phys, self.stats, self.ws, stream)
 
     def pool_args(self):
         """(kv, stride_page, stride_head, pool_pages) for sparse_decode_attn."""

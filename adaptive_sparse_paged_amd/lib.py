@@ -76,7 +76,7 @@ _SIGS = {
     "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     "sparse_append_tokens": (_I32, [_D, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
-    "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P, _P,
+    "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
 }
 
@@ -184,15 +184,18 @@ def cache_workspace_bytes(dims, capacity):
 
 
 def hbm_cache_resolve(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity, slot_tag,
-                      slot_stamp, unit_slot, step, sel_phys, stats, ws, stream=None):
-    """host_kv must be pinned host memory (torch pin_memory) addressable by the GPU."""
-    _dev(sel_counts, sel_pages, cache_kv, slot_tag, slot_stamp, unit_slot, sel_phys, stats, ws)
+                      slot_stamp, unit_slot, step_counter, sel_phys, stats, ws, stream=None):
+    """host_kv must be pinned host memory (torch pin_memory) addressable by the GPU;
+    step_counter is a 1-element int32 device tensor the call reads and advances."""
+    _dev(sel_counts, sel_pages, cache_kv, slot_tag, slot_stamp, unit_slot, step_counter,
+         sel_phys, stats, ws)
     if not host_kv.is_pinned():
         raise ValueError("host_kv must be pinned host memory")
     nbytes = ws.numel() * ws.element_size()
     _check("sparse_hbm_cache_resolve", load().sparse_hbm_cache_resolve(
         ctypes.byref(dims), _ptr(sel_counts), _ptr(sel_pages), _ptr(host_kv), _ptr(cache_kv),
-        capacity, _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), step, _ptr(sel_phys),
+        capacity, _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), _ptr(step_counter),
+        _ptr(sel_phys),
         _ptr(stats), _ptr(ws), nbytes, _stream(stream)))
 
 

@@ -167,7 +167,7 @@ def host_tier_bench(args):
         st.buf.sel_pages[:, :LP].copy_(lists_dev[t])
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
-        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, t, st.buf.sel_phys)
+        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
         e[1].record()
         st.attend(q, kv, s_page, s_head, ppages, ctx)
         e[2].record()

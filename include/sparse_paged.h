@@ -254,7 +254,7 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
  * v = h * max_pages + p.  Per request, the requested set R is the union of the
  * request's KV-head lists (sel_pages / sel_counts, as written by
  * sparse_select_coverage or supplied by the caller).  Units of R already
- * resident are hits (their stamp becomes `step`).  Misses, in ascending unit
+ * resident are hits (their stamp becomes the current step).  Misses, in ascending unit
  * id, take slots in ascending slot index from the available set: the lowest
  * free slots if they suffice, else every free slot plus the
  * r = misses - free least recently used resident units outside R, ordered by
@@ -274,7 +274,9 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
  *   unit_slot  int32 [B][Hkv * max_pages]  slot of each unit, -1 = not resident
  *              (the caller initialises tags/stamps/unit_slot to -1 once; the
  *              library keeps them consistent afterwards)
- *   step       >= 0, increasing from call to call
+ *   step_counter  int32 [1] device: the step number this call stamps with
+ *              (start it at 0); the call advances it by one, so a captured
+ *              graph replays with fresh steps
  *   sel_phys   int32 [U][max_pages] out: global slot id b * capacity + slot
  *   stats      int32 [B][4] out: hits, misses, evictions, overflow flag
  *   capacity   slots per request, 1..8192; num_kv_heads <= 64
@@ -284,9 +286,9 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
 sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* sel_counts,
                                        const int32_t* sel_pages, const uint16_t* host_kv,
                                        uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
-                                       int32_t* slot_stamp, int32_t* unit_slot, int32_t step,
-                                       int32_t* sel_phys, int32_t* stats, void* ws,
-                                       size_t ws_bytes, void* stream);
+                                       int32_t* slot_stamp, int32_t* unit_slot,
+                                       int32_t* step_counter, int32_t* sel_phys, int32_t* stats,
+                                       void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

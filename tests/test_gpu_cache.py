@@ -39,7 +39,7 @@ def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=N
     for t in range(lists.shape[0]):
         feed_lists(st, layer, {b * H + h: lists[t, b, h] for b in range(B) for h in range(H)})
         phys_hbm = st.buf.sel_phys.clone()
-        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, t, st.buf.sel_phys)
+        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
         torch.cuda.synchronize()
         tags = cache.slot_tag.cpu().numpy()
         stamps = cache.slot_stamp.cpu().numpy()
@@ -126,3 +126,48 @@ def test_cache_resolver_host_tier_shape(gpu_lib):
     stats = _case(w, C=ex["capacity"], list_pages=ex["list_pages"], steps=4, drift=ex["drift"],
                   chunk=128, check_all_slots=False)
     assert stats[-1]["misses"] > 0 and stats[-1]["hits"] > 0
+
+
+def test_cache_resolver_in_graph(gpu_lib):
+    """Resolve + attention + merge captured once and replayed per step, with
+    the lists changed in place between replays: the LRU state follows the
+    oracle exactly (the step number lives on the device)."""
+    from adaptive_sparse_paged_amd.step import capture
+    w = I.custom_workload("cache_graph", 2, 8, 2, ("fixed", 3200), index=123)
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
+    C, H, B = 40, w.kv_heads, w.batch
+    cache = HbmPageCache(dims, host, C)
+    lists = I.drift_lists(w, I.pages_of(lens[0]), 16, 10, 0.25)
+    st = SparseDecodeStep(dims, 0.99, 4, scale=w.scale)
+    layer = types.SimpleNamespace(w=w, dims=dims, li=li)
+    feed_lists(st, layer, {b * H + h: lists[0, b, h] for b in range(B) for h in range(H)})
+    kv, s_page, s_head, ppages = cache.pool_args()
+
+    def step():
+        cache.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
+        st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)
+
+    say("[cache] graph capture of resolve + attention, 10 replays")
+    g = capture(step)
+    for t_ in (cache.slot_tag, cache.slot_stamp, cache.unit_slot):
+        t_.fill_(-1)
+    cache.step_counter.zero_()
+    cache.cache_kv.zero_()
+    states = [O.LRUState(C, H * MP) for _ in range(B)]
+    for t in range(lists.shape[0]):
+        feed_lists(st, layer, {b * H + h: lists[t, b, h] for b in range(B) for h in range(H)})
+        g.replay()
+        torch.cuda.synchronize()
+        replay_out = st.buf.out.clone()
+        assert cache.step_counter.item() == t + 1
+        for b in range(B):
+            r = O.resolve_step(states[b], [h * MP + int(p) for h in range(H) for p in lists[t, b, h]], t)
+            assert np.array_equal(cache.slot_tag[b].cpu().numpy(), states[b].tag), (t, b)
+            assert np.array_equal(cache.slot_stamp[b].cpu().numpy(), states[b].stamp), (t, b)
+            assert cache.stats[b].cpu().tolist() == [r["hits"], r["misses"], r["evictions"], 0]
+        st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)   # eager, same lists
+        torch.cuda.synchronize()
+        assert torch.equal(replay_out, st.buf.out)
