@@ -4,9 +4,9 @@
 // derives its share of the work from the list lengths, with no host-side
 // plan, so the step stays inside the graph).
 //
-// The grid is fixed (one workgroup per possible chunk).  Workgroup c finds its
-// unit by a wave-parallel search over the device-written chunk prefix sums,
-// then its 4 waves split the chunk's pages; each wave runs an online softmax
+// The grid is fixed (one workgroup per possible chunk).  Workgroup c derives
+// its unit and chunk from the list lengths themselves (a wave prefix sum over
+// the per-unit chunk counts), then its 4 waves split the chunk's pages; each wave runs an online softmax
 // for the unit's G query heads on the bf16 matrix cores:
 //   QK:  S^T[t][g] = K[t][:] . q[g][:]   v_mfma_f32_16x16x32_bf16, 4 k-slices
 //        (A = K tile rows = tokens, read straight from HBM in 16-byte runs;
@@ -24,23 +24,6 @@
 namespace sp {
 
 constexpr int kAttnWaves = 4;
-
-// Largest u in [0, U) with offs[u] <= c (offs non-decreasing, offs[0] = 0 <= c).
-__device__ __forceinline__ int find_unit(const int32_t* __restrict__ offs, int U, int c) {
-  const int lane = lane_id();
-  int lo = 0, n = U;
-  while (n > 64) {
-    const int step = (n + 63) / 64;
-    const bool ok = (lane * step < n) && offs[lo + lane * step] <= c;
-    const unsigned long long mask = __ballot(ok);
-    const int last = 63 - __clzll(mask);
-    lo += last * step;
-    n = min(step, n - last * step);
-  }
-  const bool ok = (lane < n) && offs[lo + lane] <= c;
-  const unsigned long long mask = __ballot(ok);
-  return lo + (63 - __clzll(mask));
-}
 
 struct PageFrag {
   u32x4 k[4];   // K tile: token (lane & 15), channels 32 s + 8 (lane >> 4) .. +7
@@ -131,20 +114,20 @@ __device__ __forceinline__ void attend_page(PageFrag& f, const bf16x8* qf, bool 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
     int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ chunk_offsets,
-    const int32_t* __restrict__ sel_pages, const int32_t* __restrict__ sel_phys,
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_phys,
     float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int U,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
   const int c = blockIdx.x;
-  const int total = chunk_offsets[U];
-  if (c >= total) return;
+  int u, local;
+  plan_locate(sel_counts, U, max_pages, chunk_pages, c, u, local);
+  if (u < 0) return;                   // past the last chunk of the step
   const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
-  const int u = find_unit(chunk_offsets, U, c);
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   const int L = min(max(ctx_lens[b], 0), max_pages * kP);
   const int cnt = min(sel_counts[u], max_pages);
-  const int i0 = (c - chunk_offsets[u]) * chunk_pages;
+  const int i0 = local * chunk_pages;
   const int i1 = min(i0 + chunk_pages, cnt);
   const int32_t* lp = sel_pages + (int64_t)u * max_pages;
   const int32_t* lx = sel_phys + (int64_t)u * max_pages;
@@ -241,15 +224,13 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
                                             const uint16_t* kv, int64_t stride_page,
                                             int64_t stride_head, int64_t pool_pages,
                                             const int32_t* ctx_lens, const int32_t* sel_counts,
-                                            const int32_t* chunk_offsets,
                                             const int32_t* sel_pages, const int32_t* sel_phys,
                                             float scale, int32_t chunk_pages, float* part_o,
                                             float* part_lse, int64_t max_parts, void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if ((st = sp::check_pool(kv, stride_page, stride_head, pool_pages)) != SPARSE_OK) return st;
-  if (!q || !ctx_lens || !sel_counts || !chunk_offsets || !sel_pages || !sel_phys || !part_o ||
-      !part_lse)
+  if (!q || !ctx_lens || !sel_counts || !sel_pages || !sel_phys || !part_o || !part_lse)
     return SPARSE_ERR_INVALID;
   if (!sp::aligned(q, 16) || !sp::aligned(part_o, 16) || !isfinite(scale))
     return SPARSE_ERR_INVALID;
@@ -262,7 +243,7 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)max_parts), dim3(256), lds,
                      (hipStream_t)stream, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
-                     sel_counts, chunk_offsets, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
+                     sel_counts, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
                      group, dims->max_pages, U, part_o, part_lse);
   return sp::launch_status();
 }

@@ -90,6 +90,76 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
   return total;
 }
 
+// ---- the chunk plan, derived on the device from the list lengths ------------
+// Unit u's list of k_u = min(count_u, max_pages) pages splits into
+// ceil(k_u / chunk) chunks, numbered across units in unit order.  A wave
+// derives where chunk c falls with one round of loads (lane l reads the
+// counts of units l*8 .. l*8+7 of each 512-unit segment) and a wave prefix
+// sum -- no host plan and no precomputed offsets.
+constexpr int kPlanVU = 8;
+
+__device__ __forceinline__ int plan_chunks(const int32_t* __restrict__ counts, int idx, int U,
+                                           int max_pages, int chunk) {
+  const int k = (idx < U) ? min(max(counts[idx], 0), max_pages) : 0;
+  return (k + chunk - 1) / chunk;
+}
+
+// Unit of global chunk c and the chunk's index within that unit (unit = -1
+// when c is past the last chunk).  Wave-uniform results; every lane calls.
+__device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, int U,
+                                            int max_pages, int chunk, int c, int& unit,
+                                            int& local) {
+  const int lane = lane_id();
+  int running = 0;
+  unit = -1;
+  local = 0;
+  for (int seg = 0; seg < U; seg += 64 * kPlanVU) {
+    int ch[kPlanVU];
+    int s = 0;
+#pragma unroll
+    for (int v = 0; v < kPlanVU; ++v) {
+      ch[v] = plan_chunks(counts, seg + lane * kPlanVU + v, U, max_pages, chunk);
+      s += ch[v];
+    }
+    const int incl = wave_incl_scan(s);
+    const int seg_total = __shfl(incl, 63, 64);
+    if (c < running + seg_total) {
+      const unsigned long long hit_mask = __ballot(running + incl > c);
+      const int hit = __ffsll((long long)hit_mask) - 1;
+      int acc = running + incl - s, fu = -1, fl = 0;
+#pragma unroll
+      for (int v = 0; v < kPlanVU; ++v) {
+        if (fu < 0 && c < acc + ch[v]) {
+          fu = seg + lane * kPlanVU + v;
+          fl = c - acc;
+        }
+        acc += ch[v];
+      }
+      unit = __builtin_amdgcn_readlane(fu, hit);
+      local = __builtin_amdgcn_readlane(fl, hit);
+      return;
+    }
+    running += seg_total;
+  }
+}
+
+// Number of chunks of units 0 .. u-1 (wave-uniform; every lane calls).
+__device__ __forceinline__ int plan_prefix(const int32_t* __restrict__ counts, int U,
+                                           int max_pages, int chunk, int u) {
+  const int lane = lane_id();
+  int running = 0;
+  for (int seg = 0; seg < u; seg += 64 * kPlanVU) {
+    int s = 0;
+#pragma unroll
+    for (int v = 0; v < kPlanVU; ++v) {
+      const int idx = seg + lane * kPlanVU + v;
+      if (idx < u) s += plan_chunks(counts, idx, U, max_pages, chunk);
+    }
+    running += __shfl(wave_incl_scan(s), 63, 64);
+  }
+  return running;
+}
+
 // ---- host-side argument checks ----------------------------------------------
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

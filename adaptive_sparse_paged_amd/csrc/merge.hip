@@ -15,13 +15,21 @@ constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
 // (max, sum, weighted sum); the 32 slots are then combined through LDS.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ chunk_offsets, int hkv, int group, float* __restrict__ out,
-    float* __restrict__ out_lse) {
+    const int32_t* __restrict__ sel_counts, int U, int max_pages, int chunk, int hkv, int group,
+    float* __restrict__ out, float* __restrict__ out_lse) {
   __shared__ floatx4 s_acc[kMergeSlots][32];
   __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
+  __shared__ int s_c0;
   const int u = blockIdx.x, g = blockIdx.y;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
-  const int c0 = chunk_offsets[u], c1 = chunk_offsets[u + 1];
+  // this unit's chunks, from the list lengths (as the attention planned them)
+  if (threadIdx.x < 64) {
+    const int c0w = plan_prefix(sel_counts, U, max_pages, chunk, u);
+    if (threadIdx.x == 0) s_c0 = c0w;
+  }
+  __syncthreads();
+  const int c0 = s_c0;
+  const int c1 = c0 + plan_chunks(sel_counts, u, U, max_pages, chunk);
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
 
   float m = -INFINITY, s = 0.f;
@@ -74,18 +82,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 
 extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                              const float* part_lse, const int32_t* sel_counts,
-                                             const int32_t* chunk_offsets, int32_t chunk_pages,
-                                             float* out, float* out_lse, void* stream) {
+                                             int32_t chunk_pages, float* out, float* out_lse,
+                                             void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
-  if (!part_o || !part_lse || !sel_counts || !chunk_offsets || !out || !out_lse)
+  if (!part_o || !part_lse || !sel_counts || !out || !out_lse)
     return SPARSE_ERR_INVALID;
   if (!sp::aligned(part_o, 16) || !sp::aligned(out, 16)) return SPARSE_ERR_INVALID;
   if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
   hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
-                     (hipStream_t)stream, part_o, part_lse, chunk_offsets, hkv, group, out,
-                     out_lse);
+                     (hipStream_t)stream, part_o, part_lse, sel_counts, U, dims->max_pages,
+                     chunk_pages, hkv, group, out, out_lse);
   return sp::launch_status();
 }

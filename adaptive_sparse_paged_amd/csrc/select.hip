@@ -403,7 +403,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
 
-  // ---- 5. last workgroup: prefix sums over units --------------------------
+  // ---- 5. optional: the last workgroup writes prefix sums over units ------
+  if (sel_offsets == nullptr) {
+    if (tid == 0) sel_counts[u] = count;
+    return;
+  }
   __syncthreads();   // every thread's list writes are issued before the ticket
   if (tid == 0) {
     sel_counts[u] = count;
@@ -475,11 +479,12 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
                                   size_t ws_bytes, void* stream) {
   sparse_status st = check_dims(dims);
   if (st != SPARSE_OK) return st;
-  if (!logits || !ctx_lens || !page_table || !sel_counts || !sel_offsets || !chunk_offsets ||
-      !sel_pages || !sel_phys)
+  if (!logits || !ctx_lens || !page_table || !sel_counts || !sel_pages || !sel_phys)
     return SPARSE_ERR_INVALID;
+  if ((sel_offsets == nullptr) != (chunk_offsets == nullptr)) return SPARSE_ERR_INVALID;
   if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
-  if (!ws || ws_bytes < sparse_select_workspace_bytes(dims) || !aligned(ws, 4))
+  if (sel_offsets != nullptr &&
+      (!ws || ws_bytes < sparse_select_workspace_bytes(dims) || !aligned(ws, 4)))
     return SPARSE_ERR_WORKSPACE;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;

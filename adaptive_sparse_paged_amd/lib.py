@@ -69,9 +69,9 @@ _SIGS = {
     "sparse_select_coverage": (_I32, [_D, _P, _P, _P, _F, _I32, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
     "sparse_decode_max_parts": (_I64, [_D, _I32]),
-    "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _F, _I32,
+    "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
                                   _P, _P, _I64, _P]),
-    "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P]),
     "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
     "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
@@ -148,6 +148,7 @@ def select_workspace_bytes(dims):
 
 def select_coverage(dims, logits, ctx_lens, page_table, gamma, chunk_pages, sel_counts,
                     sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
+    """sel_offsets / chunk_offsets / ws may all be None (no whole-batch prefix sums)."""
     _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
          sel_phys, ws)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -162,21 +163,20 @@ def decode_max_parts(dims, chunk_pages):
 
 
 def decode_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
-                chunk_offsets, sel_pages, sel_phys, scale, chunk_pages, part_o, part_lse,
-                max_parts, stream=None):
-    _dev(q, kv, ctx_lens, sel_counts, chunk_offsets, sel_pages, sel_phys, part_o, part_lse)
+                sel_pages, sel_phys, scale, chunk_pages, part_o, part_lse, max_parts,
+                stream=None):
+    _dev(q, kv, ctx_lens, sel_counts, sel_pages, sel_phys, part_o, part_lse)
     _check("sparse_decode_attn", load().sparse_decode_attn(
         ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
-        _ptr(ctx_lens), _ptr(sel_counts), _ptr(chunk_offsets), _ptr(sel_pages), _ptr(sel_phys),
-        scale, chunk_pages, _ptr(part_o), _ptr(part_lse), max_parts, _stream(stream)))
+        _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, chunk_pages,
+        _ptr(part_o), _ptr(part_lse), max_parts, _stream(stream)))
 
 
-def merge_splits(dims, part_o, part_lse, sel_counts, chunk_offsets, chunk_pages, out, out_lse,
-                 stream=None):
-    _dev(part_o, part_lse, sel_counts, chunk_offsets, out, out_lse)
+def merge_splits(dims, part_o, part_lse, sel_counts, chunk_pages, out, out_lse, stream=None):
+    _dev(part_o, part_lse, sel_counts, out, out_lse)
     _check("sparse_merge_splits", load().sparse_merge_splits(
-        ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), _ptr(chunk_offsets),
-        chunk_pages, _ptr(out), _ptr(out_lse), _stream(stream)))
+        ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), chunk_pages,
+        _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
 def cache_workspace_bytes(dims, capacity):
@@ -203,7 +203,7 @@ def select_topk(dims, logits, ctx_lens, page_table, k_pages, chunk_pages, sel_co
                 sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
     _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
          sel_phys, ws)
-    nbytes = ws.numel() * ws.element_size()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("sparse_select_topk", load().sparse_select_topk(
         ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), k_pages, chunk_pages,
         _ptr(sel_counts), _ptr(sel_offsets), _ptr(chunk_offsets), _ptr(sel_pages),

@@ -52,8 +52,12 @@ class SparseDecodeStep:
     the default is one group.
     """
 
-    def __init__(self, dims, gamma, chunk_pages=32, scale=None, device="cuda", groups=1):
+    def __init__(self, dims, gamma, chunk_pages=32, scale=None, device="cuda", groups=1,
+                 offsets=True):
+        """offsets: also write the whole-batch prefix sums (sel_offsets,
+        chunk_offsets) in the selection; the attention does not need them."""
         self.dims = dims
+        self.offsets = bool(offsets)
         self.gamma = float(gamma)
         self.chunk_pages = int(min(chunk_pages, dims.max_pages))
         self.scale = float(scale if scale is not None else HEAD_DIM ** -0.5)
@@ -122,13 +126,11 @@ class SparseDecodeStep:
                                     b.sel_phys[u0:u1], gr["ws"], s)
                 gr["selected"].record(s)
                 lib.decode_attn(dg, q[b0:b1], kv, stride_page, stride_head, pool_pages,
-                                ctx_lens[b0:b1], b.sel_counts[u0:u1], gr["chunk_offsets"],
-                                b.sel_pages[u0:u1], b.sel_phys[u0:u1], self.scale,
-                                self.chunk_pages, gr["part_o"], gr["part_lse"],
-                                gr["max_parts"], s)
+                                ctx_lens[b0:b1], b.sel_counts[u0:u1], b.sel_pages[u0:u1],
+                                b.sel_phys[u0:u1], self.scale, self.chunk_pages, gr["part_o"],
+                                gr["part_lse"], gr["max_parts"], s)
                 lib.merge_splits(dg, gr["part_o"], gr["part_lse"], b.sel_counts[u0:u1],
-                                 gr["chunk_offsets"], self.chunk_pages, out[b0:b1],
-                                 out_lse[b0:b1], s)
+                                 self.chunk_pages, out[b0:b1], out_lse[b0:b1], s)
             prev = gr
         for gr in self.groups:
             cur.wait_stream(gr["stream"])
@@ -137,9 +139,11 @@ class SparseDecodeStep:
     def score_select(self, q, summ, pool_pages, page_table, ctx_lens, stream=None):
         d, b = self.dims, self.buf
         lib.score_pages(d, q, summ, pool_pages, page_table, ctx_lens, self.scale, b.logits, stream)
+        on = self.offsets
         lib.select_coverage(d, b.logits, ctx_lens, page_table, self.gamma, self.chunk_pages,
-                            b.sel_counts, b.sel_offsets, b.chunk_offsets, b.sel_pages, b.sel_phys,
-                            b.ws, stream)
+                            b.sel_counts, b.sel_offsets if on else None,
+                            b.chunk_offsets if on else None, b.sel_pages, b.sel_phys,
+                            b.ws if on else None, stream)
 
     def attend(self, q, kv, stride_page, stride_head, pool_pages, ctx_lens, out=None,
                out_lse=None, stream=None, sel_pages=None, sel_phys=None):
@@ -149,10 +153,10 @@ class SparseDecodeStep:
         sp = b.sel_pages if sel_pages is None else sel_pages
         sx = b.sel_phys if sel_phys is None else sel_phys
         lib.decode_attn(d, q, kv, stride_page, stride_head, pool_pages, ctx_lens, b.sel_counts,
-                        b.chunk_offsets, sp, sx, self.scale, self.chunk_pages, b.part_o,
-                        b.part_lse, self.max_parts, stream)
-        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, b.chunk_offsets,
-                         self.chunk_pages, out, out_lse, stream)
+                        sp, sx, self.scale, self.chunk_pages, b.part_o, b.part_lse,
+                        self.max_parts, stream)
+        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, self.chunk_pages, out, out_lse,
+                         stream)
         return out, out_lse
 
     def run(self, q, summ, kv, stride_page, stride_head, pool_pages, page_table, ctx_lens,

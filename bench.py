@@ -158,9 +158,6 @@ def host_tier_bench(args):
     ctx = torch.from_numpy(lens.astype(np.int32)).cuda()
     lists_dev = torch.from_numpy(lists.reshape(steps, U, LP)).cuda()
     st.buf.sel_counts.fill_(LP)
-    nch = -(-LP // chunk)
-    st.buf.chunk_offsets.copy_(torch.arange(U + 1, dtype=torch.int32) * nch)
-    st.buf.sel_offsets.copy_(torch.arange(U + 1, dtype=torch.int32) * LP)
     kv, s_page, s_head, ppages = cache.pool_args()
 
     def run_step(t, marks=None):
@@ -271,9 +268,8 @@ def pmc_probe(args):
     ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, st.chunk_pages) for u in range(len(c)))
     for _ in range(3):
         lib.decode_attn(dims, li.q, li.kv_pool, sp_, sh_, li.pool_pages, li.ctx_lens,
-                        st.buf.sel_counts, st.buf.chunk_offsets, st.buf.sel_pages,
-                        st.buf.sel_phys, st.scale, st.chunk_pages, st.buf.part_o,
-                        st.buf.part_lse, st.max_parts)
+                        st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys, st.scale,
+                        st.chunk_pages, st.buf.part_o, st.buf.part_lse, st.max_parts)
     src = torch.empty(512 * 1024 * 1024, dtype=torch.int16, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
@@ -326,7 +322,8 @@ def main():
     max_pages = L_in[0].max_pages
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
     groups = max(1, min(args.groups, w.batch))
-    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev, groups=groups)
+    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev, groups=groups,
+                          offsets=False)
     outs = [torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     lses = [torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev) for _ in range(layers)]
     counts = [torch.empty_like(st.buf.sel_counts) for _ in range(layers)]
@@ -382,12 +379,12 @@ def main():
             a1 = torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             lib.decode_attn(dims, li.q, li.kv_pool, stride_page, stride_head, li.pool_pages,
-                            li.ctx_lens, st.buf.sel_counts, st.buf.chunk_offsets,
-                            st.buf.sel_pages, st.buf.sel_phys, st.scale, st.chunk_pages,
-                            st.buf.part_o, st.buf.part_lse, st.max_parts)
+                            li.ctx_lens, st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys,
+                            st.scale, st.chunk_pages, st.buf.part_o, st.buf.part_lse,
+                            st.max_parts)
             a1.record(stream)
             lib.merge_splits(dims, st.buf.part_o, st.buf.part_lse, st.buf.sel_counts,
-                             st.buf.chunk_offsets, st.chunk_pages, outs[l], lses[l])
+                             st.chunk_pages, outs[l], lses[l])
             marks.append((a0, a1))
     torch.cuda.synchronize()
     attn_us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / len(marks)

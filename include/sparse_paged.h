@@ -144,15 +144,18 @@ size_t sparse_select_workspace_bytes(const sparse_dims* dims);
  *   sel_counts    int32 [U]            k* of each unit (0 when L_b = 0)
  *   sel_pages     int32 [U][max_pages] kept logical pages, ascending, first k* valid
  *   sel_phys      int32 [U][max_pages] page_table[b][sel_pages[..]]
+ * Optional whole-batch prefix sums (both NULL, or both given):
  *   sel_offsets   int32 [U + 1]        exclusive prefix sum of sel_counts
  *   chunk_offsets int32 [U + 1]        exclusive prefix sum of ceil(k* / chunk_pages)
- * The prefix sums are written by whichever workgroup finishes last (a
- * device-side ticket in the workspace), so no host plan is involved.
+ * They are written by whichever workgroup finishes last (a device-side
+ * ticket in the workspace).  The attention and merge calls do not need them:
+ * they derive their chunk plan from sel_counts.
  *
- *   ws / ws_bytes  device workspace of at least sparse_select_workspace_bytes();
- *                  it must be zero-filled ONCE before its first use and is
- *                  left zero-filled by every call.  Calls sharing one
- *                  workspace must not overlap in time.
+ *   ws / ws_bytes  device workspace of at least sparse_select_workspace_bytes(),
+ *                  needed only with the prefix sums (NULL otherwise); it must
+ *                  be zero-filled ONCE before its first use and is left
+ *                  zero-filled by every call.  Calls sharing one workspace
+ *                  must not overlap in time.
  *   gamma          in (0, 1]; chunk_pages in [1, max_pages]
  */
 sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
@@ -205,13 +208,14 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
  * its own share of the work from the list lengths, so no host-side plan is
  * needed and the step stays inside the graph).
  *
- * The grid has max_parts workgroups, fixed at enqueue time.  Workgroup c
- * finds the unit u with chunk_offsets[u] <= c < chunk_offsets[u+1] by a
- * search over the prefix sums, takes list entries
- * [(c - chunk_offsets[u]) * chunk_pages, +chunk_pages) of that unit, and
- * computes exact attention of the unit's G query heads over the valid
- * tokens of those pages; workgroups past chunk_offsets[U] exit.
- * Writes, for each chunk c and head g:
+ * Unit u's list (k_u = sel_counts[u] entries) splits into ceil(k_u /
+ * chunk_pages) chunks, numbered across units in unit order.  The grid has
+ * max_parts workgroups, fixed at enqueue time; workgroup c derives, from
+ * sel_counts alone (a wave prefix sum over the per-unit chunk counts), the
+ * unit and the list entries [local * chunk_pages, +chunk_pages) it owns, and
+ * computes exact attention of the unit's G query heads over the valid tokens
+ * of those pages; workgroups past the last chunk exit.  Writes, for each
+ * chunk c and head g:
  *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the chunk)
  *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
  * K/V are read from the pool at sel_phys (physical ids or cache slots).
@@ -222,22 +226,22 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
 sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
                                  int64_t stride_page, int64_t stride_head, int64_t pool_pages,
                                  const int32_t* ctx_lens, const int32_t* sel_counts,
-                                 const int32_t* chunk_offsets, const int32_t* sel_pages,
-                                 const int32_t* sel_phys, float scale, int32_t chunk_pages,
-                                 float* part_o, float* part_lse, int64_t max_parts,
-                                 void* stream);
+                                 const int32_t* sel_pages, const int32_t* sel_phys, float scale,
+                                 int32_t chunk_pages, float* part_o, float* part_lse,
+                                 int64_t max_parts, void* stream);
 
 /*
  * sparse_merge_splits -- log-sum-exp merge of the chunk partials of each unit:
  *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) * o_c
- * (the identity that makes the split over chunks exact).
+ * (the identity that makes the split over chunks exact).  Each unit's
+ * chunks are located from sel_counts exactly as sparse_decode_attn numbered
+ * them (same chunk_pages).
  *   out      fp32 [B][Hq][128];  out_lse fp32 [B][Hq]
  * A unit with no kept page gets o = 0 and lse = -inf.
  */
 sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                   const float* part_lse, const int32_t* sel_counts,
-                                  const int32_t* chunk_offsets, int32_t chunk_pages, float* out,
-                                  float* out_lse, void* stream);
+                                  int32_t chunk_pages, float* out, float* out_lse, void* stream);
 
 /* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
  * list of placed misses handed from the resolve kernel to the fetch kernel. */

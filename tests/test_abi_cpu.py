@@ -92,12 +92,23 @@ def test_null_and_value_checks(L):
     assert sel(0.99, 8, None, 256) == lib.ERR_WORKSPACE
     assert sel(0.99, 8, FAKE, 1) == lib.ERR_WORKSPACE
     attn = lambda kvp, sp_, sh, mp: L.sparse_decode_attn(
-        ctypes.byref(d), FAKE, kvp, sp_, sh, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 16, FAKE,
+        ctypes.byref(d), FAKE, kvp, sp_, sh, 100, FAKE, FAKE, FAKE, FAKE, 0.1, 16, FAKE,
         FAKE, mp, None)
     assert attn(FAKE, 8192, 4096, 15) == lib.ERR_INVALID          # wrong max_parts
     assert attn(ctypes.c_void_p(0x10002), 8192, 4096, 16) == lib.ERR_INVALID  # misaligned pool
     assert attn(FAKE, 8191, 4096, 16) == lib.ERR_INVALID          # stride not 16-byte
-    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == lib.ERR_INVALID
+    # the prefix sums are optional, but both or neither
+    assert L.sparse_select_coverage(ctypes.byref(d), FAKE, FAKE, FAKE, 0.9, 8, FAKE, FAKE, None,
+                                    FAKE, FAKE, FAKE, 256, None) == lib.ERR_INVALID
+    assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 8, FAKE, None, None,
+                                FAKE, FAKE, None, 0, None) == lib.ERR_INVALID
+    assert L.sparse_append_tokens(ctypes.byref(d), None, FAKE, FAKE, 8192, 4096, 100, FAKE,
+                                  FAKE, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_hbm_cache_resolve(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 9000, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == lib.ERR_UNSUPPORTED
+    assert L.sparse_hbm_cache_resolve(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == lib.ERR_WORKSPACE
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
 
