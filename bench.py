@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--gamma", type=float, default=0.99)
-    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--chunk", type=int, default=256)
     ap.add_argument("--groups", type=int, default=1,
                     help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
@@ -400,7 +400,8 @@ def main():
     if os.path.exists(tfile):
         rec = json.load(open(tfile))
         src = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc", "attn.hip")
-        if rec.get("source_sha256_16") == source_hash(src) and rec.get("workload") == w.name:
+        if (rec.get("source_sha256_16") == source_hash(src) and rec.get("workload") == w.name
+                and rec.get("chunk_pages") == st.chunk_pages and rec.get("gamma") == args.gamma):
             traffic = rec.get("bytes_per_launch")
 
     result = {

@@ -1,5 +1,5 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (chunk 128): sampled units against the fp64 oracle (regenerated on the
+times (chunk 256): sampled units against the fp64 oracle (regenerated on the
 host from the seeded generator), structural properties on every unit, and the
 select kernel fed with oracle logits."""
 
@@ -16,7 +16,7 @@ from _gpu_case import GpuLayer, check_unit, say
 
 pytestmark = pytest.mark.gpu
 
-BENCH_CHUNK = 128
+BENCH_CHUNK = 256
 
 
 def _free():
