@@ -25,18 +25,32 @@ constexpr int kScorePagesPerBlock = 16 * kScoreTilesPerWave * kScoreWaves;
 // Here rows = pages of the tile, columns = query heads of the group, and
 // k-slice s covers summary elements [32 s, 32 s + 32) (s < 4: kmin channels,
 // s >= 4: kmax channels).
+//
+// Grid (KV head, page block, request): the KV heads of one request and page
+// block are consecutive workgroups, so the Hkv summary rows of a physical
+// page (adjacent 512-byte rows, one 4 KiB run) are read close together in
+// time.  A wave loads the page ids of both its tiles, then the summaries of
+// tile t + 1 while the matrix cores work on tile t.
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ summ, int64_t pool_pages,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ ctx_lens, float scale,
     float* __restrict__ logits, int hkv, int group, int max_pages) {
-  const int u = blockIdx.y;
-  const int b = u / hkv, h = u - (u / hkv) * hkv;
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int u = b * hkv + h;
   const int L = min(max(ctx_lens[b], 0), max_pages * kP);
   const int n = (L + kP - 1) / kP;
-  const int wave = blockIdx.x * kScoreWaves + (threadIdx.x >> 6);
+  const int wave = blockIdx.y * kScoreWaves + (threadIdx.x >> 6);
   const int p_begin = wave * kScoreTilesPerWave * 16;
   if (p_begin >= n) return;
   const int lane = lane_id(), row = lane & 15, j = lane >> 4;
+  const int32_t* pt = page_table + (int64_t)b * max_pages;
+
+  int xs[kScoreTilesPerWave];
+#pragma unroll
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    const int p = p_begin + t * 16 + row;
+    xs[t] = (p < n) ? pt[p] : -1;
+  }
 
   // B operands: q- for the kmin half, q+ for the kmax half (bf16 bit masks).
   bf16x8 qneg[4], qpos[4];
@@ -66,44 +80,37 @@ __global__ __launch_bounds__(256) void score_kernel(
 
   const float ln16 = 2.772588722239781f;
   float* out = logits + (int64_t)u * group * max_pages;
-  const int32_t* pt = page_table + (int64_t)b * max_pages;
-
-  // Page ids of every tile first, then every summary load, then the math:
-  // two memory round trips per wave in all.
-  int xs[kScoreTilesPerWave];
-  bool oks[kScoreTilesPerWave];
-#pragma unroll
-  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
-    const int p = p_begin + tile * 16 + row;
-    xs[tile] = (p < n) ? pt[p] : -1;
-  }
-  u32x4 a[kScoreTilesPerWave][8];
-#pragma unroll
-  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
-    const int x = xs[tile];
-    oks[tile] = (x >= 0) && (x < pool_pages);
-    const uint16_t* src = summ + ((int64_t)(oks[tile] ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
+  u32x4 a[2][8];
+  bool oks[2];
+  auto issue = [&](int t, int slot) {
+    const int x = xs[t];
+    const bool ok = (x >= 0) && (x < pool_pages);
+    oks[slot] = ok;
+    const uint16_t* src = summ + ((int64_t)(ok ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      a[tile][s] = oks[tile] ? *reinterpret_cast<const u32x4*>(src + 32 * s)
-                             : u32x4{0u, 0u, 0u, 0u};
-  }
+      a[slot][s] = ok ? *reinterpret_cast<const u32x4*>(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+  };
+  issue(0, 0);
 #pragma unroll
-  for (int tile = 0; tile < kScoreTilesPerWave; ++tile) {
-    const int p0 = p_begin + tile * 16;
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    const int p0 = p_begin + t * 16;
     if (p0 >= n) break;
+    if (t + 1 < kScoreTilesPerWave && p0 + 16 < n) issue(t + 1, (t + 1) & 1);
+    const int slot = t & 1;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[tile][s]), qneg[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[slot][s]), qneg[s], acc, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[tile][4 + s]), qpos[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[slot][4 + s]), qpos[s], acc, 0, 0,
+                                                    0);
     // lane (g = row, j) now holds u for pages p0 + 4j + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pi = p0 + 4 * j + i;
-      const bool oki = __shfl(oks[tile] ? 1 : 0, 4 * j + i, 64) != 0;
+      const bool oki = __shfl(oks[slot] ? 1 : 0, 4 * j + i, 64) != 0;
       if (row < group && pi < n) {
         const int nv = min(kP, L - kP * pi);
         const float lnv = (nv == kP) ? ln16 : logf((float)nv);
@@ -127,8 +134,9 @@ extern "C" sparse_status sparse_score_pages(const sparse_dims* dims, const uint1
     return SPARSE_ERR_INVALID;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  dim3 grid((dims->max_pages + sp::kScorePagesPerBlock - 1) / sp::kScorePagesPerBlock, U);
-  if (grid.y > 65535) return SPARSE_ERR_UNSUPPORTED;
+  dim3 grid(hkv, (dims->max_pages + sp::kScorePagesPerBlock - 1) / sp::kScorePagesPerBlock,
+            dims->batch);
+  if (U < 1 || grid.z > 65535) return SPARSE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(sp::score_kernel, grid, dim3(256), 0, (hipStream_t)stream, q, summ,
                      pool_pages, page_table, ctx_lens, scale, logits, hkv, group,
                      dims->max_pages);

@@ -85,8 +85,11 @@ def source_hash(path):
 
 
 def cpu_baseline(w, lens, gamma, budget_s):
-    """Time the fp64 oracle (score, masses, cut, attention) unit by unit on the
-    host until about budget_s seconds have passed; scale to one layer."""
+    """Time the fp64 oracle (score, masses, cut, attention) on every
+    (request, KV head) unit of layer 0, on one host thread.  Each unit is
+    generated once (untimed) and its oracle call repeated R times, with R
+    chosen from the first unit so the timed total is about budget_s; the mean
+    per-unit time is scaled to one layer."""
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=1)
@@ -94,30 +97,38 @@ def cpu_baseline(w, lens, gamma, budget_s):
         limiter = None
     import oracle as O
     from adaptive_sparse_paged_amd import inputs as I
-    spent, units = 0.0, 0
+    n_units = w.batch * w.kv_heads
+    spent, calls, reps = 0.0, 0, None
     t_total = time.time()
     for b in range(w.batch):
         for h in range(w.kv_heads):
             L = int(lens[b])
             k, v, q, nv = I.unit_host(w, 0, b, h, L)
             lo, hi = O.summaries(k, nv)        # prefill-time, not timed
-            Kf, Vf = O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v)
-            t0 = time.perf_counter()
-            sel = O.select_unit(q, lo, hi, nv, w.scale, gamma)
-            O.attend_pages(O.bf16_bits_to_f64(q), Kf, Vf, nv, sel["list"], w.scale)
-            spent += time.perf_counter() - t0
-            units += 1
-            if spent >= budget_s or time.time() - t_total > 4 * budget_s:
+            Kf, Vf, qf = O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v), O.bf16_bits_to_f64(q)
+            r = 0
+            while reps is None or r < reps:
+                t0 = time.perf_counter()
+                sel = O.select_unit(q, lo, hi, nv, w.scale, gamma)
+                O.attend_pages(qf, Kf, Vf, nv, sel["list"], w.scale)
+                dt = time.perf_counter() - t0
+                spent += dt
+                calls += 1
+                r += 1
+                if reps is None:
+                    reps = int(min(16, max(1, round(budget_s / (dt * n_units)))))
+            if time.time() - t_total > 8 * budget_s:
                 break
-        if spent >= budget_s or time.time() - t_total > 4 * budget_s:
+        if time.time() - t_total > 8 * budget_s:
             break
     if limiter is not None:
         limiter.unregister()
-    per_unit = spent / units
-    us_layer = per_unit * w.batch * w.kv_heads * 1e6
+    units = -(-calls // reps)
+    us_layer = spent / calls * n_units * 1e6
     return {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{units} of {w.batch * w.kv_heads} (request, KV head) units of layer 0, "
-                      f"{spent:.1f} s of fp64 NumPy on one host thread, scaled to one layer"}
+            "sample": f"{units} of {n_units} (request, KV head) units of layer 0, each run "
+                      f"{reps} times: {spent:.1f} s of fp64 NumPy on one host thread, "
+                      f"mean per unit scaled to one layer"}
 
 
 def host_tier_bench(args):
@@ -241,6 +252,14 @@ def host_tier_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def attn_launch(lib, st, dims, li, stride_page, stride_head):
+    """The step's attention launch alone (sparse_decode_attn, without its merge)."""
+    b = st.buf
+    lib.decode_attn(dims, li.q, li.kv_pool, stride_page, stride_head, li.pool_pages, li.ctx_lens,
+                    b.sel_counts, b.sel_pages, b.sel_phys, st.scale, st.chunk_pages, b.part_o,
+                    b.part_lse, st.max_parts)
+
+
 def pmc_probe(args):
     """Launches for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE, then
     WRITE_SIZE): a plain device copy of 1 GiB (known bytes, the calibration)
@@ -267,9 +286,7 @@ def pmc_probe(args):
     tsel = kept_tokens(c, st.buf.sel_pages.cpu().numpy(), lens, w.kv_heads, li.max_pages)
     ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, st.chunk_pages) for u in range(len(c)))
     for _ in range(3):
-        lib.decode_attn(dims, li.q, li.kv_pool, sp_, sh_, li.pool_pages, li.ctx_lens,
-                        st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys, st.scale,
-                        st.chunk_pages, st.buf.part_o, st.buf.part_lse, st.max_parts)
+        attn_launch(lib, st, dims, li, sp_, sh_)
     src = torch.empty(512 * 1024 * 1024, dtype=torch.int16, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
@@ -347,13 +364,15 @@ def main():
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
         graph.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_replay = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(np.percentile(per_replay, x)) for x in (10, 50, 90))
 
     # bytes moved per step
     G, Hkv = w.group, w.kv_heads
@@ -378,10 +397,7 @@ def main():
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
             a0.record(stream)
-            lib.decode_attn(dims, li.q, li.kv_pool, stride_page, stride_head, li.pool_pages,
-                            li.ctx_lens, st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys,
-                            st.scale, st.chunk_pages, st.buf.part_o, st.buf.part_lse,
-                            st.max_parts)
+            attn_launch(lib, st, dims, li, stride_page, stride_head)
             a1.record(stream)
             lib.merge_splits(dims, st.buf.part_o, st.buf.part_lse, st.buf.sel_counts,
                              st.chunk_pages, outs[l], lses[l])
@@ -413,6 +429,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "us_per_layer": round(ms_step * 1e3 / layers, 2),
+        "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
