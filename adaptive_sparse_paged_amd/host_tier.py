@@ -11,6 +11,7 @@ import ctypes
 import torch
 
 from . import lib
+from .step import SparseDecodeStep
 
 UNIT_ELEMS = 2 * 16 * 128   # K tile + V tile of one (page, KV head)
 
@@ -59,3 +60,65 @@ class HbmPageCache:
     def pool_args(self):
         """(kv, stride_page, stride_head, pool_pages) for sparse_decode_attn."""
         return self.cache_kv, UNIT_ELEMS, 0, self.cache_kv.shape[0]
+
+
+class LayeredHostTierStep:
+    """Host-tier attention over several layers that share one set of page
+    lists per step ("HiSparse: Scaling Sparse Attention Decoding with
+    Hierarchical KV Cache", abstract: for models whose layers share their
+    selections, layer-wise prefetching overlaps the fetch of later layers'
+    misses with earlier layers' work; exact, since only placement changes).
+
+    Each layer has its own pinned host pool and HBM cache.  With
+    prefetch=False every layer runs resolve+fetch then attention+merge on the
+    current stream.  With prefetch=True the resolves (hit detection, LRU,
+    fetch) of all layers run in layer order on a second stream, each
+    recording an event, and layer l's attention waits only for layer l's
+    event -- so the PCIe fetch of layer l+1 runs under the attention of layer
+    l.  Both modes run the same kernels on the same data in the same per-layer
+    order: outputs and cache state are bitwise the same.  The step joins the
+    second stream before it returns, so it can be captured whole."""
+
+    def __init__(self, dims, host_pools, capacity, gamma, chunk_pages, scale=None,
+                 prefetch=True, device="cuda"):
+        self.dims = dims
+        self.prefetch = bool(prefetch)
+        self.caches = [HbmPageCache(dims, h, capacity, device) for h in host_pools]
+        self.attn = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+                                     offsets=False)
+        # per-layer slot lists: layer l+1's resolve writes while layer l attends
+        self.sel_phys = [torch.zeros_like(self.attn.buf.sel_phys) for _ in host_pools]
+        self.io = torch.cuda.Stream(device=device)
+        self.ready = [torch.cuda.Event() for _ in host_pools]
+
+    @property
+    def sel_counts(self):
+        return self.attn.buf.sel_counts
+
+    @property
+    def sel_pages(self):
+        return self.attn.buf.sel_pages
+
+    def run(self, qs, ctx_lens, outs, lses):
+        """One step over every layer on the lists in sel_counts / sel_pages;
+        qs[l], outs[l], lses[l]: layer l's queries and outputs."""
+        st = self.attn
+        counts, pages = st.buf.sel_counts, st.buf.sel_pages
+        if not self.prefetch:
+            for l, cache in enumerate(self.caches):
+                cache.resolve(counts, pages, self.sel_phys[l])
+                kv, sp, sh, pp = cache.pool_args()
+                st.attend(qs[l], kv, sp, sh, pp, ctx_lens, outs[l], lses[l],
+                          sel_phys=self.sel_phys[l])
+            return
+        cur = torch.cuda.current_stream()
+        self.io.wait_stream(cur)
+        for l, cache in enumerate(self.caches):
+            cache.resolve(counts, pages, self.sel_phys[l], stream=self.io)
+            self.ready[l].record(self.io)
+        for l, cache in enumerate(self.caches):
+            cur.wait_event(self.ready[l])
+            kv, sp, sh, pp = cache.pool_args()
+            st.attend(qs[l], kv, sp, sh, pp, ctx_lens, outs[l], lses[l],
+                      sel_phys=self.sel_phys[l])
+        cur.wait_stream(self.io)

@@ -160,6 +160,11 @@ WORKLOADS = {
                                ("uniform", 0.25, 4.0), ("fixed", 4),
                                extra={"capacity": 4096, "steps": 64, "drift": 0.10,
                                       "list_pages": 448}),
+    # the host tier over several layers that share their page lists
+    "host_tier_layers": Workload("host_tier_layers", 5, 16, 32, 8, 4, ("fixed", 131072),
+                                 ("uniform", 0.25, 4.0), ("fixed", 4),
+                                 extra={"capacity": 4096, "steps": 32, "drift": 0.10,
+                                        "list_pages": 448}),
 }
 
 

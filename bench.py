@@ -252,6 +252,111 @@ def host_tier_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def host_tier_layers_bench(args):
+    """Layer-wise prefetch over the host tier: 16 requests x 131072 tokens,
+    4 layers that share their page lists (448 pages per request and KV head,
+    drifting 10% per step, 32 steps), each layer with its own pinned host
+    pool (8 GiB) and 4096-slot HBM cache per request.  Times every step two
+    ways on separate caches fed the same lists: layer by layer on one stream
+    (resolve+fetch then attention+merge, with events between the phases) and
+    pipelined (all resolves on a second stream, each layer's attention waiting
+    for its own layer only)."""
+    import torch
+    from adaptive_sparse_paged_amd import inputs as I
+    from adaptive_sparse_paged_amd import lib
+    from adaptive_sparse_paged_amd.host_tier import LayeredHostTierStep
+
+    lib.load()
+    w = I.WORKLOADS["host_tier_layers"]
+    ex = w.extra
+    lens = I.context_lengths(w)
+    nl = args.layers or w.layers
+    t0 = time.time()
+    hosts = [I.build_host_pool(w, l, lens=lens)[0] for l in range(nl)]
+    MP = hosts[0].shape[1]
+    print(f"# host pools {nl} x {hosts[0].numel() * 2 / 2**30:.0f} GiB pinned "
+          f"({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    steps, LP, C = ex["steps"], ex["list_pages"], ex["capacity"]
+    lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"])
+    B, H = w.batch, w.kv_heads
+    U = B * H
+    dims = lib.make_dims(B, w.q_heads, H, MP)
+    chunk = min(args.chunk, LP)
+    seq = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=False)
+    pre = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=True)
+    qs = []
+    for l in range(nl):
+        q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
+        for b in range(B):
+            for h in range(H):
+                q[b, h * w.group:(h + 1) * w.group] = I.unit_query_bits(w, l, b, h, int(lens[b]))
+        qs.append(q.cuda())
+    ctx = torch.from_numpy(lens.astype(np.int32)).cuda()
+    lists_dev = torch.from_numpy(lists.reshape(steps, U, LP)).cuda()
+    outs = [torch.empty((B, w.q_heads, D), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    lses = [torch.empty((B, w.q_heads), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    seq_io, seq_att, pre_step, misses = [], [], [], []
+    for t in range(steps):
+        for stp in (seq, pre):
+            stp.sel_counts.fill_(LP)
+            stp.sel_pages[:, :LP].copy_(lists_dev[t])
+        # layer by layer, with the phases timed apart
+        marks = []
+        st = seq.attn
+        for l, cache in enumerate(seq.caches):
+            e = [ev(), ev(), ev()]
+            e[0].record()
+            cache.resolve(st.buf.sel_counts, st.buf.sel_pages, seq.sel_phys[l])
+            e[1].record()
+            kv, sp_, sh_, pp = cache.pool_args()
+            st.attend(qs[l], kv, sp_, sh_, pp, ctx, outs[l], lses[l], sel_phys=seq.sel_phys[l])
+            e[2].record()
+            marks.append(e)
+        p0, p1 = ev(), ev()
+        p0.record()
+        pre.run(qs, ctx, outs, lses)
+        p1.record()
+        torch.cuda.synchronize()
+        seq_io.append(sum(m[0].elapsed_time(m[1]) for m in marks) * 1e3)
+        seq_att.append(sum(m[1].elapsed_time(m[2]) for m in marks) * 1e3)
+        pre_step.append(p0.elapsed_time(p1) * 1e3)
+        misses.append(int(sum(int(c.stats[:, 1].sum()) for c in pre.caches)))
+        for a, b_ in zip(seq.caches, pre.caches):
+            assert torch.equal(a.stats, b_.stats)
+    seq_io, seq_att, pre_step = (np.array(x[1:]) for x in (seq_io, seq_att, pre_step))
+    seq_step = seq_io + seq_att
+    hide = np.minimum(seq_io, seq_att)
+    hidden = (seq_step - pre_step) / hide
+    unit_bytes = 2 * PAGE * D * 2
+    result = {
+        "metric": "host-tier decode step us over 4 layers sharing page lists, layer-wise prefetch",
+        "value": round(float(np.median(pre_step)), 1),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps - 1,
+        "warmup": 1,
+        "ms_per_step": round(float(np.median(pre_step)) / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "ctx": int(lens.max()), "layers": nl,
+                   "kv_heads": H, "q_heads": w.q_heads, "capacity_slots": C,
+                   "list_pages": LP, "drift": ex["drift"], "chunk_pages": chunk},
+        "sequential_step_us_median": round(float(np.median(seq_step)), 1),
+        "sequential_resolve_fetch_us_median": round(float(np.median(seq_io)), 1),
+        "sequential_attention_merge_us_median": round(float(np.median(seq_att)), 1),
+        "prefetch_saving_us_median": round(float(np.median(seq_step - pre_step)), 1),
+        "hidden_frac_of_overlappable_median": round(float(np.median(hidden)), 3),
+        "misses_per_step_median": int(np.median(misses[1:])),
+        "h2d_gbs_sequential_median": round(float(np.median(
+            np.array(misses[1:]) * unit_bytes / (seq_io * 1e-6) / 1e9)), 1),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def attn_launch(lib, st, dims, li, stride_page, stride_head):
     """The step's attention launch alone (sparse_decode_attn, without its merge)."""
     b = st.buf
@@ -308,6 +413,9 @@ def main():
         return
     if args.workload == "host_tier_512k":
         host_tier_bench(args)
+        return
+    if args.workload == "host_tier_layers":
+        host_tier_layers_bench(args)
         return
     import torch
     from adaptive_sparse_paged_amd import inputs as I
