@@ -21,6 +21,12 @@ are this library's reading, stated once here:
 * If fewer slots can be made available than there are misses, the step sets
   the overflow flag, the misses that got no slot keep slot -1, and the step's
   outputs are not meaningful.
+
+Bucketed LRU ("SPIN", abstract, technique (2): a GPU-friendly bucketed LRU
+policy in the KV cache manager; the page gives no bucket rule, so this is
+this library's reading): with recency shift s, stamps are compared only in
+buckets of 2**s steps -- victims are ordered by (stamp >> s, unit id), so
+within one bucket the lower unit id goes first.  s = 0 is exact LRU.
 """
 
 from collections import OrderedDict
@@ -45,10 +51,11 @@ class LRUState:
         return c
 
 
-def resolve_step(state, requested_units, step):
+def resolve_step(state, requested_units, step, recency_shift=0):
     """Apply one step to ``state`` in place.
 
-    requested_units: iterable of unit ids (duplicates allowed).  Returns a dict
+    requested_units: iterable of unit ids (duplicates allowed); recency_shift:
+    victims are ordered by (stamp >> recency_shift, unit id).  Returns a dict
     with 'hits', 'misses', 'evictions', 'overflow' and 'placed' (list of
     (unit, slot) for the misses, ascending unit id; slot -1 if unplaced).
     """
@@ -66,7 +73,7 @@ def resolve_step(state, requested_units, step):
         inR = np.zeros(state.slot_of.shape[0], dtype=bool)
         inR[R] = True
         cand = np.nonzero((state.tag >= 0) & ~inR[np.maximum(state.tag, 0)])[0]
-        order = np.lexsort((state.tag[cand], state.stamp[cand]))
+        order = np.lexsort((state.tag[cand], state.stamp[cand] >> int(recency_shift)))
         victims = cand[order[:r]]
         avail = np.sort(np.concatenate([free, victims]))
 
@@ -120,4 +127,42 @@ def textbook_lru_trace(capacity, steps_units):
         for u in R:
             lru[u] = True
         out.append((len(hits), len(misses), ev, frozenset(lru.keys())))
+    return out
+
+
+def textbook_bucketed_trace(capacity, steps_units, shift):
+    """Bucketed LRU kept as recency buckets: bucket k holds the resident units
+    last used in steps [k * 2**shift, (k + 1) * 2**shift).  A miss in a full
+    cache evicts the lowest unit id of the oldest non-empty bucket, among the
+    units the step does not request.  Returns per step (hits, misses,
+    evictions, resident set)."""
+    buckets = {}          # bucket -> set of units
+    where = {}            # unit -> bucket
+    out = []
+    for t, units in enumerate(steps_units):
+        R = sorted(set(int(u) for u in units))
+        Rset = set(R)
+        hits = [u for u in R if u in where]
+        misses = [u for u in R if u not in where]
+        ev = 0
+        for u in misses:
+            if len(where) >= capacity:
+                victim = None
+                for k in sorted(buckets):
+                    cands = [v for v in buckets[k] if v not in Rset]
+                    if cands:
+                        victim = min(cands)
+                        break
+                if victim is None:
+                    raise OverflowError("more distinct units in one step than slots")
+                buckets[where.pop(victim)].discard(victim)
+                ev += 1
+            where[u] = None
+        now = t >> shift
+        for u in R:
+            if where[u] is not None:
+                buckets[where[u]].discard(u)
+            where[u] = now
+            buckets.setdefault(now, set()).add(u)
+        out.append((len(hits), len(misses), ev, frozenset(where)))
     return out

@@ -353,6 +353,42 @@ def test_lru_matches_textbook_trace():
         assert [s for _, s in placed] == sorted(s for _, s in placed)
 
 
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+def test_bucketed_lru_matches_bucket_model(shift):
+    """Victims ordered by (stamp >> s, unit id) against a model that keeps
+    recency buckets explicitly; s = 0 is also the textbook LRU."""
+    C, n_units = 40, 300
+    rng = np.random.default_rng(11 + shift)
+    steps = []
+    cur = rng.choice(n_units, size=30, replace=False)
+    for t in range(50):
+        steps.append(cur.copy())
+        keep = rng.choice(cur, size=24, replace=False)
+        fresh = rng.choice(np.setdiff1d(np.arange(n_units), keep), size=6, replace=False)
+        cur = np.concatenate([keep, fresh])
+    ref = O.textbook_bucketed_trace(C, steps, shift)
+    if shift == 0:
+        assert [r[:3] for r in ref] == [r[:3] for r in O.textbook_lru_trace(C, steps)]
+    st = O.LRUState(C, n_units)
+    for t, units in enumerate(steps):
+        r = O.resolve_step(st, units, t, recency_shift=shift)
+        hits, misses, ev, resident = ref[t]
+        assert (r["hits"], r["misses"], r["evictions"], r["overflow"]) == (hits, misses, ev, 0)
+        assert set(st.tag[st.tag >= 0].tolist()) == set(resident)
+
+
+def test_bucketed_lru_worked_case():
+    """Three slots; units 2, 1, 3 used at steps 0, 1, 2, then unit 4 misses.
+    Exact LRU evicts unit 2 (oldest); with buckets of 2 steps, units 2 and 1
+    share the oldest bucket and the lower id, 1, goes."""
+    steps = [[2], [1], [3], [4]]
+    for shift, victim in ((0, 2), (1, 1)):
+        st = O.LRUState(3, 10)
+        for t, units in enumerate(steps):
+            O.resolve_step(st, units, t, recency_shift=shift)
+        assert set(st.tag.tolist()) == {1, 2, 3, 4} - {victim}
+
+
 def test_lru_overflow_flagged():
     st = O.LRUState(8, 100)
     r = O.resolve_step(st, range(12), 0)
