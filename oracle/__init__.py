@@ -38,4 +38,5 @@ from .sparse_oracle import (  # noqa: F401
     list_accepted,
     unit_pages,
 )
-from .lru import LRUState, resolve_step, textbook_bucketed_trace, textbook_lru_trace  # noqa: F401
+from .lru import (LRUState, pooled_unit, resolve_pooled_step, resolve_step,  # noqa: F401
+                  textbook_bucketed_trace, textbook_lru_trace)

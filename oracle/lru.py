@@ -79,6 +79,7 @@ def resolve_step(state, requested_units, step, recency_shift=0):
 
     evictions = 0
     placed = []
+    evicting = []
     for i, u in enumerate(misses):
         if i >= avail.size:
             placed.append((int(u), -1))
@@ -88,13 +89,48 @@ def resolve_step(state, requested_units, step, recency_shift=0):
         if old >= 0:
             state.slot_of[old] = -1
             evictions += 1
+            evicting.append(int(u))
         state.tag[s] = u
         state.stamp[s] = step
         state.slot_of[u] = s
         placed.append((int(u), s))
     overflow = int(misses.size > avail.size)
     return {"hits": int(hits.size), "misses": int(misses.size),
-            "evictions": evictions, "overflow": overflow, "placed": placed}
+            "evictions": evictions, "overflow": overflow, "placed": placed,
+            "hit_units": hits, "evicting_units": evicting}
+
+
+def pooled_unit(b, h, p, kv_heads, max_pages):
+    """Unit id in a pool shared by every request: (b * Hkv + h) * max_pages + p."""
+    return (b * kv_heads + h) * max_pages + p
+
+
+def resolve_pooled_step(state, units_per_request, step, units_per_req_space, recency_shift=0):
+    """One step of a cache pool shared by all requests ("SPIN", abstract,
+    technique (2): per-request HBM budgets sized dynamically -- here a
+    request holds as many slots as the pool-wide replacement leaves it).
+    The rule is resolve_step's over pooled unit ids (ascending pooled id
+    places the misses, so request b's misses precede request b+1's).
+    units_per_request[b]: pooled ids requested by request b;
+    units_per_req_space = Hkv * max_pages.  Returns resolve_step's dict plus
+    'per_request': [B][4] hits, misses, evictions (slots taken from resident
+    units by that request's misses), overflow (a miss of that request got no
+    slot)."""
+    allu = [u for us in units_per_request for u in us]
+    r = resolve_step(state, allu, step, recency_shift)
+    B = len(units_per_request)
+    per = np.zeros((B, 4), dtype=np.int64)
+    for u in r["hit_units"]:
+        per[int(u) // units_per_req_space, 0] += 1
+    for u, s in r["placed"]:
+        b = u // units_per_req_space
+        per[b, 1] += 1
+        if s < 0:
+            per[b, 3] = 1
+    for u in r["evicting_units"]:
+        per[u // units_per_req_space, 2] += 1
+    r["per_request"] = per
+    return r
 
 
 def textbook_lru_trace(capacity, steps_units):

@@ -389,6 +389,37 @@ def test_bucketed_lru_worked_case():
         assert set(st.tag.tolist()) == {1, 2, 3, 4} - {victim}
 
 
+def test_pooled_cache_without_pressure_equals_per_request_caches():
+    """A pool large enough never to evict gives every request the hits and
+    misses it would have in a cache of its own; under pressure the pool is
+    one LRU over pooled ids, matching the textbook trace on those ids."""
+    B, H, MP = 3, 2, 50
+    space = H * MP
+    rng = np.random.default_rng(21)
+    steps = []
+    for t in range(12):
+        steps.append([sorted(set(O.pooled_unit(b, h, int(p), H, MP)
+                                 for h in range(H)
+                                 for p in rng.choice(MP, size=6, replace=False)))
+                      for b in range(B)])
+    big = O.LRUState(B * space, B * space)
+    own = [O.LRUState(space, space) for _ in range(B)]
+    for t, per_req in enumerate(steps):
+        r = O.resolve_pooled_step(big, per_req, t, space)
+        assert r["evictions"] == 0
+        for b in range(B):
+            rb = O.resolve_step(own[b], [u - b * space for u in per_req[b]], t)
+            assert r["per_request"][b].tolist() == [rb["hits"], rb["misses"], 0, 0]
+    small = O.LRUState(40, B * space)
+    ref = O.textbook_lru_trace(40, [[u for us in pr for u in us] for pr in steps])
+    for t, per_req in enumerate(steps):
+        r = O.resolve_pooled_step(small, per_req, t, space)
+        hits, misses, ev, resident = ref[t]
+        assert (r["hits"], r["misses"], r["evictions"]) == (hits, misses, ev)
+        assert r["per_request"][:, :3].sum(0).tolist() == [hits, misses, ev]
+        assert set(small.tag[small.tag >= 0].tolist()) == set(resident)
+
+
 def test_lru_overflow_flagged():
     st = O.LRUState(8, 100)
     r = O.resolve_step(st, range(12), 0)
