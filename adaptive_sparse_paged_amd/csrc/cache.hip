@@ -20,7 +20,10 @@
 // wave per missed unit copies its 8 KiB from pinned host memory into the slot
 // (device-initiated reads over PCIe; no host involvement).
 
+#include <algorithm>
+
 #include "common.h"
+#include "lru_select.h"
 
 namespace sp {
 
@@ -36,18 +39,17 @@ struct MissRec {
 
 __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
-    int max_pages, int C, const int32_t* __restrict__ step_counter, int32_t* __restrict__ slot_tag,
+    int max_pages, int C, int recency_shift, const int32_t* __restrict__ step_counter,
+    int32_t* __restrict__ slot_tag,
     int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
     int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats, MissRec* __restrict__ misses,
     int32_t* __restrict__ miss_count) {
   __shared__ uint8_t req[kMaxSlots];       // slot holds a unit requested this step
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
-  __shared__ uint32_t hist[2048];
+  __shared__ SelectScratch sel;
   __shared__ uint32_t scan32[kResThreads / 64];
   __shared__ unsigned long long scan64[kResThreads / 64];
   __shared__ int32_t head_off[kMaxKvHeads + 1];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_below;
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -144,80 +146,21 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   block_excl_scan<uint32_t, kResThreads>(ncand, scan32, NC);
   const uint32_t r = (M > F) ? min(M - F, NC) : 0u;   // victims to take
 
-  // ---- r least recently used candidates: radix select on (stamp, unit) --
-  // key = stamp * 2^32 + unit; keys are distinct, so exactly r keys are <= kappa
+  // ---- r least recently used candidates: radix select on the keys -------
+  // key = (stamp >> shift) * 2^32 + unit; keys are distinct, so exactly r
+  // keys are <= kappa
   unsigned long long kappa = 0ull;
   bool take_all = (r == NC);
   if (r > 0u && !take_all) {
-    unsigned long long kmin = ~0ull, kmax = 0ull;
-    for (int k = 0; k < kSPT; ++k) {
-      const int s = k * kResThreads + tid;
-      if (s < C && tags[s] >= 0 && !req[s]) {
-        const unsigned long long key =
-            ((unsigned long long)(uint32_t)stamps[s] << 32) | (uint32_t)tags[s];
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
-    }
-    // block min / max through the 64-bit lane shuffles and LDS
-    __shared__ unsigned long long red_lo[kResThreads / 64], red_hi[kResThreads / 64];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, (unsigned long long)__shfl_xor((long long)kmin, o, 64));
-      kmax = max(kmax, (unsigned long long)__shfl_xor((long long)kmax, o, 64));
-    }
-    if (lane_id() == 0) {
-      red_lo[tid >> 6] = kmin;
-      red_hi[tid >> 6] = kmax;
-    }
-    __syncthreads();
-    kmin = ~0ull;
-    kmax = 0ull;
-    for (int w = 0; w < kResThreads / 64; ++w) {
-      kmin = min(kmin, red_lo[w]);
-      kmax = max(kmax, red_hi[w]);
-    }
-    const int top = 63 - __clzll(kmin ^ kmax);   // kmin != kmax since r < NC
-    unsigned long long hi_mask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
-    unsigned long long prefix = kmin & hi_mask;
-    uint32_t need = r;                            // keys still to take, ascending
-    int lo = top + 1;
-    while (lo > 0) {
-      const int width = min(11, lo);
-      const int sh = lo - width, nb = 1 << width;
-      for (int k = tid; k < nb; k += kResThreads) hist[k] = 0u;
-      __syncthreads();
-      for (int k = 0; k < kSPT; ++k) {
-        const int s = k * kResThreads + tid;
-        if (s < C && tags[s] >= 0 && !req[s]) {
-          const unsigned long long key =
-              ((unsigned long long)(uint32_t)stamps[s] << 32) | (uint32_t)tags[s];
-          if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-        }
-      }
-      __syncthreads();
-      // the bin where the count from the bottom reaches `need`
-      const int b0 = 2 * tid, b1 = 2 * tid + 1;
-      const uint32_t c0 = (b0 < nb) ? hist[b0] : 0u, c1 = (b1 < nb) ? hist[b1] : 0u;
-      uint32_t tot;
-      const uint32_t below0 = block_excl_scan<uint32_t, kResThreads>(c0 + c1, scan32, tot);
-      const uint32_t below1 = below0 + c0;
-      if (b0 < nb && below0 < need && need <= below0 + c0) {
-        s_bin = b0;
-        s_below = below0;
-      }
-      if (b1 < nb && below1 < need && need <= below1 + c1) {
-        s_bin = b1;
-        s_below = below1;
-      }
-      __syncthreads();
-      need -= s_below;
-      prefix |= (unsigned long long)s_bin << sh;
-      hi_mask |= (unsigned long long)(nb - 1) << sh;
-      lo = sh;
-      __syncthreads();
-    }
-    kappa = prefix;   // the r-th smallest key
+    kappa = select_rth_key<kResThreads>(
+        C, r,
+        [&](int s, unsigned long long& key) {
+          const int tg = tags[s];
+          if (tg < 0 || req[s]) return false;
+          key = lru_key(stamps[s], tg, recency_shift);
+          return true;
+        },
+        sel);
   }
 
   // ---- available slots in ascending order: free, plus victims -------------
@@ -230,11 +173,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     if (s >= C) break;
     const int tg = tags[s];
     bool av = tg < 0;
-    if (!av && r > 0u && !req[s]) {
-      const unsigned long long key =
-          ((unsigned long long)(uint32_t)stamps[s] << 32) | (uint32_t)tg;
-      av = take_all || key <= kappa;
-    }
+    if (!av && r > 0u && !req[s])
+      av = take_all || lru_key(stamps[s], tg, recency_shift) <= kappa;
     navail += av ? 1u : 0u;
   }
   uint32_t A;
@@ -244,11 +184,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     if (s >= C) break;
     const int tg = tags[s];
     bool av = tg < 0;
-    if (!av && r > 0u && !req[s]) {
-      const unsigned long long key =
-          ((unsigned long long)(uint32_t)stamps[s] << 32) | (uint32_t)tg;
-      av = take_all || key <= kappa;
-    }
+    if (!av && r > 0u && !req[s])
+      av = take_all || lru_key(stamps[s], tg, recency_shift) <= kappa;
     if (av) avail[rank++] = s;
   }
   const uint32_t placed = min(M, A);
@@ -333,6 +270,236 @@ __global__ __launch_bounds__(256) void fetch_kernel(const uint16_t* __restrict__
   }
 }
 
+
+// ---- one pool shared by every request --------------------------------------
+// Pooled unit id g = (b * Hkv + h) * max_pages + p; slots 0 .. S-1 belong to
+// no request in particular.  The rules above apply over pooled ids: the
+// requested set is the union over requests, and misses in ascending pooled
+// id (so request by request) take the available slots in ascending order --
+// a request holds as many slots as the pool-wide replacement leaves it.
+//   pool_mark_kernel   one workgroup per request: hits (stamp, mark, slot id)
+//                      and the request's hit and miss counts;
+//   pool_victim_kernel one workgroup: each request's miss-rank offset, free
+//                      slots, the victims (radix select over the pool), the
+//                      ascending list of available slots; clears the marks;
+//   pool_place_kernel  one workgroup per request: its misses, ascending, take
+//                      avail[offset + rank]; statistics;
+//   pool_fetch_kernel  copies every placed miss from pinned host memory.
+constexpr int kMaxPoolSlots = 1 << 22;
+
+__device__ __forceinline__ void request_heads(const int32_t* __restrict__ sel_counts, int b,
+                                              int hkv, int max_pages, int32_t* head_off) {
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int h = 0; h < hkv; ++h) {
+      head_off[h] = acc;
+      acc += min(max(sel_counts[b * hkv + h], 0), max_pages);
+    }
+    head_off[hkv] = acc;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
+    int max_pages, int S, const int32_t* __restrict__ step_counter,
+    int32_t* __restrict__ slot_stamp, const int32_t* __restrict__ unit_slot,
+    int32_t* __restrict__ sel_phys, uint8_t* __restrict__ req, int32_t* __restrict__ counts) {
+  __shared__ int32_t head_off[kMaxKvHeads + 1];
+  __shared__ unsigned long long scan64[kResThreads / 64];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int step = *step_counter;
+  request_heads(sel_counts, b, hkv, max_pages, head_off);
+  const int E = head_off[hkv];
+  uint32_t m_local = 0u, h_local = 0u;
+  for (int e = tid; e < E; e += kResThreads) {
+    int h = 0;
+    while (e >= head_off[h + 1]) ++h;
+    const int64_t li = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
+    const int p = sel_pages[li];
+    int sk = -2;
+    if (p >= 0 && p < max_pages) {
+      sk = unit_slot[(int64_t)(b * hkv + h) * max_pages + p];
+      if (sk >= S) sk = -2;                  // corrupt state: never index past the pool
+    }
+    if (sk >= 0) {
+      ++h_local;
+      req[sk] = 1;
+      slot_stamp[sk] = step;
+      sel_phys[li] = sk;
+    } else if (sk == -1) {
+      ++m_local;
+    } else {
+      sel_phys[li] = -1;                     // page id out of range: an empty page
+    }
+  }
+  unsigned long long tot;
+  block_excl_scan<unsigned long long, kResThreads>(
+      ((unsigned long long)h_local << 32) | m_local, scan64, tot);
+  if (tid == 0) {
+    counts[2 * b] = (int32_t)(tot >> 32);
+    counts[2 * b + 1] = (int32_t)(uint32_t)tot;
+  }
+}
+
+__global__ __launch_bounds__(kResThreads) void pool_victim_kernel(
+    int B, int S, int recency_shift, const int32_t* __restrict__ slot_tag,
+    const int32_t* __restrict__ slot_stamp, uint8_t* __restrict__ req,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ moff, int32_t* __restrict__ avail,
+    int32_t* __restrict__ placed_out) {
+  __shared__ SelectScratch sel;
+  __shared__ uint32_t scan32[kResThreads / 64];
+  const int tid = threadIdx.x;
+  // each request's miss-rank offset: exclusive prefix of the miss counts
+  uint32_t M = 0u;
+  for (int base = 0; base < B; base += kResThreads) {
+    const int b = base + tid;
+    const uint32_t m = (b < B) ? (uint32_t)counts[2 * b + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t, kResThreads>(m, scan32, tot);
+    if (b < B) moff[b] = (int32_t)(M + ex);
+    M += tot;
+  }
+  uint32_t placed = 0u;
+  if (M > 0u) {
+    uint32_t nfree = 0u, ncand = 0u;
+    for (int s = tid; s < S; s += kResThreads) {
+      const int tg = slot_tag[s];
+      nfree += (tg < 0) ? 1u : 0u;
+      ncand += (tg >= 0 && !req[s]) ? 1u : 0u;
+    }
+    uint32_t F, NC;
+    block_excl_scan<uint32_t, kResThreads>(nfree, scan32, F);
+    block_excl_scan<uint32_t, kResThreads>(ncand, scan32, NC);
+    const uint32_t r = (M > F) ? min(M - F, NC) : 0u;
+    unsigned long long kappa = 0ull;
+    const bool take_all = (r == NC);
+    if (r > 0u && !take_all) {
+      kappa = select_rth_key<kResThreads>(
+          S, r,
+          [&](int s, unsigned long long& key) {
+            const int tg = slot_tag[s];
+            if (tg < 0 || req[s]) return false;
+            key = lru_key(slot_stamp[s], tg, recency_shift);
+            return true;
+          },
+          sel);
+    }
+    // available slots, ascending: each thread ranks a blocked run
+    const int run = (S + kResThreads - 1) / kResThreads;
+    const int s0 = tid * run;
+    auto available = [&](int s) {
+      const int tg = slot_tag[s];
+      if (tg < 0) return true;
+      if (r == 0u || req[s]) return false;
+      return take_all || lru_key(slot_stamp[s], tg, recency_shift) <= kappa;
+    };
+    uint32_t navail = 0u;
+    for (int k = 0; k < run && s0 + k < S; ++k) navail += available(s0 + k) ? 1u : 0u;
+    uint32_t A;
+    uint32_t rank = block_excl_scan<uint32_t, kResThreads>(navail, scan32, A);
+    for (int k = 0; k < run && s0 + k < S; ++k)
+      if (available(s0 + k)) avail[rank++] = s0 + k;
+    placed = min(M, A);
+  }
+  __syncthreads();                           // every read of the marks is done
+  for (int s = tid; s < S; s += kResThreads) req[s] = 0;
+  if (tid == 0) *placed_out = (int32_t)placed;
+}
+
+__global__ __launch_bounds__(kResThreads) void pool_place_kernel(
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
+    int max_pages, const int32_t* __restrict__ step_counter, int32_t* __restrict__ slot_tag,
+    int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
+    int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ moff,
+    const int32_t* __restrict__ avail, const int32_t* __restrict__ placed_in,
+    MissRec* __restrict__ misses) {
+  __shared__ int32_t head_off[kMaxKvHeads + 1];
+  __shared__ uint32_t scan32[kResThreads / 64];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int step = *step_counter;
+  request_heads(sel_counts, b, hkv, max_pages, head_off);
+  const int E = head_off[hkv];
+  const uint32_t P = (uint32_t)*placed_in, off = (uint32_t)moff[b];
+  const uint32_t Mb = (uint32_t)counts[2 * b + 1];
+  const int64_t n_units = (int64_t)gridDim.x * hkv * max_pages;
+  uint32_t ev_local = 0u, mbase = 0u;
+  if (Mb > 0u) {
+    for (int base = 0; base < E; base += kResThreads) {
+      const int e = base + tid;
+      uint32_t miss = 0u;
+      int64_t v = -1, li = 0;
+      if (e < E) {
+        int h = 0;
+        while (e >= head_off[h + 1]) ++h;
+        li = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
+        const int p = sel_pages[li];
+        if (p >= 0 && p < max_pages) {
+          v = (int64_t)(b * hkv + h) * max_pages + p;
+          miss = (unit_slot[v] == -1) ? 1u : 0u;
+        }
+      }
+      uint32_t tot;
+      const uint32_t mr = off + mbase + block_excl_scan<uint32_t, kResThreads>(miss, scan32, tot);
+      if (miss) {
+        if (mr < P) {
+          const int sl = avail[mr];
+          const int old = slot_tag[sl];
+          if (old >= 0) {
+            if (old < n_units) unit_slot[old] = -1;
+            ++ev_local;
+          }
+          slot_tag[sl] = (int32_t)v;
+          slot_stamp[sl] = step;
+          unit_slot[v] = sl;
+          sel_phys[li] = sl;
+          misses[mr] = MissRec{(int32_t)v, sl};
+        } else {
+          sel_phys[li] = -1;
+        }
+      }
+      mbase += tot;
+    }
+  }
+  uint32_t evictions;
+  block_excl_scan<uint32_t, kResThreads>(ev_local, scan32, evictions);
+  if (tid == 0) {
+    stats[b * 4 + 0] = counts[2 * b];
+    stats[b * 4 + 1] = (int32_t)Mb;
+    stats[b * 4 + 2] = (int32_t)evictions;
+    stats[b * 4 + 3] = (off + Mb > P) ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void pool_fetch_kernel(const uint16_t* __restrict__ host_kv,
+                                                         uint16_t* __restrict__ cache_kv, int hkv,
+                                                         int max_pages,
+                                                         const MissRec* __restrict__ misses,
+                                                         const int32_t* __restrict__ placed_in,
+                                                         int waves,
+                                                         int32_t* __restrict__ step_counter) {
+  // every workgroup of the earlier kernels has read the step: advance it
+  if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int P = *placed_in;
+  const int64_t per_req = (int64_t)hkv * max_pages;
+  for (int i = w; i < P; i += waves) {
+    const MissRec m = misses[i];
+    const int64_t b = m.unit / per_req, rest = m.unit - b * per_req;
+    const int64_t h = rest / max_pages, p = rest - h * max_pages;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        host_kv + ((b * max_pages + p) * hkv + h) * kUnitElems);
+    u32x4* dst = reinterpret_cast<u32x4*>(cache_kv + (int64_t)m.slot * kUnitElems);
+    u32x4 t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = __builtin_nontemporal_load(src + k * 64 + lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = t[k];
+  }
+}
+
 }  // namespace sp
 
 extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity) {
@@ -340,32 +507,135 @@ extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t 
   return (size_t)dims->batch * ((size_t)capacity * sizeof(sp::MissRec) + sizeof(int32_t)) + 256;
 }
 
-extern "C" sparse_status sparse_hbm_cache_resolve(
-    const sparse_dims* dims, const int32_t* sel_counts, const int32_t* sel_pages,
-    const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
-    int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter, int32_t* sel_phys,
-    int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Per-request workspace: miss records [B][C], then the per-request counts.
+// Pooled workspace: marks [S] (padded), avail [S], miss records [S],
+// counts [B][2], offsets [B], placed [1].
+size_t pooled_ws_bytes(int B, int S) {
+  const size_t req = ((size_t)S + 255) / 256 * 256;
+  return req + (size_t)S * sizeof(int32_t) + (size_t)S * sizeof(sp::MissRec) +
+         (size_t)B * 3 * sizeof(int32_t) + sizeof(int32_t) + 256;
+}
+
+sparse_status check_cache_args(const sparse_dims* dims, const int32_t* sel_counts,
+                               const int32_t* sel_pages, const uint16_t* host_kv,
+                               uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
+                               int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                               int32_t* sel_phys, int32_t* stats) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!sel_counts || !sel_pages || !host_kv || !cache_kv || !slot_tag || !slot_stamp ||
       !unit_slot || !step_counter || !sel_phys || !stats)
     return SPARSE_ERR_INVALID;
   if (capacity < 1) return SPARSE_ERR_INVALID;
-  if (capacity > sp::kMaxSlots || dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
   if (!sp::aligned(host_kv, 16) || !sp::aligned(cache_kv, 16)) return SPARSE_ERR_INVALID;
-  if (!ws || ws_bytes < sparse_cache_workspace_bytes(dims, capacity) || !sp::aligned(ws, 8))
-    return SPARSE_ERR_WORKSPACE;
+  if (dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
+  return SPARSE_OK;
+}
+
+// About 256 fetching waves in all (each has one 8 KiB unit in flight) keep the
+// PCIe link busy; more only take compute units from the attention that may
+// run beside the fetch.
+constexpr int kFetchWaves = 256;
+
+sparse_status resolve_per_request(const sparse_dims* dims, int shift, const int32_t* sel_counts,
+                                  const int32_t* sel_pages, const uint16_t* host_kv,
+                                  uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
+                                  int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                                  int32_t* sel_phys, int32_t* stats, void* ws, hipStream_t s) {
   const int B = dims->batch, hkv = dims->num_kv_heads;
   sp::MissRec* misses = static_cast<sp::MissRec*>(ws);
   int32_t* miss_count = reinterpret_cast<int32_t*>(misses + (size_t)B * capacity);
-  hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(sp::resolve_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
-                     sel_pages, hkv, dims->max_pages, capacity, step_counter, slot_tag, slot_stamp,
-                     unit_slot, sel_phys, stats, misses, miss_count);
+                     sel_pages, hkv, dims->max_pages, capacity, shift, step_counter, slot_tag,
+                     slot_stamp, unit_slot, sel_phys, stats, misses, miss_count);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  const int waves_per_req = 256;   // 64 workgroups of 4 waves per request
+  // at least 8 waves per request, a multiple of 4
+  const int waves_per_req = std::max(8, std::min(256, (kFetchWaves / B + 3) / 4 * 4));
   hipLaunchKernelGGL(sp::fetch_kernel, dim3(waves_per_req / 4, B), dim3(256), 0, s, host_kv,
                      cache_kv, hkv, dims->max_pages, capacity, misses, miss_count,
                      waves_per_req, step_counter);
   return sp::launch_status();
+}
+
+sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* sel_counts,
+                             const int32_t* sel_pages, const uint16_t* host_kv,
+                             uint16_t* cache_kv, int32_t S, int32_t* slot_tag,
+                             int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                             int32_t* sel_phys, int32_t* stats, void* ws, hipStream_t s) {
+  const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* req = base;
+  int32_t* avail = reinterpret_cast<int32_t*>(base + ((size_t)S + 255) / 256 * 256);
+  sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(avail + S);
+  int32_t* counts = reinterpret_cast<int32_t*>(misses + S);
+  int32_t* moff = counts + 2 * (size_t)B;
+  int32_t* placed = moff + B;
+  hipLaunchKernelGGL(sp::pool_mark_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
+                     sel_pages, hkv, MP, S, step_counter, slot_stamp, unit_slot, sel_phys, req,
+                     counts);
+  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  hipLaunchKernelGGL(sp::pool_victim_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, S, shift,
+                     slot_tag, slot_stamp, req, counts, moff, avail, placed);
+  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
+                     sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,
+                     stats, counts, moff, avail, placed, misses);
+  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  hipLaunchKernelGGL(sp::pool_fetch_kernel, dim3(kFetchWaves / 4), dim3(256), 0, s, host_kv,
+                     cache_kv, hkv, MP, misses, placed, kFetchWaves, step_counter);
+  return sp::launch_status();
+}
+
+}  // namespace
+
+extern "C" sparse_status sparse_hbm_cache_resolve(
+    const sparse_dims* dims, const int32_t* sel_counts, const int32_t* sel_pages,
+    const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
+    int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter, int32_t* sel_phys,
+    int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  const sparse_cache_policy exact = {0, 0};
+  return sparse_hbm_cache_resolve_policy(dims, &exact, sel_counts, sel_pages, host_kv, cache_kv,
+                                         capacity, slot_tag, slot_stamp, unit_slot, step_counter,
+                                         sel_phys, stats, ws, ws_bytes, stream);
+}
+
+extern "C" size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
+                                                      const sparse_cache_policy* policy,
+                                                      int32_t capacity) {
+  if (!policy || sp::check_dims(dims) != SPARSE_OK || capacity < 1) return 0;
+  if (policy->pooled) return pooled_ws_bytes(dims->batch, capacity);
+  return sparse_cache_workspace_bytes(dims, capacity);
+}
+
+extern "C" sparse_status sparse_hbm_cache_resolve_policy(
+    const sparse_dims* dims, const sparse_cache_policy* policy, const int32_t* sel_counts,
+    const int32_t* sel_pages, const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity,
+    int32_t* slot_tag, int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+    int32_t* sel_phys, int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  sparse_status st = check_cache_args(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity,
+                                      slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
+                                      stats);
+  if (st != SPARSE_OK) return st;
+  if (!policy || policy->recency_shift < 0 || policy->recency_shift > 30 ||
+      (policy->pooled != 0 && policy->pooled != 1))
+    return SPARSE_ERR_INVALID;
+  const int64_t units = (int64_t)dims->batch * dims->num_kv_heads * dims->max_pages;
+  if (policy->pooled) {
+    if (capacity > sp::kMaxPoolSlots || units > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
+  } else if (capacity > sp::kMaxSlots) {
+    return SPARSE_ERR_UNSUPPORTED;
+  }
+  if (!ws || ws_bytes < sparse_cache_policy_workspace_bytes(dims, policy, capacity) ||
+      !sp::aligned(ws, 8))
+    return SPARSE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (policy->pooled)
+    return resolve_pooled(dims, policy->recency_shift, sel_counts, sel_pages, host_kv, cache_kv,
+                          capacity, slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
+                          stats, ws, s);
+  return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, host_kv,
+                             cache_kv, capacity, slot_tag, slot_stamp, unit_slot, step_counter,
+                             sel_phys, stats, ws, s);
 }

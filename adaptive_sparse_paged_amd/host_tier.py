@@ -31,31 +31,38 @@ def device_view_ok(host):
 
 
 class HbmPageCache:
-    """Per-request HBM caches of `capacity` units over a pinned host KV pool
-    [B][max_pages][Hkv][2][2048] (bf16 bits)."""
+    """HBM page cache over a pinned host KV pool [B][max_pages][Hkv][2][2048]
+    (bf16 bits): per request `capacity` units (pooled=False), or one pool of
+    `capacity` units shared by all requests (pooled=True).  recency_shift > 0
+    compares stamps in buckets of 2**recency_shift steps (bucketed LRU)."""
 
-    def __init__(self, dims, host_kv, capacity, device="cuda"):
+    def __init__(self, dims, host_kv, capacity, device="cuda", recency_shift=0, pooled=False):
         device_view_ok(host_kv)
         B, H, MP = dims.batch, dims.num_kv_heads, dims.max_pages
         if tuple(host_kv.shape[:3]) != (B, MP, H):
             raise ValueError("host_kv must be [B][max_pages][Hkv][2][2048]")
         self.dims, self.host_kv, self.capacity = dims, host_kv, int(capacity)
+        self.policy = lib.CachePolicy(int(recency_shift), 1 if pooled else 0)
+        self.pooled = bool(pooled)
+        slots = capacity if pooled else B * capacity
+        tag_shape = (capacity,) if pooled else (B, capacity)
         i32 = dict(dtype=torch.int32, device=device)
-        self.cache_kv = torch.zeros((B * capacity, UNIT_ELEMS), dtype=torch.int16, device=device)
-        self.slot_tag = torch.full((B, capacity), -1, **i32)
-        self.slot_stamp = torch.full((B, capacity), -1, **i32)
+        self.cache_kv = torch.zeros((slots, UNIT_ELEMS), dtype=torch.int16, device=device)
+        self.slot_tag = torch.full(tag_shape, -1, **i32)
+        self.slot_stamp = torch.full(tag_shape, -1, **i32)
         self.unit_slot = torch.full((B, H * MP), -1, **i32)
         self.stats = torch.zeros((B, 4), **i32)
         self.step_counter = torch.zeros(1, **i32)
-        self.ws = torch.zeros(lib.cache_workspace_bytes(dims, capacity), dtype=torch.uint8,
-                              device=device)
+        self.ws = torch.zeros(lib.cache_policy_workspace_bytes(dims, self.policy, capacity),
+                              dtype=torch.uint8, device=device)
 
     def resolve(self, sel_counts, sel_pages, sel_phys, stream=None):
         """Resolve one step's lists; the step number comes from (and advances)
         the device counter, so this can be captured and replayed."""
-        lib.hbm_cache_resolve(self.dims, sel_counts, sel_pages, self.host_kv, self.cache_kv,
-                              self.capacity, self.slot_tag, self.slot_stamp, self.unit_slot,
-                              self.step_counter, sel_phys, self.stats, self.ws, stream)
+        lib.hbm_cache_resolve_policy(self.dims, self.policy, sel_counts, sel_pages,
+                                     self.host_kv, self.cache_kv, self.capacity, self.slot_tag,
+                                     self.slot_stamp, self.unit_slot, self.step_counter,
+                                     sel_phys, self.stats, self.ws, stream)
 
     def pool_args(self):
         """(kv, stride_page, stride_head, pool_pages) for sparse_decode_attn."""

@@ -30,6 +30,8 @@ EXPORTS = (
     "sparse_hbm_cache_resolve",
     "sparse_select_topk",
     "sparse_append_tokens",
+    "sparse_cache_policy_workspace_bytes",
+    "sparse_hbm_cache_resolve_policy",
 )
 
 
@@ -54,11 +56,19 @@ def make_dims(batch, q_heads, kv_heads, max_pages, head_dim=128, page_size=16):
     return Dims(batch, q_heads, kv_heads, head_dim, page_size, max_pages)
 
 
+class CachePolicy(ctypes.Structure):
+    _fields_ = [
+        ("recency_shift", ctypes.c_int32),
+        ("pooled", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _D = ctypes.POINTER(Dims)
+_CP = ctypes.POINTER(CachePolicy)
 
 _SIGS = {
     "sparse_version": (ctypes.c_char_p, []),
@@ -78,6 +88,9 @@ _SIGS = {
     "sparse_append_tokens": (_I32, [_D, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "sparse_cache_policy_workspace_bytes": (ctypes.c_size_t, [_D, _CP, _I32]),
+    "sparse_hbm_cache_resolve_policy": (_I32, [_D, _CP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                               _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -197,6 +210,27 @@ def hbm_cache_resolve(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity, 
         capacity, _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), _ptr(step_counter),
         _ptr(sel_phys),
         _ptr(stats), _ptr(ws), nbytes, _stream(stream)))
+
+
+def cache_policy_workspace_bytes(dims, policy, capacity):
+    return int(load().sparse_cache_policy_workspace_bytes(ctypes.byref(dims),
+                                                          ctypes.byref(policy), capacity))
+
+
+def hbm_cache_resolve_policy(dims, policy, sel_counts, sel_pages, host_kv, cache_kv, capacity,
+                             slot_tag, slot_stamp, unit_slot, step_counter, sel_phys, stats, ws,
+                             stream=None):
+    """hbm_cache_resolve under a CachePolicy (bucketed recency, pooled slots)."""
+    _dev(sel_counts, sel_pages, cache_kv, slot_tag, slot_stamp, unit_slot, step_counter,
+         sel_phys, stats, ws)
+    if not host_kv.is_pinned():
+        raise ValueError("host_kv must be pinned host memory")
+    nbytes = ws.numel() * ws.element_size()
+    _check("sparse_hbm_cache_resolve_policy", load().sparse_hbm_cache_resolve_policy(
+        ctypes.byref(dims), ctypes.byref(policy), _ptr(sel_counts), _ptr(sel_pages),
+        _ptr(host_kv), _ptr(cache_kv), capacity, _ptr(slot_tag), _ptr(slot_stamp),
+        _ptr(unit_slot), _ptr(step_counter), _ptr(sel_phys), _ptr(stats), _ptr(ws), nbytes,
+        _stream(stream)))
 
 
 def select_topk(dims, logits, ctx_lens, page_table, k_pages, chunk_pages, sel_counts,

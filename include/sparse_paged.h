@@ -294,6 +294,64 @@ sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* s
                                        int32_t* step_counter, int32_t* sel_phys, int32_t* stats,
                                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Replacement policy of the host-tier cache (sparse_hbm_cache_resolve_policy).
+ *
+ * recency_shift -- bucketed LRU ([P1] page, the SPIN abstract, technique
+ *   (2): a GPU-friendly bucketed LRU policy; no bucket rule is given, this is
+ *   the library's reading): resident units are ordered for eviction by
+ *   (stamp >> recency_shift, unit id), i.e. stamps compared in buckets of
+ *   2^recency_shift steps, the lower unit id first within a bucket.
+ *   0 = exact LRU (sparse_hbm_cache_resolve).  0..30.
+ * pooled -- 0: one cache of `capacity` slots per request (as
+ *   sparse_hbm_cache_resolve).  1: one pool of `capacity` slots shared by all
+ *   requests ([P1] page, SPIN abstract, same technique: per-request HBM
+ *   budgets sized dynamically -- a request holds as many slots as the pool-wide
+ *   replacement leaves it).  Pooled unit id g = (b * Hkv + h) * max_pages +
+ *   p; every rule of sparse_hbm_cache_resolve applies over pooled ids (the
+ *   requested set is the union over requests; misses in ascending pooled id
+ *   take the available slots in ascending slot index).
+ */
+typedef struct {
+  int32_t recency_shift;
+  int32_t pooled;
+} sparse_cache_policy;
+
+/* Bytes of workspace sparse_hbm_cache_resolve_policy needs (host); 0 for
+ * invalid arguments.  Per-request: as sparse_cache_workspace_bytes.  Pooled:
+ * about 13 bytes per slot plus 12 per request. */
+size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
+                                           const sparse_cache_policy* policy,
+                                           int32_t capacity);
+
+/*
+ * sparse_hbm_cache_resolve_policy -- sparse_hbm_cache_resolve under a
+ * replacement policy (see sparse_cache_policy).  Arguments as
+ * sparse_hbm_cache_resolve, except when policy->pooled = 1:
+ *   capacity   slots of the pool, 1 .. 2^22 (B * Hkv * max_pages < 2^31)
+ *   cache_kv   bf16 [capacity][2][2048] device (stride_page 4096, stride_head
+ *              0, pool_pages = capacity for sparse_decode_attn)
+ *   slot_tag   int32 [capacity] pooled unit id held by each slot, -1 = free
+ *   slot_stamp int32 [capacity]
+ *   unit_slot  int32 [B][Hkv * max_pages] (the same shape: index = pooled id)
+ *   sel_phys   int32 [U][max_pages] out: slot index
+ *   stats      int32 [B][4] out: hits, misses, evictions made by that
+ *              request's misses, overflow (one of its misses got no slot)
+ * Enqueues three resolve kernels (per request, one over the pool, per
+ * request) and one fetch kernel.  Lists must hold distinct pages (as the
+ * selection writes them).  Errors: as sparse_hbm_cache_resolve; policy
+ * missing or out of range -> INVALID.
+ */
+sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
+                                              const sparse_cache_policy* policy,
+                                              const int32_t* sel_counts,
+                                              const int32_t* sel_pages, const uint16_t* host_kv,
+                                              uint16_t* cache_kv, int32_t capacity,
+                                              int32_t* slot_tag, int32_t* slot_stamp,
+                                              int32_t* unit_slot, int32_t* step_counter,
+                                              int32_t* sel_phys, int32_t* stats, void* ws,
+                                              size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -109,6 +109,21 @@ def test_null_and_value_checks(L):
                                       FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == lib.ERR_UNSUPPORTED
     assert L.sparse_hbm_cache_resolve(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
                                       FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == lib.ERR_WORKSPACE
+    pol = lambda shift, pooled, cap, nb, ws=FAKE: L.sparse_hbm_cache_resolve_policy(
+        ctypes.byref(d), ctypes.byref(lib.CachePolicy(shift, pooled)), FAKE, FAKE, FAKE, FAKE,
+        cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    assert L.sparse_hbm_cache_resolve_policy(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 64,
+                                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                             None) == lib.ERR_INVALID
+    assert pol(31, 0, 64, 1 << 30) == lib.ERR_INVALID
+    assert pol(-1, 0, 64, 1 << 30) == lib.ERR_INVALID
+    assert pol(0, 2, 64, 1 << 30) == lib.ERR_INVALID
+    assert pol(0, 0, 9000, 1 << 30) == lib.ERR_UNSUPPORTED      # per-request slot limit
+    assert pol(0, 1, (1 << 22) + 1, 1 << 40) == lib.ERR_UNSUPPORTED
+    need = L.sparse_cache_policy_workspace_bytes(ctypes.byref(d), ctypes.byref(lib.CachePolicy(3, 1)), 9000)
+    assert need >= 9000 * 13
+    assert pol(3, 1, 9000, need - 1) == lib.ERR_WORKSPACE
+    assert pol(3, 1, 9000, need, None) == lib.ERR_WORKSPACE
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
 

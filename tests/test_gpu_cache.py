@@ -20,18 +20,23 @@ from _gpu_case import feed_lists, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=None):
+def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=None,
+          shift=0, pooled=False):
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
     host, MP = I.build_host_pool(w, 0, lens=lens)
     assert MP == li.max_pages
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
-    cache = HbmPageCache(dims, host, C)
+    cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
     n_pages = min(I.pages_of(L) for L in lens)
     if lists is None:
         lists = I.drift_lists(w, n_pages, list_pages, steps, drift)
     B, H = w.batch, w.kv_heads
-    states = [O.LRUState(C, H * MP) for _ in range(B)]
+    space = H * MP
+    if pooled:
+        pool_state = O.LRUState(C, B * space)
+    else:
+        states = [O.LRUState(C, space) for _ in range(B)]
     st = SparseDecodeStep(dims, 0.99, chunk, scale=w.scale)
     layer = types.SimpleNamespace(w=w, dims=dims, li=li)
     sp_, sh_ = canonical_strides(H)
@@ -46,31 +51,61 @@ def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=N
         umap = cache.unit_slot.cpu().numpy()
         stats = cache.stats.cpu().numpy()
         phys = st.buf.sel_phys.cpu().numpy()
-        for b in range(B):
-            units = [h * MP + int(p) for h in range(H) for p in lists[t, b, h]]
-            r = O.resolve_step(states[b], units, t)
-            assert np.array_equal(tags[b], states[b].tag), (t, b, "tags")
-            assert np.array_equal(stamps[b], states[b].stamp), (t, b, "stamps")
-            assert np.array_equal(umap[b], states[b].slot_of), (t, b, "unit map")
-            assert stats[b].tolist() == [r["hits"], r["misses"], r["evictions"], r["overflow"]], (t, b)
-            for h in range(H):
-                u = b * H + h
-                k = len(lists[t, b, h])
-                want = [states[b].slot_of[h * MP + int(p)] for p in lists[t, b, h]]
-                want = [b * C + s if s >= 0 else -1 for s in want]
-                assert phys[u, :k].tolist() == want, (t, b, h, "slot ids")
-            out_stats.append(r)
-        # resident slots hold their units' bytes
-        cache_kv = cache.cache_kv.view(B, C, -1)
-        for b in range(B):
-            res = np.nonzero(tags[b] >= 0)[0]
+        if pooled:
+            per_req = [[O.pooled_unit(b, h, int(p), H, MP) for h in range(H) for p in lists[t, b, h]]
+                       for b in range(B)]
+            r = O.resolve_pooled_step(pool_state, per_req, t, space, recency_shift=shift)
+            assert np.array_equal(tags, pool_state.tag), (t, "tags")
+            assert np.array_equal(stamps, pool_state.stamp), (t, "stamps")
+            assert np.array_equal(umap.reshape(-1), pool_state.slot_of), (t, "unit map")
+            assert np.array_equal(stats, r["per_request"]), (t, "stats")
+            for b in range(B):
+                for h in range(H):
+                    u = b * H + h
+                    k = len(lists[t, b, h])
+                    want = [pool_state.slot_of[O.pooled_unit(b, h, int(p), H, MP)]
+                            for p in lists[t, b, h]]
+                    assert phys[u, :k].tolist() == [int(x) for x in want], (t, b, h, "slot ids")
+                out_stats.append(dict(hits=int(r["per_request"][b, 0]),
+                                      misses=int(r["per_request"][b, 1]),
+                                      evictions=int(r["per_request"][b, 2]),
+                                      overflow=int(r["per_request"][b, 3])))
+            # resident slots hold their units' bytes
+            res = np.nonzero(tags >= 0)[0]
             if not check_all_slots:
                 res = res[:: max(1, len(res) // 64)]
-            v = tags[b][res]
-            h, p = v // MP, v % MP
-            want = host[b, torch.from_numpy(p), torch.from_numpy(h)].reshape(len(res), -1)
-            got = cache_kv[b, torch.from_numpy(res).cuda()].cpu()
-            assert torch.equal(got, want), (t, b, "slot contents")
+            g = tags[res]
+            b_, rest = g // space, g % space
+            h_, p_ = rest // MP, rest % MP
+            want = host[torch.from_numpy(b_), torch.from_numpy(p_), torch.from_numpy(h_)]
+            got = cache.cache_kv[torch.from_numpy(res).cuda()].cpu()
+            assert torch.equal(got, want.reshape(len(res), -1)), (t, "slot contents")
+        else:
+            for b in range(B):
+                units = [h * MP + int(p) for h in range(H) for p in lists[t, b, h]]
+                r = O.resolve_step(states[b], units, t, recency_shift=shift)
+                assert np.array_equal(tags[b], states[b].tag), (t, b, "tags")
+                assert np.array_equal(stamps[b], states[b].stamp), (t, b, "stamps")
+                assert np.array_equal(umap[b], states[b].slot_of), (t, b, "unit map")
+                assert stats[b].tolist() == [r["hits"], r["misses"], r["evictions"], r["overflow"]], (t, b)
+                for h in range(H):
+                    u = b * H + h
+                    k = len(lists[t, b, h])
+                    want = [states[b].slot_of[h * MP + int(p)] for p in lists[t, b, h]]
+                    want = [b * C + s if s >= 0 else -1 for s in want]
+                    assert phys[u, :k].tolist() == want, (t, b, h, "slot ids")
+                out_stats.append(r)
+            # resident slots hold their units' bytes
+            cache_kv = cache.cache_kv.view(B, C, -1)
+            for b in range(B):
+                res = np.nonzero(tags[b] >= 0)[0]
+                if not check_all_slots:
+                    res = res[:: max(1, len(res) // 64)]
+                v = tags[b][res]
+                h, p = v // MP, v % MP
+                want = host[b, torch.from_numpy(p), torch.from_numpy(h)].reshape(len(res), -1)
+                got = cache_kv[b, torch.from_numpy(res).cuda()].cpu()
+                assert torch.equal(got, want), (t, b, "slot contents")
         # attention through the cache is bit-identical to attention over HBM
         if not any(r["overflow"] for r in out_stats[-B:]):
             kv, s_page, s_head, ppages = cache.pool_args()
@@ -171,3 +206,49 @@ def test_cache_resolver_in_graph(gpu_lib):
         st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)   # eager, same lists
         torch.cuda.synchronize()
         assert torch.equal(replay_out, st.buf.out)
+
+
+@pytest.mark.parametrize("shift", [1, 3])
+def test_cache_resolver_bucketed_lru(gpu_lib, shift):
+    """Bucketed recency (stamps compared in buckets of 2**shift steps, then
+    unit id) against the oracle, on lists that drift fast enough to evict."""
+    w = I.custom_workload("cache_bucket", 2, 8, 2, ("fixed", 3200), index=124)
+    say(f"[cache] bucketed LRU shift {shift}: B=2 Hkv=2, 48 slots, lists of 20, drift 25%")
+    stats = _case(w, C=48, list_pages=20, steps=16, drift=0.25, shift=shift)
+    assert sum(r["evictions"] for r in stats) > 0
+
+
+@pytest.mark.parametrize("shift", [0, 2])
+def test_cache_pool_shared_by_requests(gpu_lib, shift):
+    """One pool of slots for every request, with requests of different list
+    lengths (so their slot holdings differ), against the pooled oracle."""
+    w = I.custom_workload("cache_pool", 3, 8, 2, ("fixed", 3200), index=125)
+    rng = np.random.default_rng(7 + shift)
+    steps, H, n = 12, 2, 200
+    sizes = [6, 14, 24]                     # pages per list, per request
+    L = max(sizes)
+    lists = np.full((steps, 3, H, L), -1, dtype=np.int32)
+    cur = [[rng.choice(n, size=sizes[b], replace=False) for h in range(H)] for b in range(3)]
+    for t in range(steps):
+        for b in range(3):
+            for h in range(H):
+                lists[t, b, h, :sizes[b]] = np.sort(cur[b][h])
+                keep = rng.choice(cur[b][h], size=sizes[b] - sizes[b] // 3, replace=False)
+                fresh = rng.choice(np.setdiff1d(np.arange(n), keep), size=sizes[b] // 3,
+                                   replace=False)
+                cur[b][h] = np.concatenate([keep, fresh])
+    say(f"[cache] pooled, shift {shift}: 3 requests with lists of {sizes} pages, 100 slots")
+    stats = _case(w, C=100, list_pages=0, steps=steps, drift=0.0, chunk=5,
+                  lists=_ragged(lists, sizes), shift=shift, pooled=True)
+    assert sum(r["evictions"] for r in stats) > 0
+
+
+def _ragged(lists, sizes):
+    """Lists of per-request length as an object array [steps][B][H] of arrays."""
+    steps, B, H, _ = lists.shape
+    out = np.empty((steps, B, H), dtype=object)
+    for t in range(steps):
+        for b in range(B):
+            for h in range(H):
+                out[t, b, h] = lists[t, b, h, :sizes[b]]
+    return out
