@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
         C, r,
         [&](int s, unsigned long long& key) {
           const int tg = tags[s];
-          if (tg < 0 || req[s]) return false;
-          key = lru_key(stamps[s], tg, recency_shift);
-          return true;
+          const int st = stamps[s];
+          key = lru_key(st, tg, recency_shift);
+          return tg >= 0 && !req[s];
         },
         sel);
   }
@@ -346,9 +346,10 @@ __global__ __launch_bounds__(kResThreads) void pool_victim_kernel(
     int B, int S, int recency_shift, const int32_t* __restrict__ slot_tag,
     const int32_t* __restrict__ slot_stamp, uint8_t* __restrict__ req,
     const int32_t* __restrict__ counts, int32_t* __restrict__ moff, int32_t* __restrict__ avail,
-    int32_t* __restrict__ placed_out) {
+    unsigned long long* __restrict__ ckeys, int32_t* __restrict__ placed_out) {
   __shared__ SelectScratch sel;
   __shared__ uint32_t scan32[kResThreads / 64];
+  __shared__ unsigned long long scan64[kResThreads / 64];
   const int tid = threadIdx.x;
   // each request's miss-rank offset: exclusive prefix of the miss counts
   uint32_t M = 0u;
@@ -362,48 +363,85 @@ __global__ __launch_bounds__(kResThreads) void pool_victim_kernel(
   }
   uint32_t placed = 0u;
   if (M > 0u) {
-    uint32_t nfree = 0u, ncand = 0u;
-    for (int s = tid; s < S; s += kResThreads) {
-      const int tg = slot_tag[s];
-      nfree += (tg < 0) ? 1u : 0u;
-      ncand += (tg >= 0 && !req[s]) ? 1u : 0u;
+    // one pass over the pool: free slots counted, the keys of the victim
+    // candidates (resident, not requested) compacted into ckeys
+    constexpr int kB = 8;   // slots per thread whose loads are issued together
+    uint32_t F = 0u, NC = 0u;
+    for (int base = 0; base < S; base += kB * kResThreads) {
+      unsigned long long key[kB];
+      bool cand[kB];
+      uint32_t nf = 0u, nc = 0u;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int s = base + k * kResThreads + tid;
+        const bool in = s < S;
+        const int tg = in ? slot_tag[s] : 0;
+        const uint8_t rq = in ? req[s] : 1;
+        const int st = in ? slot_stamp[s] : 0;
+        cand[k] = in && tg >= 0 && !rq;
+        nf += (in && tg < 0) ? 1u : 0u;
+        nc += cand[k] ? 1u : 0u;
+        key[k] = lru_key(st, tg, recency_shift);
+      }
+      unsigned long long tot;
+      // candidates in the high word, free slots in the low word
+      unsigned long long ex = block_excl_scan<unsigned long long, kResThreads>(
+          ((unsigned long long)nc << 32) | nf, scan64, tot);
+      uint32_t at = NC + (uint32_t)(ex >> 32);
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (cand[k]) ckeys[at++] = key[k];
+      NC += (uint32_t)(tot >> 32);
+      F += (uint32_t)tot;
     }
-    uint32_t F, NC;
-    block_excl_scan<uint32_t, kResThreads>(nfree, scan32, F);
-    block_excl_scan<uint32_t, kResThreads>(ncand, scan32, NC);
     const uint32_t r = (M > F) ? min(M - F, NC) : 0u;
     unsigned long long kappa = 0ull;
     const bool take_all = (r == NC);
     if (r > 0u && !take_all) {
+      __syncthreads();                       // every candidate key is written
       kappa = select_rth_key<kResThreads>(
-          S, r,
-          [&](int s, unsigned long long& key) {
-            const int tg = slot_tag[s];
-            if (tg < 0 || req[s]) return false;
-            key = lru_key(slot_stamp[s], tg, recency_shift);
+          (int)NC, r,
+          [&](int i, unsigned long long& key) {
+            key = ckeys[i];
             return true;
           },
           sel);
     }
-    // available slots, ascending: each thread ranks a blocked run
-    const int run = (S + kResThreads - 1) / kResThreads;
-    const int s0 = tid * run;
+    // available slots, ascending: rounds of kB * 1024 slots, thread t taking
+    // the kB consecutive slots kB * t .. of the round (loads issued together)
     auto available = [&](int s) {
       const int tg = slot_tag[s];
+      const uint8_t rq = req[s];
+      const int st = slot_stamp[s];
       if (tg < 0) return true;
-      if (r == 0u || req[s]) return false;
-      return take_all || lru_key(slot_stamp[s], tg, recency_shift) <= kappa;
+      if (r == 0u || rq) return false;
+      return take_all || lru_key(st, tg, recency_shift) <= kappa;
     };
-    uint32_t navail = 0u;
-    for (int k = 0; k < run && s0 + k < S; ++k) navail += available(s0 + k) ? 1u : 0u;
-    uint32_t A;
-    uint32_t rank = block_excl_scan<uint32_t, kResThreads>(navail, scan32, A);
-    for (int k = 0; k < run && s0 + k < S; ++k)
-      if (available(s0 + k)) avail[rank++] = s0 + k;
+    uint32_t A = 0u;
+    for (int base = 0; base < S; base += kB * kResThreads) {
+      const int s0 = base + kB * tid;
+      bool av[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) av[k] = (s0 + k < S) && available(s0 + k);
+      uint32_t n = 0u;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) n += av[k] ? 1u : 0u;
+      uint32_t tot;
+      uint32_t rank = A + block_excl_scan<uint32_t, kResThreads>(n, scan32, tot);
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (av[k]) avail[rank++] = s0 + k;
+      A += tot;
+    }
     placed = min(M, A);
   }
   __syncthreads();                           // every read of the marks is done
-  for (int s = tid; s < S; s += kResThreads) req[s] = 0;
+  for (int s = 4 * tid; s < S; s += 4 * kResThreads) {
+    if (s + 4 <= S)
+      *reinterpret_cast<uint32_t*>(req + s) = 0u;
+    else
+      for (int k = s; k < S; ++k) req[k] = 0;
+  }
   if (tid == 0) *placed_out = (int32_t)placed;
 }
 
@@ -484,10 +522,10 @@ __global__ __launch_bounds__(256) void pool_fetch_kernel(const uint16_t* __restr
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   const int P = *placed_in;
-  const int64_t per_req = (int64_t)hkv * max_pages;
+  const int per_req = hkv * max_pages;       // pooled ids fit in 31 bits
   for (int i = w; i < P; i += waves) {
     const MissRec m = misses[i];
-    const int64_t b = m.unit / per_req, rest = m.unit - b * per_req;
+    const int b = m.unit / per_req, rest = m.unit - b * per_req;
     const int64_t h = rest / max_pages, p = rest - h * max_pages;
     const u32x4* src = reinterpret_cast<const u32x4*>(
         host_kv + ((b * max_pages + p) * hkv + h) * kUnitElems);
@@ -510,12 +548,13 @@ extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t 
 namespace {
 
 // Per-request workspace: miss records [B][C], then the per-request counts.
-// Pooled workspace: marks [S] (padded), avail [S], miss records [S],
-// counts [B][2], offsets [B], placed [1].
+// Pooled workspace: marks [S] (padded to 256 bytes), candidate keys [S],
+// avail [S], miss records [S], counts [B][2], offsets [B], placed [1].
 size_t pooled_ws_bytes(int B, int S) {
   const size_t req = ((size_t)S + 255) / 256 * 256;
   return req + (size_t)S * sizeof(int32_t) + (size_t)S * sizeof(sp::MissRec) +
-         (size_t)B * 3 * sizeof(int32_t) + sizeof(int32_t) + 256;
+         (size_t)S * sizeof(unsigned long long) + (size_t)B * 3 * sizeof(int32_t) +
+         sizeof(int32_t) + 256;
 }
 
 sparse_status check_cache_args(const sparse_dims* dims, const int32_t* sel_counts,
@@ -567,7 +606,9 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
   const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* req = base;
-  int32_t* avail = reinterpret_cast<int32_t*>(base + ((size_t)S + 255) / 256 * 256);
+  unsigned long long* ckeys =
+      reinterpret_cast<unsigned long long*>(base + ((size_t)S + 255) / 256 * 256);
+  int32_t* avail = reinterpret_cast<int32_t*>(ckeys + S);
   sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(avail + S);
   int32_t* counts = reinterpret_cast<int32_t*>(misses + S);
   int32_t* moff = counts + 2 * (size_t)B;
@@ -577,7 +618,7 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
                      counts);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_victim_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, S, shift,
-                     slot_tag, slot_stamp, req, counts, moff, avail, placed);
+                     slot_tag, slot_stamp, req, counts, moff, avail, ckeys, placed);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,

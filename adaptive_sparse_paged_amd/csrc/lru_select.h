@@ -12,6 +12,22 @@ __device__ __forceinline__ unsigned long long lru_key(int32_t stamp, int32_t tag
   return ((unsigned long long)((uint32_t)stamp >> shift) << 32) | (uint32_t)tag;
 }
 
+// hist[bin] += 1 for every lane with `valid`.  Keys of resident units
+// cluster (few distinct stamps), so in the first radix pass the lanes of a
+// wave often all fall in one bin: then one atomic adds their count.  Every
+// lane of the wave calls (wave-uniform control flow).
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, int bin, bool valid) {
+  const unsigned long long act = __ballot(valid);
+  if (!act) return;
+  const int l0 = __ffsll((long long)act) - 1;
+  const int b0 = __shfl(bin, l0, 64);
+  if ((__ballot(bin == b0) & act) == act) {
+    if (lane_id() == l0) atomicAdd(&hist[b0], (uint32_t)__popcll(act));
+  } else if (valid) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
 struct SelectScratch {
   uint32_t hist[2048];
   uint32_t scan32[16];
@@ -27,13 +43,22 @@ struct SelectScratch {
 template <int NT, typename KeyOf>
 __device__ unsigned long long select_rth_key(int C, uint32_t r, KeyOf key_of, SelectScratch& sc) {
   const int tid = threadIdx.x;
+  constexpr int kB = 8;   // slots per thread whose loads are issued together
   unsigned long long kmin = ~0ull, kmax = 0ull;
-  for (int s = tid; s < C; s += NT) {
-    unsigned long long key;
-    if (key_of(s, key)) {
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
+  for (int base = 0; base < C; base += kB * NT) {
+    unsigned long long key[kB] = {};
+    bool ok[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int s = base + k * NT + tid;
+      ok[k] = (s < C) && key_of(s, key[k]);
     }
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (ok[k]) {
+        kmin = min(kmin, key[k]);
+        kmax = max(kmax, key[k]);
+      }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -61,10 +86,19 @@ __device__ unsigned long long select_rth_key(int C, uint32_t r, KeyOf key_of, Se
     const int sh = lo - width, nb = 1 << width;
     for (int k = tid; k < nb; k += NT) sc.hist[k] = 0u;
     __syncthreads();
-    for (int s = tid; s < C; s += NT) {
-      unsigned long long key;
-      if (key_of(s, key) && (key & hi_mask) == prefix)
-        atomicAdd(&sc.hist[(key >> sh) & (nb - 1)], 1u);
+    // uniform trip count over the workgroup: the wave votes stay converged
+    for (int base = 0; base < C; base += kB * NT) {
+      unsigned long long key[kB] = {};
+      bool ok[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int s = base + k * NT + tid;
+        ok[k] = (s < C) && key_of(s, key[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        hist_add_wave(sc.hist, (int)((key[k] >> sh) & (nb - 1)),
+                      ok[k] && (key[k] & hi_mask) == prefix);
     }
     __syncthreads();
     // the bin where the count from the bottom reaches `need`

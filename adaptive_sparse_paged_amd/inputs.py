@@ -327,26 +327,37 @@ def unit_host(w, layer, b, h, L, seed=0):
 # Host-resident KV tier: host pool and drifting page lists
 # ----------------------------------------------------------------------------
 
-def drift_lists(w, n_pages, list_pages, steps, drift, seed=0):
+def drift_lists(w, n_pages, list_pages, steps, drift, seed=0, sizes=None):
     """Synthetic page lists for the host-tier workload: per (request, KV head)
-    a list of `list_pages` distinct logical pages; each step replaces
-    round(drift * list_pages) of them, chosen uniformly, with pages drawn
-    uniformly from those not in the list.  Returns int32
-    [steps][B][Hkv][list_pages], each list ascending."""
+    a list of `list_pages` distinct logical pages (sizes[b] for request b when
+    given); each step replaces round(drift * size) of them, chosen uniformly,
+    with pages drawn uniformly from those not in the list.  Returns int32
+    [steps][B][Hkv][max size], each list ascending, padded with -1."""
     B, H = w.batch, w.kv_heads
-    out = np.empty((steps, B, H, list_pages), dtype=np.int32)
-    k = int(round(drift * list_pages))
+    sizes = [int(list_pages)] * B if sizes is None else [int(x) for x in sizes]
+    out = np.full((steps, B, H, max(sizes)), -1, dtype=np.int32)
     for b in range(B):
+        size = sizes[b]
+        k = int(round(drift * size))
         for h in range(H):
             r = _rng(w, 5, b, h, seed=seed)
-            cur = r.choice(n_pages, size=list_pages, replace=False)
+            cur = r.choice(n_pages, size=size, replace=False)
             for t in range(steps):
-                out[t, b, h] = np.sort(cur)
-                drop = r.choice(list_pages, size=k, replace=False)
+                out[t, b, h, :size] = np.sort(cur)
+                drop = r.choice(size, size=k, replace=False)
                 keep = np.delete(cur, drop)
                 pool = np.setdiff1d(np.arange(n_pages), cur)
                 cur = np.concatenate([keep, r.choice(pool, size=k, replace=False)])
     return out
+
+
+def spread_sizes(batch, list_pages, spread):
+    """Per-request list lengths from list_pages * (1 - spread) up to
+    list_pages * (1 + spread), evenly over the requests (mean list_pages)."""
+    if batch == 1 or spread == 0:
+        return [int(list_pages)] * batch
+    return [int(round(list_pages * (1 + spread * (2 * b / (batch - 1) - 1))))
+            for b in range(batch)]
 
 
 def build_host_pool(w, layer=0, seed=0, lens=None, device="cuda"):

@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cache-policy", default="exact",
+                    help="host tier: exact | bucketed:S | pooled | pooled:S")
+    ap.add_argument("--list-spread", type=float, default=0.0,
+                    help="host tier: per-request list lengths spread +-f around the mean")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch what the hardware-counter runs measure")
     return ap.parse_args()
@@ -154,12 +158,20 @@ def host_tier_bench(args):
     print(f"# host pool {host.numel() * 2 / 2**30:.0f} GiB pinned ({time.time() - t0:.0f} s)",
           file=sys.stderr, flush=True)
     steps, LP, C = ex["steps"], ex["list_pages"], ex["capacity"]
-    lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"])
     B, H = w.batch, w.kv_heads
     U = B * H
+    sizes = I.spread_sizes(B, LP, args.list_spread)
+    lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"], sizes=sizes)
+    LM = lists.shape[-1]
     dims = lib.make_dims(B, w.q_heads, H, MP)
-    cache = HbmPageCache(dims, host, C)
-    chunk = min(args.chunk, LP)
+    name, _, sh = args.cache_policy.partition(":")
+    if name not in ("exact", "bucketed", "pooled"):
+        raise SystemExit(f"unknown cache policy {args.cache_policy}")
+    shift = int(sh or 0)
+    pooled = name == "pooled"
+    cap = B * C if pooled else C          # the same HBM either way
+    cache = HbmPageCache(dims, host, cap, recency_shift=shift, pooled=pooled)
+    chunk = min(args.chunk, LM)
     st = SparseDecodeStep(dims, args.gamma, chunk, scale=w.scale)
     q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
     for b in range(B):
@@ -167,12 +179,12 @@ def host_tier_bench(args):
             q[b, h * w.group:(h + 1) * w.group] = I.unit_query_bits(w, 0, b, h, int(lens[b]))
     q = q.cuda()
     ctx = torch.from_numpy(lens.astype(np.int32)).cuda()
-    lists_dev = torch.from_numpy(lists.reshape(steps, U, LP)).cuda()
-    st.buf.sel_counts.fill_(LP)
+    lists_dev = torch.from_numpy(lists.reshape(steps, U, LM)).cuda()
+    st.buf.sel_counts.copy_(torch.tensor([sizes[u // H] for u in range(U)], dtype=torch.int32))
     kv, s_page, s_head, ppages = cache.pool_args()
 
     def run_step(t, marks=None):
-        st.buf.sel_pages[:, :LP].copy_(lists_dev[t])
+        st.buf.sel_pages[:, :LM].copy_(lists_dev[t])
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
         cache.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
@@ -204,7 +216,8 @@ def host_tier_bench(args):
     torch.cuda.synchronize()
     allhit_res = np.array([m[0].elapsed_time(m[1]) * 1e3 for m in allhit])
     allhit_att = np.array([m[1].elapsed_time(m[2]) * 1e3 for m in allhit])
-    assert int(cache.stats[:, 1].sum().item()) == 0
+    if overflow == 0:           # with overflow some units can never be resident
+        assert int(cache.stats[:, 1].sum().item()) == 0
     # the link: pinned host -> device copy of 1 GiB
     src = host.view(-1)[: 512 * 1024 * 1024]
     dst = torch.empty(src.shape, dtype=src.dtype, device="cuda")
@@ -217,7 +230,12 @@ def host_tier_bench(args):
     torch.cuda.synchronize()
     link = src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     step_us = res_us[1:] + att_us[1:]
-    kept_bytes = U * LP * unit_bytes
+    kept_bytes = H * sum(sizes) * unit_bytes
+    tags = cache.slot_tag.cpu().numpy()
+    if pooled:
+        held = np.bincount(tags[tags >= 0] // (H * MP), minlength=B)
+    else:
+        held = (tags >= 0).sum(1)
     result = {
         "metric": "host-tier sparse decode step us (resolve + attention + merge), 4096-slot HBM cache",
         "value": round(float(np.median(step_us)), 1),
@@ -233,8 +251,12 @@ def host_tier_bench(args):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "ctx": int(lens.max()), "kv_heads": H,
                    "q_heads": w.q_heads, "capacity_slots": C, "list_pages": LP,
-                   "drift": ex["drift"], "chunk_pages": chunk},
+                   "drift": ex["drift"], "chunk_pages": chunk,
+                   "cache_policy": args.cache_policy, "list_spread": args.list_spread,
+                   "list_pages_min_max": [min(sizes), max(sizes)]},
         "cold_step_us": round(float(res_us[0] + att_us[0]), 1),
+        "slots_held_min_max": [int(held.min()), int(held.max())],
+        "overflow_steps": int((st_np[:, :, 3].max(1) > 0).sum()),
         "resolve_fetch_us_median": round(float(np.median(res_us[1:])), 1),
         "attention_merge_us_median": round(float(np.median(att_us[1:])), 1),
         "hit_rate_steady": round(float(hits[1:].sum() / (hits[1:].sum() + misses[1:].sum())), 4),

@@ -13,6 +13,9 @@
  *        Hierarchy" (thelatestinai.com/papers/2610.13708), MOIRA abstract.
  *   [P2] "HiSparse: Scaling Sparse Attention Decoding with Hierarchical KV
  *        Cache" (scholarbro.com/p/47450), abstract.
+ *   [P3] "Unifying Sparse Attention with Hierarchical Memory for Scalable
+ *        Long-Context LLM Serving" (thelatestinai.com/papers/2604.26837),
+ *        the SPIN abstract.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -297,16 +300,16 @@ sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* s
 /*
  * Replacement policy of the host-tier cache (sparse_hbm_cache_resolve_policy).
  *
- * recency_shift -- bucketed LRU ([P1] page, the SPIN abstract, technique
- *   (2): a GPU-friendly bucketed LRU policy; no bucket rule is given, this is
- *   the library's reading): resident units are ordered for eviction by
+ * recency_shift -- bucketed LRU ([P3], abstract, technique (2): a
+ *   GPU-friendly bucketed LRU policy; no bucket rule is given, this is the
+ *   library's reading): resident units are ordered for eviction by
  *   (stamp >> recency_shift, unit id), i.e. stamps compared in buckets of
  *   2^recency_shift steps, the lower unit id first within a bucket.
  *   0 = exact LRU (sparse_hbm_cache_resolve).  0..30.
  * pooled -- 0: one cache of `capacity` slots per request (as
  *   sparse_hbm_cache_resolve).  1: one pool of `capacity` slots shared by all
- *   requests ([P1] page, SPIN abstract, same technique: per-request HBM
- *   budgets sized dynamically -- a request holds as many slots as the pool-wide
+ *   requests ([P3], abstract, same technique: per-request HBM budgets
+ *   sized dynamically -- a request holds as many slots as the pool-wide
  *   replacement leaves it).  Pooled unit id g = (b * Hkv + h) * max_pages +
  *   p; every rule of sparse_hbm_cache_resolve applies over pooled ids (the
  *   requested set is the union over requests; misses in ascending pooled id
@@ -319,7 +322,7 @@ typedef struct {
 
 /* Bytes of workspace sparse_hbm_cache_resolve_policy needs (host); 0 for
  * invalid arguments.  Per-request: as sparse_cache_workspace_bytes.  Pooled:
- * about 13 bytes per slot plus 12 per request. */
+ * about 21 bytes per slot plus 12 per request. */
 size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
                                            const sparse_cache_policy* policy,
                                            int32_t capacity);

@@ -22,10 +22,10 @@ are this library's reading, stated once here:
   the overflow flag, the misses that got no slot keep slot -1, and the step's
   outputs are not meaningful.
 
-Bucketed LRU ([P1] page "Adaptive DHiSparse: Speculative Decoding over a
-Load-Adaptive KV Hierarchy", the SPIN abstract, technique (2): a GPU-friendly
-bucketed LRU policy in the KV cache manager; no bucket rule is given, so this
-is this library's reading): with recency shift s, stamps are compared only in
+Bucketed LRU ([P3] "Unifying Sparse Attention with Hierarchical Memory for
+Scalable Long-Context LLM Serving", the SPIN abstract, technique (2): a
+GPU-friendly bucketed LRU policy in the KV cache manager; no bucket rule is
+given, so this is this library's reading): with recency shift s, stamps are compared only in
 buckets of 2**s steps -- victims are ordered by (stamp >> s, unit id), so
 within one bucket the lower unit id goes first.  s = 0 is exact LRU.
 """
@@ -107,7 +107,7 @@ def pooled_unit(b, h, p, kv_heads, max_pages):
 
 
 def resolve_pooled_step(state, units_per_request, step, units_per_req_space, recency_shift=0):
-    """One step of a cache pool shared by all requests ([P1] page, the SPIN
+    """One step of a cache pool shared by all requests ([P3], the SPIN
     abstract, technique (2): per-request HBM budgets sized dynamically -- here
     a request holds as many slots as the pool-wide replacement leaves it).
     The rule is resolve_step's over pooled unit ids (ascending pooled id
