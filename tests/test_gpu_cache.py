@@ -163,9 +163,11 @@ def test_cache_resolver_host_tier_shape(gpu_lib):
     assert stats[-1]["misses"] > 0 and stats[-1]["hits"] > 0
 
 
-def test_cache_resolver_in_graph(gpu_lib):
+@pytest.mark.parametrize("shift,pooled", [(0, False), (2, True)],
+                         ids=["exact_per_request", "bucketed_pooled"])
+def test_cache_resolver_in_graph(gpu_lib, shift, pooled):
     """Resolve + attention + merge captured once and replayed per step, with
-    the lists changed in place between replays: the LRU state follows the
+    the lists changed in place between replays: the cache state follows the
     oracle exactly (the step number lives on the device)."""
     from adaptive_sparse_paged_amd.step import capture
     w = I.custom_workload("cache_graph", 2, 8, 2, ("fixed", 3200), index=123)
@@ -173,8 +175,9 @@ def test_cache_resolver_in_graph(gpu_lib):
     li = I.build_layer(w, 0, "cuda", lens=lens)
     host, MP = I.build_host_pool(w, 0, lens=lens)
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
-    C, H, B = 40, w.kv_heads, w.batch
-    cache = HbmPageCache(dims, host, C)
+    H, B = w.kv_heads, w.batch
+    C = 80 if pooled else 40
+    cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
     lists = I.drift_lists(w, I.pages_of(lens[0]), 16, 10, 0.25)
     st = SparseDecodeStep(dims, 0.99, 4, scale=w.scale)
     layer = types.SimpleNamespace(w=w, dims=dims, li=li)
@@ -185,24 +188,34 @@ def test_cache_resolver_in_graph(gpu_lib):
         cache.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
         st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)
 
-    say("[cache] graph capture of resolve + attention, 10 replays")
+    say(f"[cache] graph capture of resolve + attention, 10 replays (shift {shift}, pooled {pooled})")
     g = capture(step)
     for t_ in (cache.slot_tag, cache.slot_stamp, cache.unit_slot):
         t_.fill_(-1)
     cache.step_counter.zero_()
     cache.cache_kv.zero_()
-    states = [O.LRUState(C, H * MP) for _ in range(B)]
+    space = H * MP
+    states = [O.LRUState(C, B * space)] if pooled else [O.LRUState(C, space) for _ in range(B)]
     for t in range(lists.shape[0]):
         feed_lists(st, layer, {b * H + h: lists[t, b, h] for b in range(B) for h in range(H)})
         g.replay()
         torch.cuda.synchronize()
         replay_out = st.buf.out.clone()
         assert cache.step_counter.item() == t + 1
-        for b in range(B):
-            r = O.resolve_step(states[b], [h * MP + int(p) for h in range(H) for p in lists[t, b, h]], t)
-            assert np.array_equal(cache.slot_tag[b].cpu().numpy(), states[b].tag), (t, b)
-            assert np.array_equal(cache.slot_stamp[b].cpu().numpy(), states[b].stamp), (t, b)
-            assert cache.stats[b].cpu().tolist() == [r["hits"], r["misses"], r["evictions"], 0]
+        if pooled:
+            per_req = [[O.pooled_unit(b, h, int(p), H, MP) for h in range(H) for p in lists[t, b, h]]
+                       for b in range(B)]
+            r = O.resolve_pooled_step(states[0], per_req, t, space, recency_shift=shift)
+            assert np.array_equal(cache.slot_tag.cpu().numpy(), states[0].tag), t
+            assert np.array_equal(cache.slot_stamp.cpu().numpy(), states[0].stamp), t
+            assert np.array_equal(cache.stats.cpu().numpy(), r["per_request"]), t
+        else:
+            for b in range(B):
+                r = O.resolve_step(states[b], [h * MP + int(p) for h in range(H)
+                                               for p in lists[t, b, h]], t, recency_shift=shift)
+                assert np.array_equal(cache.slot_tag[b].cpu().numpy(), states[b].tag), (t, b)
+                assert np.array_equal(cache.slot_stamp[b].cpu().numpy(), states[b].stamp), (t, b)
+                assert cache.stats[b].cpu().tolist() == [r["hits"], r["misses"], r["evictions"], 0]
         st.attend(li.q, kv, s_page, s_head, ppages, li.ctx_lens)   # eager, same lists
         torch.cuda.synchronize()
         assert torch.equal(replay_out, st.buf.out)
