@@ -150,6 +150,17 @@ def test_cache_overflow_flagged(gpu_lib):
     assert all(r["overflow"] == 1 for r in stats)
 
 
+def test_cache_pool_overflow_flagged(gpu_lib):
+    """A shared pool too small for the step's demand: misses rank request by
+    request, so the last request's misses go unplaced and only it (and any
+    request that shares the boundary) is flagged, as in the oracle."""
+    w = I.custom_workload("cache_povf", 3, 8, 2, ("fixed", 1600), index=126)
+    say("[cache] pooled overflow: 3 requests x 2 heads x 20 pages into 100 slots")
+    stats = _case(w, C=100, list_pages=20, steps=2, drift=0.1, chunk=4, pooled=True)
+    flags = [r["overflow"] for r in stats]
+    assert flags[:3] == [0, 0, 1]
+
+
 @pytest.mark.timeout(300)
 def test_cache_resolver_host_tier_shape(gpu_lib):
     """The host-tier workload's shape (524288-token contexts, 8 KV heads,
