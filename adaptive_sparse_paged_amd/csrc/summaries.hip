@@ -18,7 +18,8 @@ __device__ __forceinline__ uint32_t key_bits(uint32_t k) {
 }
 
 // One wave per (listed page, KV head); lane l owns channels 2l and 2l+1, so
-// each token row of the tile is one coalesced 256-byte wave load.
+// each token row of the tile is one coalesced 256-byte wave load, and the
+// loads of all valid rows are issued before the first comparison.
 __global__ __launch_bounds__(256) void summaries_kernel(
     const uint16_t* __restrict__ kv, int64_t stride_page, int64_t stride_head, int64_t pool_pages,
     const int32_t* __restrict__ pages, const int32_t* __restrict__ valid, int n, int hkv,
@@ -32,10 +33,15 @@ __global__ __launch_bounds__(256) void summaries_kernel(
   if (x < 0 || x >= pool_pages || nv == 0) return;
   const uint32_t* tile =
       reinterpret_cast<const uint32_t*>(kv + (int64_t)x * stride_page + (int64_t)h * stride_head);
+  uint32_t w[kP];
+#pragma unroll
+  for (int t = 0; t < kP; ++t)
+    w[t] = (t < nv) ? __builtin_nontemporal_load(tile + t * (kD / 2) + lane) : 0u;
   uint32_t lo0 = 0xFFFFu, lo1 = 0xFFFFu, hi0 = 0u, hi1 = 0u;
-  for (int t = 0; t < nv; ++t) {
-    const uint32_t w = tile[t * (kD / 2) + lane];
-    const uint32_t k0 = order_key(w & 0xFFFFu), k1 = order_key(w >> 16);
+#pragma unroll
+  for (int t = 0; t < kP; ++t) {
+    if (t >= nv) break;
+    const uint32_t k0 = order_key(w[t] & 0xFFFFu), k1 = order_key(w[t] >> 16);
     lo0 = min(lo0, k0);
     hi0 = max(hi0, k0);
     lo1 = min(lo1, k1);
