@@ -551,7 +551,7 @@ def main():
             traffic = rec.get("bytes_per_launch")
 
     result = {
-        "metric": "sparse decode step us/layer + achieved HBM GB/s vs peak at 128k ctx, gamma=0.99",
+        "metric": "sparse decode step \u00b5s/layer + achieved HBM GB/s vs peak at 128k ctx, \u03b3=0.99",
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
