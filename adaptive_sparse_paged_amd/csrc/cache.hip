@@ -279,9 +279,14 @@ __global__ __launch_bounds__(256) void fetch_kernel(const uint16_t* __restrict__
 // a request holds as many slots as the pool-wide replacement leaves it.
 //   pool_mark_kernel   one workgroup per request: hits (stamp, mark, slot id)
 //                      and the request's hit and miss counts;
-//   pool_victim_kernel one workgroup: each request's miss-rank offset, free
-//                      slots, the victims (radix select over the pool), the
-//                      ascending list of available slots; clears the marks;
+//   pool_scan_kernel   one workgroup per block of 1024 slots: the block's
+//                      free slots counted, its victim candidates' keys
+//                      compacted into the block's segment;
+//   pool_select_kernel one workgroup: each request's miss-rank offset, the
+//                      victims (radix select over the compacted keys), each
+//                      block's offset in the list of available slots;
+//   pool_avail_kernel  one workgroup per block: its available slots, in
+//                      ascending order, at the block's offset; clears marks;
 //   pool_place_kernel  one workgroup per request: its misses, ascending, take
 //                      avail[offset + rank]; statistics;
 //   pool_fetch_kernel  copies every placed miss from pinned host memory.
@@ -342,14 +347,73 @@ __global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
   }
 }
 
-__global__ __launch_bounds__(kResThreads) void pool_victim_kernel(
-    int B, int S, int recency_shift, const int32_t* __restrict__ slot_tag,
-    const int32_t* __restrict__ slot_stamp, uint8_t* __restrict__ req,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ moff, int32_t* __restrict__ avail,
-    unsigned long long* __restrict__ ckeys, int32_t* __restrict__ placed_out) {
+constexpr int kPoolBlk = 1024;          // slots per scan / avail workgroup
+constexpr int kPoolBlkThreads = 256;    // 4 consecutive slots per thread
+
+// Selection state handed from pool_select_kernel to pool_avail_kernel.
+struct PoolSel {
+  unsigned long long kappa;   // the r-th smallest candidate key
+  uint32_t r;                 // victims to take
+  uint32_t take_all;          // every candidate is a victim
+  uint32_t placed;            // misses that get a slot
+  uint32_t pad;
+};
+
+__global__ __launch_bounds__(kPoolBlkThreads) void pool_scan_kernel(
+    int S, int recency_shift, const int32_t* __restrict__ slot_tag,
+    const int32_t* __restrict__ slot_stamp, const uint8_t* __restrict__ req,
+    unsigned long long* __restrict__ ckeys, int32_t* __restrict__ cblk,
+    int32_t* __restrict__ blk_free, uint32_t* __restrict__ totals) {
+  __shared__ unsigned long long scan64[kPoolBlkThreads / 64];
+  __shared__ uint32_t s_base;
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int s0 = blk * kPoolBlk + 4 * tid;
+  int tg[4], st[4];
+  bool fr[4], cd[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool in = s0 + k < S;
+    tg[k] = in ? slot_tag[s0 + k] : 0;
+    st[k] = in ? slot_stamp[s0 + k] : 0;
+    const uint8_t rq = in ? req[s0 + k] : 1;
+    fr[k] = in && tg[k] < 0;
+    cd[k] = in && tg[k] >= 0 && !rq;
+  }
+  uint32_t nf = 0u, nc = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    nf += fr[k] ? 1u : 0u;
+    nc += cd[k] ? 1u : 0u;
+  }
+  unsigned long long tot;
+  const unsigned long long ex = block_excl_scan<unsigned long long, kPoolBlkThreads>(
+      ((unsigned long long)nc << 32) | nf, scan64, tot);
+  // the block's candidates go to one contiguous run of the compacted list
+  // (run order across blocks does not matter to the selection)
+  if (tid == 0) {
+    s_base = atomicAdd(&totals[0], (uint32_t)(tot >> 32));
+    atomicAdd(&totals[1], (uint32_t)tot);
+    blk_free[blk] = (int32_t)(uint32_t)tot;
+  }
+  __syncthreads();
+  uint32_t at = s_base + (uint32_t)(ex >> 32);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (cd[k]) {
+      ckeys[at] = lru_key(st[k], tg[k], recency_shift);
+      cblk[at] = blk;
+      ++at;
+    }
+}
+
+__global__ __launch_bounds__(kResThreads) void pool_select_kernel(
+    int B, int nblk, const int32_t* __restrict__ counts, int32_t* __restrict__ moff,
+    const unsigned long long* __restrict__ ckeys, const int32_t* __restrict__ cblk,
+    const int32_t* __restrict__ blk_free, uint32_t* __restrict__ totals,
+    int32_t* __restrict__ blk_off, PoolSel* __restrict__ sel_out) {
   __shared__ SelectScratch sel;
   __shared__ uint32_t scan32[kResThreads / 64];
-  __shared__ unsigned long long scan64[kResThreads / 64];
+  __shared__ uint32_t s_vict[kMaxPoolSlots / kPoolBlk];
   const int tid = threadIdx.x;
   // each request's miss-rank offset: exclusive prefix of the miss counts
   uint32_t M = 0u;
@@ -361,88 +425,80 @@ __global__ __launch_bounds__(kResThreads) void pool_victim_kernel(
     if (b < B) moff[b] = (int32_t)(M + ex);
     M += tot;
   }
-  uint32_t placed = 0u;
-  if (M > 0u) {
-    // one pass over the pool: free slots counted, the keys of the victim
-    // candidates (resident, not requested) compacted into ckeys
-    constexpr int kB = 8;   // slots per thread whose loads are issued together
-    uint32_t F = 0u, NC = 0u;
-    for (int base = 0; base < S; base += kB * kResThreads) {
-      unsigned long long key[kB];
-      bool cand[kB];
-      uint32_t nf = 0u, nc = 0u;
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const int s = base + k * kResThreads + tid;
-        const bool in = s < S;
-        const int tg = in ? slot_tag[s] : 0;
-        const uint8_t rq = in ? req[s] : 1;
-        const int st = in ? slot_stamp[s] : 0;
-        cand[k] = in && tg >= 0 && !rq;
-        nf += (in && tg < 0) ? 1u : 0u;
-        nc += cand[k] ? 1u : 0u;
-        key[k] = lru_key(st, tg, recency_shift);
-      }
-      unsigned long long tot;
-      // candidates in the high word, free slots in the low word
-      unsigned long long ex = block_excl_scan<unsigned long long, kResThreads>(
-          ((unsigned long long)nc << 32) | nf, scan64, tot);
-      uint32_t at = NC + (uint32_t)(ex >> 32);
-#pragma unroll
-      for (int k = 0; k < kB; ++k)
-        if (cand[k]) ckeys[at++] = key[k];
-      NC += (uint32_t)(tot >> 32);
-      F += (uint32_t)tot;
-    }
-    const uint32_t r = (M > F) ? min(M - F, NC) : 0u;
-    unsigned long long kappa = 0ull;
-    const bool take_all = (r == NC);
-    if (r > 0u && !take_all) {
-      __syncthreads();                       // every candidate key is written
-      kappa = select_rth_key<kResThreads>(
-          (int)NC, r,
-          [&](int i, unsigned long long& key) {
-            key = ckeys[i];
-            return true;
-          },
-          sel);
-    }
-    // available slots, ascending: rounds of kB * 1024 slots, thread t taking
-    // the kB consecutive slots kB * t .. of the round (loads issued together)
-    auto available = [&](int s) {
-      const int tg = slot_tag[s];
-      const uint8_t rq = req[s];
-      const int st = slot_stamp[s];
-      if (tg < 0) return true;
-      if (r == 0u || rq) return false;
-      return take_all || lru_key(st, tg, recency_shift) <= kappa;
-    };
-    uint32_t A = 0u;
-    for (int base = 0; base < S; base += kB * kResThreads) {
-      const int s0 = base + kB * tid;
-      bool av[kB];
-#pragma unroll
-      for (int k = 0; k < kB; ++k) av[k] = (s0 + k < S) && available(s0 + k);
-      uint32_t n = 0u;
-#pragma unroll
-      for (int k = 0; k < kB; ++k) n += av[k] ? 1u : 0u;
-      uint32_t tot;
-      uint32_t rank = A + block_excl_scan<uint32_t, kResThreads>(n, scan32, tot);
-#pragma unroll
-      for (int k = 0; k < kB; ++k)
-        if (av[k]) avail[rank++] = s0 + k;
-      A += tot;
-    }
-    placed = min(M, A);
+  const uint32_t NC = totals[0], F = totals[1];
+  for (int k = tid; k < nblk; k += kResThreads) s_vict[k] = 0u;
+  __syncthreads();
+  const uint32_t r = (M > F) ? min(M - F, NC) : 0u;
+  const bool take_all = r == NC;
+  unsigned long long kappa = 0ull;
+  if (r > 0u && !take_all) {
+    kappa = select_rth_key<kResThreads>(
+        (int)NC, r,
+        [&](int i, unsigned long long& key) {
+          key = ckeys[i];
+          return true;
+        },
+        sel);
   }
-  __syncthreads();                           // every read of the marks is done
-  for (int s = 4 * tid; s < S; s += 4 * kResThreads) {
-    if (s + 4 <= S)
-      *reinterpret_cast<uint32_t*>(req + s) = 0u;
-    else
-      for (int k = s; k < S; ++k) req[k] = 0;
+  // victims per block: a block's keys are one contiguous run, so a wave's
+  // lanes mostly share the block and hist_add_wave adds them with one atomic
+  if (r > 0u) {
+    for (int base = 0; base < (int)NC; base += kResThreads) {
+      const int i = base + tid;
+      const bool in = i < (int)NC;
+      const bool v = in && (take_all || ckeys[i] <= kappa);
+      hist_add_wave(s_vict, in ? cblk[i] : 0, v);
+    }
   }
-  if (tid == 0) *placed_out = (int32_t)placed;
+  __syncthreads();
+  uint32_t A = 0u;
+  for (int base = 0; base < nblk; base += kResThreads) {
+    const int k = base + tid;
+    const uint32_t a = (k < nblk) ? (uint32_t)blk_free[k] + s_vict[k] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t, kResThreads>(a, scan32, tot);
+    if (k < nblk) blk_off[k] = (int32_t)(A + ex);
+    A += tot;
+  }
+  if (tid == 0) {
+    *sel_out = PoolSel{kappa, r, take_all ? 1u : 0u, min(M, A), 0u};
+    totals[0] = 0u;                            // re-armed for the next call
+    totals[1] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kPoolBlkThreads) void pool_avail_kernel(
+    int S, int recency_shift, const int32_t* __restrict__ slot_tag,
+    const int32_t* __restrict__ slot_stamp, uint8_t* __restrict__ req,
+    const PoolSel* __restrict__ sel_in, const int32_t* __restrict__ blk_off,
+    int32_t* __restrict__ avail, int32_t* __restrict__ placed_out) {
+  __shared__ uint32_t scan32[kPoolBlkThreads / 64];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const PoolSel sl = *sel_in;
+  const int s0 = blk * kPoolBlk + 4 * tid;
+  bool av[4];
+  uint32_t n = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int sk = s0 + k;
+    av[k] = false;
+    if (sk < S) {
+      const int tg = slot_tag[sk];
+      const uint8_t rq = req[sk];
+      const int st = slot_stamp[sk];
+      if (tg < 0) av[k] = true;
+      else if (sl.r > 0u && !rq)
+        av[k] = sl.take_all || lru_key(st, tg, recency_shift) <= sl.kappa;
+      req[sk] = 0;                             // marks are read only here: clear them
+    }
+    n += av[k] ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t rank = (uint32_t)blk_off[blk] + block_excl_scan<uint32_t, kPoolBlkThreads>(n, scan32, tot);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (av[k]) avail[rank++] = s0 + k;
+  if (blk == 0 && tid == 0) *placed_out = (int32_t)sl.placed;
 }
 
 __global__ __launch_bounds__(kResThreads) void pool_place_kernel(
@@ -548,13 +604,18 @@ extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t 
 namespace {
 
 // Per-request workspace: miss records [B][C], then the per-request counts.
-// Pooled workspace: marks [S] (padded to 256 bytes), candidate keys [S],
-// avail [S], miss records [S], counts [B][2], offsets [B], placed [1].
+// Pooled workspace (S rounded up to whole blocks of 1024 slots, nblk of
+// them): marks [S], compacted candidate keys [S] and their blocks [S],
+// avail [S], miss records [S], the selection state, two running totals, per
+// block free counts and offsets, then counts [B][2], offsets [B], placed [1].
+// The marks and the totals must be zero before the first call; every call
+// leaves them zero.
 size_t pooled_ws_bytes(int B, int S) {
-  const size_t req = ((size_t)S + 255) / 256 * 256;
-  return req + (size_t)S * sizeof(int32_t) + (size_t)S * sizeof(sp::MissRec) +
-         (size_t)S * sizeof(unsigned long long) + (size_t)B * 3 * sizeof(int32_t) +
-         sizeof(int32_t) + 256;
+  const size_t nblk = ((size_t)S + sp::kPoolBlk - 1) / sp::kPoolBlk;
+  const size_t Sr = nblk * sp::kPoolBlk;
+  return Sr + Sr * sizeof(unsigned long long) + Sr * sizeof(int32_t) + Sr * sizeof(int32_t) +
+         Sr * sizeof(sp::MissRec) + sizeof(sp::PoolSel) + 2 * sizeof(uint32_t) +
+         nblk * 2 * sizeof(int32_t) + (size_t)B * 3 * sizeof(int32_t) + sizeof(int32_t) + 256;
 }
 
 sparse_status check_cache_args(const sparse_dims* dims, const int32_t* sel_counts,
@@ -604,21 +665,33 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
                              int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
                              int32_t* sel_phys, int32_t* stats, void* ws, hipStream_t s) {
   const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
+  const int nblk = (S + sp::kPoolBlk - 1) / sp::kPoolBlk;
+  const size_t Sr = (size_t)nblk * sp::kPoolBlk;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint8_t* req = base;
-  unsigned long long* ckeys =
-      reinterpret_cast<unsigned long long*>(base + ((size_t)S + 255) / 256 * 256);
-  int32_t* avail = reinterpret_cast<int32_t*>(ckeys + S);
-  sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(avail + S);
-  int32_t* counts = reinterpret_cast<int32_t*>(misses + S);
+  uint8_t* req = base;                                           // Sr is a multiple of 1024
+  unsigned long long* ckeys = reinterpret_cast<unsigned long long*>(base + Sr);
+  int32_t* cblk = reinterpret_cast<int32_t*>(ckeys + Sr);
+  int32_t* avail = cblk + Sr;
+  sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(avail + Sr);
+  sp::PoolSel* psel = reinterpret_cast<sp::PoolSel*>(misses + Sr);
+  uint32_t* totals = reinterpret_cast<uint32_t*>(psel + 1);
+  int32_t* blk_free = reinterpret_cast<int32_t*>(totals + 2);
+  int32_t* blk_off = blk_free + nblk;
+  int32_t* counts = blk_off + nblk;
   int32_t* moff = counts + 2 * (size_t)B;
   int32_t* placed = moff + B;
   hipLaunchKernelGGL(sp::pool_mark_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, S, step_counter, slot_stamp, unit_slot, sel_phys, req,
                      counts);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  hipLaunchKernelGGL(sp::pool_victim_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, S, shift,
-                     slot_tag, slot_stamp, req, counts, moff, avail, ckeys, placed);
+  hipLaunchKernelGGL(sp::pool_scan_kernel, dim3(nblk), dim3(sp::kPoolBlkThreads), 0, s, S, shift,
+                     slot_tag, slot_stamp, req, ckeys, cblk, blk_free, totals);
+  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  hipLaunchKernelGGL(sp::pool_select_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, nblk,
+                     counts, moff, ckeys, cblk, blk_free, totals, blk_off, psel);
+  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  hipLaunchKernelGGL(sp::pool_avail_kernel, dim3(nblk), dim3(sp::kPoolBlkThreads), 0, s, S, shift,
+                     slot_tag, slot_stamp, req, psel, blk_off, avail, placed);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,

@@ -322,7 +322,7 @@ typedef struct {
 
 /* Bytes of workspace sparse_hbm_cache_resolve_policy needs (host); 0 for
  * invalid arguments.  Per-request: as sparse_cache_workspace_bytes.  Pooled:
- * about 21 bytes per slot plus 12 per request. */
+ * about 25 bytes per slot plus 12 per request. */
 size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
                                            const sparse_cache_policy* policy,
                                            int32_t capacity);
@@ -340,10 +340,14 @@ size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
  *   sel_phys   int32 [U][max_pages] out: slot index
  *   stats      int32 [B][4] out: hits, misses, evictions made by that
  *              request's misses, overflow (one of its misses got no slot)
- * Enqueues three resolve kernels (per request, one over the pool, per
- * request) and one fetch kernel.  Lists must hold distinct pages (as the
- * selection writes them).  Errors: as sparse_hbm_cache_resolve; policy
- * missing or out of range -> INVALID.
+ *   ws         pooled: zero it once before the first call (it carries the
+ *              requested-slot marks and two running totals, which every
+ *              call leaves zero)
+ * Pooled mode enqueues five resolve kernels (per request; per block of 1024
+ * slots; one workgroup selecting the victims; per block; per request) and
+ * one fetch kernel.  Lists must hold distinct pages (as the selection writes
+ * them).  Errors: as sparse_hbm_cache_resolve; policy missing or out of
+ * range -> INVALID.
  */
 sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
                                               const sparse_cache_policy* policy,
