@@ -37,7 +37,9 @@ class SparseDecodeStep:
     """Fixed-shape decode step for one layer shape.
 
     dims: lib.Dims; gamma in (0, 1]; chunk_pages: pages per attention
-    workgroup.  Intermediate buffers are shared by every layer run through
+    workgroup (256, the fastest of 96-384 measured on MI355X at 32k-128k
+    contexts, is 64 pages per wave: one batch of list ids each; clamped to
+    max_pages).  Intermediate buffers are shared by every layer run through
     this object; outputs can be given per call.
 
     groups > 1 splits the requests into that many contiguous groups, each on a
@@ -52,7 +54,7 @@ class SparseDecodeStep:
     the default is one group.
     """
 
-    def __init__(self, dims, gamma, chunk_pages=32, scale=None, device="cuda", groups=1,
+    def __init__(self, dims, gamma, chunk_pages=256, scale=None, device="cuda", groups=1,
                  offsets=True):
         """offsets: also write the whole-batch prefix sums (sel_offsets,
         chunk_offsets) in the selection; the attention does not need them."""

@@ -174,6 +174,19 @@ def test_cache_resolver_host_tier_shape(gpu_lib):
     assert stats[-1]["misses"] > 0 and stats[-1]["hits"] > 0
 
 
+@pytest.mark.timeout(300)
+def test_cache_pool_host_tier_scale(gpu_lib):
+    """A pool shared by 8 requests of 131072 tokens: 32768 slots (32 blocks of
+    the pooled resolver), lists of 448 pages per KV head drifting 10%, 4
+    steps, against the pooled oracle."""
+    base = I.WORKLOADS["host_tier_512k"]
+    w = I.custom_workload("pool_scale", 8, 32, 8, ("fixed", 131072), alpha=base.alpha, index=127)
+    say("[cache] pooled at scale: 8 x 131072 tokens, 32768 shared slots, 448-page lists")
+    stats = _case(w, C=8 * 4096, list_pages=448, steps=4, drift=0.1, chunk=128,
+                  check_all_slots=False, pooled=True, shift=1)
+    assert sum(r["misses"] for r in stats[-8:]) > 0 and sum(r["hits"] for r in stats[-8:]) > 0
+
+
 @pytest.mark.parametrize("shift,pooled", [(0, False), (2, True)],
                          ids=["exact_per_request", "bucketed_pooled"])
 def test_cache_resolver_in_graph(gpu_lib, shift, pooled):
