@@ -1,8 +1,8 @@
 // Self-planning split-K decode attention over variable-length page lists
 // ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
-// Hierarchy", MOIRA abstract, sentence on self-planning attention: each block
-// derives its share of the work from the list lengths, with no host-side
-// plan, so the step stays inside the graph).
+// Hierarchy", MOIRA abstract, sentence on self-planning attention: every block
+// works out from the per-head list lengths which part it handles, so no plan
+// is made on the host and the step stays inside the graph).
 //
 // The grid is fixed (one workgroup per possible chunk).  Workgroup c derives
 // its unit and chunk from the list lengths themselves (a wave prefix sum over

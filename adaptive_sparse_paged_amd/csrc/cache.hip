@@ -1,9 +1,9 @@
 // Host-resident KV tier with a fixed-size HBM page cache, resolved inside the
 // decode graph ("HiSparse: Scaling Sparse Attention Decoding with
 // Hierarchical KV Cache", abstract: full KV history in host memory, a small
-// fixed-size GPU cache per request, and one in-graph resolver doing hit
-// detection, LRU replacement and host-to-device fetch; only placement changes,
-// so outputs are unchanged).
+// fixed-size GPU cache per request, and one resolver inside the graph that
+// finds hits, replaces least recently used entries and fetches misses from the
+// host; outputs stay the same because only where KV lives changes).
 //
 // Cache unit = one (logical page p, KV head h) of a request: its K tile and
 // channel-major V tile (8 KiB), unit id v = h * max_pages + p.  Rules:

@@ -1,5 +1,5 @@
-// The coverage rule: per (request, KV head) unit, the smallest page set whose
-// estimated attention mass reaches a fraction gamma of the total ("Adaptive
+// The coverage rule: per (request, KV head) unit, the fewest pages that
+// together hold at least gamma of the unit's estimated attention mass ("Adaptive
 // DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", MOIRA
 // abstract, coverage-rule sentence).
 //

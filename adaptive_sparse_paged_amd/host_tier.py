@@ -1,8 +1,8 @@
 """Host-resident KV tier with a fixed-size HBM page cache per request.
 
 State and buffers for sparse_hbm_cache_resolve, all caller-owned (torch
-memory); the resolve itself -- hit detection, LRU replacement and the
-host-to-device fetch of misses -- runs in the library's kernels on the stream,
+memory); the resolve itself -- finding hits, choosing replacements and
+fetching the misses from host memory -- runs in the library's kernels on the stream,
 so it can sit inside the captured decode graph.
 """
 

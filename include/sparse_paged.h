@@ -2,8 +2,8 @@
  * sparse_paged.h -- C ABI of the MI355X (gfx950) sparse paged decode step.
  *
  * One decode step, per (request, KV head) "unit": score every KV page of the
- * request with a cheap upper bound of its attention mass, keep the smallest
- * page set whose estimated mass reaches a fraction gamma, then run exact
+ * request with a cheap upper bound of its attention mass, keep the fewest
+ * pages holding at least gamma of the estimated mass, then run exact
  * attention for the unit's GQA group over that variable-length page list,
  * split into fixed-size chunks that each workgroup finds for itself from the
  * prefix-summed list lengths, and merge the chunk partials.
@@ -207,9 +207,9 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
 
 /*
  * sparse_decode_attn -- self-planning split-K attention over the page lists
- * ([P1], abstract, sentence on self-planning attention: each block derives
- * its own share of the work from the list lengths, so no host-side plan is
- * needed and the step stays inside the graph).
+ * ([P1], abstract, sentence on self-planning attention: every block works
+ * out from the per-head list lengths which part it handles, so no plan is
+ * made on the host and the step stays inside the graph).
  *
  * Unit u's list (k_u = sel_counts[u] entries) splits into ceil(k_u /
  * chunk_pages) chunks, numbered across units in unit order.  The grid has
@@ -254,8 +254,9 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
  * sparse_hbm_cache_resolve -- host-resident KV tier behind a fixed-size HBM
  * page cache, resolved on the device inside the step ([P2], abstract: full KV
  * history in host memory, a small fixed-size GPU cache per request, and one
- * in-graph resolver doing hit detection, LRU replacement and host-to-device
- * fetch; only placement changes, so attention outputs are unchanged).
+ * resolver inside the graph that finds hits, replaces least recently used
+ * entries and fetches misses from the host; attention outputs stay the same
+ * because only where KV lives changes).
  *
  * Cache unit = (logical page p, KV head h) of request b, unit id
  * v = h * max_pages + p.  Per request, the requested set R is the union of the

@@ -2,9 +2,9 @@
 
 Oracle of the in-graph cache resolver described on [P2] "HiSparse: Scaling
 Sparse Attention Decoding with Hierarchical KV Cache" (abstract, sentence on the
-fused resolver: hit detection, LRU replacement and host-to-device fetch inside
-the decode graph; and the sentence stating that only placement changes, so
-outputs are unchanged).  The pages give no slot or tie rules; the ones below
+fused resolver, which finds hits, replaces least recently used entries and
+fetches misses from the host inside the decode graph; and the sentence on
+outputs staying the same because only where KV lives changes).  The pages give no slot or tie rules; the ones below
 are this library's reading, stated once here:
 
 * A cache unit is one (logical page, KV head) of one request: its K tile and V

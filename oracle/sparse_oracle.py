@@ -13,8 +13,8 @@ abstract and its RaBitQCache card).
 What the pages fix and what is read into them:
 
 * The coverage rule [P1, abstract, coverage-rule sentence]: per request, layer,
-  KV head and step, keep the smallest page set whose *estimated* attention mass
-  reaches a fraction gamma.  The pages name no estimator.  Reading used here:
+  KV head and step, keep the fewest pages that together hold at least gamma of
+  the *estimated* attention mass.  The pages name no estimator.  Reading used here:
   the Quest-style per-channel min/max key bound (Quest is named as a family on
   [P2, abstract, evaluation sentence]), turned into a per-page mass by a
   softmax over s*u + ln(n_valid), averaged over the G query heads of the KV
