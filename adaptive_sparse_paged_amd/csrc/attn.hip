@@ -116,17 +116,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_phys,
-    float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int U,
+    float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int cap, int U,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
   const int c = blockIdx.x;
   int u, local;
-  plan_locate(sel_counts, U, max_pages, chunk_pages, c, u, local);
+  plan_locate(sel_counts, U, cap, chunk_pages, c, u, local);
   if (u < 0) return;                   // past the last chunk of the step
   const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   const int L = min(max(ctx_lens[b], 0), max_pages * kP);
-  const int cnt = min(sel_counts[u], max_pages);
+  const int cnt = min(sel_counts[u], cap);
   const int i0 = local * chunk_pages;
   const int i1 = min(i0 + chunk_pages, cnt);
   const int32_t* lp = sel_pages + (int64_t)u * max_pages;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages) {
   if (sp::check_dims(dims) != SPARSE_OK || chunk_pages < 1) return -1;
   const int64_t U = (int64_t)dims->batch * dims->num_kv_heads;
-  return U * ((dims->max_pages + chunk_pages - 1) / chunk_pages);
+  return U * ((sp::list_cap(dims) + chunk_pages - 1) / chunk_pages);
 }
 
 extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q,
@@ -244,6 +244,6 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
   hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)max_parts), dim3(256), lds,
                      (hipStream_t)stream, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
                      sel_counts, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
-                     group, dims->max_pages, U, part_o, part_lse);
+                     group, dims->max_pages, sp::list_cap(dims), U, part_o, part_lse);
   return sp::launch_status();
 }

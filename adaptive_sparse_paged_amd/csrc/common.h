@@ -91,7 +91,8 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 }
 
 // ---- the chunk plan, derived on the device from the list lengths ------------
-// Unit u's list of k_u = min(count_u, max_pages) pages splits into
+// Unit u's list of k_u = min(count_u, cap) pages (cap: the dims' list bound)
+// splits into
 // ceil(k_u / chunk) chunks, numbered across units in unit order.  A wave
 // derives where chunk c falls with one round of loads (lane l reads the
 // counts of units l*8 .. l*8+7 of each 512-unit segment) and a wave prefix
@@ -99,15 +100,15 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 constexpr int kPlanVU = 8;
 
 __device__ __forceinline__ int plan_chunks(const int32_t* __restrict__ counts, int idx, int U,
-                                           int max_pages, int chunk) {
-  const int k = (idx < U) ? min(max(counts[idx], 0), max_pages) : 0;
+                                           int cap, int chunk) {
+  const int k = (idx < U) ? min(max(counts[idx], 0), cap) : 0;
   return (k + chunk - 1) / chunk;
 }
 
 // Unit of global chunk c and the chunk's index within that unit (unit = -1
 // when c is past the last chunk).  Wave-uniform results; every lane calls.
 __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, int U,
-                                            int max_pages, int chunk, int c, int& unit,
+                                            int cap, int chunk, int c, int& unit,
                                             int& local) {
   const int lane = lane_id();
   int running = 0;
@@ -118,7 +119,7 @@ __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, 
     int s = 0;
 #pragma unroll
     for (int v = 0; v < kPlanVU; ++v) {
-      ch[v] = plan_chunks(counts, seg + lane * kPlanVU + v, U, max_pages, chunk);
+      ch[v] = plan_chunks(counts, seg + lane * kPlanVU + v, U, cap, chunk);
       s += ch[v];
     }
     const int incl = wave_incl_scan(s);
@@ -145,7 +146,7 @@ __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, 
 
 // Number of chunks of units 0 .. u-1 (wave-uniform; every lane calls).
 __device__ __forceinline__ int plan_prefix(const int32_t* __restrict__ counts, int U,
-                                           int max_pages, int chunk, int u) {
+                                           int cap, int chunk, int u) {
   const int lane = lane_id();
   int running = 0;
   for (int seg = 0; seg < u; seg += 64 * kPlanVU) {
@@ -153,7 +154,7 @@ __device__ __forceinline__ int plan_prefix(const int32_t* __restrict__ counts, i
 #pragma unroll
     for (int v = 0; v < kPlanVU; ++v) {
       const int idx = seg + lane * kPlanVU + v;
-      if (idx < u) s += plan_chunks(counts, idx, U, max_pages, chunk);
+      if (idx < u) s += plan_chunks(counts, idx, U, cap, chunk);
     }
     running += __shfl(wave_incl_scan(s), 63, 64);
   }
@@ -171,7 +172,13 @@ inline sparse_status check_dims(const sparse_dims* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim != kD || d->page_size != kP || G > kMaxGroup || d->max_pages > kMaxPages)
     return SPARSE_ERR_UNSUPPORTED;
+  if (d->max_list_pages < 0 || d->max_list_pages > d->max_pages) return SPARSE_ERR_INVALID;
   return SPARSE_OK;
+}
+
+// The length every page list is planned for (attention and merge).
+inline int list_cap(const sparse_dims* d) {
+  return d->max_list_pages > 0 ? d->max_list_pages : d->max_pages;
 }
 
 inline sparse_status check_pool(const void* kv, int64_t stride_page, int64_t stride_head,

@@ -15,7 +15,7 @@ constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
 // (max, sum, weighted sum); the 32 slots are then combined through LDS.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ sel_counts, int U, int max_pages, int chunk, int hkv, int group,
+    const int32_t* __restrict__ sel_counts, int U, int cap, int chunk, int hkv, int group,
     float* __restrict__ out, float* __restrict__ out_lse) {
   __shared__ floatx4 s_acc[kMergeSlots][32];
   __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
@@ -24,12 +24,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   // this unit's chunks, from the list lengths (as the attention planned them)
   if (threadIdx.x < 64) {
-    const int c0w = plan_prefix(sel_counts, U, max_pages, chunk, u);
+    const int c0w = plan_prefix(sel_counts, U, cap, chunk, u);
     if (threadIdx.x == 0) s_c0 = c0w;
   }
   __syncthreads();
   const int c0 = s_c0;
-  const int c1 = c0 + plan_chunks(sel_counts, u, U, max_pages, chunk);
+  const int c1 = c0 + plan_chunks(sel_counts, u, U, cap, chunk);
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
 
   float m = -INFINITY, s = 0.f;
@@ -93,7 +93,7 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
   hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
-                     (hipStream_t)stream, part_o, part_lse, sel_counts, U, dims->max_pages,
+                     (hipStream_t)stream, part_o, part_lse, sel_counts, U, sp::list_cap(dims),
                      chunk_pages, hkv, group, out, out_lse);
   return sp::launch_status();
 }

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ page_table, float gamma, int k_pages, int chunk_pages, int hkv,
     int group,
-    int max_pages, int U, int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_offsets,
+    int max_pages, int cap, int U, int32_t* __restrict__ sel_counts,
+    int32_t* __restrict__ sel_offsets,
     int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
   // Page keys, staged so that loads are coalesced (thread t reads pages
@@ -423,7 +424,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int v = base + tid;
     uint32_t c = 0u;
     if (v < U) c = (uint32_t)__hip_atomic_load(sel_counts + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t ch = (c + (uint32_t)chunk_pages - 1u) / (uint32_t)chunk_pages;
+    // chunks as the attention plans them: lists beyond the dims' bound are cut
+    const uint32_t ch = (min(c, (uint32_t)cap) + (uint32_t)chunk_pages - 1u) / (uint32_t)chunk_pages;
     // both prefix sums in one scan: count in the high word, chunks in the low
     unsigned long long tot;
     const unsigned long long ex = block_excl_scan<unsigned long long, kSelThreads>(
@@ -445,11 +447,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 template <int NPT, bool COUNT>
 static void launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
                           const int32_t* page_table, float gamma, int k_pages, int chunk_pages,
-                          int hkv, int group, int max_pages, int32_t* sel_counts,
+                          int hkv, int group, int max_pages, int cap, int32_t* sel_counts,
                           int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
                           int32_t* sel_phys, uint32_t* ticket) {
   hipLaunchKernelGGL((select_kernel<NPT, COUNT>), dim3(U), dim3(kSelThreads), 0, st, logits,
-                     ctx_lens, page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, U,
+                     ctx_lens, page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, cap,
+                     U,
                      sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket);
 }
 
@@ -493,7 +496,8 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
   uint32_t* ticket = static_cast<uint32_t*>(ws);
 #define SP_SEL(N)                                                                           \
   launch_select<N, COUNT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages, \
-                          hkv, group, dims->max_pages, sel_counts, sel_offsets,           \
+                          hkv, group, dims->max_pages, list_cap(dims), sel_counts,        \
+                          sel_offsets,                                                      \
                           chunk_offsets, sel_pages, sel_phys, ticket)
   if (npt <= 1) SP_SEL(1);
   else if (npt <= 2) SP_SEL(2);

@@ -49,11 +49,15 @@ class Dims(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
         ("max_pages", ctypes.c_int32),
+        ("max_list_pages", ctypes.c_int32),
     ]
 
 
-def make_dims(batch, q_heads, kv_heads, max_pages, head_dim=128, page_size=16):
-    return Dims(batch, q_heads, kv_heads, head_dim, page_size, max_pages)
+def make_dims(batch, q_heads, kv_heads, max_pages, head_dim=128, page_size=16,
+              max_list_pages=0):
+    """max_list_pages: 0, or a bound on every page list's length that the
+    attention and merge plan for (a smaller grid for short lists)."""
+    return Dims(batch, q_heads, kv_heads, head_dim, page_size, max_pages, max_list_pages)
 
 
 class CachePolicy(ctypes.Structure):

@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--gamma", type=float, default=0.99)
-    ap.add_argument("--chunk", type=int, default=256)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="pages per attention workgroup (default 256; 128 for the host tier)")
     ap.add_argument("--groups", type=int, default=1,
                     help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
@@ -163,7 +164,8 @@ def host_tier_bench(args):
     sizes = I.spread_sizes(B, LP, args.list_spread)
     lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"], sizes=sizes)
     LM = lists.shape[-1]
-    dims = lib.make_dims(B, w.q_heads, H, MP)
+    # every list holds at most LM pages: the attention plans for that
+    dims = lib.make_dims(B, w.q_heads, H, MP, max_list_pages=LM)
     name, _, sh = args.cache_policy.partition(":")
     if name not in ("exact", "bucketed", "pooled"):
         raise SystemExit(f"unknown cache policy {args.cache_policy}")
@@ -302,7 +304,7 @@ def host_tier_layers_bench(args):
     lists = I.drift_lists(w, I.pages_of(lens[0]), LP, steps, ex["drift"])
     B, H = w.batch, w.kv_heads
     U = B * H
-    dims = lib.make_dims(B, w.q_heads, H, MP)
+    dims = lib.make_dims(B, w.q_heads, H, MP, max_list_pages=LP)
     chunk = min(args.chunk, LP)
     seq = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=False)
     pre = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=True)
@@ -426,6 +428,8 @@ def pmc_probe(args):
 
 def main():
     args = parse()
+    if not args.chunk:
+        args.chunk = 128 if args.workload.startswith("host_tier") else 256
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)

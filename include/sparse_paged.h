@@ -73,6 +73,10 @@ typedef struct {
   int32_t head_dim;     /* D: 128 */
   int32_t page_size;    /* P: 16 */
   int32_t max_pages;    /* row length of page_table and of the page lists */
+  int32_t max_list_pages; /* 0, or a bound 1..max_pages on every page list's
+                             length: the attention and merge plan for lists
+                             no longer (entries past it are not attended), so
+                             short lists in long rows launch a small grid */
 } sparse_dims;
 
 /* Library version string (host, static storage). */

@@ -61,6 +61,16 @@ def test_max_parts_and_workspace(L):
     assert L.sparse_decode_max_parts(ctypes.byref(d), 5) == 4 * 13
     assert L.sparse_decode_max_parts(ctypes.byref(d), 0) == -1
     assert L.sparse_select_workspace_bytes(ctypes.byref(d)) >= 4
+    # a bound on the list lengths plans a smaller grid
+    d.max_list_pages = 20
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 2
+    d.max_list_pages = 64
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 4
+    for bad in (-1, 65):
+        d.max_list_pages = bad
+        assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == -1
+        assert L.sparse_score_pages(ctypes.byref(d), FAKE, FAKE, 10, FAKE, FAKE, 0.1, FAKE,
+                                    None) == lib.ERR_INVALID
 
 
 @pytest.mark.parametrize("kw,code", [

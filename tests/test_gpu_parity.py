@@ -230,3 +230,37 @@ def test_grouped_streams_match_single_stream(gpu_lib):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(grp.buf.out, ref.buf.out)
+
+
+def test_list_bound_plans_smaller_grid_same_outputs(gpu_lib):
+    """Short caller-supplied lists in long page-table rows: with dims'
+    max_list_pages set to the longest list, the attention launches
+    U * ceil(bound / chunk) workgroups instead of U * ceil(max_pages / chunk)
+    and every output is bitwise the same."""
+    w = I.custom_workload("bound", 3, 8, 2, ("fixed", 20000), index=113)
+    say("[bound] 3 x 20000 tokens (1250 pages per row), lists of up to 40 pages")
+    layer = GpuLayer(w)
+    rng = np.random.default_rng(17)
+    n = I.pages_of(20000)
+    lists = {u: np.sort(rng.choice(n, size=int(rng.integers(1, 41)), replace=False))
+             for u in range(w.batch * w.kv_heads)}
+    li = layer.li
+    outs = []
+    for bound in (0, 40):
+        d = lib.make_dims(w.batch, w.q_heads, w.kv_heads, li.max_pages, max_list_pages=bound)
+        st = SparseDecodeStep(d, 0.9, 8, scale=w.scale)
+        feed_lists(st, layer, lists)
+        st.attend(li.q, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages,
+                  li.ctx_lens)
+        torch.cuda.synchronize()
+        outs.append((st.max_parts, st.buf.out.clone(), st.buf.out_lse.clone()))
+    assert outs[1][0] == w.batch * w.kv_heads * 5 < outs[0][0]
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
+    for u, lst in lists.items():
+        b, h = divmod(u, w.kv_heads)
+        un = layer.unit_oracle(b, h)
+        o_ref, _ = O.attend_pages(O.bf16_bits_to_f64(un["q"]), O.bf16_bits_to_f64(un["k"]),
+                                  O.bf16_bits_to_f64(un["v"]), un["nv"], lst, w.scale)
+        G = w.group
+        o = outs[1][1][b, h * G:(h + 1) * G].double().cpu().numpy()
+        assert np.abs(o - o_ref).max() <= ATTN_TOL
