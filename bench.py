@@ -582,6 +582,8 @@ def main():
                      "avg_launch_us": round(attn_us, 2),
                      "bytes_per_launch": int(attn_launch_bytes)},
     }
+    result["env"] = {"hip": torch.version.hip, "library": lib.version(),
+                     "device": torch.cuda.get_device_name(0)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lens, args.gamma, args.cpu_seconds)
     print(json.dumps(result), flush=True)
