@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void score_kernel(
 
   const float ln16 = 2.772588722239781f;
   float* out = logits + (int64_t)u * group * max_pages;
+  const bool vec_ok = (max_pages & 3) == 0 && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   u32x4 a[2][8];
   bool oks[2];
   auto issue = [&](int t, int slot) {
@@ -106,15 +107,27 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int s = 0; s < 4; ++s)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[slot][4 + s]), qpos[s], acc, 0, 0,
                                                     0);
-    // lane (g = row, j) now holds u for pages p0 + 4j + i
+    // lane (g = row, j) now holds u for pages p0 + 4j + i: one 16-byte store
+    // of its 4 consecutive pages when they are all in range and aligned
+    float val[4];
+    bool okv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pi = p0 + 4 * j + i;
-      const bool oki = __shfl(oks[slot] ? 1 : 0, 4 * j + i, 64) != 0;
-      if (row < group && pi < n) {
-        const int nv = min(kP, L - kP * pi);
-        const float lnv = (nv == kP) ? ln16 : logf((float)nv);
-        out[(int64_t)row * max_pages + pi] = oki ? fmaf(scale, acc[i], lnv) : -INFINITY;
+      okv[i] = __shfl(oks[slot] ? 1 : 0, 4 * j + i, 64) != 0;
+      const int nv = min(kP, L - kP * pi);
+      const float lnv = (nv >= kP) ? ln16 : logf((float)max(nv, 1));
+      val[i] = okv[i] ? fmaf(scale, acc[i], lnv) : -INFINITY;
+    }
+    if (row < group) {
+      const int pq = p0 + 4 * j;
+      if (vec_ok && pq + 4 <= n) {
+        *reinterpret_cast<floatx4*>(out + (int64_t)row * max_pages + pq) =
+            floatx4{val[0], val[1], val[2], val[3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (pq + i < n) out[(int64_t)row * max_pages + pq + i] = val[i];
       }
     }
   }
