@@ -33,22 +33,19 @@ struct PageFrag {
 
 // Issue the loads of one page's K and V fragments.  p is the logical page,
 // x its physical page (or cache slot); both are wave-uniform.  K/V are read
-// once per step, so the loads are non-temporal (streaming).
+// once per step, so the loads are non-temporal (streaming).  The loads are
+// unconditional: a page that is out of range or past the context reads page
+// 0 of the pool instead (always in bounds) and is marked empty, so
+// attend_page skips it.  (Zero-filling the registers instead would be a
+// write that has to wait for every load still in flight.)
 __device__ __forceinline__ void load_page(PageFrag& f, const uint16_t* __restrict__ kv,
                                           int64_t stride_page, int64_t stride_head,
                                           int64_t pool_pages, int h, int L, int p, int x) {
   const int lane = lane_id(), row = lane & 15, j = lane >> 4;
-  int nv = min(kP, L - kP * p);
-  if (x < 0 || x >= pool_pages || p < 0) nv = 0;
-  f.valid = max(nv, 0);
-  if (f.valid == 0) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) f.k[s] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) f.v[m] = u32x2{0u, 0u};
-    return;
-  }
-  const uint16_t* kt = kv + (int64_t)x * stride_page + (int64_t)h * stride_head;
+  const int nv = min(kP, L - kP * p);
+  const bool ok = x >= 0 && x < pool_pages && p >= 0 && nv > 0;
+  f.valid = ok ? nv : 0;
+  const uint16_t* kt = kv + (int64_t)(ok ? x : 0) * stride_page + (int64_t)h * stride_head;
   const uint16_t* vt = kt + kTile;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -122,11 +119,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int c = blockIdx.x;
   int u, local;
   plan_locate(sel_counts, U, cap, chunk_pages, c, u, local);
+  u = __builtin_amdgcn_readfirstlane(u);
+  local = __builtin_amdgcn_readfirstlane(local);
   if (u < 0) return;                   // past the last chunk of the step
   const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
-  const int L = min(max(ctx_lens[b], 0), max_pages * kP);
-  const int cnt = min(sel_counts[u], cap);
+  const int L = __builtin_amdgcn_readfirstlane(min(max(ctx_lens[b], 0), max_pages * kP));
+  const int cnt = __builtin_amdgcn_readfirstlane(min(sel_counts[u], cap));
   const int i0 = local * chunk_pages;
   const int i1 = min(i0 + chunk_pages, cnt);
   const int32_t* lp = sel_pages + (int64_t)u * max_pages;
@@ -159,16 +158,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int ie = i0 + wv + kAttnWaves * (base + lane);
     const int pl = (lane < cnt_k) ? lp[ie] : -1;
     const int xl = (lane < cnt_k) ? lx[ie] : -1;
-    PageFrag cur, nxt;
-    load_page(cur, kv, stride_page, stride_head, pool_pages, h, L,
+    // Two page buffers in turn, so a page's loads are in flight while the
+    // other page is attended and no register copy waits on them.  In the
+    // steady-state loop every load is unconditional (a branch around a load
+    // makes the compiler wait for all loads where the paths meet); the last
+    // one or two pages are handled after it.
+    PageFrag fa, fb;
+    load_page(fa, kv, stride_page, stride_head, pool_pages, h, L,
               __builtin_amdgcn_readlane(pl, 0), __builtin_amdgcn_readlane(xl, 0));
-    for (int k = 0; k < cnt_k; ++k) {
-      const bool more = k + 1 < cnt_k;
-      if (more)
-        load_page(nxt, kv, stride_page, stride_head, pool_pages, h, L,
-                  __builtin_amdgcn_readlane(pl, k + 1), __builtin_amdgcn_readlane(xl, k + 1));
-      attend_page(cur, qf, gok, j, scale_log2, m_run, l_run, o);
-      if (more) cur = nxt;
+    int k = 0;
+    for (; k + 2 < cnt_k; k += 2) {
+      load_page(fb, kv, stride_page, stride_head, pool_pages, h, L,
+                __builtin_amdgcn_readlane(pl, k + 1), __builtin_amdgcn_readlane(xl, k + 1));
+      attend_page(fa, qf, gok, j, scale_log2, m_run, l_run, o);
+      load_page(fa, kv, stride_page, stride_head, pool_pages, h, L,
+                __builtin_amdgcn_readlane(pl, k + 2), __builtin_amdgcn_readlane(xl, k + 2));
+      attend_page(fb, qf, gok, j, scale_log2, m_run, l_run, o);
+    }
+    if (k + 1 < cnt_k) {
+      load_page(fb, kv, stride_page, stride_head, pool_pages, h, L,
+                __builtin_amdgcn_readlane(pl, k + 1), __builtin_amdgcn_readlane(xl, k + 1));
+      attend_page(fa, qf, gok, j, scale_log2, m_run, l_run, o);
+      attend_page(fb, qf, gok, j, scale_log2, m_run, l_run, o);
+    } else {
+      attend_page(fa, qf, gok, j, scale_log2, m_run, l_run, o);
     }
   }
 

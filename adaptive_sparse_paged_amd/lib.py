@@ -32,6 +32,7 @@ EXPORTS = (
     "sparse_append_tokens",
     "sparse_cache_policy_workspace_bytes",
     "sparse_hbm_cache_resolve_policy",
+    "sparse_read_blocks",
 )
 
 
@@ -95,6 +96,7 @@ _SIGS = {
     "sparse_cache_policy_workspace_bytes": (ctypes.c_size_t, [_D, _CP, _I32]),
     "sparse_hbm_cache_resolve_policy": (_I32, [_D, _CP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                                _P, _P, ctypes.c_size_t, _P]),
+    "sparse_read_blocks": (_I32, [_P, _I64, _P, _I64, _P, _P]),
 }
 
 _lib = None
@@ -254,3 +256,18 @@ def append_tokens(dims, k_new, v_new, kv, stride_page, stride_head, pool_pages, 
     _check("sparse_append_tokens", load().sparse_append_tokens(
         ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(kv), stride_page, stride_head,
         pool_pages, _ptr(page_table), _ptr(ctx_lens), _ptr(summ), _stream(stream)))
+
+
+READ_BLOCKS_GROUPS = 2048   # SPARSE_READ_BLOCKS_GROUPS
+
+
+def read_blocks(pool, pool_blocks, order, xor_out, stream=None):
+    """Measurement helper: read the 8 KiB blocks order[:] of pool.  xor_out
+    (int32 [READ_BLOCKS_GROUPS]) receives one XOR fold per workgroup; their
+    XOR is the XOR of every 32-bit word of the listed blocks."""
+    _dev(pool, order, xor_out)
+    if xor_out.numel() * xor_out.element_size() < 4 * READ_BLOCKS_GROUPS:
+        raise ValueError(f"xor_out must hold {READ_BLOCKS_GROUPS} 32-bit words")
+    _check("sparse_read_blocks", load().sparse_read_blocks(
+        _ptr(pool), int(pool_blocks), _ptr(order), order.numel(), _ptr(xor_out),
+        _stream(stream)))

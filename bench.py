@@ -85,6 +85,33 @@ def kept_tokens(counts, pages, lens, Hkv, max_pages):
     return tsel
 
 
+def read_ceiling(lib, pool, nblocks, reps):
+    """Read rate of one layer's KV pool in whole 8 KiB (page, KV head) blocks,
+    the attention's access unit, with nothing else to do: in a seeded random
+    order (the practical ceiling for the attention kernel) and in address
+    order (the streaming-read ceiling).  HIP events around each launch."""
+    import torch
+    rng = np.random.default_rng(1234)
+    out = {}
+    for name, ids in (("random_8k_blocks_gbs", rng.permutation(nblocks)),
+                      ("sequential_8k_blocks_gbs", np.arange(nblocks))):
+        order = torch.from_numpy(ids.astype(np.int32)).cuda()
+        sink = torch.empty(lib.READ_BLOCKS_GROUPS, dtype=torch.int32, device="cuda")
+        lib.read_blocks(pool, nblocks, order, sink)
+        marks = []
+        for _ in range(max(reps, 3)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            lib.read_blocks(pool, nblocks, order, sink)
+            b.record()
+            marks.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in marks]))
+        out[name] = round(nblocks * 8192 / (us * 1e-6) / 1e9, 1)
+    out["bytes_per_launch"] = int(nblocks * 8192)
+    return out
+
+
 def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -554,6 +581,8 @@ def main():
                 and rec.get("chunk_pages") == st.chunk_pages and rec.get("gamma") == args.gamma):
             traffic = rec.get("bytes_per_launch")
 
+    ceiling = read_ceiling(lib, L_in[0].kv_pool, L_in[0].pool_pages * w.kv_heads, args.steps)
+
     result = {
         "metric": "sparse decode step \u00b5s/layer + achieved HBM GB/s vs peak at 128k ctx, \u03b3=0.99",
         "value": round(gbs, 1),
@@ -581,6 +610,9 @@ def main():
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_us, 2),
                      "bytes_per_launch": int(attn_launch_bytes)},
+        "read_ceiling": dict(ceiling,
+                             attn_frac_of_random=round(attn_gbs / ceiling["random_8k_blocks_gbs"], 4),
+                             value_frac_of_random=round(gbs / ceiling["random_8k_blocks_gbs"], 4)),
     }
     result["env"] = {"hip": torch.version.hip, "library": lib.version(),
                      "device": torch.cuda.get_device_name(0)}

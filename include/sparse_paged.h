@@ -364,6 +364,31 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
                                               int32_t* sel_phys, int32_t* stats, void* ws,
                                               size_t ws_bytes, void* stream);
 
+/*
+ * Measurement helper (not a step of the decode path).
+ *
+ * sparse_read_blocks -- read whole 8 KiB blocks of a pool in a given order,
+ * with nothing else to do, to measure the read rate that the attention
+ * kernel's own access unit (one (page, KV head) K+V block) allows.  Block i
+ * is the 4096 bf16 values starting at element pool + i * 4096 (the canonical
+ * pool [Ppool][Hkv][2][2048] has Ppool * Hkv blocks).  The kernel reads
+ * blocks order[0 .. n) -- a random permutation gives the random-block
+ * ceiling, ascending ids the streaming-read ceiling -- with
+ * SPARSE_READ_BLOCKS_GROUPS workgroups of 4 waves, 2 blocks in flight per
+ * wave and non-temporal loads.  Workgroup g writes the XOR of every 32-bit
+ * word it read to xor_out[g]; the XOR of all SPARSE_READ_BLOCKS_GROUPS words
+ * is the XOR over the listed blocks (a block listed twice cancels itself).
+ * Ids outside [0, pool_blocks) are skipped.  Every call writes all of
+ * xor_out.  order may be NULL when n == 0.
+ *   xor_out  uint32 [SPARSE_READ_BLOCKS_GROUPS], 4-byte aligned
+ * INVALID: n < 0, pool_blocks < 0, a NULL pool or xor_out (or order with
+ * n > 0), pool not 16-byte aligned.
+ */
+#define SPARSE_READ_BLOCKS_GROUPS 2048
+sparse_status sparse_read_blocks(const uint16_t* pool, int64_t pool_blocks,
+                                 const int32_t* order, int64_t n, uint32_t* xor_out,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,6 +136,13 @@ def test_null_and_value_checks(L):
     assert pol(3, 1, 9000, need, None) == lib.ERR_WORKSPACE
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
+    # the read-ceiling helper
+    assert L.sparse_read_blocks(FAKE, 100, FAKE, -1, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_read_blocks(FAKE, -1, FAKE, 10, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_read_blocks(None, 100, FAKE, 10, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_read_blocks(FAKE, 100, FAKE, 10, None, None) == lib.ERR_INVALID
+    assert L.sparse_read_blocks(ctypes.c_void_p(0x10002), 100, FAKE, 10, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_read_blocks(FAKE, 100, FAKE, 10, ctypes.c_void_p(0x10002), None) == lib.ERR_INVALID
 
 
 def test_missing_library_fails_loudly(tmp_path):
