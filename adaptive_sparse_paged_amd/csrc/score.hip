@@ -45,25 +45,29 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int lane = lane_id(), row = lane & 15, j = lane >> 4;
   const int32_t* pt = page_table + (int64_t)b * max_pages;
 
+  // Every load below is unconditional (out-of-range rows read a valid
+  // address and are discarded later): a load under a per-lane condition
+  // becomes a branch, and where the paths meet the compiler waits for every
+  // load in flight -- which would drain tile 1's loads before tile 0's math.
   int xs[kScoreTilesPerWave];
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
     const int p = p_begin + t * 16 + row;
-    xs[t] = (p < n) ? pt[p] : -1;
+    const int x = pt[min(p, n - 1)];
+    xs[t] = (p < n) ? x : -1;
   }
 
   // B operands: q- for the kmin half, q+ for the kmax half (bf16 bit masks).
   bf16x8 qneg[4], qpos[4];
   {
     const int g = row;
+    const int hq = h * group + min(g, group - 1);
+    const uint32_t gmask = (g < group) ? 0xFFFFFFFFu : 0u;    // padding columns are zero
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (g < group) {
-        const int hq = h * group + g;
-        w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hkv * group + hq) * kD + 32 * s +
-                                            8 * j);
-      }
+      u32x4 w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hkv * group + hq) * kD + 32 * s +
+                                                8 * j);
+      w &= gmask;
       u32x4 neg, pos;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -83,21 +87,23 @@ __global__ __launch_bounds__(256) void score_kernel(
   const bool vec_ok = (max_pages & 3) == 0 && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   u32x4 a[2][8];
   bool oks[2];
+  // A row whose page is out of range reads page 0's summary (always in
+  // bounds); MFMA rows are independent and that row's logit is written as
+  // -inf, so the values it read never matter.
   auto issue = [&](int t, int slot) {
     const int x = xs[t];
     const bool ok = (x >= 0) && (x < pool_pages);
     oks[slot] = ok;
     const uint16_t* src = summ + ((int64_t)(ok ? x : 0) * hkv + h) * (2 * kD) + 8 * j;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      a[slot][s] = ok ? *reinterpret_cast<const u32x4*>(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 8; ++s) a[slot][s] = *reinterpret_cast<const u32x4*>(src + 32 * s);
   };
   issue(0, 0);
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
     const int p0 = p_begin + t * 16;
     if (p0 >= n) break;
-    if (t + 1 < kScoreTilesPerWave && p0 + 16 < n) issue(t + 1, (t + 1) & 1);
+    if (t + 1 < kScoreTilesPerWave) issue(t + 1, (t + 1) & 1);
     const int slot = t & 1;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
