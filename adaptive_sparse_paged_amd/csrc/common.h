@@ -99,10 +99,30 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 // sum -- no host plan and no precomputed offsets.
 constexpr int kPlanVU = 8;
 
-__device__ __forceinline__ int plan_chunks(const int32_t* __restrict__ counts, int idx, int U,
-                                           int cap, int chunk) {
-  const int k = (idx < U) ? min(max(counts[idx], 0), cap) : 0;
+// Chunks of one unit u < U.
+__device__ __forceinline__ int unit_chunks(const int32_t* __restrict__ counts, int u, int cap,
+                                           int chunk) {
+  const int k = min(max(counts[u], 0), cap);
   return (k + chunk - 1) / chunk;
+}
+
+// Chunk counts of units base .. base + kPlanVU - 1 (0 past the last unit).
+// The loads are unconditional -- an index past the last unit re-reads unit
+// U-1 -- and all are issued before any is used.  The empty asm statement
+// pins each loaded value in a register; without it the compiler moves each
+// load under the `idx < U` test, and a load under a per-lane condition
+// becomes a branch that waits for it: 8 round trips instead of one.
+__device__ __forceinline__ void plan_chunks8(const int32_t* __restrict__ counts, int base, int U,
+                                             int cap, int chunk, int (&ch)[kPlanVU]) {
+  int raw[kPlanVU];
+#pragma unroll
+  for (int v = 0; v < kPlanVU; ++v) raw[v] = counts[min(base + v, U - 1)];
+#pragma unroll
+  for (int v = 0; v < kPlanVU; ++v) {
+    asm volatile("" : "+v"(raw[v]));
+    const int k = (base + v < U) ? min(max(raw[v], 0), cap) : 0;
+    ch[v] = (k + chunk - 1) / chunk;
+  }
 }
 
 // Unit of global chunk c and the chunk's index within that unit (unit = -1
@@ -116,12 +136,10 @@ __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, 
   local = 0;
   for (int seg = 0; seg < U; seg += 64 * kPlanVU) {
     int ch[kPlanVU];
+    plan_chunks8(counts, seg + lane * kPlanVU, U, cap, chunk, ch);
     int s = 0;
 #pragma unroll
-    for (int v = 0; v < kPlanVU; ++v) {
-      ch[v] = plan_chunks(counts, seg + lane * kPlanVU + v, U, cap, chunk);
-      s += ch[v];
-    }
+    for (int v = 0; v < kPlanVU; ++v) s += ch[v];
     const int incl = wave_incl_scan(s);
     const int seg_total = __shfl(incl, 63, 64);
     if (c < running + seg_total) {
@@ -150,12 +168,11 @@ __device__ __forceinline__ int plan_prefix(const int32_t* __restrict__ counts, i
   const int lane = lane_id();
   int running = 0;
   for (int seg = 0; seg < u; seg += 64 * kPlanVU) {
+    int ch[kPlanVU];
+    plan_chunks8(counts, seg + lane * kPlanVU, U, cap, chunk, ch);
     int s = 0;
 #pragma unroll
-    for (int v = 0; v < kPlanVU; ++v) {
-      const int idx = seg + lane * kPlanVU + v;
-      if (idx < u) s += plan_chunks(counts, idx, U, cap, chunk);
-    }
+    for (int v = 0; v < kPlanVU; ++v) s += (seg + lane * kPlanVU + v < u) ? ch[v] : 0;
     running += __shfl(wave_incl_scan(s), 63, 64);
   }
   return running;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
   __syncthreads();
   const int c0 = s_c0;
-  const int c1 = c0 + plan_chunks(sel_counts, u, U, cap, chunk);
+  const int c1 = c0 + unit_chunks(sel_counts, u, cap, chunk);
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
 
   float m = -INFINITY, s = 0.f;
@@ -38,10 +38,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const bool two = c + kMergeSlots < c1;
     const int64_t r0 = (int64_t)c * group + g;
     const int64_t r1 = (int64_t)(two ? c + kMergeSlots : c) * group + g;
-    const float l0 = part_lse[r0];
-    const float l1 = two ? part_lse[r1] : -INFINITY;
-    const floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
-    const floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
+    // All four loads are issued before any is used (one round trip): the
+    // empty asm statements keep the compiler from moving a load under the
+    // `two` or `mn` tests, where it would become a branch that waits for it.
+    float l0 = part_lse[r0], l1 = part_lse[r1];
+    floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
+    floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
+    asm volatile("" : "+v"(l0), "+v"(l1), "+v"(o0), "+v"(o1));
+    if (!two) l1 = -INFINITY;
     const float mn = fmaxf(m, fmaxf(l0, l1));
     if (mn == -INFINITY) continue;
     const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);

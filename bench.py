@@ -112,8 +112,12 @@ def read_ceiling(lib, pool, nblocks, reps):
     return out
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(*paths):
+    """First 16 hex digits of the sha256 over the given sources, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, lens, gamma, budget_s):
@@ -576,8 +580,10 @@ def main():
     tfile = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
     if os.path.exists(tfile):
         rec = json.load(open(tfile))
-        src = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc", "attn.hip")
-        if (rec.get("source_sha256_16") == source_hash(src) and rec.get("workload") == w.name
+        csrc = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc")
+        # the attention kernel is compiled from attn.hip and the helpers it includes
+        src_hash = source_hash(os.path.join(csrc, "attn.hip"), os.path.join(csrc, "common.h"))
+        if (rec.get("source_sha256_16") == src_hash and rec.get("workload") == w.name
                 and rec.get("chunk_pages") == st.chunk_pages and rec.get("gamma") == args.gamma):
             traffic = rec.get("bytes_per_launch")
 
