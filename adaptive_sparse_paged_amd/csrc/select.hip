@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
         const float M = red_m[g0 + hh][0], inv = red_s[g0 + hh][0];
+        if (M == -INFINITY) continue;      // a head with no finite logit adds no mass
 #pragma unroll
         for (int k = 0; k < NPT; ++k) m[k] += __expf(xv[hh][k] - M) * inv;
       }

@@ -157,6 +157,32 @@ def test_zero_length_request_and_single_token(gpu_lib):
     assert np.array_equal(offs, np.concatenate([[0], np.cumsum(st.buf.sel_counts.cpu().numpy())]))
 
 
+def test_request_without_valid_pages(gpu_lib):
+    """A request whose page-table row holds no page of the pool: every one of
+    its logits is -inf, its per-head normalisers are empty, and the selection
+    must not turn that into NaN masses.  It keeps one (empty) page, its
+    attention sees no token (output 0, lse -inf), and the other requests are
+    unaffected."""
+    w = I.custom_workload("nopages", 3, 8, 2, ("fixed", 700), index=110)
+    say("[edge] request 1 with every page id out of range")
+    layer = GpuLayer(w)
+    li = layer.li
+    li.page_table[1].fill_(-1)
+    st = layer.step(0.95, 8)
+    layer.run(st)
+    G = w.group
+    assert not torch.isnan(st.buf.out).any() and not torch.isnan(st.buf.out_lse).any()
+    for h in range(w.kv_heads):
+        u = 1 * w.kv_heads + h
+        assert st.buf.sel_counts[u].item() == 1
+        assert torch.all(st.buf.sel_phys[u, :1] == -1)
+        assert torch.all(st.buf.out[1, h * G:(h + 1) * G] == 0)
+        assert torch.all(torch.isneginf(st.buf.out_lse[1, h * G:(h + 1) * G]))
+    for b in (0, 2):
+        for h in range(w.kv_heads):
+            check_unit(layer, st, b, h, 0.95)
+
+
 def test_graph_replay_after_inputs_change(gpu_lib):
     w = I.custom_workload("graph", 4, 8, 2, ("uniform", 500, 6000), alpha=("uniform", 1, 8),
                           index=108)
