@@ -28,8 +28,11 @@ __global__ __launch_bounds__(256) void summaries_kernel(
   const int lane = lane_id();
   if (item >= n * hkv) return;
   const int i = item / hkv, h = item - (item / hkv) * hkv;
-  const int x = pages[i];
-  const int nv = min(max(valid[i], 0), kP);
+  // both ids in one round trip: the empty asm keeps the compiler from
+  // issuing the second load only after the first one's test
+  int x = pages[i], nv = valid[i];
+  asm volatile("" : "+v"(x), "+v"(nv));
+  nv = min(max(nv, 0), kP);
   if (x < 0 || x >= pool_pages || nv == 0) return;
   const uint32_t* tile =
       reinterpret_cast<const uint32_t*>(kv + (int64_t)x * stride_page + (int64_t)h * stride_head);
