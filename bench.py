@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--gamma", type=float, default=0.99)
     ap.add_argument("--chunk", type=int, default=0,
-                    help="pages per attention workgroup (default 256; 128 for the host tier)")
+                    help="pages per attention workgroup (default: the workload's entry in "
+                         "DEFAULT_CHUNK, else 256)")
     ap.add_argument("--groups", type=int, default=1,
                     help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
@@ -56,6 +57,15 @@ def parse():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only launch what the hardware-counter runs measure")
     return ap.parse_args()
+
+
+# Pages per attention workgroup, measured per workload on MI355X with the
+# full 32- or 4-layer step: 512 wins where every request has the same long
+# context (fewer workgroup starts), 256 where lengths are ragged (a unit's last,
+# partial chunk unbalances the grid less), and 128 for the host tier's short
+# 448-page lists.
+DEFAULT_CHUNK = {"long_128k": 512, "llama8b_32k": 512, "serving_b64": 256,
+                 "host_tier_512k": 128, "host_tier_layers": 128}
 
 
 def counted_bytes(n, k, tsel, G, Hkv, chunk):
@@ -460,7 +470,7 @@ def pmc_probe(args):
 def main():
     args = parse()
     if not args.chunk:
-        args.chunk = 128 if args.workload.startswith("host_tier") else 256
+        args.chunk = DEFAULT_CHUNK.get(args.workload, 256)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)
