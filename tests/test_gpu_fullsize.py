@@ -1,5 +1,5 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (chunk 256): sampled units against the fp64 oracle (regenerated on the
+times (its per-workload attention chunk): sampled units against the fp64 oracle (regenerated on the
 host from the seeded generator), structural properties on every unit, and the
 select kernel fed with oracle logits."""
 
@@ -13,10 +13,9 @@ import oracle as O
 from adaptive_sparse_paged_amd import inputs as I
 
 from _gpu_case import GpuLayer, check_unit, say
+from bench import DEFAULT_CHUNK
 
 pytestmark = pytest.mark.gpu
-
-BENCH_CHUNK = 256
 
 
 def _free():
@@ -62,7 +61,7 @@ def test_fullsize_sampled(gpu_lib, name, layer_idx, gamma, samples):
     w = I.WORKLOADS[name]
     say(f"[fullsize] {name} layer {layer_idx} gamma {gamma}: generating")
     layer = GpuLayer(w, layer=layer_idx)
-    st = layer.step(gamma, BENCH_CHUNK)
+    st = layer.step(gamma, DEFAULT_CHUNK.get(name, 256))
     layer.run(st)
     counts = _structural(layer, st)
     say(f"  structural ok; mean kept fraction "
@@ -86,7 +85,7 @@ def test_host_tier_context_score_select(gpu_lib):
     w = I.WORKLOADS["host_tier_512k"]
     say("[fullsize] host_tier_512k: generating 16 x 524288 tokens")
     layer = GpuLayer(w)
-    st = layer.step(0.99, BENCH_CHUNK)
+    st = layer.step(0.99, 256)          # the whole HBM step at this context, library default
     layer.run(st)
     _structural(layer, st)
     for b, h in [(3, 5), (15, 0)]:
