@@ -122,6 +122,16 @@ def read_ceiling(lib, pool, nblocks, reps):
     return out
 
 
+def library_source_hash():
+    """sha256 (first 16 hex digits) over the library's sources: the C ABI
+    header and every file under csrc/, in name order."""
+    csrc = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc")
+    files = [os.path.join(ROOT, "include", "sparse_paged.h")]
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
+              if f.endswith((".hip", ".h"))]
+    return source_hash(*files)
+
+
 def source_hash(*paths):
     """First 16 hex digits of the sha256 over the given sources, in order."""
     h = hashlib.sha256()
@@ -130,12 +140,18 @@ def source_hash(*paths):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, lens, gamma, budget_s):
+def cpu_baseline(w, lens, gamma, budget_s, gpu=None):
     """Time the fp64 oracle (score, masses, cut, attention) on every
     (request, KV head) unit of layer 0, on one host thread.  Each unit is
     generated once (untimed) and its oracle call repeated R times, with R
     chosen from the first unit so the timed total is about budget_s; the mean
-    per-unit time is scaled to one layer."""
+    per-unit time is scaled to one layer.
+
+    gpu = (counts, pages, out) of the timed run's layer 0: then every unit
+    the oracle ran is also checked, untimed, against what the GPU produced --
+    its list accepted by the coverage predicate, exact-match with the
+    oracle's list, and attention on the GPU's list within 1e-2 -- and the
+    summary is returned as a second dict (else None)."""
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=1)
@@ -145,6 +161,7 @@ def cpu_baseline(w, lens, gamma, budget_s):
     from adaptive_sparse_paged_amd import inputs as I
     n_units = w.batch * w.kv_heads
     spent, calls, reps = 0.0, 0, None
+    chk = {"units": 0, "accepted": 0, "exact": 0, "max_abs_err": 0.0}
     t_total = time.time()
     for b in range(w.batch):
         for h in range(w.kv_heads):
@@ -163,6 +180,17 @@ def cpu_baseline(w, lens, gamma, budget_s):
                 r += 1
                 if reps is None:
                     reps = int(min(16, max(1, round(budget_s / (dt * n_units)))))
+            if gpu is not None:                # untimed: the timed run's own outputs
+                counts, pages, out = gpu
+                u = b * w.kv_heads + h
+                lst = pages[u, :int(counts[u])]
+                ok, _ = O.list_accepted(lst, sel["m"], gamma, 1e-5)
+                chk["units"] += 1
+                chk["accepted"] += int(ok)
+                chk["exact"] += int(len(lst) == sel["count"] and np.array_equal(lst, sel["list"]))
+                o_ref, _ = O.attend_pages(qf, Kf, Vf, nv, lst, w.scale)
+                o_gpu = out[b, h * w.group:(h + 1) * w.group].astype(np.float64)
+                chk["max_abs_err"] = max(chk["max_abs_err"], float(np.abs(o_gpu - o_ref).max()))
             if time.time() - t_total > 8 * budget_s:
                 break
         if time.time() - t_total > 8 * budget_s:
@@ -171,10 +199,17 @@ def cpu_baseline(w, lens, gamma, budget_s):
         limiter.unregister()
     units = -(-calls // reps)
     us_layer = spent / calls * n_units * 1e6
-    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+    base = {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
             "sample": f"{units} of {n_units} (request, KV head) units of layer 0, each run "
                       f"{reps} times: {spent:.1f} s of fp64 NumPy on one host thread, "
                       f"mean per unit scaled to one layer"}
+    if gpu is None:
+        return base, None
+    chk["max_abs_err"] = float(f"{chk['max_abs_err']:.3g}")
+    chk["what"] = ("layer 0 of the timed run against the fp64 oracle: lists accepted by the "
+                   "coverage predicate (1e-5 relative mass), lists equal to the oracle's, "
+                   "max-abs error of attention on the GPU's lists (bar 1e-2)")
+    return base, chk
 
 
 def host_tier_bench(args):
@@ -534,6 +569,8 @@ def main():
         c = st.buf.sel_counts.cpu().numpy()
         pg = st.buf.sel_pages.cpu().numpy()
         sel_stats.append((c, kept_tokens(c, pg, lens, w.kv_heads, max_pages)))
+        if l == 0:
+            layer0 = (c.copy(), pg.copy())
     graph = capture(step_fn)
 
     for _ in range(args.warmup):
@@ -631,9 +668,13 @@ def main():
                              value_frac_of_random=round(gbs / ceiling["random_8k_blocks_gbs"], 4)),
     }
     result["env"] = {"hip": torch.version.hip, "library": lib.version(),
-                     "device": torch.cuda.get_device_name(0)}
+                     "device": torch.cuda.get_device_name(0),
+                     "sources_sha256_16": library_source_hash()}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, lens, args.gamma, args.cpu_seconds)
+        torch.cuda.synchronize()
+        gpu0 = (layer0[0], layer0[1], outs[0].cpu().numpy())
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(
+            w, lens, args.gamma, args.cpu_seconds, gpu=gpu0)
     print(json.dumps(result), flush=True)
 
 
