@@ -136,7 +136,8 @@ def source_hash(*paths):
     """First 16 hex digits of the sha256 over the given sources, in order."""
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        with open(p, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -626,7 +627,8 @@ def main():
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
     if os.path.exists(tfile):
-        rec = json.load(open(tfile))
+        with open(tfile) as f:
+            rec = json.load(f)
         csrc = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc")
         # the attention kernel is compiled from attn.hip and the helpers it includes
         src_hash = source_hash(os.path.join(csrc, "attn.hip"), os.path.join(csrc, "common.h"))

@@ -2,7 +2,6 @@
 seeded generator, run the library's step, and compare against the fp64
 oracle on units regenerated on the host."""
 
-import math
 import sys
 
 import numpy as np

@@ -5,6 +5,7 @@ any HIP call is made."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -15,7 +16,8 @@ HEADER = os.path.join(ROOT, "include", "sparse_paged.h")
 
 
 def _declared():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sparse_[a-z_0-9]+)\s*\(", text)))
 
@@ -34,7 +36,8 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lib.EXPORTS)
-    out = os.popen(f"nm -D --defined-only {lib.LIB_PATH}").read()
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
     for n in names:
         assert re.search(rf"\bT {n}\b", out), n
 

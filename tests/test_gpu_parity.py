@@ -6,7 +6,6 @@ predicate under 1e-5 relative mass perturbation (exact match rate reported);
 attention outputs within 1e-2 max-abs of exact fp64 attention, both on the
 GPU's own lists and on oracle-supplied lists."""
 
-import math
 
 import numpy as np
 import pytest

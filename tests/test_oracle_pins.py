@@ -25,7 +25,8 @@ def _bits(x):
 
 def test_bf16_roundtrip_all_patterns():
     b = np.arange(65536, dtype=np.int64)
-    f = O.bf16_bits_to_f64(b)
+    with np.errstate(invalid="ignore"):      # the NaN patterns (signalling ones warn on cast)
+        f = O.bf16_bits_to_f64(b)
     ok = ~np.isnan(f)
     assert np.array_equal(O.f64_to_bf16_bits(f[ok]).astype(np.int64), b[ok])
 
@@ -146,7 +147,8 @@ def test_mass_sums_to_one_and_is_exact_for_constant_pages():
 
 
 def test_golden_worked_example_masses_cuts_attention():
-    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
     s = math.log(2.0)
     q = np.array(ex["q"])
     nv = np.array([p["valid"] for p in ex["pages"]])
@@ -181,7 +183,8 @@ def test_golden_worked_example_masses_cuts_attention():
 # ---------------------------------------------------------------- the cut
 
 def test_golden_dyadic_cuts():
-    ex = json.load(open(os.path.join(GOLDEN, "coverage_dyadic.json")))
+    with open(os.path.join(GOLDEN, "coverage_dyadic.json")) as f:
+        ex = json.load(f)
     m = np.array(ex["mass_num"], dtype=np.float64) / ex["mass_den"]
     for g_str, lst in ex["cuts"].items():
         got, k, _, _ = O.coverage_cut(m, float(g_str))
