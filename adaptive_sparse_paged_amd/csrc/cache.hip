@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int max_pages, int C, int recency_shift, const int32_t* __restrict__ step_counter,
     int32_t* __restrict__ slot_tag,
     int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
-    int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats, MissRec* __restrict__ misses,
-    int32_t* __restrict__ miss_count) {
+    int32_t* __restrict__ sel_phys, int32_t* __restrict__ hit_phys, int32_t* __restrict__ stats,
+    MissRec* __restrict__ misses, int32_t* __restrict__ miss_count) {
   __shared__ uint8_t req[kMaxSlots];       // slot holds a unit requested this step
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
   __shared__ SelectScratch sel;
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
         if (li[k] < 0) continue;
         int sk = s[k];
         if (sk >= C) sk = -2;                // corrupt state: never index past the cache
+        if (hit_phys) hit_phys[li[k]] = (sk >= 0) ? b * C + sk : -1;
         if (sk >= 0) {
           ++h_local;
           req[sk] = 1;
@@ -241,22 +242,39 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   }
 }
 
-// One wave per missed unit: 8 KiB from pinned host memory into the slot.
-__global__ __launch_bounds__(256) void fetch_kernel(const uint16_t* __restrict__ host_kv,
-                                                    uint16_t* __restrict__ cache_kv, int hkv,
-                                                    int max_pages, int C,
-                                                    const MissRec* __restrict__ misses,
-                                                    const int32_t* __restrict__ miss_count,
-                                                    int waves_per_req,
-                                                    int32_t* __restrict__ step_counter) {
-  const int b = blockIdx.y;
+// The fetch runs in a few whole compute units that it keeps to itself: each
+// workgroup is 8 waves and reserves the unit's entire LDS, so no other
+// workgroup that uses LDS (the attention, merges, resolves) is placed beside
+// it.  A fetch wave holds its PCIe reads in flight for microseconds, and
+// workgroups sharing its compute unit were measured to stall behind them:
+// attention launched beside a fetch ran up to 9x longer.  (8 waves per unit
+// over 32 units fetched faster than 16 waves over 16.)
+constexpr int kFetchThreads = 512;
+constexpr int kFetchWavesPerGroup = kFetchThreads / 64;
+constexpr int kFetchLdsWords = 40960;    // 160 KiB, the whole LDS of a compute unit
+
+// Wave w of waves_per_req * B copies request b = w % B's misses
+// w / B, w / B + waves_per_req, ...: 8 KiB each, from pinned host memory into
+// the slot.
+__global__ __launch_bounds__(kFetchThreads) void fetch_kernel(
+    const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv, int hkv,
+    int max_pages, int C, const MissRec* __restrict__ misses,
+    const int32_t* __restrict__ miss_count, int B, int waves_per_req,
+    int32_t* __restrict__ step_counter) {
+  __shared__ uint32_t cu_reserve[kFetchLdsWords];
   // every resolve workgroup has read the step (the resolve kernel ran first on
   // this stream): advance it for the next call
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *step_counter += 1;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
+  const int w = blockIdx.x * kFetchWavesPerGroup + (threadIdx.x >> 6);
   const int lane = lane_id();
+  if (w >= waves_per_req * B) return;
+  const int b = w % B;
   const int cnt = miss_count[b];
-  for (int i = w; i < cnt; i += waves_per_req) {
+  if (cnt < 0) {                               // never taken; keeps the reservation
+    cu_reserve[threadIdx.x] = 0u;
+    asm volatile("" ::"v"(cu_reserve[threadIdx.x ^ 1u]));
+  }
+  for (int i = w / B; i < cnt; i += waves_per_req) {
     const MissRec m = misses[(int64_t)b * C + i];
     const int h = m.unit / max_pages, p = m.unit - (m.unit / max_pages) * max_pages;
     const u32x4* src = reinterpret_cast<const u32x4*>(
@@ -309,7 +327,8 @@ __global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
     int max_pages, int S, const int32_t* __restrict__ step_counter,
     int32_t* __restrict__ slot_stamp, const int32_t* __restrict__ unit_slot,
-    int32_t* __restrict__ sel_phys, uint8_t* __restrict__ req, int32_t* __restrict__ counts) {
+    int32_t* __restrict__ sel_phys, int32_t* __restrict__ hit_phys, uint8_t* __restrict__ req,
+    int32_t* __restrict__ counts) {
   __shared__ int32_t head_off[kMaxKvHeads + 1];
   __shared__ unsigned long long scan64[kResThreads / 64];
   const int tid = threadIdx.x, b = blockIdx.x;
@@ -327,6 +346,7 @@ __global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
       sk = unit_slot[(int64_t)(b * hkv + h) * max_pages + p];
       if (sk >= S) sk = -2;                  // corrupt state: never index past the pool
     }
+    if (hit_phys) hit_phys[li] = (sk >= 0) ? sk : -1;
     if (sk >= 0) {
       ++h_local;
       req[sk] = 1;
@@ -566,18 +586,22 @@ __global__ __launch_bounds__(kResThreads) void pool_place_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void pool_fetch_kernel(const uint16_t* __restrict__ host_kv,
-                                                         uint16_t* __restrict__ cache_kv, int hkv,
-                                                         int max_pages,
-                                                         const MissRec* __restrict__ misses,
-                                                         const int32_t* __restrict__ placed_in,
-                                                         int waves,
-                                                         int32_t* __restrict__ step_counter) {
+// The pool's fetch, in whole compute units like fetch_kernel: wave w copies
+// the placed misses w, w + waves, ...
+__global__ __launch_bounds__(kFetchThreads) void pool_fetch_kernel(
+    const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv, int hkv,
+    int max_pages, const MissRec* __restrict__ misses, const int32_t* __restrict__ placed_in,
+    int waves, int32_t* __restrict__ step_counter) {
+  __shared__ uint32_t cu_reserve[kFetchLdsWords];
   // every workgroup of the earlier kernels has read the step: advance it
   if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int w = blockIdx.x * kFetchWavesPerGroup + (threadIdx.x >> 6);
   const int lane = lane_id();
   const int P = *placed_in;
+  if (P < 0) {                                 // never taken; keeps the reservation
+    cu_reserve[threadIdx.x] = 0u;
+    asm volatile("" ::"v"(cu_reserve[threadIdx.x ^ 1u]));
+  }
   const int per_req = hkv * max_pages;       // pooled ids fit in 31 bits
   for (int i = w; i < P; i += waves) {
     const MissRec m = misses[i];
@@ -592,6 +616,42 @@ __global__ __launch_bounds__(256) void pool_fetch_kernel(const uint16_t* __restr
 #pragma unroll
     for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = t[k];
   }
+}
+
+// One workgroup per (request, KV head) unit: the unit's list entries that
+// were placed this step but were not resident before it (hit_phys < 0,
+// sel_phys >= 0), compacted in list order -- ascending page order -- into
+// the unit's miss list.
+constexpr int kSplitThreads = 256;
+
+__global__ __launch_bounds__(kSplitThreads) void split_misses_kernel(
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ hit_phys, int max_pages,
+    int32_t* __restrict__ miss_counts, int32_t* __restrict__ miss_pages,
+    int32_t* __restrict__ miss_phys) {
+  __shared__ uint32_t scan32[kSplitThreads / 64];
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int n = min(max(sel_counts[u], 0), max_pages);
+  const int64_t row = (int64_t)u * max_pages;
+  uint32_t base = 0u;
+  for (int i0 = 0; i0 < n; i0 += kSplitThreads) {
+    const int i = i0 + tid;
+    int page = -1, phys = -1;
+    uint32_t miss = 0u;
+    if (i < n) {
+      page = sel_pages[row + i];
+      phys = sel_phys[row + i];
+      miss = (hit_phys[row + i] < 0 && phys >= 0) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t r = base + block_excl_scan<uint32_t, kSplitThreads>(miss, scan32, tot);
+    if (miss) {
+      miss_pages[row + r] = page;
+      miss_phys[row + r] = phys;
+    }
+    base += tot;
+  }
+  if (tid == 0) miss_counts[u] = (int32_t)base;
 }
 
 }  // namespace sp
@@ -618,87 +678,137 @@ size_t pooled_ws_bytes(int B, int S) {
          nblk * 2 * sizeof(int32_t) + (size_t)B * 3 * sizeof(int32_t) + sizeof(int32_t) + 256;
 }
 
-sparse_status check_cache_args(const sparse_dims* dims, const int32_t* sel_counts,
-                               const int32_t* sel_pages, const uint16_t* host_kv,
-                               uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
-                               int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
-                               int32_t* sel_phys, int32_t* stats) {
+// Arguments of the resolve itself (lists, cache state, outputs).
+sparse_status check_resolve_args(const sparse_dims* dims, const int32_t* sel_counts,
+                                 const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag,
+                                 int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                                 int32_t* sel_phys, int32_t* stats) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
-  if (!sel_counts || !sel_pages || !host_kv || !cache_kv || !slot_tag || !slot_stamp ||
-      !unit_slot || !step_counter || !sel_phys || !stats)
+  if (!sel_counts || !sel_pages || !slot_tag || !slot_stamp || !unit_slot || !step_counter ||
+      !sel_phys || !stats)
     return SPARSE_ERR_INVALID;
   if (capacity < 1) return SPARSE_ERR_INVALID;
-  if (!sp::aligned(host_kv, 16) || !sp::aligned(cache_kv, 16)) return SPARSE_ERR_INVALID;
   if (dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
   return SPARSE_OK;
 }
 
-// About 256 fetching waves in all (each has one 8 KiB unit in flight) keep the
-// PCIe link busy; more only take compute units from the attention that may
-// run beside the fetch.
+// Arguments of the fetch: the pinned host pool and the HBM cache pool.
+sparse_status check_pool_args(const uint16_t* host_kv, const uint16_t* cache_kv) {
+  if (!host_kv || !cache_kv) return SPARSE_ERR_INVALID;
+  if (!sp::aligned(host_kv, 16) || !sp::aligned(cache_kv, 16)) return SPARSE_ERR_INVALID;
+  return SPARSE_OK;
+}
+
+// About 256 fetching waves in all (each has one 8 KiB unit in flight; 32
+// compute units in all) keep the PCIe link busy; more only take compute
+// units from the attention that may run beside the fetch.
 constexpr int kFetchWaves = 256;
 
-sparse_status resolve_per_request(const sparse_dims* dims, int shift, const int32_t* sel_counts,
-                                  const int32_t* sel_pages, const uint16_t* host_kv,
-                                  uint16_t* cache_kv, int32_t capacity, int32_t* slot_tag,
-                                  int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
-                                  int32_t* sel_phys, int32_t* stats, void* ws, hipStream_t s) {
-  const int B = dims->batch, hkv = dims->num_kv_heads;
+// Per-request workspace views: miss records [B][C], then the per-request counts.
+struct PerRequestWs {
+  sp::MissRec* misses;
+  int32_t* miss_count;
+};
+PerRequestWs per_request_ws(int B, int32_t capacity, void* ws) {
   sp::MissRec* misses = static_cast<sp::MissRec*>(ws);
-  int32_t* miss_count = reinterpret_cast<int32_t*>(misses + (size_t)B * capacity);
+  return {misses, reinterpret_cast<int32_t*>(misses + (size_t)B * capacity)};
+}
+
+sparse_status resolve_per_request(const sparse_dims* dims, int shift, const int32_t* sel_counts,
+                                  const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag,
+                                  int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                                  int32_t* sel_phys, int32_t* hit_phys, int32_t* stats, void* ws,
+                                  hipStream_t s) {
+  const int B = dims->batch, hkv = dims->num_kv_heads;
+  const PerRequestWs w = per_request_ws(B, capacity, ws);
   hipLaunchKernelGGL(sp::resolve_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, dims->max_pages, capacity, shift, step_counter, slot_tag,
-                     slot_stamp, unit_slot, sel_phys, stats, misses, miss_count);
-  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  // at least 8 waves per request, a multiple of 4
-  const int waves_per_req = std::max(8, std::min(256, (kFetchWaves / B + 3) / 4 * 4));
-  hipLaunchKernelGGL(sp::fetch_kernel, dim3(waves_per_req / 4, B), dim3(256), 0, s, host_kv,
-                     cache_kv, hkv, dims->max_pages, capacity, misses, miss_count,
+                     slot_stamp, unit_slot, sel_phys, hit_phys, stats, w.misses, w.miss_count);
+  return sp::launch_status();
+}
+
+sparse_status fetch_per_request(const sparse_dims* dims, const uint16_t* host_kv,
+                                uint16_t* cache_kv, int32_t capacity, int32_t* step_counter,
+                                void* ws, hipStream_t s) {
+  const int B = dims->batch, hkv = dims->num_kv_heads;
+  const PerRequestWs w = per_request_ws(B, capacity, ws);
+  const int waves_per_req = std::max(1, kFetchWaves / B);
+  const int groups = (waves_per_req * B + sp::kFetchWavesPerGroup - 1) / sp::kFetchWavesPerGroup;
+  hipLaunchKernelGGL(sp::fetch_kernel, dim3(groups), dim3(sp::kFetchThreads), 0, s, host_kv,
+                     cache_kv, hkv, dims->max_pages, capacity, w.misses, w.miss_count, B,
                      waves_per_req, step_counter);
   return sp::launch_status();
 }
 
-sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* sel_counts,
-                             const int32_t* sel_pages, const uint16_t* host_kv,
-                             uint16_t* cache_kv, int32_t S, int32_t* slot_tag,
-                             int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
-                             int32_t* sel_phys, int32_t* stats, void* ws, hipStream_t s) {
-  const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
-  const int nblk = (S + sp::kPoolBlk - 1) / sp::kPoolBlk;
-  const size_t Sr = (size_t)nblk * sp::kPoolBlk;
+// Pooled workspace views (layout above pooled_ws_bytes).
+struct PooledWs {
+  uint8_t* req;
+  unsigned long long* ckeys;
+  int32_t* cblk;
+  int32_t* avail;
+  sp::MissRec* misses;
+  sp::PoolSel* psel;
+  uint32_t* totals;
+  int32_t* blk_free;
+  int32_t* blk_off;
+  int32_t* counts;
+  int32_t* moff;
+  int32_t* placed;
+  int nblk;
+};
+PooledWs pooled_ws(int B, int32_t S, void* ws) {
+  PooledWs w;
+  w.nblk = (S + sp::kPoolBlk - 1) / sp::kPoolBlk;
+  const size_t Sr = (size_t)w.nblk * sp::kPoolBlk;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint8_t* req = base;                                           // Sr is a multiple of 1024
-  unsigned long long* ckeys = reinterpret_cast<unsigned long long*>(base + Sr);
-  int32_t* cblk = reinterpret_cast<int32_t*>(ckeys + Sr);
-  int32_t* avail = cblk + Sr;
-  sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(avail + Sr);
-  sp::PoolSel* psel = reinterpret_cast<sp::PoolSel*>(misses + Sr);
-  uint32_t* totals = reinterpret_cast<uint32_t*>(psel + 1);
-  int32_t* blk_free = reinterpret_cast<int32_t*>(totals + 2);
-  int32_t* blk_off = blk_free + nblk;
-  int32_t* counts = blk_off + nblk;
-  int32_t* moff = counts + 2 * (size_t)B;
-  int32_t* placed = moff + B;
+  w.req = base;                                                  // Sr is a multiple of 1024
+  w.ckeys = reinterpret_cast<unsigned long long*>(base + Sr);
+  w.cblk = reinterpret_cast<int32_t*>(w.ckeys + Sr);
+  w.avail = w.cblk + Sr;
+  w.misses = reinterpret_cast<sp::MissRec*>(w.avail + Sr);
+  w.psel = reinterpret_cast<sp::PoolSel*>(w.misses + Sr);
+  w.totals = reinterpret_cast<uint32_t*>(w.psel + 1);
+  w.blk_free = reinterpret_cast<int32_t*>(w.totals + 2);
+  w.blk_off = w.blk_free + w.nblk;
+  w.counts = w.blk_off + w.nblk;
+  w.moff = w.counts + 2 * (size_t)B;
+  w.placed = w.moff + B;
+  return w;
+}
+
+sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* sel_counts,
+                             const int32_t* sel_pages, int32_t S, int32_t* slot_tag,
+                             int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+                             int32_t* sel_phys, int32_t* hit_phys, int32_t* stats, void* ws,
+                             hipStream_t s) {
+  const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
+  const PooledWs w = pooled_ws(B, S, ws);
   hipLaunchKernelGGL(sp::pool_mark_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
-                     sel_pages, hkv, MP, S, step_counter, slot_stamp, unit_slot, sel_phys, req,
-                     counts);
+                     sel_pages, hkv, MP, S, step_counter, slot_stamp, unit_slot, sel_phys,
+                     hit_phys, w.req, w.counts);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  hipLaunchKernelGGL(sp::pool_scan_kernel, dim3(nblk), dim3(sp::kPoolBlkThreads), 0, s, S, shift,
-                     slot_tag, slot_stamp, req, ckeys, cblk, blk_free, totals);
+  hipLaunchKernelGGL(sp::pool_scan_kernel, dim3(w.nblk), dim3(sp::kPoolBlkThreads), 0, s, S,
+                     shift, slot_tag, slot_stamp, w.req, w.ckeys, w.cblk, w.blk_free, w.totals);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  hipLaunchKernelGGL(sp::pool_select_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, nblk,
-                     counts, moff, ckeys, cblk, blk_free, totals, blk_off, psel);
+  hipLaunchKernelGGL(sp::pool_select_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, w.nblk,
+                     w.counts, w.moff, w.ckeys, w.cblk, w.blk_free, w.totals, w.blk_off, w.psel);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  hipLaunchKernelGGL(sp::pool_avail_kernel, dim3(nblk), dim3(sp::kPoolBlkThreads), 0, s, S, shift,
-                     slot_tag, slot_stamp, req, psel, blk_off, avail, placed);
+  hipLaunchKernelGGL(sp::pool_avail_kernel, dim3(w.nblk), dim3(sp::kPoolBlkThreads), 0, s, S,
+                     shift, slot_tag, slot_stamp, w.req, w.psel, w.blk_off, w.avail, w.placed);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,
-                     stats, counts, moff, avail, placed, misses);
-  if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
-  hipLaunchKernelGGL(sp::pool_fetch_kernel, dim3(kFetchWaves / 4), dim3(256), 0, s, host_kv,
-                     cache_kv, hkv, MP, misses, placed, kFetchWaves, step_counter);
+                     stats, w.counts, w.moff, w.avail, w.placed, w.misses);
+  return sp::launch_status();
+}
+
+sparse_status fetch_pooled(const sparse_dims* dims, const uint16_t* host_kv, uint16_t* cache_kv,
+                           int32_t S, int32_t* step_counter, void* ws, hipStream_t s) {
+  const PooledWs w = pooled_ws(dims->batch, S, ws);
+  hipLaunchKernelGGL(sp::pool_fetch_kernel, dim3(kFetchWaves / sp::kFetchWavesPerGroup),
+                     dim3(sp::kFetchThreads), 0, s, host_kv, cache_kv, dims->num_kv_heads,
+                     dims->max_pages, w.misses, w.placed, kFetchWaves, step_counter);
   return sp::launch_status();
 }
 
@@ -723,15 +833,10 @@ extern "C" size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
   return sparse_cache_workspace_bytes(dims, capacity);
 }
 
-extern "C" sparse_status sparse_hbm_cache_resolve_policy(
-    const sparse_dims* dims, const sparse_cache_policy* policy, const int32_t* sel_counts,
-    const int32_t* sel_pages, const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity,
-    int32_t* slot_tag, int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
-    int32_t* sel_phys, int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
-  sparse_status st = check_cache_args(dims, sel_counts, sel_pages, host_kv, cache_kv, capacity,
-                                      slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
-                                      stats);
-  if (st != SPARSE_OK) return st;
+namespace {
+
+sparse_status check_policy(const sparse_dims* dims, const sparse_cache_policy* policy,
+                           int32_t capacity, const void* ws, size_t ws_bytes) {
   if (!policy || policy->recency_shift < 0 || policy->recency_shift > 30 ||
       (policy->pooled != 0 && policy->pooled != 1))
     return SPARSE_ERR_INVALID;
@@ -744,12 +849,90 @@ extern "C" sparse_status sparse_hbm_cache_resolve_policy(
   if (!ws || ws_bytes < sparse_cache_policy_workspace_bytes(dims, policy, capacity) ||
       !sp::aligned(ws, 8))
     return SPARSE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
+  return SPARSE_OK;
+}
+
+sparse_status resolve_any(const sparse_dims* dims, const sparse_cache_policy* policy,
+                          const int32_t* sel_counts, const int32_t* sel_pages, int32_t capacity,
+                          int32_t* slot_tag, int32_t* slot_stamp, int32_t* unit_slot,
+                          int32_t* step_counter, int32_t* sel_phys, int32_t* hit_phys,
+                          int32_t* stats, void* ws, hipStream_t s) {
   if (policy->pooled)
-    return resolve_pooled(dims, policy->recency_shift, sel_counts, sel_pages, host_kv, cache_kv,
-                          capacity, slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
-                          stats, ws, s);
-  return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, host_kv,
-                             cache_kv, capacity, slot_tag, slot_stamp, unit_slot, step_counter,
-                             sel_phys, stats, ws, s);
+    return resolve_pooled(dims, policy->recency_shift, sel_counts, sel_pages, capacity, slot_tag,
+                          slot_stamp, unit_slot, step_counter, sel_phys, hit_phys, stats, ws, s);
+  return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, capacity,
+                             slot_tag, slot_stamp, unit_slot, step_counter, sel_phys, hit_phys,
+                             stats, ws, s);
+}
+
+sparse_status fetch_any(const sparse_dims* dims, const sparse_cache_policy* policy,
+                        const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity,
+                        int32_t* step_counter, void* ws, hipStream_t s) {
+  if (policy->pooled) return fetch_pooled(dims, host_kv, cache_kv, capacity, step_counter, ws, s);
+  return fetch_per_request(dims, host_kv, cache_kv, capacity, step_counter, ws, s);
+}
+
+}  // namespace
+
+extern "C" sparse_status sparse_hbm_cache_resolve_policy(
+    const sparse_dims* dims, const sparse_cache_policy* policy, const int32_t* sel_counts,
+    const int32_t* sel_pages, const uint16_t* host_kv, uint16_t* cache_kv, int32_t capacity,
+    int32_t* slot_tag, int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
+    int32_t* sel_phys, int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  sparse_status st = check_resolve_args(dims, sel_counts, sel_pages, capacity, slot_tag,
+                                        slot_stamp, unit_slot, step_counter, sel_phys, stats);
+  if (st != SPARSE_OK) return st;
+  if ((st = check_pool_args(host_kv, cache_kv)) != SPARSE_OK) return st;
+  if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = resolve_any(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
+                        unit_slot, step_counter, sel_phys, nullptr, stats, ws, s)) != SPARSE_OK)
+    return st;
+  return fetch_any(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, s);
+}
+
+extern "C" sparse_status sparse_hbm_cache_resolve_split(
+    const sparse_dims* dims, const sparse_cache_policy* policy, const int32_t* sel_counts,
+    const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag, int32_t* slot_stamp,
+    int32_t* unit_slot, int32_t* step_counter, int32_t* sel_phys, int32_t* hit_phys,
+    int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  sparse_status st = check_resolve_args(dims, sel_counts, sel_pages, capacity, slot_tag,
+                                        slot_stamp, unit_slot, step_counter, sel_phys, stats);
+  if (st != SPARSE_OK) return st;
+  if (!hit_phys) return SPARSE_ERR_INVALID;
+  if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
+  return resolve_any(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
+                     unit_slot, step_counter, sel_phys, hit_phys, stats, ws, (hipStream_t)stream);
+}
+
+extern "C" sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims,
+                                                const sparse_cache_policy* policy,
+                                                const uint16_t* host_kv, uint16_t* cache_kv,
+                                                int32_t capacity, int32_t* step_counter,
+                                                void* ws, size_t ws_bytes, void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if (!step_counter || capacity < 1) return SPARSE_ERR_INVALID;
+  if ((st = check_pool_args(host_kv, cache_kv)) != SPARSE_OK) return st;
+  if (dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
+  if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
+  return fetch_any(dims, policy, host_kv, cache_kv, capacity, step_counter, ws,
+                   (hipStream_t)stream);
+}
+
+extern "C" sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_counts,
+                                             const int32_t* sel_pages, const int32_t* sel_phys,
+                                             const int32_t* hit_phys, int32_t* miss_counts,
+                                             int32_t* miss_pages, int32_t* miss_phys,
+                                             void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if (!sel_counts || !sel_pages || !sel_phys || !hit_phys || !miss_counts || !miss_pages ||
+      !miss_phys)
+    return SPARSE_ERR_INVALID;
+  const int U = dims->batch * dims->num_kv_heads;
+  hipLaunchKernelGGL(sp::split_misses_kernel, dim3(U), dim3(sp::kSplitThreads), 0,
+                     (hipStream_t)stream, sel_counts, sel_pages, sel_phys, hit_phys,
+                     dims->max_pages, miss_counts, miss_pages, miss_phys);
+  return sp::launch_status();
 }

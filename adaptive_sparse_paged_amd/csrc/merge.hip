@@ -101,3 +101,43 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
                      chunk_pages, hkv, group, out, out_lse);
   return sp::launch_status();
 }
+
+namespace sp {
+
+// Two attention results over disjoint token sets, combined by the same
+// identity: one 128-thread workgroup per (request, query head) row.
+__global__ __launch_bounds__(kD) void lse_combine_kernel(
+    const float* __restrict__ out_a, const float* __restrict__ lse_a,
+    const float* __restrict__ out_b, const float* __restrict__ lse_b, float* __restrict__ out,
+    float* __restrict__ out_lse) {
+  const int64_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  const float la = lse_a[row], lb = lse_b[row];
+  const float m = fmaxf(la, lb);
+  float o = 0.f, l = -INFINITY;
+  if (m != -INFINITY) {
+    const float wa = (la == -INFINITY) ? 0.f : __expf(la - m);
+    const float wb = (lb == -INFINITY) ? 0.f : __expf(lb - m);
+    const float s = wa + wb;
+    o = (wa * out_a[row * kD + d] + wb * out_b[row * kD + d]) / s;
+    l = m + __logf(s);
+  }
+  out[row * kD + d] = o;
+  if (d == 0) out_lse[row] = l;
+}
+
+}  // namespace sp
+
+extern "C" sparse_status sparse_lse_combine(const sparse_dims* dims, const float* out_a,
+                                            const float* lse_a, const float* out_b,
+                                            const float* lse_b, float* out, float* out_lse,
+                                            void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !out_lse) return SPARSE_ERR_INVALID;
+  if (out_lse == lse_a || out_lse == lse_b) return SPARSE_ERR_INVALID;
+  const int rows = dims->batch * dims->num_q_heads;
+  hipLaunchKernelGGL(sp::lse_combine_kernel, dim3(rows), dim3(sp::kD), 0, (hipStream_t)stream,
+                     out_a, lse_a, out_b, lse_b, out, out_lse);
+  return sp::launch_status();
+}

@@ -64,9 +64,91 @@ class HbmPageCache:
                                      self.slot_stamp, self.unit_slot, self.step_counter,
                                      sel_phys, self.stats, self.ws, stream)
 
+    def resolve_split(self, sel_counts, sel_pages, sel_phys, hit_phys, stream=None):
+        """The resolve alone (no copy): sel_phys as resolve() writes it, and
+        hit_phys -- the slot of every entry that was resident before this
+        step, -1 for the others.  fetch() must follow."""
+        lib.hbm_cache_resolve_split(self.dims, self.policy, sel_counts, sel_pages, self.capacity,
+                                    self.slot_tag, self.slot_stamp, self.unit_slot,
+                                    self.step_counter, sel_phys, hit_phys, self.stats, self.ws,
+                                    stream)
+
+    def fetch(self, stream=None):
+        """Copy the misses placed by the last resolve_split; advances the step."""
+        lib.hbm_cache_fetch(self.dims, self.policy, self.host_kv, self.cache_kv, self.capacity,
+                            self.step_counter, self.ws, stream)
+
     def pool_args(self):
         """(kv, stride_page, stride_head, pool_pages) for sparse_decode_attn."""
         return self.cache_kv, UNIT_ELEMS, 0, self.cache_kv.shape[0]
+
+
+class SplitHostTierStep:
+    """One host-tier layer whose attention over the hits runs while the
+    misses cross PCIe.  A hit's slot is never a victim of the same step, so
+    the hits are final once the resolve has run; attention over a partition
+    of a list, merged by log-sum-exp, is attention over the whole list.
+
+    Current stream: resolve (no copy) -> fetch -> attention over the miss
+    lists -> combine.  Second stream, after the resolve: the miss lists
+    (sparse_split_misses) -> attention over the lists with hit_phys, which
+    skips the misses.  Cache state, statistics and slot ids equal those of
+    HbmPageCache.resolve; outputs equal the one-pass attention up to the
+    order of the log-sum-exp merge.  The step joins the second stream before
+    it returns, so it can be captured whole."""
+
+    def __init__(self, dims, cache, gamma, chunk_pages, scale=None, device="cuda"):
+        self.dims, self.cache = dims, cache
+        self.hits = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+                                     offsets=False)
+        self.miss = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+                                     offsets=False)
+        self.hit_phys = torch.zeros_like(self.hits.buf.sel_phys)
+        B, Hq = dims.batch, dims.num_q_heads
+        f32 = dict(dtype=torch.float32, device=device)
+        self.out_hit = torch.empty((B, Hq, 128), **f32)
+        self.lse_hit = torch.empty((B, Hq), **f32)
+        self.out_miss = torch.empty((B, Hq, 128), **f32)
+        self.lse_miss = torch.empty((B, Hq), **f32)
+        self.side = torch.cuda.Stream(device=device)
+        self.resolved = torch.cuda.Event()
+        self.split_done = torch.cuda.Event()
+        self.hits_done = torch.cuda.Event()
+
+    @property
+    def sel_counts(self):
+        return self.hits.buf.sel_counts
+
+    @property
+    def sel_pages(self):
+        return self.hits.buf.sel_pages
+
+    @property
+    def sel_phys(self):
+        return self.hits.buf.sel_phys
+
+    def run(self, q, ctx_lens, out, out_lse):
+        """One step on the lists in sel_counts / sel_pages."""
+        cur = torch.cuda.current_stream()
+        hb, mb = self.hits.buf, self.miss.buf
+        kv, sp_, sh_, pp = self.cache.pool_args()
+        self.cache.resolve_split(hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys)
+        self.resolved.record(cur)
+        self.side.wait_event(self.resolved)
+        with torch.cuda.stream(self.side):
+            lib.split_misses(self.dims, hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys,
+                             mb.sel_counts, mb.sel_pages, mb.sel_phys, self.side)
+            self.split_done.record(self.side)
+            self.hits.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_hit, self.lse_hit,
+                             stream=self.side, sel_phys=self.hit_phys)
+            self.hits_done.record(self.side)
+        self.cache.fetch()
+        cur.wait_event(self.split_done)
+        self.miss.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_miss, self.lse_miss)
+        cur.wait_event(self.hits_done)
+        lib.lse_combine(self.dims, self.out_hit, self.lse_hit, self.out_miss, self.lse_miss, out,
+                        out_lse)
+        return out, out_lse
 
 
 class LayeredHostTierStep:

@@ -33,6 +33,10 @@ EXPORTS = (
     "sparse_cache_policy_workspace_bytes",
     "sparse_hbm_cache_resolve_policy",
     "sparse_read_blocks",
+    "sparse_hbm_cache_resolve_split",
+    "sparse_hbm_cache_fetch",
+    "sparse_split_misses",
+    "sparse_lse_combine",
 )
 
 
@@ -97,6 +101,11 @@ _SIGS = {
     "sparse_hbm_cache_resolve_policy": (_I32, [_D, _CP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                                _P, _P, ctypes.c_size_t, _P]),
     "sparse_read_blocks": (_I32, [_P, _I64, _P, _I64, _P, _P]),
+    "sparse_hbm_cache_resolve_split": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, ctypes.c_size_t, _P]),
+    "sparse_hbm_cache_fetch": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "sparse_split_misses": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -271,3 +280,37 @@ def read_blocks(pool, pool_blocks, order, xor_out, stream=None):
     _check("sparse_read_blocks", load().sparse_read_blocks(
         _ptr(pool), int(pool_blocks), _ptr(order), order.numel(), _ptr(xor_out),
         _stream(stream)))
+
+
+def hbm_cache_resolve_split(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
+                            unit_slot, step_counter, sel_phys, hit_phys, stats, ws, stream=None):
+    _dev(sel_counts, sel_pages, slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
+         hit_phys, stats, ws)
+    _check("sparse_hbm_cache_resolve_split", load().sparse_hbm_cache_resolve_split(
+        ctypes.byref(dims), ctypes.byref(policy), _ptr(sel_counts), _ptr(sel_pages), capacity,
+        _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), _ptr(step_counter), _ptr(sel_phys),
+        _ptr(hit_phys), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hbm_cache_fetch(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, stream=None):
+    _dev(cache_kv, step_counter, ws)
+    if not host_kv.is_pinned():
+        raise ValueError("host_kv must be pinned host memory")
+    _check("sparse_hbm_cache_fetch", load().sparse_hbm_cache_fetch(
+        ctypes.byref(dims), ctypes.byref(policy), _ptr(host_kv), _ptr(cache_kv), capacity,
+        _ptr(step_counter), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def split_misses(dims, sel_counts, sel_pages, sel_phys, hit_phys, miss_counts, miss_pages,
+                 miss_phys, stream=None):
+    _dev(sel_counts, sel_pages, sel_phys, hit_phys, miss_counts, miss_pages, miss_phys)
+    _check("sparse_split_misses", load().sparse_split_misses(
+        ctypes.byref(dims), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), _ptr(hit_phys),
+        _ptr(miss_counts), _ptr(miss_pages), _ptr(miss_phys), _stream(stream)))
+
+
+def lse_combine(dims, out_a, lse_a, out_b, lse_b, out, out_lse, stream=None):
+    _dev(out_a, lse_a, out_b, lse_b, out, out_lse)
+    _check("sparse_lse_combine", load().sparse_lse_combine(
+        ctypes.byref(dims), _ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out),
+        _ptr(out_lse), _stream(stream)))

@@ -365,6 +365,80 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
                                               size_t ws_bytes, void* stream);
 
 /*
+ * The host tier in two halves, so that attention over the hits can run while
+ * the misses are still crossing PCIe (the split the resolver's placement
+ * rule allows: a hit's slot is never a victim of the same step, so the hits
+ * are final once the resolve has run).  One step is:
+ *   sparse_hbm_cache_resolve_split   hits, victims, slots; no copy
+ *   sparse_hbm_cache_fetch           the misses' copies; advances the step
+ *   sparse_split_misses              each unit's misses as a short list
+ * then attention over (sel_counts, sel_pages, hit_phys) -- it may overlap
+ * the fetch -- and attention over the miss lists after the fetch, merged by
+ * sparse_lse_combine.  Cache state, statistics and sel_phys equal those of
+ * sparse_hbm_cache_resolve_policy on the same inputs.
+ *
+ * sparse_hbm_cache_resolve_split -- the resolve of
+ * sparse_hbm_cache_resolve_policy without the fetch.  Arguments as there
+ * (no pools: the resolve never reads them), plus
+ *   hit_phys  int32 [U][max_pages] out: for list entry i of unit u, the slot
+ *             (as in sel_phys) if the unit was resident before this step,
+ *             else -1; entries past sel_counts[u] are not written
+ * The misses it placed are recorded in ws for the next
+ * sparse_hbm_cache_fetch on the same ws, which must follow it in stream
+ * order before ws is used again.  Errors as sparse_hbm_cache_resolve_policy;
+ * NULL hit_phys -> INVALID.
+ */
+sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
+                                             const sparse_cache_policy* policy,
+                                             const int32_t* sel_counts,
+                                             const int32_t* sel_pages, int32_t capacity,
+                                             int32_t* slot_tag, int32_t* slot_stamp,
+                                             int32_t* unit_slot, int32_t* step_counter,
+                                             int32_t* sel_phys, int32_t* hit_phys,
+                                             int32_t* stats, void* ws, size_t ws_bytes,
+                                             void* stream);
+
+/*
+ * sparse_hbm_cache_fetch -- copy every miss placed by the last
+ * sparse_hbm_cache_resolve_split on this ws from host_kv into its slot of
+ * cache_kv (device-initiated reads of pinned host memory), and advance
+ * *step_counter.  Arguments as sparse_hbm_cache_resolve_policy.
+ */
+sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims, const sparse_cache_policy* policy,
+                                     const uint16_t* host_kv, uint16_t* cache_kv,
+                                     int32_t capacity, int32_t* step_counter, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/*
+ * sparse_split_misses -- for each unit u, the list entries i < sel_counts[u]
+ * with hit_phys < 0 and sel_phys >= 0 (placed this step, not resident
+ * before), in list order, as
+ *   miss_counts int32 [U]              their number
+ *   miss_pages  int32 [U][max_pages]   their logical pages (ascending)
+ *   miss_phys   int32 [U][max_pages]   their slots
+ * -- lists that sparse_decode_attn takes as (sel_counts, sel_pages,
+ * sel_phys).  One 256-thread workgroup per unit.
+ */
+sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_counts,
+                                  const int32_t* sel_pages, const int32_t* sel_phys,
+                                  const int32_t* hit_phys, int32_t* miss_counts,
+                                  int32_t* miss_pages, int32_t* miss_phys, void* stream);
+
+/*
+ * sparse_lse_combine -- two attention results over disjoint token sets of
+ * the same rows, combined by the identity of sparse_merge_splits:
+ *   lse = ln(exp(lse_a) + exp(lse_b)),
+ *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b
+ * (a side with lse = -inf contributes nothing; both -inf gives out = 0 and
+ * lse = -inf).  out_a, out_b, out fp32 [B][Hq][128]; lse_a, lse_b, out_lse
+ * fp32 [B][Hq].  out may be out_a or out_b; out_lse must not be lse_a or
+ * lse_b (INVALID).
+ */
+sparse_status sparse_lse_combine(const sparse_dims* dims, const float* out_a, const float* lse_a,
+                                 const float* out_b, const float* lse_b, float* out,
+                                 float* out_lse, void* stream);
+
+/*
  * Measurement helper (not a step of the decode path).
  *
  * sparse_read_blocks -- read whole 8 KiB blocks of a pool in a given order,

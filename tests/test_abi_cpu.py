@@ -139,6 +139,27 @@ def test_null_and_value_checks(L):
     assert pol(3, 1, 9000, need, None) == lib.ERR_WORKSPACE
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
+    # the host tier in two halves
+    split = lambda cap, ws_bytes, hit=FAKE, pol=lib.CachePolicy(0, 0): L.sparse_hbm_cache_resolve_split(
+        ctypes.byref(d), ctypes.byref(pol), FAKE, FAKE, cap, FAKE, FAKE, FAKE, FAKE, FAKE, hit,
+        FAKE, FAKE, ws_bytes, None)
+    assert split(64, 1 << 30, hit=None) == lib.ERR_INVALID
+    assert split(0, 1 << 30) == lib.ERR_INVALID
+    assert split(9000, 1 << 30) == lib.ERR_UNSUPPORTED          # per-request slot limit
+    assert split(64, 16) == lib.ERR_WORKSPACE
+    assert split(64, 1 << 30, pol=lib.CachePolicy(0, 3)) == lib.ERR_INVALID
+    fetch = lambda host, cache, ws_bytes: L.sparse_hbm_cache_fetch(
+        ctypes.byref(d), ctypes.byref(lib.CachePolicy(0, 0)), host, cache, 64, FAKE, FAKE,
+        ws_bytes, None)
+    assert fetch(None, FAKE, 1 << 30) == lib.ERR_INVALID
+    assert fetch(FAKE, ctypes.c_void_p(0x10002), 1 << 30) == lib.ERR_INVALID
+    assert fetch(FAKE, FAKE, 16) == lib.ERR_WORKSPACE
+    assert L.sparse_split_misses(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                 None) == lib.ERR_INVALID
+    assert L.sparse_lse_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                None) == lib.ERR_INVALID
+    assert L.sparse_lse_combine(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.c_void_p(0x20000), FAKE,
+                                ctypes.c_void_p(0x20000), None) == lib.ERR_INVALID   # lse aliased
     # the read-ceiling helper
     assert L.sparse_read_blocks(FAKE, 100, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_read_blocks(FAKE, -1, FAKE, 10, FAKE, None) == lib.ERR_INVALID

@@ -1,0 +1,115 @@
+"""The host tier in two halves -- attention over the hits beside the fetch of
+the misses, then attention over the misses and a log-sum-exp combine --
+against the one-call resolve and one-pass attention on a second cache fed
+the same lists: cache state, statistics and slot ids bitwise at every step;
+hit_phys equal to the residency before the step; the miss lists equal to
+their definition; outputs equal up to the order of the merge and within the
+oracle's bar; eagerly and replayed from a captured graph."""
+
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from adaptive_sparse_paged_amd import inputs as I
+from adaptive_sparse_paged_amd import lib
+from adaptive_sparse_paged_amd.host_tier import HbmPageCache, SplitHostTierStep
+from adaptive_sparse_paged_amd.step import SparseDecodeStep, capture
+
+from _gpu_case import ATTN_TOL, feed_lists, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, C, LP, steps, drift, pooled=False, shift=0, chunk=8, graph_from=None):
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
+    B, H, G = w.batch, w.kv_heads, w.group
+    U = B * H
+    ref_cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
+    spl_cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
+    ref = SparseDecodeStep(dims, 0.99, chunk, scale=w.scale)
+    spl = SplitHostTierStep(dims, spl_cache, 0.99, chunk, scale=w.scale)
+    layer = types.SimpleNamespace(w=w, dims=dims, li=li)
+    lists = I.drift_lists(w, min(I.pages_of(L) for L in lens), LP, steps, drift)
+    out = torch.empty((B, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, w.q_heads), dtype=torch.float32, device="cuda")
+    graph, misses_total, worst = None, 0, 0.0
+    for t in range(steps):
+        feed_lists(ref, layer, {b * H + h: lists[t, b, h] for b in range(B) for h in range(H)})
+        spl.sel_counts.copy_(ref.buf.sel_counts)
+        spl.sel_pages.copy_(ref.buf.sel_pages)
+        before = spl_cache.unit_slot.clone()
+        ref_cache.resolve(ref.buf.sel_counts, ref.buf.sel_pages, ref.buf.sel_phys)
+        o_ref, l_ref = ref.attend(li.q, *ref_cache.pool_args(), li.ctx_lens)
+        if graph_from is not None and t >= graph_from:
+            if graph is None:
+                graph = capture(lambda: spl.run(li.q, li.ctx_lens, out, lse), warmup=0)
+            out.zero_()
+            graph.replay()
+        else:
+            spl.run(li.q, li.ctx_lens, out, lse)
+        torch.cuda.synchronize()
+        for name in ("slot_tag", "slot_stamp", "unit_slot", "stats", "step_counter"):
+            assert torch.equal(getattr(ref_cache, name), getattr(spl_cache, name)), (t, name)
+        assert int(spl_cache.stats[:, 3].sum()) == 0, "case sized to never overflow"
+        misses_total += int(spl_cache.stats[:, 1].sum())
+        counts = ref.buf.sel_counts.cpu().numpy()
+        pages = ref.buf.sel_pages.cpu().numpy()
+        phys = ref.buf.sel_phys.cpu().numpy()
+        hit = spl.hit_phys.cpu().numpy()
+        prev = before.cpu().numpy().reshape(-1)
+        mc = spl.miss.buf.sel_counts.cpu().numpy()
+        mp = spl.miss.buf.sel_pages.cpu().numpy()
+        mx = spl.miss.buf.sel_phys.cpu().numpy()
+        for u in range(U):
+            b, h = divmod(u, H)
+            k = counts[u]
+            assert np.array_equal(spl.sel_phys.cpu().numpy()[u, :k], phys[u, :k]), (t, u)
+            units = (b * H + h) * MP + pages[u, :k] if pooled else b * H * MP + h * MP + pages[u, :k]
+            resident = prev[units] >= 0
+            want_hit = np.where(resident, phys[u, :k], -1)
+            assert np.array_equal(hit[u, :k], want_hit), (t, u, "hit_phys")
+            is_miss = (~resident) & (phys[u, :k] >= 0)
+            assert mc[u] == is_miss.sum(), (t, u, "miss count")
+            assert np.array_equal(mp[u, :mc[u]], pages[u, :k][is_miss]), (t, u, "miss pages")
+            assert np.array_equal(mx[u, :mc[u]], phys[u, :k][is_miss]), (t, u, "miss slots")
+        # the same attention up to the order of the log-sum-exp merge
+        d = float((out - o_ref).abs().max())
+        assert d <= 1e-5, (t, "output", d)
+        assert float((lse - l_ref).abs().max()) <= 1e-5, (t, "lse")
+        worst = max(worst, d)
+    # and within the oracle's bar on a few units of the last step
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        u = b * H + h
+        k_, v_, q_, nv = I.unit_host(w, 0, b, h, int(lens[b]))
+        lst = pages[u, :counts[u]]
+        o_or, _ = O.attend_pages(O.bf16_bits_to_f64(q_), O.bf16_bits_to_f64(k_),
+                                 O.bf16_bits_to_f64(v_), nv, lst, w.scale)
+        o_gpu = out[b, h * G:(h + 1) * G].double().cpu().numpy()
+        assert np.abs(o_gpu - o_or).max() <= ATTN_TOL
+    return misses_total, worst
+
+
+@pytest.mark.parametrize("pooled,shift", [(False, 0), (True, 0), (False, 2)],
+                         ids=["exact", "pooled", "bucketed2"])
+def test_split_host_tier_matches_one_pass(gpu_lib, pooled, shift):
+    w = I.custom_workload("split", 2, 8, 2, ("fixed", 3200), index=124)
+    say(f"[split] B=2 Hkv=2, 64 slots, lists of 24 drifting 25%, pooled={pooled} shift={shift}")
+    C = 2 * 64 if pooled else 64
+    misses, worst = _run(w, C, 24, 10, 0.25, pooled=pooled, shift=shift, graph_from=5)
+    say(f"  10 steps (graph from step 5), {misses} misses, max |split - one pass| {worst:.1e}")
+    assert misses > 0
+
+
+def test_split_cold_step_all_misses(gpu_lib):
+    """The first step misses everything: the hit pass sees only empty pages
+    (lse -inf), and the result is the miss pass alone."""
+    w = I.custom_workload("split_cold", 3, 16, 4, ("fixed", 2000), index=125)
+    say("[split] cold start, B=3 Hkv=4, 256 slots, lists of 40")
+    misses, worst = _run(w, 256, 40, 2, 0.5, chunk=16)
+    assert misses > 0
