@@ -6,9 +6,11 @@
 // One 1024-thread workgroup per unit.  Logits are read coalesced (thread t:
 // pages t, t + 1024, ...); the page keys then pass through LDS so that for the
 // cut thread t owns the blocked run [t*NPT, t*NPT + NPT).  Steps:
-//   1. per query head g: (max, sum of exp) over the unit's pages (block
-//      reduction of all heads at once), then m[p] += exp(x_g[p] - max_g) /
-//      sum_g;  m /= G.
+//   0. one round of loads: the context length, the logits and the request's
+//      page-table row (staged in LDS for the list's physical ids).
+//   1. per query head g: the max M_g over the unit's pages, then the sum S_g
+//      of exp(x_g[p] - M_g) (two block reductions, each over all heads at
+//      once); m[p] = (1/G) sum_g exp(x_g[p] - M_g) / S_g.
 //   2. weights w[p] = floor(m[p] * 2^52) (exact 64-bit fixed point, so the
 //      cut's sums are exact and order independent) and keys = fp32 bits of
 //      m[p] (monotone for m >= 0).
@@ -33,10 +35,6 @@ namespace sp {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-struct PairMS {
-  float m, s;
-};
-
 // fixed-point weight of a page from its fp32 mass bits: floor(m * 2^52)
 __device__ __forceinline__ unsigned long long weight_of(uint32_t key) {
   return (unsigned long long)(__uint_as_float(key) * 4503599627370496.0f);
@@ -48,12 +46,157 @@ __device__ __forceinline__ unsigned long long wgt_of(uint32_t key) {
   else return weight_of(key);
 }
 
-__device__ __forceinline__ PairMS combine(PairMS a, PairMS b) {
-  const float M = fmaxf(a.m, b.m);
-  if (M == -INFINITY) return {M, 0.f};
-  const float sa = (a.m == -INFINITY) ? 0.f : a.s * __expf(a.m - M);
-  const float sb = (b.m == -INFINITY) ? 0.f : b.s * __expf(b.m - M);
-  return {M, sa + sb};
+
+// Logits of heads g0 .. g0 + HPR - 1 for this thread's pages (thread t:
+// pages t, t + 1024, ...); -inf for a page past the context or a head past
+// the group.
+template <int NPT, int HPR>
+__device__ __forceinline__ void load_logits(const float* __restrict__ X, int g0, int group,
+                                            int max_pages, int n, int tid,
+                                            float (&xv)[HPR][NPT]) {
+#pragma unroll
+  for (int hh = 0; hh < HPR; ++hh) {
+    const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int p = k * kSelThreads + tid;
+      xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
+    }
+  }
+}
+
+// ---- reductions on the DPP crossbar ----------------------------------------
+// A lane-shuffle through __shfl_xor is an LDS permute; sixteen waves doing
+// many of them queue on the LDS.  Within a row of 16 lanes the butterfly runs
+// on DPP moves instead: quad swaps (lane ^ 1, lane ^ 2), then the half-row and
+// row mirrors (i <-> 7 - i, i <-> 15 - i) -- after the quad steps a mirror
+// pairs every lane with the other half's total.  Each step combines a and b
+// as op(a, b) in one lane and op(b, a) in its partner; the ops are
+// commutative, so every lane ends with the same bits.  Across the four rows,
+// four readlanes and a fixed combination order.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  return (unsigned long long)dpp_u32<CTRL>((uint32_t)v) |
+         ((unsigned long long)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32);
+}
+
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpAdd {
+  __device__ float operator()(float a, float b) const { return a + b; }
+  __device__ unsigned long long operator()(unsigned long long a, unsigned long long b) const {
+    return a + b;
+  }
+};
+struct OpAddU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMinU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct OpMaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+
+// every lane of a row of 16 ends with the row's total
+template <typename Op>
+__device__ __forceinline__ float row16_f32(float v, Op op) {
+  v = op(v, dpp_f32<kDppXor1>(v));
+  v = op(v, dpp_f32<kDppXor2>(v));
+  v = op(v, dpp_f32<kDppHalfMirror>(v));
+  v = op(v, dpp_f32<kDppMirror>(v));
+  return v;
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t row16_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppHalfMirror>(v));
+  v = op(v, dpp_u32<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ unsigned long long row16_sum_u64(unsigned long long v) {
+  v += dpp_u64<kDppXor1>(v);
+  v += dpp_u64<kDppXor2>(v);
+  v += dpp_u64<kDppHalfMirror>(v);
+  v += dpp_u64<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// the wave's total, the same value in every lane
+template <typename Op>
+__device__ __forceinline__ float wave_total_f32(float v, Op op) {
+  v = row16_f32(v, op);
+  const float r0 = __uint_as_float(lane_u32(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(lane_u32(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(lane_u32(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(lane_u32(__float_as_uint(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_total_u32(uint32_t v, Op op) {
+  v = row16_u32(v, op);
+  return op(op(lane_u32(v, 0), lane_u32(v, 16)), op(lane_u32(v, 32), lane_u32(v, 48)));
+}
+__device__ __forceinline__ unsigned long long wave_total_u64(unsigned long long v) {
+  v = row16_sum_u64(v);
+  unsigned long long t = 0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    t += (unsigned long long)lane_u32((uint32_t)v, 16 * r) |
+         ((unsigned long long)lane_u32((uint32_t)(v >> 32), 16 * r) << 32);
+  return t;
+}
+
+// Inclusive prefix sums over the wave on DPP: row_shr 1, 2, 4, 8 within each
+// row of 16 (a lane whose source falls outside its row adds 0), then lane 15
+// of rows 0 and 2 into rows 1 and 3 (row_bcast15), then lane 31 into rows 2
+// and 3 (row_bcast31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_upd_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_upd_u64(unsigned long long v) {
+  return (unsigned long long)dpp_upd_u32<CTRL, ROWS>((uint32_t)v) |
+         ((unsigned long long)dpp_upd_u32<CTRL, ROWS>((uint32_t)(v >> 32)) << 32);
+}
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+  x += dpp_upd_u32<0x111, 0xF>(x);
+  x += dpp_upd_u32<0x112, 0xF>(x);
+  x += dpp_upd_u32<0x114, 0xF>(x);
+  x += dpp_upd_u32<0x118, 0xF>(x);
+  x += dpp_upd_u32<0x142, 0xA>(x);
+  x += dpp_upd_u32<0x143, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x) {
+  x += dpp_upd_u64<0x111, 0xF>(x);
+  x += dpp_upd_u64<0x112, 0xF>(x);
+  x += dpp_upd_u64<0x114, 0xF>(x);
+  x += dpp_upd_u64<0x118, 0xF>(x);
+  x += dpp_upd_u64<0x142, 0xA>(x);
+  x += dpp_upd_u64<0x143, 0xC>(x);
+  return x;
+}
+
+// Head g's max (MAX) or sum over the 16 wave partials part[g][w], computed by
+// every lane of the calling wave (lane l takes partial l & 15; one row
+// butterfly).  The result is the same in every lane and every wave.
+template <bool MAX>
+__device__ __forceinline__ float head_total(const float (*part)[kSelWaves], int g) {
+  const float v = part[g][lane_id() & (kSelWaves - 1)];
+  return MAX ? row16_f32(v, OpMax()) : row16_f32(v, OpAdd());
 }
 
 // COUNT = false: the coverage cut (page weight = its fixed-point mass, target
@@ -71,7 +214,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // Page keys, staged so that loads are coalesced (thread t reads pages
   // t, t + 1024, ...) while the cut works on blocked runs (thread t owns
   // pages t*NPT .. t*NPT + NPT-1); later reused for the kept page list.
-  __shared__ uint32_t keys_lds[NPT * kSelThreads];
+  __shared__ __attribute__((aligned(16))) uint32_t keys_lds[NPT * kSelThreads];
+  // The request's page-table row, staged while the logits load so that the
+  // list's physical ids need no dependent global gather at the end (when the
+  // row fits beside the keys and histograms in LDS).
+  constexpr bool kStagePt = NPT <= 8;
+  __shared__ int32_t ptl[kStagePt ? NPT * kSelThreads : 1];
   // radix histograms: two buffers (alternate passes) while LDS allows
   constexpr int kHistBufs = (NPT <= 16) ? 2 : 1;
   __shared__ uint32_t hcnt[kHistBufs][2048];
@@ -90,30 +238,71 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const int u = blockIdx.x;
   const int b = u / hkv;
-  const int L = min(max(ctx_lens[b], 0), max_pages * kP);
+  const float* X = logits + (int64_t)u * group * max_pages;
+  const int32_t* pt = page_table + (int64_t)b * max_pages;
+
+  // Every load the selection starts from is issued in one round, before the
+  // context length is known: the length, the first HPR heads' logits and
+  // (when staged) the page-table row.  Indices are clamped to the row, so a
+  // page past the context reads an in-bounds word that is masked below; the
+  // empty asm statements keep the compiler from moving the loads under the
+  // length test, where each would wait behind the length's round trip.
+  constexpr int HPR = (NPT >= 32) ? 1 : 32 / NPT;
+  const int Lraw = ctx_lens[b];
+  float xv[HPR][NPT];
+#pragma unroll
+  for (int hh = 0; hh < HPR; ++hh) {
+    const float* Xg = X + (int64_t)min(hh, group - 1) * max_pages;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      xv[hh][k] = (hh < group) ? Xg[min(k * kSelThreads + tid, max_pages - 1)] : -INFINITY;
+  }
+  int ptv[kStagePt ? NPT : 1];
+  if constexpr (kStagePt) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) ptv[k] = pt[min(k * kSelThreads + tid, max_pages - 1)];
+  }
+  // the first radix pass's histogram is cleared while the loads are in flight
+  for (int k = tid; k < 2048; k += kSelThreads) {
+    hcnt[0][k] = 0u;
+    hw[0][k] = 0ull;
+  }
+  if (tid == 0) {
+    s_ncand = 0u;
+    s_bin[0] = s_bin[1] = 0;
+    s_wgt[0] = s_wgt[1] = 0ull;
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPR; ++hh)
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) asm volatile("" : "+v"(xv[hh][k]));
+  if constexpr (kStagePt) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) asm volatile("" : "+v"(ptv[k]));
+  }
+  const int L = min(max(Lraw, 0), max_pages * kP);
   const int n = (L + kP - 1) / kP;
   int count = 0;
 
   if (n > 0) {
-    const float* X = logits + (int64_t)u * group * max_pages;
-
     // ---- 1. per-head softmax normalisers -----------------------------------
-    // Logits of HPR heads at a time, every load issued before the first use.
-    // (max, sum of exp) per head: thread-local, wave shuffles, then one lane
-    // per head combines the wave partials.  When all heads fit one round the
-    // values stay in registers for step 2; otherwise they are read again.
-    constexpr int HPR = (NPT >= 32) ? 1 : 32 / NPT;
+    // Two passes per head, neither spending an exp on combining partials:
+    // the max M_g (thread-local, wave shuffles, one partial per wave in LDS),
+    // then e = exp(x - M_g) and its sum S_g the same way.  After each
+    // barrier every wave reduces the 16 wave partials itself, so no second
+    // barrier hands a result on.  Heads go HPR at a time (the first round
+    // from the loads above); when all heads fit one round, e stays in
+    // registers for step 2, otherwise the logits are read again.
     const bool one_round = group <= HPR;
-    float xv[HPR][NPT];
     for (int g0 = 0; g0 < group; g0 += HPR) {
+      if (g0 == 0) {
 #pragma unroll
-      for (int hh = 0; hh < HPR; ++hh) {
-        const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
+        for (int hh = 0; hh < HPR; ++hh)
 #pragma unroll
-        for (int k = 0; k < NPT; ++k) {
-          const int p = k * kSelThreads + tid;
-          xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
-        }
+          for (int k = 0; k < NPT; ++k)
+            if (!(hh < group && k * kSelThreads + tid < n)) xv[hh][k] = -INFINITY;
+      } else {
+        load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
       }
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
@@ -121,38 +310,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         float mx = -INFINITY;
 #pragma unroll
         for (int k = 0; k < NPT; ++k) mx = fmaxf(mx, xv[hh][k]);
-        float se = 0.f;
-        if (mx != -INFINITY) {
-#pragma unroll
-          for (int k = 0; k < NPT; ++k) se += __expf(xv[hh][k] - mx);
-        }
-        PairMS pr = {mx, se};
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          PairMS other = {__shfl_xor(pr.m, o, 64), __shfl_xor(pr.s, o, 64)};
-          pr = combine(pr, other);
-        }
-        if (lane == 0) {
-          red_m[g0 + hh][wv] = pr.m;
-          red_s[g0 + hh][wv] = pr.s;
-        }
+        mx = wave_total_f32(mx, OpMax());
+        if (lane == 0) red_m[g0 + hh][wv] = mx;
       }
     }
     __syncthreads();
-    if (wv == 0) {
-      // lane l combines wave partial (l & 15) of head g0 + (l >> 4)
-      for (int g0 = 0; g0 < group; g0 += 4) {
-        const int g = g0 + (lane >> 4), w = lane & 15;
-        PairMS pr = (g < group) ? PairMS{red_m[g][w], red_s[g][w]} : PairMS{-INFINITY, 0.f};
+    for (int g0 = 0; g0 < group; g0 += HPR) {
+      if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          PairMS other = {__shfl_xor(pr.m, o, 64), __shfl_xor(pr.s, o, 64)};
-          pr = combine(pr, other);
+      for (int hh = 0; hh < HPR; ++hh) {
+        if (g0 + hh >= group) break;
+        const float M = head_total<true>(red_m, g0 + hh);
+        float se = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+          // a head with no finite logit (M = -inf) adds no mass
+          xv[hh][k] = (M == -INFINITY) ? 0.f : __expf(xv[hh][k] - M);
+          se += xv[hh][k];
         }
-        if (w == 0 && g < group) {
-          red_m[g][0] = pr.m;
-          red_s[g][0] = 1.f / pr.s;
-        }
+        se = wave_total_f32(se, OpAdd());
+        if (lane == 0) red_s[g0 + hh][wv] = se;
       }
     }
     __syncthreads();
@@ -162,24 +339,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 #pragma unroll
     for (int k = 0; k < NPT; ++k) m[k] = 0.f;
     for (int g0 = 0; g0 < group; g0 += HPR) {
-      if (!one_round) {
-#pragma unroll
-        for (int hh = 0; hh < HPR; ++hh) {
-          const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
-#pragma unroll
-          for (int k = 0; k < NPT; ++k) {
-            const int p = k * kSelThreads + tid;
-            xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
-          }
-        }
-      }
+      if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
-        const float M = red_m[g0 + hh][0], inv = red_s[g0 + hh][0];
-        if (M == -INFINITY) continue;      // a head with no finite logit adds no mass
+        const float S = head_total<false>(red_s, g0 + hh);
+        if (!(S > 0.f)) continue;            // no finite logit: no mass
+        const float inv = 1.f / S;
+        if (one_round) {
 #pragma unroll
-        for (int k = 0; k < NPT; ++k) m[k] += __expf(xv[hh][k] - M) * inv;
+          for (int k = 0; k < NPT; ++k) m[k] += xv[hh][k] * inv;
+        } else {
+          const float M = head_total<true>(red_m, g0 + hh);
+#pragma unroll
+          for (int k = 0; k < NPT; ++k) m[k] += __expf(xv[hh][k] - M) * inv;
+        }
       }
     }
     const float invg = 1.f / (float)group;
@@ -191,47 +365,41 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       if (p < n) {
         const uint32_t key = __float_as_uint(m[k] * invg);
         keys_lds[p] = key;
+        if constexpr (kStagePt) ptl[p] = ptv[k];
         zl += wgt_of<COUNT>(key);
         klo = min(klo, key);
         khi = max(khi, key);
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      zl += __shfl_xor(zl, o, 64);
-      klo = min(klo, (uint32_t)__shfl_xor((int)klo, o, 64));
-      khi = max(khi, (uint32_t)__shfl_xor((int)khi, o, 64));
-    }
+    zl = wave_total_u64(zl);
+    klo = wave_total_u32(klo, OpMinU());
+    khi = wave_total_u32(khi, OpMaxU());
     if (lane == 0) {
       red_z[wv] = zl;
       red_lo[wv] = klo;
       red_hi[wv] = khi;
     }
     __syncthreads();
-    if (wv == 0) {
-      unsigned long long z = (lane < kSelWaves) ? red_z[lane] : 0ull;
-      uint32_t lo2 = (lane < kSelWaves) ? red_lo[lane] : 0xFFFFFFFFu;
-      uint32_t hi2 = (lane < kSelWaves) ? red_hi[lane] : 0u;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        z += __shfl_xor(z, o, 64);
-        lo2 = min(lo2, (uint32_t)__shfl_xor((int)lo2, o, 64));
-        hi2 = max(hi2, (uint32_t)__shfl_xor((int)hi2, o, 64));
-      }
-      if (lane == 0) {
-        red_z[0] = z;
-        red_lo[0] = lo2;
-        red_hi[0] = hi2;
-      }
-    }
-    __syncthreads();
-    const unsigned long long Z = red_z[0];
-    const uint32_t KLO = red_lo[0], KHI = red_hi[0];
+    // every wave combines the 16 wave partials itself (lane l: partial l & 15)
+    const unsigned long long Z = row16_sum_u64(red_z[lane & (kSelWaves - 1)]);
+    const uint32_t KLO = row16_u32(red_lo[lane & (kSelWaves - 1)], OpMinU());
+    const uint32_t KHI = row16_u32(red_hi[lane & (kSelWaves - 1)], OpMaxU());
     // this thread's blocked run of keys
     const int pbase = tid * NPT;
     uint32_t key[NPT];
+    if constexpr (NPT >= 4) {
+      // 16-byte LDS reads: the run's words are consecutive, so one read per
+      // four keys instead of four bank-conflicting single-word reads
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) key[i] = (pbase + i < n) ? keys_lds[pbase + i] : 0u;
+      for (int v = 0; v < NPT / 4; ++v) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&keys_lds[pbase + 4 * v]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * v + e] = (pbase + 4 * v + e < n) ? w[e] : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) key[i] = (pbase + i < n) ? keys_lds[pbase + i] : 0u;
+    }
 
     // ---- 3. the cut: key tau and the number of ties at tau to keep -------
     const bool all = COUNT ? (k_pages >= n) : !(gamma < 1.0f);
@@ -251,18 +419,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         uint32_t hi_mask = ~((2u << top) - 1u);
         uint32_t prefix = KHI & hi_mask;
         int lo = top + 1, buf = 0;
-        bool resolved = false;
+        bool resolved = false, first = true;
         while (lo > 0) {
           const int width = min(11, lo);
           const int sh = lo - width, nb = 1 << width;
           uint32_t* cnt = hcnt[buf];
           unsigned long long* wgt = hw[buf];
-          for (int k = tid; k < nb; k += kSelThreads) {
-            cnt[k] = 0u;
-            wgt[k] = 0ull;
+          if (!first) {   // the first pass's buffer was cleared at the start
+            for (int k = tid; k < nb; k += kSelThreads) {
+              cnt[k] = 0u;
+              wgt[k] = 0ull;
+            }
+            if (tid == 0) s_ncand = 0u;
+            __syncthreads();
           }
-          if (tid == 0) s_ncand = 0u;
-          __syncthreads();
+          first = false;
 #pragma unroll
           for (int i = 0; i < NPT; ++i) {
             if (pbase + i < n && (key[i] & hi_mask) == prefix) {
@@ -273,27 +444,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           }
           __syncthreads();
           {
-            // thread t owns bins 2t, 2t+1; the weight of all bins above a
-            // thread's comes from one block prefix sum
+            // thread t owns bins 2t, 2t+1, wave w bins [128 w, 128 w + 128).
+            // One barrier for the wave totals; then only the wave whose bins
+            // hold the crossing scans them.
             const int b0 = 2 * tid, b1 = 2 * tid + 1;
             const unsigned long long w0 = (b0 < nb) ? wgt[b0] : 0ull;
             const unsigned long long w1 = (b1 < nb) ? wgt[b1] : 0ull;
-            unsigned long long total;
-            const unsigned long long ex =
-                block_excl_scan<unsigned long long, kSelThreads>(w0 + w1, scan64, total);
-            const unsigned long long gt1 = total - (ex + w0 + w1);  // weight above bin b1
-            const unsigned long long gt0 = gt1 + w1;                // weight above bin b0
-            if (b1 < nb && gt1 < T && T <= gt1 + w1) {
-              s_bin[buf & 1] = b1;
-              s_wgt[buf & 1] = gt1;
-            }
-            if (b0 < nb && gt0 < T && T <= gt0 + w0) {
-              s_bin[buf & 1] = b0;
-              s_wgt[buf & 1] = gt0;
+            const unsigned long long ws = w0 + w1;
+            const unsigned long long wtot = wave_total_u64(ws);
+            if (lane == 0) scan64[wv] = wtot;
+            __syncthreads();
+            const unsigned long long tw = scan64[lane & (kSelWaves - 1)];
+            // weight of the bins of the waves above this one (same in every lane)
+            const unsigned long long above =
+                row16_sum_u64(((lane & (kSelWaves - 1)) > wv) ? tw : 0ull);
+            if (above < T && T <= above + wtot) {
+              const unsigned long long gt1 = above + (wtot - wave_scan_u64(ws));  // above bin b1
+              const unsigned long long gt0 = gt1 + w1;                            // above bin b0
+              if (b1 < nb && gt1 < T && T <= gt1 + w1) {
+                s_bin[buf & 1] = b1;
+                s_wgt[buf & 1] = gt1;
+              }
+              if (b0 < nb && gt0 < T && T <= gt0 + w0) {
+                s_bin[buf & 1] = b0;
+                s_wgt[buf & 1] = gt0;
+              }
             }
           }
           __syncthreads();
-          const int bin = s_bin[buf & 1];
+          const int bin = s_bin[buf & 1] & (nb - 1);
           T -= s_wgt[buf & 1];
           prefix |= (uint32_t)bin << sh;
           hi_mask |= (uint32_t)(nb - 1) << sh;
@@ -320,6 +499,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
               const bool ok = (uint32_t)lane < nc;
               unsigned long long c =
                   ok ? (((unsigned long long)(~cand_key[lane]) << 32) | cand_page[lane]) : ~0ull;
+              // bitonic network, stopped once a sorted block covers the
+              // candidates (lanes 0 .. nc-1, the rest hold the largest key)
 #pragma unroll
               for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
@@ -329,10 +510,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                   const bool up = (lane & k) == 0, low = (lane & jj) == 0;
                   c = (low == up) ? min(c, o) : max(c, o);
                 }
+                if ((uint32_t)k >= nc) break;
               }
               const uint32_t kk = ~(uint32_t)(c >> 32);
               const unsigned long long wk = ok ? wgt_of<COUNT>(kk) : 0ull;
-              const unsigned long long cum = wave_incl_scan(wk);
+              const unsigned long long cum = wave_scan_u64(wk);
               const unsigned long long reach = __ballot(ok && cum >= T);
               const int at = __ffsll((long long)reach) - 1;     // first lane reaching T
               const uint32_t t_key = (uint32_t)__shfl((int)kk, at, 64);
@@ -376,8 +558,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         else if (key[i] == tau) packed += 1u;
       }
     }
-    uint32_t tot_packed;
-    const uint32_t ex = block_excl_scan<uint32_t, kSelThreads>(packed, scan32, tot_packed);
+    // block prefix sum with one barrier: wave scans, wave totals in LDS,
+    // then every wave sums the totals of the waves before it
+    const uint32_t incl = wave_scan_u32(packed);
+    if (lane == 63) scan32[wv] = incl;
+    __syncthreads();
+    const uint32_t tq = scan32[lane & (kSelWaves - 1)];
+    const uint32_t tot_packed = row16_u32(tq, OpAddU());
+    const uint32_t ex =
+        row16_u32(((lane & (kSelWaves - 1)) < wv) ? tq : 0u, OpAddU()) + incl - packed;
     // every thread has its keys in registers by now: reuse keys_lds for the list
     uint32_t gtb = ex >> 16, tb = ex & 0xFFFFu;
 #pragma unroll
@@ -391,9 +580,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if ((unsigned long long)tb < need) pos = (int)(gtb + tb);
         ++tb;
       }
-      if (pos >= 0) keys_lds[pos] = (uint32_t)(pbase + i);
+      if (pos >= 0 && pos < n) keys_lds[pos] = (uint32_t)(pbase + i);
     }
-    count = (int)((tot_packed >> 16) + min((unsigned long long)(tot_packed & 0xFFFFu), need));
+    count = min((int)((tot_packed >> 16) + min((unsigned long long)(tot_packed & 0xFFFFu), need)),
+                n);
     __syncthreads();
     int32_t* lp = sel_pages + (int64_t)u * max_pages;
     int32_t* lx = sel_phys + (int64_t)u * max_pages;
@@ -401,7 +591,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int i = tid; i < count; i += kSelThreads) {
       const int p = (int)keys_lds[i];
       lp[i] = p;
-      lx[i] = pt[p];
+      if constexpr (kStagePt) lx[i] = ptl[p];
+      else lx[i] = pt[p];
     }
   }
 
