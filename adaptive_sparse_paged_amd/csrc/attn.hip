@@ -17,7 +17,9 @@
 //        into a bf16 high part and a bf16 residual, two products, so the
 //        weights keep ~16 significant bits.
 // The 4 waves' (max, sum, O) are merged in LDS into one normalised partial
-// and its log-sum-exp per head.
+// and its log-sum-exp per head, written to the unit's own slot for that
+// chunk (unit u, chunk i: slot u * ceil(list bound / chunk) + i), so the
+// merge finds a unit's partials without the plan.
 
 #include "common.h"
 
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_phys,
     float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int cap, int U,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int unit_parts, float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
   const int c = blockIdx.x;
   int u, local;
@@ -219,7 +221,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         den += a * sl[w * group + gg];
       }
     }
-    const int64_t slot = (int64_t)c * group + gg;
+    // unit u's chunks have the fixed slots u * unit_parts + local
+    const int64_t slot = ((int64_t)u * unit_parts + local) * group + gg;
     part_o[slot * kD + d] = (den > 0.f) ? num / den : 0.f;
     if (d == 0) part_lse[slot] = (den > 0.f) ? (M + log2f(den)) * ln2 : -INFINITY;
   }
@@ -257,6 +260,7 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
   hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)max_parts), dim3(256), lds,
                      (hipStream_t)stream, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
                      sel_counts, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
-                     group, dims->max_pages, sp::list_cap(dims), U, part_o, part_lse);
+                     group, dims->max_pages, sp::list_cap(dims), U,
+                     (sp::list_cap(dims) + chunk_pages - 1) / chunk_pages, part_o, part_lse);
   return sp::launch_status();
 }

@@ -162,22 +162,6 @@ __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, 
   }
 }
 
-// Number of chunks of units 0 .. u-1 (wave-uniform; every lane calls).
-__device__ __forceinline__ int plan_prefix(const int32_t* __restrict__ counts, int U,
-                                           int cap, int chunk, int u) {
-  const int lane = lane_id();
-  int running = 0;
-  for (int seg = 0; seg < u; seg += 64 * kPlanVU) {
-    int ch[kPlanVU];
-    plan_chunks8(counts, seg + lane * kPlanVU, U, cap, chunk, ch);
-    int s = 0;
-#pragma unroll
-    for (int v = 0; v < kPlanVU; ++v) s += (seg + lane * kPlanVU + v < u) ? ch[v] : 0;
-    running += __shfl(wave_incl_scan(s), 63, 64);
-  }
-  return running;
-}
-
 // ---- host-side argument checks ----------------------------------------------
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -9,49 +9,51 @@ namespace sp {
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
 
-// One 1024-thread workgroup per (unit, query head).  Thread t reads channel
-// quad t % 32 of chunks c0 + t / 32, c0 + t / 32 + 32, ... (each chunk's 128
-// floats are one coalesced 512-byte read by 32 threads), keeping an online
-// (max, sum, weighted sum); the 32 slots are then combined through LDS.
+// One 1024-thread workgroup per (unit, query head).  Unit u's chunks sit in
+// the fixed slots u * unit_parts + [0, chunks of u), so the unit's length and
+// the first round of partials are loaded together in one round trip.  Thread
+// t reads channel quad t % 32 of slots t / 32, t / 32 + 32, ... (each
+// chunk's 128 floats are one coalesced 512-byte read by 32 threads), keeping
+// an online (max, sum, weighted sum); the 32 slots are then combined through
+// LDS.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ sel_counts, int U, int cap, int chunk, int hkv, int group,
-    float* __restrict__ out, float* __restrict__ out_lse) {
+    const int32_t* __restrict__ sel_counts, int cap, int chunk, int unit_parts, int hkv,
+    int group, float* __restrict__ out, float* __restrict__ out_lse) {
   __shared__ floatx4 s_acc[kMergeSlots][32];
   __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
-  __shared__ int s_c0;
   const int u = blockIdx.x, g = blockIdx.y;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
-  // this unit's chunks, from the list lengths (as the attention planned them)
-  if (threadIdx.x < 64) {
-    const int c0w = plan_prefix(sel_counts, U, cap, chunk, u);
-    if (threadIdx.x == 0) s_c0 = c0w;
-  }
-  __syncthreads();
-  const int c0 = s_c0;
-  const int c1 = c0 + unit_chunks(sel_counts, u, cap, chunk);
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
+  const int64_t c0 = (int64_t)u * unit_parts;
+  const int count = sel_counts[u];
 
   float m = -INFINITY, s = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = c0 + slot; c < c1; c += 2 * kMergeSlots) {
-    const bool two = c + kMergeSlots < c1;
-    const int64_t r0 = (int64_t)c * group + g;
-    const int64_t r1 = (int64_t)(two ? c + kMergeSlots : c) * group + g;
-    // All four loads are issued before any is used (one round trip): the
-    // empty asm statements keep the compiler from moving a load under the
-    // `two` or `mn` tests, where it would become a branch that waits for it.
+  int nch = unit_parts;   // refined once the count has arrived
+  for (int i = slot; i < nch; i += 2 * kMergeSlots) {
+    // Both slots' loads are issued before any is used; indices past the
+    // unit's slots are clamped to its last slot (read, then discarded).  The
+    // empty asm statements keep the compiler from moving a load under a test,
+    // where it would become a branch that waits for it.
+    const int i1 = i + kMergeSlots;
+    const int64_t r0 = (c0 + i) * group + g;
+    const int64_t r1 = (c0 + min(i1, unit_parts - 1)) * group + g;
     float l0 = part_lse[r0], l1 = part_lse[r1];
     floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
     floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
     asm volatile("" : "+v"(l0), "+v"(l1), "+v"(o0), "+v"(o1));
-    if (!two) l1 = -INFINITY;
+    nch = (min(max(count, 0), cap) + chunk - 1) / chunk;
+    if (i >= nch) break;
+    if (i1 >= nch) l1 = -INFINITY;
     const float mn = fmaxf(m, fmaxf(l0, l1));
     if (mn == -INFINITY) continue;
     const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
     const float w0 = (l0 == -INFINITY) ? 0.f : __expf(l0 - mn);
     const float w1 = (l1 == -INFINITY) ? 0.f : __expf(l1 - mn);
-    acc = acc * a + o0 * w0 + o1 * w1;
+    // a discarded slot's floats are never read as weights: w1 = 0 and its
+    // values may be anything, so they are selected away, not multiplied
+    acc = acc * a + o0 * w0 + ((l1 == -INFINITY) ? floatx4{0.f, 0.f, 0.f, 0.f} : o1 * w1);
     s = s * a + w0 + w1;
     m = mn;
   }
@@ -96,9 +98,10 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
   if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
+  const int cap = sp::list_cap(dims);
   hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
-                     (hipStream_t)stream, part_o, part_lse, sel_counts, U, sp::list_cap(dims),
-                     chunk_pages, hkv, group, out, out_lse);
+                     (hipStream_t)stream, part_o, part_lse, sel_counts, cap, chunk_pages,
+                     (cap + chunk_pages - 1) / chunk_pages, hkv, group, out, out_lse);
   return sp::launch_status();
 }
 

@@ -113,6 +113,9 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int s = 0; s < 4; ++s)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[slot][4 + s]), qpos[s], acc, 0, 0,
                                                     0);
+    // Which of the tile's pages are in range: lane r < 16 holds page r's
+    // flag, and a ballot hands it to every lane without an LDS permute.
+    const unsigned long long okm = __ballot(oks[slot]);
     // lane (g = row, j) now holds u for pages p0 + 4j + i: one 16-byte store
     // of its 4 consecutive pages when they are all in range and aligned
     float val[4];
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pi = p0 + 4 * j + i;
-      okv[i] = __shfl(oks[slot] ? 1 : 0, 4 * j + i, 64) != 0;
+      okv[i] = (okm >> (4 * j + i)) & 1ull;
       const int nv = min(kP, L - kP * pi);
       const float lnv = (nv >= kP) ? ln16 : logf((float)max(nv, 1));
       val[i] = okv[i] ? fmaf(scale, acc[i], lnv) : -INFINITY;

@@ -221,10 +221,12 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
  * sel_counts alone (a wave prefix sum over the per-unit chunk counts), the
  * unit and the list entries [local * chunk_pages, +chunk_pages) it owns, and
  * computes exact attention of the unit's G query heads over the valid tokens
- * of those pages; workgroups past the last chunk exit.  Writes, for each
- * chunk c and head g:
+ * of those pages; workgroups past the last chunk exit.  Writes, for chunk
+ * i of unit u (slot c = u * ceil(L / chunk_pages) + i, L the dims' list
+ * bound, max_list_pages or else max_pages) and head g:
  *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the chunk)
  *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
+ * Slots past a unit's last chunk are left as they were.
  * K/V are read from the pool at sel_phys (physical ids or cache slots).
  *
  *   part_o   fp32 [max_parts][G][128];  part_lse fp32 [max_parts][G]
@@ -240,9 +242,10 @@ sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q, con
 /*
  * sparse_merge_splits -- log-sum-exp merge of the chunk partials of each unit:
  *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) * o_c
- * (the identity that makes the split over chunks exact).  Each unit's
- * chunks are located from sel_counts exactly as sparse_decode_attn numbered
- * them (same chunk_pages).
+ * (the identity that makes the split over chunks exact).  Unit u's chunks
+ * are the slots u * ceil(L / chunk_pages) + [0, ceil(k_u / chunk_pages)),
+ * k_u = min(sel_counts[u], L), as sparse_decode_attn wrote them (same
+ * chunk_pages and dims); other slots are not read as values.
  *   out      fp32 [B][Hq][128];  out_lse fp32 [B][Hq]
  * A unit with no kept page gets o = 0 and lse = -inf.
  */
