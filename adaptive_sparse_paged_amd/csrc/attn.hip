@@ -5,8 +5,9 @@
 // is made on the host and the step stays inside the graph).
 //
 // The grid is fixed (one workgroup per possible chunk).  Workgroup c derives
-// its unit and chunk from the list lengths themselves (a wave prefix sum over
-// the per-unit chunk counts), then its 4 waves split the chunk's pages; each wave runs an online softmax
+// its unit and chunk from the list lengths themselves (wave prefix sums over
+// the per-unit chunk counts; full chunks are numbered before partial ones),
+// then its 4 waves split the chunk's pages; each wave runs an online softmax
 // for the unit's G query heads on the bf16 matrix cores:
 //   QK:  S^T[t][g] = K[t][:] . q[g][:]   v_mfma_f32_16x16x32_bf16, 4 k-slices
 //        (A = K tile rows = tokens, read straight from HBM in 16-byte runs;

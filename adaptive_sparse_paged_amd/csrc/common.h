@@ -92,37 +92,57 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 
 // ---- the chunk plan, derived on the device from the list lengths ------------
 // Unit u's list of k_u = min(count_u, cap) pages (cap: the dims' list bound)
-// splits into
-// ceil(k_u / chunk) chunks, numbered across units in unit order.  A wave
-// derives where chunk c falls with one round of loads (lane l reads the
-// counts of units l*8 .. l*8+7 of each 512-unit segment) and a wave prefix
-// sum -- no host plan and no precomputed offsets.
+// splits into floor(k_u / chunk) full chunks and, when chunk does not divide
+// k_u, one partial chunk.  Chunks are numbered with every unit's full chunks
+// first (unit order), then the partial chunks (unit order), so the grid's
+// last workgroups -- the ones that run while the rest of the chip drains --
+// are the short ones.  A wave derives where chunk c falls with one round of
+// loads (lane l reads the counts of units l*8 .. l*8+7 of each 512-unit
+// segment) and wave prefix sums -- no host plan and no precomputed offsets.
 constexpr int kPlanVU = 8;
 
-// Chunks of one unit u < U.
-__device__ __forceinline__ int unit_chunks(const int32_t* __restrict__ counts, int u, int cap,
-                                           int chunk) {
-  const int k = min(max(counts[u], 0), cap);
-  return (k + chunk - 1) / chunk;
-}
-
-// Chunk counts of units base .. base + kPlanVU - 1 (0 past the last unit).
-// The loads are unconditional -- an index past the last unit re-reads unit
-// U-1 -- and all are issued before any is used.  The empty asm statement
-// pins each loaded value in a register; without it the compiler moves each
-// load under the `idx < U` test, and a load under a per-lane condition
-// becomes a branch that waits for it: 8 round trips instead of one.
-__device__ __forceinline__ void plan_chunks8(const int32_t* __restrict__ counts, int base, int U,
-                                             int cap, int chunk, int (&ch)[kPlanVU]) {
+// List lengths of units base .. base + kPlanVU - 1, clamped to [0, cap]
+// (0 past the last unit).  The loads are unconditional -- an index past the
+// last unit re-reads unit U-1 -- and all are issued before any is used.  The
+// empty asm statement pins each loaded value in a register; without it the
+// compiler moves each load under the `idx < U` test, and a load under a
+// per-lane condition becomes a branch that waits for it: 8 round trips
+// instead of one.
+__device__ __forceinline__ void plan_counts8(const int32_t* __restrict__ counts, int base, int U,
+                                             int cap, int (&k)[kPlanVU]) {
   int raw[kPlanVU];
 #pragma unroll
   for (int v = 0; v < kPlanVU; ++v) raw[v] = counts[min(base + v, U - 1)];
 #pragma unroll
   for (int v = 0; v < kPlanVU; ++v) {
     asm volatile("" : "+v"(raw[v]));
-    const int k = (base + v < U) ? min(max(raw[v], 0), cap) : 0;
-    ch[v] = (k + chunk - 1) / chunk;
+    k[v] = (base + v < U) ? min(max(raw[v], 0), cap) : 0;
   }
+}
+
+// Within one 512-unit segment whose lane-l units (seg + 8l ..) hold ch[v]
+// chunks of this numbering pass (per-lane sum s, inclusive wave prefix incl,
+// `before` chunks numbered ahead of the segment): if chunk c falls in it,
+// set unit and local (wave-uniform) and return true.
+__device__ __forceinline__ bool plan_find(int c, int before, int seg, const int (&ch)[kPlanVU],
+                                          const int (&k)[kPlanVU], int s, int incl, bool full,
+                                          int chunk, int& unit, int& local) {
+  const int lane = lane_id();
+  if (c >= before + __shfl(incl, 63, 64)) return false;
+  const unsigned long long hit_mask = __ballot(before + incl > c);
+  const int hit = __ffsll((long long)hit_mask) - 1;
+  int acc = before + incl - s, fu = -1, fl = 0;
+#pragma unroll
+  for (int v = 0; v < kPlanVU; ++v) {
+    if (fu < 0 && c < acc + ch[v]) {
+      fu = seg + lane * kPlanVU + v;
+      fl = full ? c - acc : k[v] / chunk;
+    }
+    acc += ch[v];
+  }
+  unit = __builtin_amdgcn_readlane(fu, hit);
+  local = __builtin_amdgcn_readlane(fl, hit);
+  return true;
 }
 
 // Unit of global chunk c and the chunk's index within that unit (unit = -1
@@ -131,34 +151,42 @@ __device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, 
                                             int cap, int chunk, int c, int& unit,
                                             int& local) {
   const int lane = lane_id();
-  int running = 0;
   unit = -1;
   local = 0;
-  for (int seg = 0; seg < U; seg += 64 * kPlanVU) {
-    int ch[kPlanVU];
-    plan_chunks8(counts, seg + lane * kPlanVU, U, cap, chunk, ch);
-    int s = 0;
+  int k[kPlanVU], ch[kPlanVU], cp[kPlanVU];
+  if (U <= 64 * kPlanVU) {
+    // one segment: a single round of loads serves both numbering passes
+    plan_counts8(counts, lane * kPlanVU, U, cap, k);
+    int sf = 0, sp = 0;
 #pragma unroll
-    for (int v = 0; v < kPlanVU; ++v) s += ch[v];
-    const int incl = wave_incl_scan(s);
-    const int seg_total = __shfl(incl, 63, 64);
-    if (c < running + seg_total) {
-      const unsigned long long hit_mask = __ballot(running + incl > c);
-      const int hit = __ffsll((long long)hit_mask) - 1;
-      int acc = running + incl - s, fu = -1, fl = 0;
+    for (int v = 0; v < kPlanVU; ++v) {
+      ch[v] = k[v] / chunk;
+      cp[v] = (k[v] % chunk != 0) ? 1 : 0;
+      sf += ch[v];
+      sp += cp[v];
+    }
+    const int inf = wave_incl_scan(sf), inp = wave_incl_scan(sp);
+    const int full_total = __shfl(inf, 63, 64);
+    if (plan_find(c, 0, 0, ch, k, sf, inf, true, chunk, unit, local)) return;
+    plan_find(c, full_total, 0, cp, k, sp, inp, false, chunk, unit, local);
+    return;
+  }
+  // pass 0: the full chunks of every unit; pass 1: one partial chunk per
+  // unit whose length chunk does not divide
+  int before = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int seg = 0; seg < U; seg += 64 * kPlanVU) {
+      plan_counts8(counts, seg + lane * kPlanVU, U, cap, k);
+      int s = 0;
 #pragma unroll
       for (int v = 0; v < kPlanVU; ++v) {
-        if (fu < 0 && c < acc + ch[v]) {
-          fu = seg + lane * kPlanVU + v;
-          fl = c - acc;
-        }
-        acc += ch[v];
+        ch[v] = pass == 0 ? k[v] / chunk : (k[v] % chunk != 0 ? 1 : 0);
+        s += ch[v];
       }
-      unit = __builtin_amdgcn_readlane(fu, hit);
-      local = __builtin_amdgcn_readlane(fl, hit);
-      return;
+      const int incl = wave_incl_scan(s);
+      if (plan_find(c, before, seg, ch, k, s, incl, pass == 0, chunk, unit, local)) return;
+      before += __shfl(incl, 63, 64);
     }
-    running += seg_total;
   }
 }
 

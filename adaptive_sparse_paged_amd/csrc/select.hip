@@ -22,9 +22,10 @@
 //   4. keep every page with key > tau plus the r lowest-index pages with key
 //      == tau, r = ceil((T - W(key > tau)) / w_tau); compact in ascending page
 //      order by one block prefix sum of packed (above, tie) counts.
-//   5. the last workgroup to finish (device ticket) writes the prefix sums of
-//      the counts and of the chunk counts over all units, then re-arms the
-//      ticket -- the plan the attention kernel reads, made on the device.
+//   5. optionally, the last workgroup to finish (device ticket) writes the
+//      prefix sums of the counts and of the chunk counts over all units, then
+//      re-arms the ticket (the attention and merge plan from the counts
+//      alone and do not read them).
 
 #include "common.h"
 

@@ -216,7 +216,10 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
  * made on the host and the step stays inside the graph).
  *
  * Unit u's list (k_u = sel_counts[u] entries) splits into ceil(k_u /
- * chunk_pages) chunks, numbered across units in unit order.  The grid has
+ * chunk_pages) chunks: floor(k_u / chunk_pages) full ones and, when
+ * chunk_pages does not divide k_u, one partial chunk.  Workgroups take every
+ * unit's full chunks first (unit order), then the partial chunks (unit
+ * order), so the last workgroups of the grid are the short ones.  The grid has
  * max_parts workgroups, fixed at enqueue time; workgroup c derives, from
  * sel_counts alone (a wave prefix sum over the per-unit chunk counts), the
  * unit and the list entries [local * chunk_pages, +chunk_pages) it owns, and
