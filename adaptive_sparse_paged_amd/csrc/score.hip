@@ -31,7 +31,7 @@ constexpr int kScorePagesPerBlock = 16 * kScoreTilesPerWave * kScoreWaves;
 // page (adjacent 512-byte rows, one 4 KiB run) are read close together in
 // time.  A wave loads the page ids of both its tiles, then the summaries of
 // tile t + 1 while the matrix cores work on tile t.
-__global__ __launch_bounds__(256) void score_kernel(
+__global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ summ, int64_t pool_pages,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ ctx_lens, float scale,
     float* __restrict__ logits, int hkv, int group, int max_pages) {
@@ -159,7 +159,7 @@ extern "C" sparse_status sparse_score_pages(const sparse_dims* dims, const uint1
   dim3 grid(hkv, (dims->max_pages + sp::kScorePagesPerBlock - 1) / sp::kScorePagesPerBlock,
             dims->batch);
   if (U < 1 || grid.z > 65535) return SPARSE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(sp::score_kernel, grid, dim3(256), 0, (hipStream_t)stream, q, summ,
+  hipLaunchKernelGGL(sp::score_kernel, grid, dim3(64 * sp::kScoreWaves), 0, (hipStream_t)stream, q, summ,
                      pool_pages, page_table, ctx_lens, scale, logits, hkv, group,
                      dims->max_pages);
   return sp::launch_status();
