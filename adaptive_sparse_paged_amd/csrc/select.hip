@@ -16,8 +16,9 @@
 //      m[p] (monotone for m >= 0).
 //   3. target T = ceil(gamma * sum w); a mass-weighted radix select over the
 //      key bits below the highest bit in which the unit's keys differ (up to
-//      11 bits per pass; LDS histograms of counts and weights; one wave scans
-//      the bins from the top) finds the key tau with
+//      11 bits per pass; LDS histograms of counts and weights; each wave
+//      totals its 128 bins, and the wave whose bins hold the crossing scans
+//      them) finds the key tau with
 //      W(key > tau) < T <= W(key >= tau).
 //   4. keep every page with key > tau plus the r lowest-index pages with key
 //      == tau, r = ceil((T - W(key > tau)) / w_tau); compact in ascending page
@@ -46,7 +47,6 @@ __device__ __forceinline__ unsigned long long wgt_of(uint32_t key) {
   if constexpr (COUNT) return 1ull;
   else return weight_of(key);
 }
-
 
 // Logits of heads g0 .. g0 + HPR - 1 for this thread's pages (thread t:
 // pages t, t + 1024, ...); -inf for a page past the context or a head past
