@@ -134,6 +134,10 @@ class SplitHostTierStep:
         kv, sp_, sh_, pp = self.cache.pool_args()
         self.cache.resolve_split(hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys)
         self.resolved.record(cur)
+        # The fetch is enqueued before any second-stream work, so a slow
+        # host-side launch there (the first use of the stream) cannot hold it
+        # back; the second stream waits for the resolve only.
+        self.cache.fetch()
         self.side.wait_event(self.resolved)
         with torch.cuda.stream(self.side):
             lib.split_misses(self.dims, hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys,
@@ -142,7 +146,6 @@ class SplitHostTierStep:
             self.hits.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_hit, self.lse_hit,
                              stream=self.side, sel_phys=self.hit_phys)
             self.hits_done.record(self.side)
-        self.cache.fetch()
         cur.wait_event(self.split_done)
         self.miss.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_miss, self.lse_miss)
         cur.wait_event(self.hits_done)
