@@ -63,11 +63,14 @@ def parse():
 
 
 # Pages per attention workgroup, measured per workload on MI355X with the
-# full 32- or 4-layer step: 512 wins where every request has the same long
-# context (fewer workgroup starts), 256 where lengths are ragged (a unit's last,
-# partial chunk unbalances the grid less), and 128 for the host tier's short
-# 448-page lists.
-DEFAULT_CHUNK = {"long_128k": 512, "llama8b_32k": 512, "serving_b64": 256,
+# full 32- or 4-layer step.  Where every request has the same long context,
+# the best size gives one workgroup per compute unit (256 workgroups: 1024
+# pages at 4 x 131072 tokens, 512 at 8 x 32768); sizes that leave some units
+# with two workgroups and others with one are much slower, since a
+# workgroup's rate is capped by the loads it keeps in flight.  256 where
+# lengths are ragged (a unit's last, partial chunk unbalances the grid less),
+# and 128 for the host tier's short 448-page lists.
+DEFAULT_CHUNK = {"long_128k": 1024, "llama8b_32k": 512, "serving_b64": 256,
                  "host_tier_512k": 128, "host_tier_layers": 128}
 
 
