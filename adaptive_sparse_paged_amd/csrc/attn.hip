@@ -6,8 +6,8 @@
 //
 // The grid is fixed (one workgroup per possible chunk).  Workgroup c derives
 // its unit and chunk from the list lengths themselves (wave prefix sums over
-// the per-unit chunk counts; full chunks are numbered before partial ones),
-// then its 4 waves split the chunk's pages; each wave runs an online softmax
+// the per-unit chunk counts), takes its even share of the unit's list, and
+// its 4 waves split those pages; each wave runs an online softmax
 // for the unit's G query heads on the bf16 matrix cores:
 //   QK:  S^T[t][g] = K[t][:] . q[g][:]   v_mfma_f32_16x16x32_bf16, 4 k-slices
 //        (A = K tile rows = tokens, read straight from HBM in 16-byte runs;
@@ -129,8 +129,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   const int L = __builtin_amdgcn_readfirstlane(min(max(ctx_lens[b], 0), max_pages * kP));
   const int cnt = __builtin_amdgcn_readfirstlane(min(sel_counts[u], cap));
-  const int i0 = local * chunk_pages;
-  const int i1 = min(i0 + chunk_pages, cnt);
+  // The unit's ceil(cnt / chunk_pages) chunks share its list evenly (sizes
+  // differ by at most one page), so no chunk is a short remainder.
+  const int nch = (cnt + chunk_pages - 1) / chunk_pages;
+  const int i0 = (int)(((int64_t)local * cnt) / nch);
+  const int i1 = (int)(((int64_t)(local + 1) * cnt) / nch);
   const int32_t* lp = sel_pages + (int64_t)u * max_pages;
   const int32_t* lx = sel_phys + (int64_t)u * max_pages;
 

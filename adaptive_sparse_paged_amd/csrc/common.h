@@ -92,11 +92,12 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 
 // ---- the chunk plan, derived on the device from the list lengths ------------
 // Unit u's list of k_u = min(count_u, cap) pages (cap: the dims' list bound)
-// splits into floor(k_u / chunk) full chunks and, when chunk does not divide
-// k_u, one partial chunk.  Chunks are numbered with every unit's full chunks
-// first (unit order), then the partial chunks (unit order), so the grid's
-// last workgroups -- the ones that run while the rest of the chip drains --
-// are the short ones.  A wave derives where chunk c falls with one round of
+// has ceil(k_u / chunk) chunks (the attention shares the list evenly over
+// them).  Chunks are numbered over every unit's first floor(k_u / chunk)
+// chunks (unit order), then the last chunk of each unit that chunk does not
+// divide (unit order), so the grid's last workgroups -- the ones that run
+// while the rest of the chip drains -- include every unit shorter than one
+// chunk.  A wave derives where chunk c falls with one round of
 // loads (lane l reads the counts of units l*8 .. l*8+7 of each 512-unit
 // segment) and wave prefix sums -- no host plan and no precomputed offsets.
 constexpr int kPlanVU = 8;

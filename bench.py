@@ -67,10 +67,10 @@ def parse():
 # the best size gives one workgroup per compute unit (256 workgroups: 1024
 # pages at 4 x 131072 tokens, 512 at 8 x 32768); sizes that leave some units
 # with two workgroups and others with one are much slower, since a
-# workgroup's rate is capped by the loads it keeps in flight.  256 where
-# lengths are ragged (a unit's last, partial chunk unbalances the grid less),
-# and 128 for the host tier's short 448-page lists.
-DEFAULT_CHUNK = {"long_128k": 1024, "llama8b_32k": 512, "serving_b64": 256,
+# workgroup's rate is capped by the loads it keeps in flight.  320 where
+# lengths are ragged (many rounds of workgroups; smaller chunks shorten the
+# drain at the end), and 128 for the host tier's short 448-page lists.
+DEFAULT_CHUNK = {"long_128k": 1024, "llama8b_32k": 512, "serving_b64": 320,
                  "host_tier_512k": 128, "host_tier_layers": 128}
 
 

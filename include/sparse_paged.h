@@ -215,18 +215,20 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
  * out from the per-head list lengths which part it handles, so no plan is
  * made on the host and the step stays inside the graph).
  *
- * Unit u's list (k_u = sel_counts[u] entries) splits into ceil(k_u /
- * chunk_pages) chunks: floor(k_u / chunk_pages) full ones and, when
- * chunk_pages does not divide k_u, one partial chunk.  Workgroups take every
- * unit's full chunks first (unit order), then the partial chunks (unit
- * order), so the last workgroups of the grid are the short ones.  The grid has
+ * Unit u's list (k_u = min(sel_counts[u], L) entries, L the dims' list
+ * bound) splits evenly into n_u = ceil(k_u / chunk_pages) chunks: chunk i
+ * holds entries [floor(i k_u / n_u), floor((i + 1) k_u / n_u)), so sizes
+ * differ by at most one page and none exceeds chunk_pages.  Workgroups are
+ * numbered over every unit's first floor(k_u / chunk_pages) chunks (unit
+ * order), then the last chunk of each unit that chunk_pages does not divide
+ * (unit order), so units shorter than one chunk come last.  The grid has
  * max_parts workgroups, fixed at enqueue time; workgroup c derives, from
- * sel_counts alone (a wave prefix sum over the per-unit chunk counts), the
- * unit and the list entries [local * chunk_pages, +chunk_pages) it owns, and
- * computes exact attention of the unit's G query heads over the valid tokens
- * of those pages; workgroups past the last chunk exit.  Writes, for chunk
- * i of unit u (slot c = u * ceil(L / chunk_pages) + i, L the dims' list
- * bound, max_list_pages or else max_pages) and head g:
+ * sel_counts alone (wave prefix sums over the per-unit chunk counts), the
+ * unit and the list entries it owns, and computes exact attention of the
+ * unit's G query heads over the valid tokens of those pages; workgroups past
+ * the last chunk exit.  Writes, for chunk
+ * i of unit u (slot c = u * ceil(L / chunk_pages) + i; L is max_list_pages,
+ * or else max_pages) and head g:
  *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the chunk)
  *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
  * Slots past a unit's last chunk are left as they were.
