@@ -267,7 +267,7 @@ def append_tokens(dims, k_new, v_new, kv, stride_page, stride_head, pool_pages, 
         pool_pages, _ptr(page_table), _ptr(ctx_lens), _ptr(summ), _stream(stream)))
 
 
-READ_BLOCKS_GROUPS = 2048   # SPARSE_READ_BLOCKS_GROUPS
+READ_BLOCKS_GROUPS = 4096   # SPARSE_READ_BLOCKS_GROUPS
 
 
 def read_blocks(pool, pool_blocks, order, xor_out, stream=None):

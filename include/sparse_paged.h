@@ -466,7 +466,7 @@ sparse_status sparse_lse_combine(const sparse_dims* dims, const float* out_a, co
  * INVALID: n < 0, pool_blocks < 0, a NULL pool or xor_out (or order with
  * n > 0), pool not 16-byte aligned.
  */
-#define SPARSE_READ_BLOCKS_GROUPS 2048
+#define SPARSE_READ_BLOCKS_GROUPS 4096
 sparse_status sparse_read_blocks(const uint16_t* pool, int64_t pool_blocks,
                                  const int32_t* order, int64_t n, uint32_t* xor_out,
                                  void* stream);

@@ -178,3 +178,10 @@ def test_missing_library_fails_loudly(tmp_path):
             lib.load(str(tmp_path / "nope.so"))
         finally:
             lib._lib = saved
+
+
+def test_read_blocks_grid_constant_matches_header():
+    """The binding sizes xor_out from its own copy of the header's grid."""
+    with open(HEADER) as f:
+        m = re.search(r"#define SPARSE_READ_BLOCKS_GROUPS (\d+)", f.read())
+    assert m and int(m.group(1)) == lib.READ_BLOCKS_GROUPS
