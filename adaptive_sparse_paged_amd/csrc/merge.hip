@@ -6,16 +6,18 @@
 
 namespace sp {
 
-constexpr int kMergeThreads = 1024;
+constexpr int kMergeThreads = 256;
 constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
 
-// One 1024-thread workgroup per (unit, query head).  Unit u's chunks sit in
+// One 256-thread workgroup per (unit, query head).  Unit u's chunks sit in
 // the fixed slots u * unit_parts + [0, chunks of u), so the unit's length and
 // the first round of partials are loaded together in one round trip.  Thread
-// t reads channel quad t % 32 of slots t / 32, t / 32 + 32, ... (each
-// chunk's 128 floats are one coalesced 512-byte read by 32 threads), keeping
-// an online (max, sum, weighted sum); the 32 slots are then combined through
-// LDS.
+// t reads channel quad t % 32 of chunks t / 32, t / 32 + 8, ... (each chunk's
+// 128 floats are one coalesced 512-byte read by 32 threads), keeping an
+// online (max, sum, weighted sum); the 8 chunk slots are then combined
+// through LDS.  (1024 threads ran 4.7 against 4.4 us on 4 x 131072 tokens
+// and 15.3 against 7.0 us on 64 ragged requests: most of their slots had
+// no chunk, and fewer workgroups fit a compute unit.)
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ sel_counts, int cap, int chunk, int unit_parts, int hkv,
