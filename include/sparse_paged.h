@@ -206,7 +206,8 @@ sparse_status sparse_append_tokens(const sparse_dims* dims, const uint16_t* k_ne
                                    void* stream);
 
 /* Upper bound on the number of chunks (= partial slots) of one step (host):
- * U * ceil(max_pages / chunk_pages). */
+ * U * ceil(L / chunk_pages), L = max_list_pages if set, else max_pages.
+ * Returns -1 for invalid dims or chunk_pages < 1. */
 int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
 
 /*
