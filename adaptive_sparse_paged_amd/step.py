@@ -36,11 +36,13 @@ class StepBuffers:
 class SparseDecodeStep:
     """Fixed-shape decode step for one layer shape.
 
-    dims: lib.Dims; gamma in (0, 1]; chunk_pages: pages per attention
-    workgroup (256, the fastest of 96-384 measured on MI355X at 32k-128k
-    contexts, is 64 pages per wave: one batch of list ids each; clamped to
-    max_pages).  Intermediate buffers are shared by every layer run through
-    this object; outputs can be given per call.
+    dims: lib.Dims; gamma in (0, 1]; chunk_pages: the most pages one
+    attention workgroup takes (a unit's list is split evenly over
+    ceil(count / chunk_pages) workgroups; clamped to max_pages).  On MI355X
+    the best size leaves one workgroup per compute unit when every request
+    has the same long context (1024 at 4 x 131072 tokens, 512 at 8 x 32768),
+    and about 320 for ragged lengths.  Intermediate buffers are shared by
+    every layer run through this object; outputs can be given per call.
 
     groups > 1 splits the requests into that many contiguous groups, each on a
     stream of its own, where a group's scoring starts once the previous group's
