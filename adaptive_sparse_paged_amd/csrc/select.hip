@@ -14,7 +14,8 @@
 //   2. weights w[p] = floor(m[p] * 2^52) (exact 64-bit fixed point, so the
 //      cut's sums are exact and order independent) and keys = fp32 bits of
 //      m[p] (monotone for m >= 0).
-//   3. target T = ceil(gamma * sum w); a mass-weighted radix select over the
+//   3. target T = ceil(gamma * sum w) (the sum taken from the first radix
+//      pass's histogram, which holds every page); a mass-weighted radix select over the
 //      key bits below the highest bit in which the unit's keys differ (up to
 //      11 bits per pass; LDS histograms of counts and weights; each wave
 //      totals its 128 bins, and the wave whose bins hold the crossing scans
@@ -226,7 +227,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ uint32_t hcnt[kHistBufs][2048];
   __shared__ unsigned long long hw[kHistBufs][2048];
   __shared__ float red_m[kMaxGroup][kSelWaves], red_s[kMaxGroup][kSelWaves];
-  __shared__ unsigned long long red_z[kSelWaves];
   __shared__ uint32_t red_lo[kSelWaves], red_hi[kSelWaves];
   __shared__ uint32_t scan32[kSelWaves];
   __shared__ unsigned long long scan64[kSelWaves];
@@ -358,7 +358,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       }
     }
     const float invg = 1.f / (float)group;
-    unsigned long long zl = 0ull;
     uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
@@ -367,22 +366,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const uint32_t key = __float_as_uint(m[k] * invg);
         keys_lds[p] = key;
         if constexpr (kStagePt) ptl[p] = ptv[k];
-        zl += wgt_of<COUNT>(key);
         klo = min(klo, key);
         khi = max(khi, key);
       }
     }
-    zl = wave_total_u64(zl);
     klo = wave_total_u32(klo, OpMinU());
     khi = wave_total_u32(khi, OpMaxU());
     if (lane == 0) {
-      red_z[wv] = zl;
       red_lo[wv] = klo;
       red_hi[wv] = khi;
     }
     __syncthreads();
     // every wave combines the 16 wave partials itself (lane l: partial l & 15)
-    const unsigned long long Z = row16_sum_u64(red_z[lane & (kSelWaves - 1)]);
     const uint32_t KLO = row16_u32(red_lo[lane & (kSelWaves - 1)], OpMinU());
     const uint32_t KHI = row16_u32(red_hi[lane & (kSelWaves - 1)], OpMaxU());
     // this thread's blocked run of keys
@@ -407,20 +402,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t tau = 0u;
     unsigned long long need = 0ull;
     if (!all) {
-      unsigned long long T = COUNT ? (unsigned long long)k_pages
-                                   : (unsigned long long)ceil((double)gamma * (double)Z);
-      if (T > Z) T = Z;
-      if (T < 1ull) T = 1ull;
+      // target T from the total weight Z = sum of every page's weight
+      auto target = [&](unsigned long long Z) {
+        unsigned long long t = COUNT ? (unsigned long long)k_pages
+                                     : (unsigned long long)ceil((double)gamma * (double)Z);
+        if (t > Z) t = Z;
+        if (t < 1ull) t = 1ull;
+        return t;
+      };
+      unsigned long long T = 0ull;
       unsigned long long w_tau = wgt_of<COUNT>(KHI);
       if (KLO == KHI) {
         tau = KHI;                          // every page has the same mass
+        T = target((unsigned long long)n * w_tau);
       } else {
         // radix passes over the bits below the highest bit where keys differ
         const int top = 31 - __clz(KLO ^ KHI);
         uint32_t hi_mask = ~((2u << top) - 1u);
         uint32_t prefix = KHI & hi_mask;
         int lo = top + 1, buf = 0;
-        bool resolved = false, first = true;
+        bool resolved = false, first = true, need_z = true;
         while (lo > 0) {
           const int width = min(11, lo);
           const int sh = lo - width, nb = 1 << width;
@@ -456,6 +457,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             if (lane == 0) scan64[wv] = wtot;
             __syncthreads();
             const unsigned long long tw = scan64[lane & (kSelWaves - 1)];
+            // The first pass takes in every page (all keys share the bits
+            // above the first digit), so its bins sum to Z: the target is
+            // set here instead of by a block reduction of its own.
+            if (need_z) {
+              T = target(row16_sum_u64(tw));
+              need_z = false;
+            }
             // weight of the bins of the waves above this one (same in every lane)
             const unsigned long long above =
                 row16_sum_u64(((lane & (kSelWaves - 1)) > wv) ? tw : 0ull);
