@@ -192,13 +192,25 @@ __device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x
   return x;
 }
 
-// Head g's max (MAX) or sum over the 16 wave partials part[g][w], computed by
-// every lane of the calling wave (lane l takes partial l & 15; one row
-// butterfly).  The result is the same in every lane and every wave.
-template <bool MAX>
-__device__ __forceinline__ float head_total(const float (*part)[kSelWaves], int g) {
-  const float v = part[g][lane_id() & (kSelWaves - 1)];
-  return MAX ? row16_f32(v, OpMax()) : row16_f32(v, OpAdd());
+// The max (MAX) or sum over the 16 wave partials part[g][w] of heads g0 ..
+// g0 + H - 1, computed by every lane of the calling wave: four heads per LDS
+// read (lane l takes head g0 + 4r + (l >> 4), partial l & 15), one row
+// butterfly, then each head's total is read from its row.  The results are
+// the same in every lane and every wave.
+template <bool MAX, int H>
+__device__ __forceinline__ void head_totals(const float (*part)[kSelWaves], int g0, int group,
+                                            float (&out)[H]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < (H + 3) / 4; ++r) {
+    const int g = g0 + 4 * r + (lane >> 4);
+    const float raw = part[min(g, kMaxGroup - 1)][lane & (kSelWaves - 1)];
+    float v = (g < group) ? raw : (MAX ? -INFINITY : 0.f);
+    v = MAX ? row16_f32(v, OpMax()) : row16_f32(v, OpAdd());
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * r + e < H) out[4 * r + e] = __uint_as_float(lane_u32(__float_as_uint(v), 16 * e));
+  }
 }
 
 // COUNT = false: the coverage cut (page weight = its fixed-point mass, target
@@ -318,10 +330,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     for (int g0 = 0; g0 < group; g0 += HPR) {
       if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
+      float Mh[4];
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
-        const float M = head_total<true>(red_m, g0 + hh);
+        if ((hh & 3) == 0) head_totals<true, 4>(red_m, g0 + hh, group, Mh);
+        const float M = Mh[hh & 3];
         float se = 0.f;
 #pragma unroll
         for (int k = 0; k < NPT; ++k) {
@@ -341,17 +355,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int k = 0; k < NPT; ++k) m[k] = 0.f;
     for (int g0 = 0; g0 < group; g0 += HPR) {
       if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
+      float Sh[4], Mh[4];
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
-        const float S = head_total<false>(red_s, g0 + hh);
+        if ((hh & 3) == 0) {
+          head_totals<false, 4>(red_s, g0 + hh, group, Sh);
+          if (!one_round) head_totals<true, 4>(red_m, g0 + hh, group, Mh);
+        }
+        const float S = Sh[hh & 3];
         if (!(S > 0.f)) continue;            // no finite logit: no mass
         const float inv = 1.f / S;
         if (one_round) {
 #pragma unroll
           for (int k = 0; k < NPT; ++k) m[k] += xv[hh][k] * inv;
         } else {
-          const float M = head_total<true>(red_m, g0 + hh);
+          const float M = Mh[hh & 3];
 #pragma unroll
           for (int k = 0; k < NPT; ++k) m[k] += __expf(xv[hh][k] - M) * inv;
         }
