@@ -3,8 +3,8 @@
     python -m adaptive_sparse_paged_amd.build
 
 Every .hip file under csrc/ is compiled with hipcc for gfx950 (packed-FP32
-instructions disabled) and linked into one shared library with a plain C ABI
-(include/sparse_paged.h).
+instructions disabled, kernel arguments preloaded into SGPRs) and linked into
+one shared library with a plain C ABI (include/sparse_paged.h).
 """
 
 import concurrent.futures as cf
@@ -26,6 +26,9 @@ FLAGS = [
     "-std=c++17",
     "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # gfx950 can load the first kernel arguments into SGPRs at wave launch;
+    # short-lived waves (score, select) then skip one dependent load
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]
