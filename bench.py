@@ -69,8 +69,10 @@ def parse():
 # with two workgroups and others with one are much slower, since a
 # workgroup's rate is capped by the loads it keeps in flight.  320 where
 # lengths are ragged (many rounds of workgroups; smaller chunks shorten the
-# drain at the end), and 128 for the host tier's short 448-page lists.
-DEFAULT_CHUNK = {"long_128k": 1024, "llama8b_32k": 512, "serving_b64": 320,
+# drain at the end), 128 for the host tier's short 448-page lists, and 32
+# for a single short request (its two 256-page lists spread over 16
+# workgroups instead of two).
+DEFAULT_CHUNK = {"tiny": 32, "long_128k": 1024, "llama8b_32k": 512, "serving_b64": 320,
                  "host_tier_512k": 128, "host_tier_layers": 128}
 
 
