@@ -47,6 +47,7 @@ def _structural(layer, st):
 
 
 CASES = [
+    ("tiny", 0, 0.99, 0),
     ("llama8b_32k", 0, 0.99, 4),
     ("long_128k", 0, 0.99, 3),
     ("long_128k", 31, 0.98, 2),
@@ -71,6 +72,8 @@ def test_fullsize_sampled(gpu_lib, name, layer_idx, gamma, samples):
                                                   rng.integers(0, w.kv_heads, samples))]
     if name == "serving_b64":   # the shortest and the longest request too
         units += [(int(np.argmin(layer.lens)), 0), (int(np.argmax(layer.lens)), 7)]
+    if name == "tiny":          # every unit
+        units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
     for b, h in units:
         r = check_unit(layer, st, b, h, gamma)
         say(f"  unit ({b},{h}) n={I.pages_of(layer.lens[b])} exact={r['exact']} "
