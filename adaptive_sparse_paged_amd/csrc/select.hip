@@ -3,9 +3,10 @@
 // DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", MOIRA
 // abstract, coverage-rule sentence).
 //
-// One 1024-thread workgroup per unit.  Logits are read coalesced (thread t:
-// pages t, t + 1024, ...); the page keys then pass through LDS so that for the
-// cut thread t owns the blocked run [t*NPT, t*NPT + NPT).  Steps:
+// One workgroup of NT threads per unit (256, 512 or 1024, with at most 8
+// pages per thread below 1024).  Logits are read coalesced (thread t: pages
+// t, t + NT, ...); the page keys then pass through LDS so that for the cut
+// thread t owns the blocked run [t*NPT, t*NPT + NPT).  Steps:
 //   0. one round of loads: the context length, the logits and the request's
 //      page-table row (staged in LDS for the list's physical ids).
 //   1. per query head g: the max M_g over the unit's pages, then the sum S_g
@@ -18,8 +19,8 @@
 //      pass's histogram, which holds every page); a mass-weighted radix select over the
 //      key bits below the highest bit in which the unit's keys differ (up to
 //      11 bits per pass; LDS histograms of counts and weights; each wave
-//      totals its 128 bins, and the wave whose bins hold the crossing scans
-//      them) finds the key tau with
+//      totals its share of the 2048 bins, and the wave whose bins hold the
+//      crossing scans them) finds the key tau with
 //      W(key > tau) < T <= W(key >= tau).
 //   4. keep every page with key > tau plus the r lowest-index pages with key
 //      == tau, r = ceil((T - W(key > tau)) / w_tau); compact in ascending page
@@ -35,8 +36,8 @@ extern "C" size_t sparse_select_workspace_bytes(const sparse_dims* dims);
 
 namespace sp {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelThreads = 1024;              // the largest selection workgroup
+constexpr int kSelWaves = kSelThreads / 64;    // its waves (LDS partial arrays)
 
 // fixed-point weight of a page from its fp32 mass bits: floor(m * 2^52)
 __device__ __forceinline__ unsigned long long weight_of(uint32_t key) {
@@ -50,9 +51,9 @@ __device__ __forceinline__ unsigned long long wgt_of(uint32_t key) {
 }
 
 // Logits of heads g0 .. g0 + HPR - 1 for this thread's pages (thread t:
-// pages t, t + 1024, ...); -inf for a page past the context or a head past
+// pages t, t + NT, ...); -inf for a page past the context or a head past
 // the group.
-template <int NPT, int HPR>
+template <int NPT, int HPR, int NT>
 __device__ __forceinline__ void load_logits(const float* __restrict__ X, int g0, int group,
                                             int max_pages, int n, int tid,
                                             float (&xv)[HPR][NPT]) {
@@ -61,7 +62,7 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ X, int g0,
     const float* Xg = X + (int64_t)(g0 + hh) * max_pages;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int p = k * kSelThreads + tid;
+      const int p = k * NT + tid;
       xv[hh][k] = (g0 + hh < group && p < n) ? Xg[p] : -INFINITY;
     }
   }
@@ -192,20 +193,21 @@ __device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x
   return x;
 }
 
-// The max (MAX) or sum over the 16 wave partials part[g][w] of heads g0 ..
+// The max (MAX) or sum over the NW wave partials part[g][w] of heads g0 ..
 // g0 + H - 1, computed by every lane of the calling wave: four heads per LDS
-// read (lane l takes head g0 + 4r + (l >> 4), partial l & 15), one row
+// read (lane l takes head g0 + 4r + (l >> 4), partial l & 15, the identity
+// past the NW partials), one row
 // butterfly, then each head's total is read from its row.  The results are
 // the same in every lane and every wave.
-template <bool MAX, int H>
+template <bool MAX, int H, int NW>
 __device__ __forceinline__ void head_totals(const float (*part)[kSelWaves], int g0, int group,
                                             float (&out)[H]) {
   const int lane = lane_id();
 #pragma unroll
   for (int r = 0; r < (H + 3) / 4; ++r) {
     const int g = g0 + 4 * r + (lane >> 4);
-    const float raw = part[min(g, kMaxGroup - 1)][lane & (kSelWaves - 1)];
-    float v = (g < group) ? raw : (MAX ? -INFINITY : 0.f);
+    const float raw = part[min(g, kMaxGroup - 1)][lane & 15];
+    float v = (g < group && (lane & 15) < NW) ? raw : (MAX ? -INFINITY : 0.f);
     v = MAX ? row16_f32(v, OpMax()) : row16_f32(v, OpAdd());
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -216,8 +218,8 @@ __device__ __forceinline__ void head_totals(const float (*part)[kSelWaves], int 
 // COUNT = false: the coverage cut (page weight = its fixed-point mass, target
 // ceil(gamma * total)).  COUNT = true: the fixed-budget variant (page weight 1,
 // target min(k_pages, n)) -- the k highest-mass pages, ties to lower index.
-template <int NPT, bool COUNT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+template <int NPT, bool COUNT, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ page_table, float gamma, int k_pages, int chunk_pages, int hkv,
     int group,
@@ -225,17 +227,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* __restrict__ sel_offsets,
     int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
+  // NT threads in NW waves; a workgroup takes rows of up to NPT * NT pages.
+  constexpr int NW = NT / 64;
+  static_assert(NT == 256 || NT == 512 || NT == 1024, "select workgroup size");
   // Page keys, staged so that loads are coalesced (thread t reads pages
-  // t, t + 1024, ...) while the cut works on blocked runs (thread t owns
+  // t, t + NT, ...) while the cut works on blocked runs (thread t owns
   // pages t*NPT .. t*NPT + NPT-1); later reused for the kept page list.
-  __shared__ __attribute__((aligned(16))) uint32_t keys_lds[NPT * kSelThreads];
+  __shared__ __attribute__((aligned(16))) uint32_t keys_lds[NPT * NT];
   // The request's page-table row, staged while the logits load so that the
   // list's physical ids need no dependent global gather at the end (when the
   // row fits beside the keys and histograms in LDS).
-  constexpr bool kStagePt = NPT <= 8;
-  __shared__ int32_t ptl[kStagePt ? NPT * kSelThreads : 1];
+  constexpr bool kStagePt = NPT * NT <= 8192;
+  __shared__ int32_t ptl[kStagePt ? NPT * NT : 1];
   // radix histograms: two buffers (alternate passes) while LDS allows
-  constexpr int kHistBufs = (NPT <= 16) ? 2 : 1;
+  constexpr int kHistBufs = (NPT * NT <= 16384) ? 2 : 1;
   __shared__ uint32_t hcnt[kHistBufs][2048];
   __shared__ unsigned long long hw[kHistBufs][2048];
   __shared__ float red_m[kMaxGroup][kSelWaves], red_s[kMaxGroup][kSelWaves];
@@ -260,7 +265,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // page past the context reads an in-bounds word that is masked below; the
   // empty asm statements keep the compiler from moving the loads under the
   // length test, where each would wait behind the length's round trip.
-  constexpr int HPR = (NPT >= 32) ? 1 : 32 / NPT;
+  // heads per round of loads: 32 logits per thread in a 1024-thread
+  // workgroup, 64 in a smaller one (fewer waves per SIMD leave more registers)
+  constexpr int kRegLogits = (NT == 1024) ? 32 : 64;
+  constexpr int HPR = (NPT >= kRegLogits) ? 1 : kRegLogits / NPT;
   const int Lraw = ctx_lens[b];
   float xv[HPR][NPT];
 #pragma unroll
@@ -268,15 +276,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* Xg = X + (int64_t)min(hh, group - 1) * max_pages;
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
-      xv[hh][k] = (hh < group) ? Xg[min(k * kSelThreads + tid, max_pages - 1)] : -INFINITY;
+      xv[hh][k] = (hh < group) ? Xg[min(k * NT + tid, max_pages - 1)] : -INFINITY;
   }
   int ptv[kStagePt ? NPT : 1];
   if constexpr (kStagePt) {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) ptv[k] = pt[min(k * kSelThreads + tid, max_pages - 1)];
+    for (int k = 0; k < NPT; ++k) ptv[k] = pt[min(k * NT + tid, max_pages - 1)];
   }
   // the first radix pass's histogram is cleared while the loads are in flight
-  for (int k = tid; k < 2048; k += kSelThreads) {
+  for (int k = tid; k < 2048; k += NT) {
     hcnt[0][k] = 0u;
     hw[0][k] = 0ull;
   }
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // Two passes per head, neither spending an exp on combining partials:
     // the max M_g (thread-local, wave shuffles, one partial per wave in LDS),
     // then e = exp(x - M_g) and its sum S_g the same way.  After each
-    // barrier every wave reduces the 16 wave partials itself, so no second
+    // barrier every wave reduces the NW wave partials itself, so no second
     // barrier hands a result on.  Heads go HPR at a time (the first round
     // from the loads above); when all heads fit one round, e stays in
     // registers for step 2, otherwise the logits are read again.
@@ -313,9 +321,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         for (int hh = 0; hh < HPR; ++hh)
 #pragma unroll
           for (int k = 0; k < NPT; ++k)
-            if (!(hh < group && k * kSelThreads + tid < n)) xv[hh][k] = -INFINITY;
+            if (!(hh < group && k * NT + tid < n)) xv[hh][k] = -INFINITY;
       } else {
-        load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
+        load_logits<NPT, HPR, NT>(X, g0, group, max_pages, n, tid, xv);
       }
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
@@ -329,12 +337,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     __syncthreads();
     for (int g0 = 0; g0 < group; g0 += HPR) {
-      if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
+      if (!one_round) load_logits<NPT, HPR, NT>(X, g0, group, max_pages, n, tid, xv);
       float Mh[4];
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
-        if ((hh & 3) == 0) head_totals<true, 4>(red_m, g0 + hh, group, Mh);
+        if ((hh & 3) == 0) head_totals<true, 4, NW>(red_m, g0 + hh, group, Mh);
         const float M = Mh[hh & 3];
         float se = 0.f;
 #pragma unroll
@@ -354,14 +362,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 #pragma unroll
     for (int k = 0; k < NPT; ++k) m[k] = 0.f;
     for (int g0 = 0; g0 < group; g0 += HPR) {
-      if (!one_round) load_logits<NPT, HPR>(X, g0, group, max_pages, n, tid, xv);
+      if (!one_round) load_logits<NPT, HPR, NT>(X, g0, group, max_pages, n, tid, xv);
       float Sh[4], Mh[4];
 #pragma unroll
       for (int hh = 0; hh < HPR; ++hh) {
         if (g0 + hh >= group) break;
         if ((hh & 3) == 0) {
-          head_totals<false, 4>(red_s, g0 + hh, group, Sh);
-          if (!one_round) head_totals<true, 4>(red_m, g0 + hh, group, Mh);
+          head_totals<false, 4, NW>(red_s, g0 + hh, group, Sh);
+          if (!one_round) head_totals<true, 4, NW>(red_m, g0 + hh, group, Mh);
         }
         const float S = Sh[hh & 3];
         if (!(S > 0.f)) continue;            // no finite logit: no mass
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int p = k * kSelThreads + tid;
+      const int p = k * NT + tid;
       if (p < n) {
         const uint32_t key = __float_as_uint(m[k] * invg);
         keys_lds[p] = key;
@@ -396,9 +404,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       red_hi[wv] = khi;
     }
     __syncthreads();
-    // every wave combines the 16 wave partials itself (lane l: partial l & 15)
-    const uint32_t KLO = row16_u32(red_lo[lane & (kSelWaves - 1)], OpMinU());
-    const uint32_t KHI = row16_u32(red_hi[lane & (kSelWaves - 1)], OpMaxU());
+    // every wave combines the NW wave partials itself (lane l: partial
+    // l & (NW - 1); a repeated partial leaves a min or max unchanged)
+    const uint32_t KLO = row16_u32(red_lo[lane & (NW - 1)], OpMinU());
+    const uint32_t KHI = row16_u32(red_hi[lane & (NW - 1)], OpMaxU());
+    // lane l of a row of 16 stands for wave l & 15 in the block-wide sums below
+    const int wl = lane & 15;
     // this thread's blocked run of keys
     const int pbase = tid * NPT;
     uint32_t key[NPT];
@@ -447,7 +458,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           uint32_t* cnt = hcnt[buf];
           unsigned long long* wgt = hw[buf];
           if (!first) {   // the first pass's buffer was cleared at the start
-            for (int k = tid; k < nb; k += kSelThreads) {
+            for (int k = tid; k < nb; k += NT) {
               cnt[k] = 0u;
               wgt[k] = 0ull;
             }
@@ -465,17 +476,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           }
           __syncthreads();
           {
-            // thread t owns bins 2t, 2t+1, wave w bins [128 w, 128 w + 128).
-            // One barrier for the wave totals; then only the wave whose bins
-            // hold the crossing scans them.
-            const int b0 = 2 * tid, b1 = 2 * tid + 1;
-            const unsigned long long w0 = (b0 < nb) ? wgt[b0] : 0ull;
-            const unsigned long long w1 = (b1 < nb) ? wgt[b1] : 0ull;
-            const unsigned long long ws = w0 + w1;
+            // thread t owns bins BPT t .. BPT t + BPT - 1, wave w the 64 BPT
+            // bins from 64 BPT w.  One barrier for the wave totals; then only
+            // the wave whose bins hold the crossing scans them.
+            constexpr int BPT = 2048 / NT;
+            unsigned long long wb[BPT], ws = 0ull;
+#pragma unroll
+            for (int i = 0; i < BPT; ++i) {
+              wb[i] = (BPT * tid + i < nb) ? wgt[BPT * tid + i] : 0ull;
+              ws += wb[i];
+            }
             const unsigned long long wtot = wave_total_u64(ws);
             if (lane == 0) scan64[wv] = wtot;
             __syncthreads();
-            const unsigned long long tw = scan64[lane & (kSelWaves - 1)];
+            const unsigned long long tw = (wl < NW) ? scan64[wl] : 0ull;
             // The first pass takes in every page (all keys share the bits
             // above the first digit), so its bins sum to Z: the target is
             // set here instead of by a block reduction of its own.
@@ -484,18 +498,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
               need_z = false;
             }
             // weight of the bins of the waves above this one (same in every lane)
-            const unsigned long long above =
-                row16_sum_u64(((lane & (kSelWaves - 1)) > wv) ? tw : 0ull);
+            const unsigned long long above = row16_sum_u64((wl > wv) ? tw : 0ull);
             if (above < T && T <= above + wtot) {
-              const unsigned long long gt1 = above + (wtot - wave_scan_u64(ws));  // above bin b1
-              const unsigned long long gt0 = gt1 + w1;                            // above bin b0
-              if (b1 < nb && gt1 < T && T <= gt1 + w1) {
-                s_bin[buf & 1] = b1;
-                s_wgt[buf & 1] = gt1;
-              }
-              if (b0 < nb && gt0 < T && T <= gt0 + w0) {
-                s_bin[buf & 1] = b0;
-                s_wgt[buf & 1] = gt0;
+              // weight above this thread's highest bin, then down its bins
+              unsigned long long gt = above + (wtot - wave_scan_u64(ws));
+#pragma unroll
+              for (int i = BPT - 1; i >= 0; --i) {
+                const int bi = BPT * tid + i;
+                if (bi < nb && gt < T && T <= gt + wb[i]) {
+                  s_bin[buf & 1] = bi;
+                  s_wgt[buf & 1] = gt;
+                }
+                gt += wb[i];
               }
             }
           }
@@ -591,10 +605,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t incl = wave_scan_u32(packed);
     if (lane == 63) scan32[wv] = incl;
     __syncthreads();
-    const uint32_t tq = scan32[lane & (kSelWaves - 1)];
+    const uint32_t tq = (wl < NW) ? scan32[wl] : 0u;
     const uint32_t tot_packed = row16_u32(tq, OpAddU());
     const uint32_t ex =
-        row16_u32(((lane & (kSelWaves - 1)) < wv) ? tq : 0u, OpAddU()) + incl - packed;
+        row16_u32((wl < wv) ? tq : 0u, OpAddU()) + incl - packed;
     // every thread has its keys in registers by now: reuse keys_lds for the list
     uint32_t gtb = ex >> 16, tb = ex & 0xFFFFu;
 #pragma unroll
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* lp = sel_pages + (int64_t)u * max_pages;
     int32_t* lx = sel_phys + (int64_t)u * max_pages;
     const int32_t* pt = page_table + (int64_t)b * max_pages;
-    for (int i = tid; i < count; i += kSelThreads) {
+    for (int i = tid; i < count; i += NT) {
       const int p = (int)keys_lds[i];
       lp[i] = p;
       if constexpr (kStagePt) lx[i] = ptl[p];
@@ -640,7 +654,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (!s_last) return;
   __threadfence();     // acquire every unit's count
   uint32_t run = 0u, runc = 0u;
-  for (int base = 0; base < U; base += kSelThreads) {
+  for (int base = 0; base < U; base += NT) {
     const int v = base + tid;
     uint32_t c = 0u;
     if (v < U) c = (uint32_t)__hip_atomic_load(sel_counts + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t ch = (min(c, (uint32_t)cap) + (uint32_t)chunk_pages - 1u) / (uint32_t)chunk_pages;
     // both prefix sums in one scan: count in the high word, chunks in the low
     unsigned long long tot;
-    const unsigned long long ex = block_excl_scan<unsigned long long, kSelThreads>(
+    const unsigned long long ex = block_excl_scan<unsigned long long, NT>(
         ((unsigned long long)c << 32) | ch, scan64, tot);
     if (v < U) {
       sel_offsets[v] = (int32_t)(run + (uint32_t)(ex >> 32));
@@ -664,16 +678,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
-template <int NPT, bool COUNT>
+// One workgroup per unit, NT threads, the smallest NPT with NPT * NT >=
+// max_pages (select_threads keeps NPT <= 8 below 1024 threads and >= 8 at
+// 1024, so only those forms are built).
+template <bool COUNT, int NT>
 static void launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
                           const int32_t* page_table, float gamma, int k_pages, int chunk_pages,
                           int hkv, int group, int max_pages, int cap, int32_t* sel_counts,
                           int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
                           int32_t* sel_phys, uint32_t* ticket) {
-  hipLaunchKernelGGL((select_kernel<NPT, COUNT>), dim3(U), dim3(kSelThreads), 0, st, logits,
-                     ctx_lens, page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, cap,
-                     U,
-                     sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket);
+  const int npt = (max_pages + NT - 1) / NT;
+#define SP_SEL(N)                                                                               \
+  hipLaunchKernelGGL((select_kernel<N, COUNT, NT>), dim3(U), dim3(NT), 0, st, logits, ctx_lens, \
+                     page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, cap, U,    \
+                     sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket)
+  if constexpr (NT == 256) {
+    if (npt <= 1) SP_SEL(1);
+    else if (npt <= 2) SP_SEL(2);
+    else if (npt <= 4) SP_SEL(4);
+    else SP_SEL(8);
+  } else if constexpr (NT == 512) {
+    SP_SEL(8);
+  } else {
+    if (npt <= 8) SP_SEL(8);
+    else if (npt <= 16) SP_SEL(16);
+    else SP_SEL(32);
+  }
+#undef SP_SEL
+}
+
+// Threads per selection workgroup for rows of max_pages pages: the fewest of
+// 256, 512 and 1024 that hold the row at 8 pages per thread.  The kernel is a
+// chain of block-wide steps, and with fewer waves each barrier and each LDS
+// combine is shorter; past 8 pages per thread the per-thread work costs more
+// than that saves (timed at 256, 2048 and 8192 pages).
+static int select_threads(int max_pages) {
+  if (max_pages <= 8 * 256) return 256;
+  if (max_pages <= 8 * 512) return 512;
+  return kSelThreads;
 }
 
 template <bool COUNT>
@@ -711,20 +753,17 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
     return SPARSE_ERR_WORKSPACE;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  const int npt = (dims->max_pages + kSelThreads - 1) / kSelThreads;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* ticket = static_cast<uint32_t*>(ws);
-#define SP_SEL(N)                                                                           \
-  launch_select<N, COUNT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages, \
-                          hkv, group, dims->max_pages, list_cap(dims), sel_counts,        \
-                          sel_offsets,                                                      \
-                          chunk_offsets, sel_pages, sel_phys, ticket)
-  if (npt <= 1) SP_SEL(1);
-  else if (npt <= 2) SP_SEL(2);
-  else if (npt <= 4) SP_SEL(4);
-  else if (npt <= 8) SP_SEL(8);
-  else if (npt <= 16) SP_SEL(16);
-  else SP_SEL(32);
+#define SP_SEL(NT)                                                                              \
+  launch_select<COUNT, NT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages,    \
+                           hkv, group, dims->max_pages, list_cap(dims), sel_counts, sel_offsets, \
+                           chunk_offsets, sel_pages, sel_phys, ticket)
+  switch (select_threads(dims->max_pages)) {
+    case 256: SP_SEL(256); break;
+    case 512: SP_SEL(512); break;
+    default: SP_SEL(1024); break;
+  }
 #undef SP_SEL
   return launch_status();
 }
