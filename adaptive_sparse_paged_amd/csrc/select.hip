@@ -681,8 +681,9 @@ __global__ __launch_bounds__(NT) void select_kernel(
 // One workgroup per unit, NT threads, the smallest NPT with NPT * NT >=
 // max_pages (select_threads keeps NPT <= 8 below 1024 threads and >= 8 at
 // 1024, so only those forms are built).
+// Returns false, launching nothing, when the row does not fit NPT * NT.
 template <bool COUNT, int NT>
-static void launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
+static bool launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
                           const int32_t* page_table, float gamma, int k_pages, int chunk_pages,
                           int hkv, int group, int max_pages, int cap, int32_t* sel_counts,
                           int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
@@ -696,15 +697,19 @@ static void launch_select(hipStream_t st, int U, const float* logits, const int3
     if (npt <= 1) SP_SEL(1);
     else if (npt <= 2) SP_SEL(2);
     else if (npt <= 4) SP_SEL(4);
-    else SP_SEL(8);
+    else if (npt <= 8) SP_SEL(8);
+    else return false;
   } else if constexpr (NT == 512) {
-    SP_SEL(8);
+    if (npt <= 8) SP_SEL(8);
+    else return false;
   } else {
     if (npt <= 8) SP_SEL(8);
     else if (npt <= 16) SP_SEL(16);
-    else SP_SEL(32);
+    else if (npt <= 32) SP_SEL(32);
+    else return false;
   }
 #undef SP_SEL
+  return true;
 }
 
 // Threads per selection workgroup for rows of max_pages pages: the fewest of
@@ -759,12 +764,14 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
   launch_select<COUNT, NT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages,    \
                            hkv, group, dims->max_pages, list_cap(dims), sel_counts, sel_offsets, \
                            chunk_offsets, sel_pages, sel_phys, ticket)
+  bool ok;
   switch (select_threads(dims->max_pages)) {
-    case 256: SP_SEL(256); break;
-    case 512: SP_SEL(512); break;
-    default: SP_SEL(1024); break;
+    case 256: ok = SP_SEL(256); break;
+    case 512: ok = SP_SEL(512); break;
+    default: ok = SP_SEL(1024); break;
   }
 #undef SP_SEL
+  if (!ok) return SPARSE_ERR_UNSUPPORTED;
   return launch_status();
 }
 
