@@ -2,13 +2,18 @@
 // ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
 // Hierarchy", MOIRA abstract, sentence on self-planning attention: every block
 // works out from the per-head list lengths which part it handles, so no plan
-// is made on the host and the step stays inside the graph).
+// is made on the host and the step stays inside the graph; and the sentence on
+// FA3/FlashInfer, whose padded lists, unbalanced blocks or host-side plans this
+// avoids).
 //
-// The grid is fixed (one workgroup per possible chunk).  Workgroup c derives
-// its unit and chunk from the list lengths themselves (wave prefix sums over
-// the per-unit chunk counts), takes its even share of the unit's list, and
-// its 4 waves split those pages; each wave runs an online softmax
-// for the unit's G query heads on the bf16 matrix cores:
+// The grid is fixed (W workgroups, W chosen by the caller, typically one per
+// compute unit).  Every workgroup reads the list lengths, lays the step's
+// lists end to end and takes an even 1/W of all their entries -- a slice that
+// may start in one unit's list and end in another's -- so every workgroup has
+// the same number of pages whatever the lengths (balanced plan in common.h).
+// It attends its slice one unit segment at a time; its 4 waves split a
+// segment's pages and each runs an online softmax for the unit's G query
+// heads on the bf16 matrix cores:
 //   QK:  S^T[t][g] = K[t][:] . q[g][:]   v_mfma_f32_16x16x32_bf16, 4 k-slices
 //        (A = K tile rows = tokens, read straight from HBM in 16-byte runs;
 //         B = q of the group, columns = heads)
@@ -18,9 +23,8 @@
 //        into a bf16 high part and a bf16 residual, two products, so the
 //        weights keep ~16 significant bits.
 // The 4 waves' (max, sum, O) are merged in LDS into one normalised partial
-// and its log-sum-exp per head, written to the unit's own slot for that
-// chunk (unit u, chunk i: slot u * ceil(list bound / chunk) + i), so the
-// merge finds a unit's partials without the plan.
+// and its log-sum-exp per head, written to slot u + w (unit u, worker w), so
+// the merge finds a unit's partials from the same lengths.
 
 #include "common.h"
 
@@ -111,59 +115,78 @@ __device__ __forceinline__ void attend_page(PageFrag& f, const bf16x8* qf, bool 
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
-    int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_phys,
-    float scale_log2, int chunk_pages, int hkv, int group, int max_pages, int cap, int U,
-    int unit_parts, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
-  const int c = blockIdx.x;
-  int u, local;
-  plan_locate(sel_counts, U, cap, chunk_pages, c, u, local);
-  u = __builtin_amdgcn_readfirstlane(u);
-  local = __builtin_amdgcn_readfirstlane(local);
-  if (u < 0) return;                   // past the last chunk of the step
-  const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
-  const int b = u / hkv, h = u - (u / hkv) * hkv;
-  const int L = __builtin_amdgcn_readfirstlane(min(max(ctx_lens[b], 0), max_pages * kP));
-  const int cnt = __builtin_amdgcn_readfirstlane(min(sel_counts[u], cap));
-  // The unit's ceil(cnt / chunk_pages) chunks share its list evenly (sizes
-  // differ by at most one page), so no chunk is a short remainder.
-  const int nch = (cnt + chunk_pages - 1) / chunk_pages;
-  const int i0 = (int)(((int64_t)local * cnt) / nch);
-  const int i1 = (int)(((int64_t)(local + 1) * cnt) / nch);
-  const int32_t* lp = sel_pages + (int64_t)u * max_pages;
-  const int32_t* lx = sel_phys + (int64_t)u * max_pages;
+// One unit segment of a workgroup's slice: unit u's list entries [i0, i1).
+// seg_begin issues the segment's first loads (context length, the first 64
+// list ids of each wave, q) in one round trip and returns without waiting
+// for them.  Every load is unconditional (an index past the
+// segment re-reads its last entry, a padding column of q re-reads the
+// group's last head and is zeroed when used): a load under a condition
+// becomes a branch that waits for it.
+struct Seg {
+  int u, b, h, L, i0, i1;
+  int pl, xl;        // lane k: logical / physical id of this wave's k-th page of the batch
+  u32x4 qw[4];       // lane (g, j): q of head min(g, G - 1), channels 32 s + 8 j .. +7
+};
 
+__device__ __forceinline__ void seg_begin(Seg& S, const uint16_t* __restrict__ q,
+                                          const int32_t* __restrict__ ctx_lens,
+                                          const int32_t* __restrict__ sel_pages,
+                                          const int32_t* __restrict__ sel_phys, int hkv,
+                                          int group, int max_pages, int u, int i0, int i1) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
+  S.u = u;
+  S.b = u / hkv;
+  S.h = u - S.b * hkv;
+  S.i0 = i0;
+  S.i1 = i1;
+  S.L = __builtin_amdgcn_readfirstlane(min(max(ctx_lens[S.b], 0), max_pages * kP));
+  const int64_t rowoff = (int64_t)u * max_pages;
+  const int ie = min(i0 + wv + kAttnWaves * lane, i1 - 1);
+  S.pl = sel_pages[rowoff + ie];
+  S.xl = sel_phys[rowoff + ie];
+  const uint16_t* qrow =
+      q + ((int64_t)S.b * hkv * group + S.h * group + min(row, group - 1)) * kD + 8 * j;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) S.qw[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
+}
+
+// The segment's pages: each wave takes list entries i0 + wv + 4k and runs an
+// online softmax over them (m_run, l_run, o).  The ids are read 64 at a time
+// into lanes k and broadcast with readlane, so no KV load waits on a list
+// load; each batch's ids are loaded while the previous batch is attended.
+__device__ __forceinline__ void seg_pages(Seg& S, const uint16_t* __restrict__ kv,
+                                          int64_t stride_page, int64_t stride_head,
+                                          int64_t pool_pages,
+                                          const int32_t* __restrict__ sel_pages,
+                                          const int32_t* __restrict__ sel_phys, float scale_log2,
+                                          int group, int max_pages, float& m_run, float& l_run,
+                                          floatx4 (&o)[8]) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
+  const bool gok = row < group;
+  const int h = S.h, L = S.L, i0 = S.i0, i1 = S.i1;
+  const int32_t* lp = sel_pages + (int64_t)S.u * max_pages;
+  const int32_t* lx = sel_phys + (int64_t)S.u * max_pages;
+  int pl = S.pl, xl = S.xl;
+  asm volatile("" : "+v"(pl), "+v"(xl));
   // B operand of QK: q of head g = row (zero for padding columns).
-  const int g = row;
-  const bool gok = g < group;
   bf16x8 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (gok)
-      w = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hkv * group + h * group + g) * kD +
-                                          32 * s + 8 * j);
-    qf[s] = as_bf16x8(w);
+    u32x4 w = S.qw[s];
+    asm volatile("" : "+v"(w));
+    qf[s] = as_bf16x8(gok ? w : u32x4{0u, 0u, 0u, 0u});
   }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  floatx4 o[8];
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // This wave's pages are list entries i0 + wv + 4k.  Their logical and
-  // physical ids are read once per 64 pages into lanes k and broadcast with
-  // readlane, so no KV load waits on a list load.
   const int nk = (i1 - i0 - wv + kAttnWaves - 1) / kAttnWaves;
   for (int base = 0; base < nk; base += 64) {
     const int cnt_k = min(64, nk - base);
-    const int ie = i0 + wv + kAttnWaves * (base + lane);
-    const int pl = (lane < cnt_k) ? lp[ie] : -1;
-    const int xl = (lane < cnt_k) ? lx[ie] : -1;
+    const int ie_next = min(i0 + wv + kAttnWaves * (base + 64 + lane), i1 - 1);
+    const int pl_next = lp[ie_next];
+    const int xl_next = lx[ie_next];
     // Two page buffers in turn, so a page's loads are in flight while the
     // other page is attended and no register copy waits on them.  In the
     // steady-state loop every load is unconditional (a branch around a load
@@ -189,9 +212,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     } else {
       attend_page(fa, qf, gok, j, scale_log2, m_run, l_run, o);
     }
+    pl = pl_next;
+    xl = xl_next;
   }
+}
 
-  // ---- merge the waves of the workgroup ------------------------------------
+// Merge the 4 waves' (max, sum, O) in LDS into one normalised partial and
+// its log-sum-exp per head, written to `slot`.  All 256 threads call it.
+__device__ __forceinline__ void seg_end(float m_run, float l_run, const floatx4 (&o)[8],
+                                        int group, int64_t slot, float* smem,
+                                        float* __restrict__ part_o,
+                                        float* __restrict__ part_lse) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6, g = lane & 15, j = lane >> 4;
+  const bool gok = g < group;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   float* so = smem;                                   // [kAttnWaves][group][kD]
@@ -225,19 +258,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         den += a * sl[w * group + gg];
       }
     }
-    // unit u's chunks have the fixed slots u * unit_parts + local
-    const int64_t slot = ((int64_t)u * unit_parts + local) * group + gg;
-    part_o[slot * kD + d] = (den > 0.f) ? num / den : 0.f;
-    if (d == 0) part_lse[slot] = (den > 0.f) ? (M + log2f(den)) * ln2 : -INFINITY;
+    const int64_t r = slot * group + gg;
+    part_o[r * kD + d] = (den > 0.f) ? num / den : 0.f;
+    if (d == 0) part_lse[r] = (den > 0.f) ? (M + log2f(den)) * ln2 : -INFINITY;
+  }
+  __syncthreads();   // the LDS is reused by the workgroup's next segment
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
+    int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_phys, float scale_log2, int hkv, int group, int max_pages,
+    int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
+  const int w = blockIdx.x;
+  int x, e, u, off, len;
+  {
+    PlanSeg first;
+    const int total = __builtin_amdgcn_readfirstlane(plan_total(sel_counts, U, cap, first));
+    const int W = plan_workers(total, wmax);
+    if (w >= W) return;                // the step has too few pages for this worker
+    x = plan_start(w, W, total);
+    e = plan_start(w + 1, W, total);
+    plan_find(sel_counts, U, cap, first, x, u, off, len);
+  }
+  u = __builtin_amdgcn_readfirstlane(u);
+  off = __builtin_amdgcn_readfirstlane(off);
+  len = __builtin_amdgcn_readfirstlane(len);
+  if (u < 0) return;                   // (x < T always lies in some unit)
+  Seg cur;
+  seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, x - off,
+            min(e, off + len) - off);
+  // Segment by segment.  After the first, the next unit is u + 1 (its length
+  // loaded at the segment's start), skipping empty lists.  x < e <= T, so a
+  // later unit holds position x whenever the loop goes on; the u < U - 1
+  // test only guards against lengths changed under the kernel.  (Issuing the
+  // next segment's loads before this one's epilogue gains nothing: the
+  // epilogue's workgroup barrier waits for every load still in flight.)
+  while (true) {
+    const int next_raw = sel_counts[min(u + 1, U - 1)];
+    float m_run, l_run;
+    floatx4 o[8];
+    seg_pages(cur, kv, stride_page, stride_head, pool_pages, sel_pages, sel_phys, scale_log2,
+              group, max_pages, m_run, l_run, o);
+    seg_end(m_run, l_run, o, group, (int64_t)cur.u + w, smem, part_o, part_lse);
+    x = off + cur.i1;
+    if (x >= e) break;
+    off += len;
+    ++u;
+    len = min(max(next_raw, 0), cap);
+    while (len == 0 && u < U - 1) {
+      ++u;
+      len = min(max(sel_counts[u], 0), cap);
+    }
+    if (len == 0) break;
+    seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, x - off,
+              min(e, off + len) - off);
   }
 }
 
 }  // namespace sp
 
-extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages) {
-  if (sp::check_dims(dims) != SPARSE_OK || chunk_pages < 1) return -1;
-  const int64_t U = (int64_t)dims->batch * dims->num_kv_heads;
-  return U * ((sp::list_cap(dims) + chunk_pages - 1) / chunk_pages);
+extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t workers) {
+  if (sp::check_dims(dims) != SPARSE_OK || workers < 0) return -1;
+  const int wmax = sp::resolve_workers(workers);
+  if (wmax < 1) return -1;
+  return (int64_t)dims->batch * dims->num_kv_heads + wmax;
 }
 
 extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q,
@@ -245,7 +332,7 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
                                             int64_t stride_head, int64_t pool_pages,
                                             const int32_t* ctx_lens, const int32_t* sel_counts,
                                             const int32_t* sel_pages, const int32_t* sel_phys,
-                                            float scale, int32_t chunk_pages, float* part_o,
+                                            float scale, int32_t workers, float* part_o,
                                             float* part_lse, int64_t max_parts, void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
@@ -254,17 +341,18 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
     return SPARSE_ERR_INVALID;
   if (!sp::aligned(q, 16) || !sp::aligned(part_o, 16) || !isfinite(scale))
     return SPARSE_ERR_INVALID;
-  if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
-  if (max_parts != sparse_decode_max_parts(dims, chunk_pages)) return SPARSE_ERR_INVALID;
-  if (max_parts > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
+  if (workers < 0 || workers > sp::kMaxWorkers) return SPARSE_ERR_INVALID;
+  const int wmax = sp::resolve_workers(workers);
+  if (wmax < 1) return SPARSE_ERR_HIP;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
+  if (max_parts != (int64_t)U + wmax) return SPARSE_ERR_INVALID;
+  if ((int64_t)U * dims->max_pages > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
   const size_t lds = sizeof(float) * (size_t)sp::kAttnWaves * group * (sp::kD + 2);
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)max_parts), dim3(256), lds,
-                     (hipStream_t)stream, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
-                     sel_counts, sel_pages, sel_phys, scale_log2, chunk_pages, hkv,
-                     group, dims->max_pages, sp::list_cap(dims), U,
-                     (sp::list_cap(dims) + chunk_pages - 1) / chunk_pages, part_o, part_lse);
+  hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)wmax), dim3(256), lds, (hipStream_t)stream,
+                     q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
+                     sel_pages, sel_phys, scale_log2, hkv, group, dims->max_pages,
+                     sp::list_cap(dims), U, wmax, part_o, part_lse);
   return sp::launch_status();
 }

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/sparse_paged.h"
 
 namespace sp {
@@ -90,17 +92,22 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
   return total;
 }
 
-// ---- the chunk plan, derived on the device from the list lengths ------------
-// Unit u's list of k_u = min(count_u, cap) pages (cap: the dims' list bound)
-// has ceil(k_u / chunk) chunks (the attention shares the list evenly over
-// them).  Chunks are numbered over every unit's first floor(k_u / chunk)
-// chunks (unit order), then the last chunk of each unit that chunk does not
-// divide (unit order), so the grid's last workgroups -- the ones that run
-// while the rest of the chip drains -- include every unit shorter than one
-// chunk.  A wave derives where chunk c falls with one round of
-// loads (lane l reads the counts of units l*8 .. l*8+7 of each 512-unit
-// segment) and wave prefix sums -- no host plan and no precomputed offsets.
-constexpr int kPlanVU = 8;
+// ---- the balanced plan, derived on the device from the list lengths -------
+// The step's T = sum_u k_u list entries (k_u = min(count_u, cap), cap the
+// dims' list bound) are laid end to end in unit order: entry e of unit u sits
+// at global position off_u + e, off_u = sum_{v<u} k_v.  W workers share them
+// evenly: worker w owns positions [floor(w T / W), floor((w + 1) T / W)),
+// crossing unit boundaries where they fall, and writes one partial per unit
+// it touches, in slot u + w (unit and worker indices both grow along the
+// positions, so the slots of distinct (unit, worker) pairs differ and every
+// slot is below U + W).  W is the grid size the caller gave, cut to
+// ceil(T / kMinWorkerPages) so short steps do not spread a few pages over
+// hundreds of workgroups; every worker then owns at least one entry.
+// Everything here is computed by each wave from sel_counts alone: no host
+// plan and no precomputed offsets.
+constexpr int kPlanVU = 8;                  // units per lane in one scan segment
+constexpr int kPlanSeg = 64 * kPlanVU;      // units per scan segment
+constexpr int kMinWorkerPages = SPARSE_ATTN_MIN_WORKER_PAGES;
 
 // List lengths of units base .. base + kPlanVU - 1, clamped to [0, cap]
 // (0 past the last unit).  The loads are unconditional -- an index past the
@@ -121,74 +128,117 @@ __device__ __forceinline__ void plan_counts8(const int32_t* __restrict__ counts,
   }
 }
 
-// Within one 512-unit segment whose lane-l units (seg + 8l ..) hold ch[v]
-// chunks of this numbering pass (per-lane sum s, inclusive wave prefix incl,
-// `before` chunks numbered ahead of the segment): if chunk c falls in it,
-// set unit and local (wave-uniform) and return true.
-__device__ __forceinline__ bool plan_find(int c, int before, int seg, const int (&ch)[kPlanVU],
-                                          const int (&k)[kPlanVU], int s, int incl, bool full,
-                                          int chunk, int& unit, int& local) {
-  const int lane = lane_id();
-  if (c >= before + __shfl(incl, 63, 64)) return false;
-  const unsigned long long hit_mask = __ballot(before + incl > c);
+// One scan segment of units seg .. seg + kPlanSeg - 1 held by a wave: lane l
+// has the lengths of units seg + 8l .. seg + 8l + 7, their sum s and the
+// inclusive wave prefix incl of s; total is the segment's sum (wave-uniform).
+struct PlanSeg {
+  int k[kPlanVU];
+  int s, incl, total;
+};
+
+__device__ __forceinline__ void plan_load(PlanSeg& P, const int32_t* __restrict__ counts,
+                                          int seg, int U, int cap) {
+  plan_counts8(counts, seg + lane_id() * kPlanVU, U, cap, P.k);
+  int s = 0;
+#pragma unroll
+  for (int v = 0; v < kPlanVU; ++v) s += P.k[v];
+  P.s = s;
+  P.incl = wave_incl_scan(s);
+  P.total = __shfl(P.incl, 63, 64);
+}
+
+// If global position x falls in segment P (which starts at global position
+// `before`), set the unit holding it, that unit's first position and its
+// length (wave-uniform) and return true.
+__device__ __forceinline__ bool plan_seg_find(const PlanSeg& P, int seg, int before, int x,
+                                              int& unit, int& off, int& len) {
+  if (x >= before + P.total) return false;
+  const unsigned long long hit_mask = __ballot(before + P.incl > x);
   const int hit = __ffsll((long long)hit_mask) - 1;
-  int acc = before + incl - s, fu = -1, fl = 0;
+  int acc = before + P.incl - P.s, fu = -1, fo = 0, fl = 0;
 #pragma unroll
   for (int v = 0; v < kPlanVU; ++v) {
-    if (fu < 0 && c < acc + ch[v]) {
-      fu = seg + lane * kPlanVU + v;
-      fl = full ? c - acc : k[v] / chunk;
+    if (fu < 0 && x < acc + P.k[v]) {
+      fu = seg + lane_id() * kPlanVU + v;
+      fo = acc;
+      fl = P.k[v];
     }
-    acc += ch[v];
+    acc += P.k[v];
   }
   unit = __builtin_amdgcn_readlane(fu, hit);
-  local = __builtin_amdgcn_readlane(fl, hit);
+  off = __builtin_amdgcn_readlane(fo, hit);
+  len = __builtin_amdgcn_readlane(fl, hit);
   return true;
 }
 
-// Unit of global chunk c and the chunk's index within that unit (unit = -1
-// when c is past the last chunk).  Wave-uniform results; every lane calls.
-__device__ __forceinline__ void plan_locate(const int32_t* __restrict__ counts, int U,
-                                            int cap, int chunk, int c, int& unit,
-                                            int& local) {
-  const int lane = lane_id();
+// T, the step's total list entries.  `first` receives segment 0 (units
+// 0 .. 511), which is all of them when U <= 512.
+__device__ __forceinline__ int plan_total(const int32_t* __restrict__ counts, int U, int cap,
+                                          PlanSeg& first) {
+  plan_load(first, counts, 0, U, cap);
+  int total = first.total;
+  for (int seg = kPlanSeg; seg < U; seg += kPlanSeg) {
+    PlanSeg P;
+    plan_load(P, counts, seg, U, cap);
+    total += P.total;
+  }
+  return total;
+}
+
+// The unit holding global position x < T (with its first position and
+// length).  Segment 0 comes from registers; later segments are reloaded.
+__device__ __forceinline__ void plan_find(const int32_t* __restrict__ counts, int U, int cap,
+                                          const PlanSeg& first, int x, int& unit, int& off,
+                                          int& len) {
   unit = -1;
-  local = 0;
-  int k[kPlanVU], ch[kPlanVU], cp[kPlanVU];
-  if (U <= 64 * kPlanVU) {
-    // one segment: a single round of loads serves both numbering passes
-    plan_counts8(counts, lane * kPlanVU, U, cap, k);
-    int sf = 0, sp = 0;
-#pragma unroll
-    for (int v = 0; v < kPlanVU; ++v) {
-      ch[v] = k[v] / chunk;
-      cp[v] = (k[v] % chunk != 0) ? 1 : 0;
-      sf += ch[v];
-      sp += cp[v];
-    }
-    const int inf = wave_incl_scan(sf), inp = wave_incl_scan(sp);
-    const int full_total = __shfl(inf, 63, 64);
-    if (plan_find(c, 0, 0, ch, k, sf, inf, true, chunk, unit, local)) return;
-    plan_find(c, full_total, 0, cp, k, sp, inp, false, chunk, unit, local);
-    return;
+  off = len = 0;
+  if (plan_seg_find(first, 0, 0, x, unit, off, len)) return;
+  int before = first.total;
+  for (int seg = kPlanSeg; seg < U; seg += kPlanSeg) {
+    PlanSeg P;
+    plan_load(P, counts, seg, U, cap);
+    if (plan_seg_find(P, seg, before, x, unit, off, len)) return;
+    before += P.total;
   }
-  // pass 0: the full chunks of every unit; pass 1: one partial chunk per
-  // unit whose length chunk does not divide
-  int before = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int seg = 0; seg < U; seg += 64 * kPlanVU) {
-      plan_counts8(counts, seg + lane * kPlanVU, U, cap, k);
-      int s = 0;
+}
+
+// Unit u's first global position, its length and T (wave-uniform).
+__device__ __forceinline__ void plan_unit(const int32_t* __restrict__ counts, int U, int cap,
+                                          int u, int& off, int& len, int& total) {
+  total = 0;
+  off = len = 0;
+  for (int seg = 0; seg < U; seg += kPlanSeg) {
+    PlanSeg P;
+    plan_load(P, counts, seg, U, cap);
+    if (u >= seg && u < seg + kPlanSeg) {
+      const int l = (u - seg) / kPlanVU, v = (u - seg) % kPlanVU;
+      int pre = P.incl - P.s, mine = 0;
 #pragma unroll
-      for (int v = 0; v < kPlanVU; ++v) {
-        ch[v] = pass == 0 ? k[v] / chunk : (k[v] % chunk != 0 ? 1 : 0);
-        s += ch[v];
+      for (int i = 0; i < kPlanVU; ++i) {
+        pre += (i < v) ? P.k[i] : 0;
+        mine = (i == v) ? P.k[i] : mine;
       }
-      const int incl = wave_incl_scan(s);
-      if (plan_find(c, before, seg, ch, k, s, incl, pass == 0, chunk, unit, local)) return;
-      before += __shfl(incl, 63, 64);
+      off = total + __builtin_amdgcn_readlane(pre, l);
+      len = __builtin_amdgcn_readlane(mine, l);
     }
+    total += P.total;
   }
+}
+
+// Workers the plan uses for T entries with a grid of wmax workgroups.
+__device__ __forceinline__ int plan_workers(int total, int wmax) {
+  if (total <= 0) return 0;
+  return min(wmax, (total + kMinWorkerPages - 1) / kMinWorkerPages);
+}
+
+// First position owned by worker w (of W over T entries).
+__device__ __forceinline__ int plan_start(int w, int W, int total) {
+  return (int)(((int64_t)w * total) / W);
+}
+
+// The worker that owns position x (the largest w with plan_start(w) <= x).
+__device__ __forceinline__ int plan_owner(int x, int W, int total) {
+  return (int)((((int64_t)x + 1) * W - 1) / total);
 }
 
 // ---- host-side argument checks ----------------------------------------------
@@ -200,13 +250,16 @@ inline sparse_status check_dims(const sparse_dims* d) {
     return SPARSE_ERR_INVALID;
   if (d->num_q_heads % d->num_kv_heads != 0) return SPARSE_ERR_INVALID;
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (d->head_dim != kD || d->page_size != kP || G > kMaxGroup || d->max_pages > kMaxPages)
+  // G in {1, 2, 4, 8, 16}: the kernels' head loops and row layouts assume a
+  // power of two
+  if (d->head_dim != kD || d->page_size != kP || G > kMaxGroup || (G & (G - 1)) != 0 ||
+      d->max_pages > kMaxPages)
     return SPARSE_ERR_UNSUPPORTED;
   if (d->max_list_pages < 0 || d->max_list_pages > d->max_pages) return SPARSE_ERR_INVALID;
   return SPARSE_OK;
 }
 
-// The length every page list is planned for (attention and merge).
+// The length every page list is clamped to (attention and merge).
 inline int list_cap(const sparse_dims* d) {
   return d->max_list_pages > 0 ? d->max_list_pages : d->max_pages;
 }
@@ -217,6 +270,25 @@ inline sparse_status check_pool(const void* kv, int64_t stride_page, int64_t str
   if (!aligned(kv, 16) || (stride_page % 8) != 0 || (stride_head % 8) != 0)
     return SPARSE_ERR_INVALID;
   return SPARSE_OK;
+}
+
+// Attention workgroups for a caller's `workers`: itself when positive, else
+// one per compute unit of the current device (queried once per device).
+// Returns -1 when the device cannot be queried.
+constexpr int kMaxWorkers = 1 << 20;
+inline int resolve_workers(int workers) {
+  if (workers > 0) return workers;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  static std::atomic<int> cus[64];
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n < 1) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      return -1;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 inline sparse_status launch_status() {

@@ -1,4 +1,4 @@
-// Log-sum-exp merge of the per-chunk attention partials of every unit:
+// Log-sum-exp merge of the per-segment attention partials of every unit:
 //   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) o_c,
 // the identity that makes splitting a page list over several workgroups exact.
 
@@ -7,47 +7,53 @@
 namespace sp {
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeSlots = kMergeThreads / 32;   // chunks read side by side
+constexpr int kMergeSlots = kMergeThreads / 32;   // segments read side by side
 
-// One 256-thread workgroup per (unit, query head).  Unit u's chunks sit in
-// the fixed slots u * unit_parts + [0, chunks of u), so the unit's length and
-// the first round of partials are loaded together in one round trip.  Thread
-// t reads channel quad t % 32 of chunks t / 32, t / 32 + 8, ... (each chunk's
-// 128 floats are one coalesced 512-byte read by 32 threads), keeping an
-// online (max, sum, weighted sum); the 8 chunk slots are then combined
-// through LDS.  (1024 threads ran 4.7 against 4.4 us on 4 x 131072 tokens
-// and 15.3 against 7.0 us on 64 ragged requests: most of their slots had
-// no chunk, and fewer workgroups fit a compute unit.)
+// One 256-thread workgroup per (unit, query head).  The unit's partials are
+// those of the workers its list entries fall to under the balanced plan: the
+// slots u + w for w from the owner of its first entry to the owner of its
+// last, found from the list lengths alone (one round of loads of the
+// lengths, then one of the partials).  Thread t reads channel quad t % 32 of
+// segments t / 32, t / 32 + 8, ... (each segment's 128 floats are one
+// coalesced 512-byte read by 32 threads), keeping an online (max, sum,
+// weighted sum); the 8 segment slots are then combined through LDS.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ sel_counts, int cap, int chunk, int unit_parts, int hkv,
-    int group, float* __restrict__ out, float* __restrict__ out_lse) {
+    const int32_t* __restrict__ sel_counts, int cap, int U, int wmax, int hkv, int group,
+    float* __restrict__ out, float* __restrict__ out_lse) {
   __shared__ floatx4 s_acc[kMergeSlots][32];
   __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
   const int u = blockIdx.x, g = blockIdx.y;
   const int b = u / hkv, h = u - (u / hkv) * hkv;
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
-  const int64_t c0 = (int64_t)u * unit_parts;
-  const int count = sel_counts[u];
+  int off, len, total;
+  plan_unit(sel_counts, U, cap, u, off, len, total);
+  off = __builtin_amdgcn_readfirstlane(off);
+  len = __builtin_amdgcn_readfirstlane(len);
+  total = __builtin_amdgcn_readfirstlane(total);
+  int w_lo = 0, nseg = 0;
+  if (len > 0) {
+    const int W = plan_workers(total, wmax);
+    w_lo = plan_owner(off, W, total);
+    nseg = plan_owner(off + len - 1, W, total) - w_lo + 1;
+  }
+  const int64_t c0 = (int64_t)u + w_lo;   // segment i of the unit is slot c0 + i
 
   float m = -INFINITY, s = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  int nch = unit_parts;   // refined once the count has arrived
-  for (int i = slot; i < nch; i += 2 * kMergeSlots) {
-    // Both slots' loads are issued before any is used; indices past the
-    // unit's slots are clamped to its last slot (read, then discarded).  The
+  for (int i = slot; i < nseg; i += 2 * kMergeSlots) {
+    // Both slots' loads are issued before any is used; an index past the
+    // unit's segments is clamped to its last one (read, then discarded).  The
     // empty asm statements keep the compiler from moving a load under a test,
     // where it would become a branch that waits for it.
     const int i1 = i + kMergeSlots;
     const int64_t r0 = (c0 + i) * group + g;
-    const int64_t r1 = (c0 + min(i1, unit_parts - 1)) * group + g;
+    const int64_t r1 = (c0 + min(i1, nseg - 1)) * group + g;
     float l0 = part_lse[r0], l1 = part_lse[r1];
     floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
     floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
     asm volatile("" : "+v"(l0), "+v"(l1), "+v"(o0), "+v"(o1));
-    nch = (min(max(count, 0), cap) + chunk - 1) / chunk;
-    if (i >= nch) break;
-    if (i1 >= nch) l1 = -INFINITY;
+    if (i1 >= nseg) l1 = -INFINITY;
     const float mn = fmaxf(m, fmaxf(l0, l1));
     if (mn == -INFINITY) continue;
     const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
@@ -90,20 +96,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 
 extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                              const float* part_lse, const int32_t* sel_counts,
-                                             int32_t chunk_pages, float* out, float* out_lse,
+                                             int32_t workers, float* out, float* out_lse,
                                              void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!part_o || !part_lse || !sel_counts || !out || !out_lse)
     return SPARSE_ERR_INVALID;
   if (!sp::aligned(part_o, 16) || !sp::aligned(out, 16)) return SPARSE_ERR_INVALID;
-  if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
+  if (workers < 0 || workers > sp::kMaxWorkers) return SPARSE_ERR_INVALID;
+  const int wmax = sp::resolve_workers(workers);
+  if (wmax < 1) return SPARSE_ERR_HIP;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  const int cap = sp::list_cap(dims);
   hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
-                     (hipStream_t)stream, part_o, part_lse, sel_counts, cap, chunk_pages,
-                     (cap + chunk_pages - 1) / chunk_pages, hkv, group, out, out_lse);
+                     (hipStream_t)stream, part_o, part_lse, sel_counts, sp::list_cap(dims), U,
+                     wmax, hkv, group, out, out_lse);
   return sp::launch_status();
 }
 

@@ -26,9 +26,9 @@
 //      == tau, r = ceil((T - W(key > tau)) / w_tau); compact in ascending page
 //      order by one block prefix sum of packed (above, tie) counts.
 //   5. optionally, the last workgroup to finish (device ticket) writes the
-//      prefix sums of the counts and of the chunk counts over all units, then
-//      re-arms the ticket (the attention and merge plan from the counts
-//      alone and do not read them).
+//      exclusive prefix sum of the counts over all units, then re-arms the
+//      ticket (the attention and merge plan from the counts alone and do not
+//      read it).
 
 #include "common.h"
 
@@ -221,11 +221,9 @@ __device__ __forceinline__ void head_totals(const float (*part)[kSelWaves], int 
 template <int NPT, bool COUNT, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ page_table, float gamma, int k_pages, int chunk_pages, int hkv,
-    int group,
-    int max_pages, int cap, int U, int32_t* __restrict__ sel_counts,
-    int32_t* __restrict__ sel_offsets,
-    int32_t* __restrict__ chunk_offsets, int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ page_table, float gamma, int k_pages, int hkv, int group,
+    int max_pages, int U, int32_t* __restrict__ sel_counts,
+    int32_t* __restrict__ sel_offsets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_phys, uint32_t* __restrict__ ticket) {
   // NT threads in NW waves; a workgroup takes rows of up to NPT * NT pages.
   constexpr int NW = NT / 64;
@@ -653,27 +651,20 @@ __global__ __launch_bounds__(NT) void select_kernel(
   __syncthreads();
   if (!s_last) return;
   __threadfence();     // acquire every unit's count
-  uint32_t run = 0u, runc = 0u;
+  unsigned long long run = 0ull;
   for (int base = 0; base < U; base += NT) {
     const int v = base + tid;
-    uint32_t c = 0u;
-    if (v < U) c = (uint32_t)__hip_atomic_load(sel_counts + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // chunks as the attention plans them: lists beyond the dims' bound are cut
-    const uint32_t ch = (min(c, (uint32_t)cap) + (uint32_t)chunk_pages - 1u) / (uint32_t)chunk_pages;
-    // both prefix sums in one scan: count in the high word, chunks in the low
+    unsigned long long c = 0ull;
+    if (v < U)
+      c = (unsigned long long)__hip_atomic_load(sel_counts + v, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     unsigned long long tot;
-    const unsigned long long ex = block_excl_scan<unsigned long long, NT>(
-        ((unsigned long long)c << 32) | ch, scan64, tot);
-    if (v < U) {
-      sel_offsets[v] = (int32_t)(run + (uint32_t)(ex >> 32));
-      chunk_offsets[v] = (int32_t)(runc + (uint32_t)ex);
-    }
-    run += (uint32_t)(tot >> 32);
-    runc += (uint32_t)tot;
+    const unsigned long long ex = block_excl_scan<unsigned long long, NT>(c, scan64, tot);
+    if (v < U) sel_offsets[v] = (int32_t)(run + ex);
+    run += tot;
   }
   if (tid == 0) {
     sel_offsets[U] = (int32_t)run;
-    chunk_offsets[U] = (int32_t)runc;
     __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -684,15 +675,15 @@ __global__ __launch_bounds__(NT) void select_kernel(
 // Returns false, launching nothing, when the row does not fit NPT * NT.
 template <bool COUNT, int NT>
 static bool launch_select(hipStream_t st, int U, const float* logits, const int32_t* ctx_lens,
-                          const int32_t* page_table, float gamma, int k_pages, int chunk_pages,
-                          int hkv, int group, int max_pages, int cap, int32_t* sel_counts,
-                          int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
+                          const int32_t* page_table, float gamma, int k_pages, int hkv,
+                          int group, int max_pages, int32_t* sel_counts,
+                          int32_t* sel_offsets, int32_t* sel_pages,
                           int32_t* sel_phys, uint32_t* ticket) {
   const int npt = (max_pages + NT - 1) / NT;
 #define SP_SEL(N)                                                                               \
   hipLaunchKernelGGL((select_kernel<N, COUNT, NT>), dim3(U), dim3(NT), 0, st, logits, ctx_lens, \
-                     page_table, gamma, k_pages, chunk_pages, hkv, group, max_pages, cap, U,    \
-                     sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ticket)
+                     page_table, gamma, k_pages, hkv, group, max_pages, U, sel_counts,       \
+                     sel_offsets, sel_pages, sel_phys, ticket)
   if constexpr (NT == 256) {
     if (npt <= 1) SP_SEL(1);
     else if (npt <= 2) SP_SEL(2);
@@ -726,8 +717,7 @@ static int select_threads(int max_pages) {
 template <bool COUNT>
 static sparse_status select_entry(const sparse_dims* dims, const float* logits,
                                   const int32_t* ctx_lens, const int32_t* page_table, float gamma,
-                                  int k_pages, int32_t chunk_pages, int32_t* sel_counts,
-                                  int32_t* sel_offsets, int32_t* chunk_offsets,
+                                  int k_pages, int32_t* sel_counts, int32_t* sel_offsets,
                                   int32_t* sel_pages, int32_t* sel_phys, void* ws,
                                   size_t ws_bytes, void* stream);
 
@@ -743,16 +733,13 @@ namespace sp {
 template <bool COUNT>
 static sparse_status select_entry(const sparse_dims* dims, const float* logits,
                                   const int32_t* ctx_lens, const int32_t* page_table, float gamma,
-                                  int k_pages, int32_t chunk_pages, int32_t* sel_counts,
-                                  int32_t* sel_offsets, int32_t* chunk_offsets,
+                                  int k_pages, int32_t* sel_counts, int32_t* sel_offsets,
                                   int32_t* sel_pages, int32_t* sel_phys, void* ws,
                                   size_t ws_bytes, void* stream) {
   sparse_status st = check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!logits || !ctx_lens || !page_table || !sel_counts || !sel_pages || !sel_phys)
     return SPARSE_ERR_INVALID;
-  if ((sel_offsets == nullptr) != (chunk_offsets == nullptr)) return SPARSE_ERR_INVALID;
-  if (chunk_pages < 1 || chunk_pages > dims->max_pages) return SPARSE_ERR_INVALID;
   if (sel_offsets != nullptr &&
       (!ws || ws_bytes < sparse_select_workspace_bytes(dims) || !aligned(ws, 4)))
     return SPARSE_ERR_WORKSPACE;
@@ -761,9 +748,8 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
   hipStream_t s = (hipStream_t)stream;
   uint32_t* ticket = static_cast<uint32_t*>(ws);
 #define SP_SEL(NT)                                                                              \
-  launch_select<COUNT, NT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, chunk_pages,    \
-                           hkv, group, dims->max_pages, list_cap(dims), sel_counts, sel_offsets, \
-                           chunk_offsets, sel_pages, sel_phys, ticket)
+  launch_select<COUNT, NT>(s, U, logits, ctx_lens, page_table, gamma, k_pages, hkv, group,     \
+                           dims->max_pages, sel_counts, sel_offsets, sel_pages, sel_phys, ticket)
   bool ok;
   switch (select_threads(dims->max_pages)) {
     case 256: ok = SP_SEL(256); break;
@@ -779,26 +765,22 @@ static sparse_status select_entry(const sparse_dims* dims, const float* logits,
 
 extern "C" sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
                                                 const int32_t* ctx_lens, const int32_t* page_table,
-                                                float gamma, int32_t chunk_pages,
-                                                int32_t* sel_counts, int32_t* sel_offsets,
-                                                int32_t* chunk_offsets, int32_t* sel_pages,
+                                                float gamma, int32_t* sel_counts,
+                                                int32_t* sel_offsets, int32_t* sel_pages,
                                                 int32_t* sel_phys, void* ws, size_t ws_bytes,
                                                 void* stream) {
   if (!(gamma > 0.0f && gamma <= 1.0f)) return SPARSE_ERR_INVALID;
-  return sp::select_entry<false>(dims, logits, ctx_lens, page_table, gamma, 0, chunk_pages,
-                                 sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ws,
-                                 ws_bytes, stream);
+  return sp::select_entry<false>(dims, logits, ctx_lens, page_table, gamma, 0, sel_counts,
+                                 sel_offsets, sel_pages, sel_phys, ws, ws_bytes, stream);
 }
 
 extern "C" sparse_status sparse_select_topk(const sparse_dims* dims, const float* logits,
                                             const int32_t* ctx_lens, const int32_t* page_table,
-                                            int32_t k_pages, int32_t chunk_pages,
-                                            int32_t* sel_counts, int32_t* sel_offsets,
-                                            int32_t* chunk_offsets, int32_t* sel_pages,
+                                            int32_t k_pages, int32_t* sel_counts,
+                                            int32_t* sel_offsets, int32_t* sel_pages,
                                             int32_t* sel_phys, void* ws, size_t ws_bytes,
                                             void* stream) {
   if (k_pages < 1) return SPARSE_ERR_INVALID;
-  return sp::select_entry<true>(dims, logits, ctx_lens, page_table, 1.0f, k_pages, chunk_pages,
-                                sel_counts, sel_offsets, chunk_offsets, sel_pages, sel_phys, ws,
-                                ws_bytes, stream);
+  return sp::select_entry<true>(dims, logits, ctx_lens, page_table, 1.0f, k_pages, sel_counts,
+                                sel_offsets, sel_pages, sel_phys, ws, ws_bytes, stream);
 }

@@ -97,11 +97,11 @@ class SplitHostTierStep:
     order of the log-sum-exp merge.  The step joins the second stream before
     it returns, so it can be captured whole."""
 
-    def __init__(self, dims, cache, gamma, chunk_pages, scale=None, device="cuda"):
+    def __init__(self, dims, cache, gamma, workers=0, scale=None, device="cuda"):
         self.dims, self.cache = dims, cache
-        self.hits = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+        self.hits = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
-        self.miss = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+        self.miss = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
         self.hit_phys = torch.zeros_like(self.hits.buf.sel_phys)
         B, Hq = dims.batch, dims.num_q_heads
@@ -171,12 +171,12 @@ class LayeredHostTierStep:
     order: outputs and cache state are bitwise the same.  The step joins the
     second stream before it returns, so it can be captured whole."""
 
-    def __init__(self, dims, host_pools, capacity, gamma, chunk_pages, scale=None,
+    def __init__(self, dims, host_pools, capacity, gamma, workers=0, scale=None,
                  prefetch=True, device="cuda"):
         self.dims = dims
         self.prefetch = bool(prefetch)
         self.caches = [HbmPageCache(dims, h, capacity, device) for h in host_pools]
-        self.attn = SparseDecodeStep(dims, gamma, chunk_pages, scale=scale, device=device,
+        self.attn = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
         # per-layer slot lists: layer l+1's resolve writes while layer l attends
         self.sel_phys = [torch.zeros_like(self.attn.buf.sel_phys) for _ in host_pools]

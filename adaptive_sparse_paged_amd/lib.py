@@ -60,8 +60,8 @@ class Dims(ctypes.Structure):
 
 def make_dims(batch, q_heads, kv_heads, max_pages, head_dim=128, page_size=16,
               max_list_pages=0):
-    """max_list_pages: 0, or a bound on every page list's length that the
-    attention and merge plan for (a smaller grid for short lists)."""
+    """max_list_pages: 0, or a bound on every page list's length (the
+    attention and merge clamp each list's count to it)."""
     return Dims(batch, q_heads, kv_heads, head_dim, page_size, max_pages, max_list_pages)
 
 
@@ -85,14 +85,14 @@ _SIGS = {
     "sparse_build_page_summaries": (_I32, [_D, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P]),
     "sparse_score_pages": (_I32, [_D, _P, _P, _I64, _P, _P, _F, _P, _P]),
     "sparse_select_workspace_bytes": (ctypes.c_size_t, [_D]),
-    "sparse_select_coverage": (_I32, [_D, _P, _P, _P, _F, _I32, _P, _P, _P, _P, _P, _P,
+    "sparse_select_coverage": (_I32, [_D, _P, _P, _P, _F, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
     "sparse_decode_max_parts": (_I64, [_D, _I32]),
     "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
                                   _P, _P, _I64, _P]),
     "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P]),
     "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
-    "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+    "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     "sparse_append_tokens": (_I32, [_D, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "sparse_hbm_cache_resolve": (_I32, [_D, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
@@ -174,36 +174,39 @@ def select_workspace_bytes(dims):
     return int(load().sparse_select_workspace_bytes(ctypes.byref(dims)))
 
 
-def select_coverage(dims, logits, ctx_lens, page_table, gamma, chunk_pages, sel_counts,
-                    sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
-    """sel_offsets / chunk_offsets / ws may all be None (no whole-batch prefix sums)."""
-    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
-         sel_phys, ws)
+def select_coverage(dims, logits, ctx_lens, page_table, gamma, sel_counts, sel_offsets,
+                    sel_pages, sel_phys, ws, stream=None):
+    """sel_offsets / ws may both be None (no whole-batch prefix sum)."""
+    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, sel_pages, sel_phys, ws)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("sparse_select_coverage", load().sparse_select_coverage(
-        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), gamma, chunk_pages,
-        _ptr(sel_counts), _ptr(sel_offsets), _ptr(chunk_offsets), _ptr(sel_pages),
-        _ptr(sel_phys), _ptr(ws), nbytes, _stream(stream)))
+        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), gamma,
+        _ptr(sel_counts), _ptr(sel_offsets), _ptr(sel_pages), _ptr(sel_phys), _ptr(ws), nbytes,
+        _stream(stream)))
 
 
-def decode_max_parts(dims, chunk_pages):
-    return int(load().sparse_decode_max_parts(ctypes.byref(dims), chunk_pages))
+ATTN_MIN_WORKER_PAGES = 32   # SPARSE_ATTN_MIN_WORKER_PAGES
+
+
+def decode_max_parts(dims, workers=0):
+    """Partial slots of one attention step: U + W (W = workers, or the current
+    device's compute units when 0); -1 when invalid."""
+    return int(load().sparse_decode_max_parts(ctypes.byref(dims), workers))
 
 
 def decode_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
-                sel_pages, sel_phys, scale, chunk_pages, part_o, part_lse, max_parts,
-                stream=None):
+                sel_pages, sel_phys, scale, workers, part_o, part_lse, max_parts, stream=None):
     _dev(q, kv, ctx_lens, sel_counts, sel_pages, sel_phys, part_o, part_lse)
     _check("sparse_decode_attn", load().sparse_decode_attn(
         ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
-        _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, chunk_pages,
+        _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, workers,
         _ptr(part_o), _ptr(part_lse), max_parts, _stream(stream)))
 
 
-def merge_splits(dims, part_o, part_lse, sel_counts, chunk_pages, out, out_lse, stream=None):
+def merge_splits(dims, part_o, part_lse, sel_counts, workers, out, out_lse, stream=None):
     _dev(part_o, part_lse, sel_counts, out, out_lse)
     _check("sparse_merge_splits", load().sparse_merge_splits(
-        ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), chunk_pages,
+        ctypes.byref(dims), _ptr(part_o), _ptr(part_lse), _ptr(sel_counts), workers,
         _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
@@ -248,15 +251,14 @@ def hbm_cache_resolve_policy(dims, policy, sel_counts, sel_pages, host_kv, cache
         _stream(stream)))
 
 
-def select_topk(dims, logits, ctx_lens, page_table, k_pages, chunk_pages, sel_counts,
-                sel_offsets, chunk_offsets, sel_pages, sel_phys, ws, stream=None):
-    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, chunk_offsets, sel_pages,
-         sel_phys, ws)
+def select_topk(dims, logits, ctx_lens, page_table, k_pages, sel_counts, sel_offsets,
+                sel_pages, sel_phys, ws, stream=None):
+    _dev(logits, ctx_lens, page_table, sel_counts, sel_offsets, sel_pages, sel_phys, ws)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("sparse_select_topk", load().sparse_select_topk(
-        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), k_pages, chunk_pages,
-        _ptr(sel_counts), _ptr(sel_offsets), _ptr(chunk_offsets), _ptr(sel_pages),
-        _ptr(sel_phys), _ptr(ws), nbytes, _stream(stream)))
+        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), k_pages,
+        _ptr(sel_counts), _ptr(sel_offsets), _ptr(sel_pages), _ptr(sel_phys), _ptr(ws), nbytes,
+        _stream(stream)))
 
 
 def append_tokens(dims, k_new, v_new, kv, stride_page, stride_head, pool_pages, page_table,

@@ -3,7 +3,7 @@ buffers, and its capture into a single HIP graph.
 
 Buffers are torch tensors (device memory only); every operation is a call into
 the HIP library.  The step is captured whole: nothing in it waits on the host,
-and the page lists, their lengths and the chunk plan live on the device, so a
+and the page lists, their lengths and the attention's plan live on the device, so a
 captured graph replays correctly after the queries, context lengths or page
 tables change in place.
 """
@@ -23,11 +23,10 @@ class StepBuffers:
     logits: torch.Tensor        # fp32 [B][Hkv][G][max_pages]
     sel_counts: torch.Tensor    # int32 [U]
     sel_offsets: torch.Tensor   # int32 [U+1]
-    chunk_offsets: torch.Tensor  # int32 [U+1]
     sel_pages: torch.Tensor     # int32 [U][max_pages]
     sel_phys: torch.Tensor      # int32 [U][max_pages]
     ws: torch.Tensor            # uint8 workspace (zero-filled once)
-    part_o: torch.Tensor        # fp32 [max_parts][G][D]
+    part_o: torch.Tensor        # fp32 [max_parts][G][D], max_parts = U + workers
     part_lse: torch.Tensor      # fp32 [max_parts][G]
     out: torch.Tensor           # fp32 [B][Hq][D]
     out_lse: torch.Tensor       # fp32 [B][Hq]
@@ -36,13 +35,12 @@ class StepBuffers:
 class SparseDecodeStep:
     """Fixed-shape decode step for one layer shape.
 
-    dims: lib.Dims; gamma in (0, 1]; chunk_pages: the most pages one
-    attention workgroup takes (a unit's list is split evenly over
-    ceil(count / chunk_pages) workgroups; clamped to max_pages).  On MI355X
-    the best size leaves one workgroup per compute unit when every request
-    has the same long context (1024 at 4 x 131072 tokens, 512 at 8 x 32768),
-    and about 320 for ragged lengths.  Intermediate buffers are shared by
-    every layer run through this object; outputs can be given per call.
+    dims: lib.Dims; gamma in (0, 1]; workers: the attention's grid (0 = one
+    workgroup per compute unit of the device).  The attention splits all the
+    step's list entries evenly over its workgroups on the device, whatever
+    the list lengths, so no per-workload size is needed.  Intermediate
+    buffers are shared by every layer run through this object; outputs can
+    be given per call.
 
     groups > 1 splits the requests into that many contiguous groups, each on a
     stream of its own, where a group's scoring starts once the previous group's
@@ -50,33 +48,32 @@ class SparseDecodeStep:
     unit) and attention is bandwidth-bound, so this lets one group's selection
     run under another group's attention.  Every unit's arithmetic is the same
     in both modes (bitwise); only the grouped mode leaves the whole-batch
-    prefix sums (sel_offsets / chunk_offsets) unwritten.  Measured on MI355X
+    prefix sum (sel_offsets) unwritten.  Measured on MI355X
     (ROCm 7.2, graph replay) on 4 x 131072 tokens, 32 layers: 376 us/layer
     with one group, 414 with two and 591 with four.  Each group's kernels get
     a fraction of the grid, and the last group's attention has nothing left to
     run beside it, so the default is one group.
     """
 
-    def __init__(self, dims, gamma, chunk_pages=256, scale=None, device="cuda", groups=1,
+    def __init__(self, dims, gamma, workers=0, scale=None, device="cuda", groups=1,
                  offsets=True):
-        """offsets: also write the whole-batch prefix sums (sel_offsets,
-        chunk_offsets) in the selection; the attention does not need them."""
+        """offsets: also write the whole-batch prefix sum (sel_offsets) in the
+        selection; the attention does not need it."""
         self.dims = dims
         self.offsets = bool(offsets)
         self.gamma = float(gamma)
-        self.chunk_pages = int(min(chunk_pages, dims.max_pages))
+        self.workers = int(workers)
         self.scale = float(scale if scale is not None else HEAD_DIM ** -0.5)
         B, Hq, Hkv, MP = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.max_pages
         G = Hq // Hkv
         U = B * Hkv
-        self.max_parts = lib.decode_max_parts(dims, self.chunk_pages)
+        self.max_parts = lib.decode_max_parts(dims, self.workers)
         i32 = dict(dtype=torch.int32, device=device)
         f32 = dict(dtype=torch.float32, device=device)
         self.buf = StepBuffers(
             logits=torch.empty((B, Hkv, G, MP), **f32),
             sel_counts=torch.zeros(U, **i32),
             sel_offsets=torch.zeros(U + 1, **i32),
-            chunk_offsets=torch.zeros(U + 1, **i32),
             sel_pages=torch.zeros((U, MP), **i32),
             sel_phys=torch.zeros((U, MP), **i32),
             ws=torch.zeros(lib.select_workspace_bytes(dims), dtype=torch.uint8, device=device),
@@ -99,11 +96,10 @@ class SparseDecodeStep:
                 continue
             dg = lib.make_dims(b1 - b0, d.num_q_heads, Hkv, d.max_pages)
             u0, u1 = b0 * Hkv, b1 * Hkv
-            mp = lib.decode_max_parts(dg, self.chunk_pages)
+            mp = lib.decode_max_parts(dg, self.workers)
             self.groups.append(dict(
                 b0=b0, b1=b1, u0=u0, u1=u1, dims=dg, max_parts=mp,
                 sel_offsets=torch.zeros(u1 - u0 + 1, dtype=torch.int32, device=device),
-                chunk_offsets=torch.zeros(u1 - u0 + 1, dtype=torch.int32, device=device),
                 ws=torch.zeros(lib.select_workspace_bytes(dg), dtype=torch.uint8, device=device),
                 part_o=torch.empty((mp, G, HEAD_DIM), dtype=torch.float32, device=device),
                 part_lse=torch.empty((mp, G), dtype=torch.float32, device=device),
@@ -126,16 +122,15 @@ class SparseDecodeStep:
                 lib.score_pages(dg, q[b0:b1], summ, pool_pages, page_table[b0:b1],
                                 ctx_lens[b0:b1], self.scale, b.logits[b0:b1], s)
                 lib.select_coverage(dg, b.logits[b0:b1], ctx_lens[b0:b1], page_table[b0:b1],
-                                    self.gamma, self.chunk_pages, b.sel_counts[u0:u1],
-                                    gr["sel_offsets"], gr["chunk_offsets"], b.sel_pages[u0:u1],
-                                    b.sel_phys[u0:u1], gr["ws"], s)
+                                    self.gamma, b.sel_counts[u0:u1], gr["sel_offsets"],
+                                    b.sel_pages[u0:u1], b.sel_phys[u0:u1], gr["ws"], s)
                 gr["selected"].record(s)
                 lib.decode_attn(dg, q[b0:b1], kv, stride_page, stride_head, pool_pages,
                                 ctx_lens[b0:b1], b.sel_counts[u0:u1], b.sel_pages[u0:u1],
-                                b.sel_phys[u0:u1], self.scale, self.chunk_pages, gr["part_o"],
+                                b.sel_phys[u0:u1], self.scale, self.workers, gr["part_o"],
                                 gr["part_lse"], gr["max_parts"], s)
                 lib.merge_splits(dg, gr["part_o"], gr["part_lse"], b.sel_counts[u0:u1],
-                                 self.chunk_pages, out[b0:b1], out_lse[b0:b1], s)
+                                 self.workers, out[b0:b1], out_lse[b0:b1], s)
             prev = gr
         for gr in self.groups:
             cur.wait_stream(gr["stream"])
@@ -145,9 +140,8 @@ class SparseDecodeStep:
         d, b = self.dims, self.buf
         lib.score_pages(d, q, summ, pool_pages, page_table, ctx_lens, self.scale, b.logits, stream)
         on = self.offsets
-        lib.select_coverage(d, b.logits, ctx_lens, page_table, self.gamma, self.chunk_pages,
-                            b.sel_counts, b.sel_offsets if on else None,
-                            b.chunk_offsets if on else None, b.sel_pages, b.sel_phys,
+        lib.select_coverage(d, b.logits, ctx_lens, page_table, self.gamma, b.sel_counts,
+                            b.sel_offsets if on else None, b.sel_pages, b.sel_phys,
                             b.ws if on else None, stream)
 
     def attend(self, q, kv, stride_page, stride_head, pool_pages, ctx_lens, out=None,
@@ -158,9 +152,9 @@ class SparseDecodeStep:
         sp = b.sel_pages if sel_pages is None else sel_pages
         sx = b.sel_phys if sel_phys is None else sel_phys
         lib.decode_attn(d, q, kv, stride_page, stride_head, pool_pages, ctx_lens, b.sel_counts,
-                        sp, sx, self.scale, self.chunk_pages, b.part_o, b.part_lse,
+                        sp, sx, self.scale, self.workers, b.part_o, b.part_lse,
                         self.max_parts, stream)
-        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, self.chunk_pages, out, out_lse,
+        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, self.workers, out, out_lse,
                          stream)
         return out, out_lse
 

@@ -14,8 +14,9 @@ bytes the step must move (page summaries, logits, page lists, the selected K/V
 tokens, split partials, queries and outputs -- counted from the device's own
 page counts); `us_per_layer` is the step time divided by the layers.
 `roofline` covers the attention kernel (the dominant one), timed with HIP
-events on its own stream; `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload.
+events on its own stream; `cpu_baseline` times the fp64 oracle on layer 0 of
+the same workload over the host's cores (one process per core), with the
+one-thread figure beside it.
 """
 
 import argparse
@@ -42,9 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_128k")
     ap.add_argument("--gamma", type=float, default=0.99)
-    ap.add_argument("--chunk", type=int, default=0,
-                    help="pages per attention workgroup (default: the workload's entry in "
-                         "DEFAULT_CHUNK, else 256)")
+    ap.add_argument("--workers", type=int, default=0,
+                    help="attention workgroups (default 0: one per compute unit); the step's "
+                         "list entries are split evenly over them on the device")
     ap.add_argument("--groups", type=int, default=1,
                     help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
@@ -53,6 +54,9 @@ def parse():
                     help="host tier: split = attention over the hits beside the fetch of the "
                          "misses (default); one_pass = resolve and fetch, then one attention")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-procs", type=int, default=0,
+                    help="oracle processes for the multi-core CPU baseline (default: the "
+                         "usable host cores, at most 16)")
     ap.add_argument("--cache-policy", default="exact",
                     help="host tier: exact | bucketed:S | pooled | pooled:S")
     ap.add_argument("--list-spread", type=float, default=0.0,
@@ -62,34 +66,42 @@ def parse():
     return ap.parse_args()
 
 
-# Pages per attention workgroup, measured per workload on MI355X with the
-# full 32- or 4-layer step.  Where every request has the same long context,
-# the best size gives one workgroup per compute unit (256 workgroups: 1024
-# pages at 4 x 131072 tokens, 512 at 8 x 32768); sizes that leave some units
-# with two workgroups and others with one are much slower, since a
-# workgroup's rate is capped by the loads it keeps in flight.  320 where
-# lengths are ragged (many rounds of workgroups; smaller chunks shorten the
-# drain at the end), 128 for the host tier's short 448-page lists, and 32
-# for a single short request (its two 256-page lists spread over 16
-# workgroups instead of two).
-DEFAULT_CHUNK = {"tiny": 32, "long_128k": 1024, "llama8b_32k": 512, "serving_b64": 320,
-                 "host_tier_512k": 128, "host_tier_layers": 128}
+def plan_segments(counts, workers, min_pages, cap=None):
+    """Partials each unit's list is split into by the attention's balanced
+    plan (the formulas of sparse_decode_attn in include/sparse_paged.h): the
+    lists laid end to end, T entries over W' = min(workers, ceil(T /
+    min_pages)) workers, worker w owning [floor(w T / W'), floor((w+1) T / W')).
+    Returns int64 [U]: the number of workers each unit's entries fall to."""
+    k = np.asarray(counts, dtype=np.int64).clip(min=0)
+    if cap is not None:
+        k = np.minimum(k, cap)
+    T = int(k.sum())
+    out = np.zeros(k.shape[0], dtype=np.int64)
+    if T == 0:
+        return out
+    W = min(int(workers), -(-T // int(min_pages)))
+    off = np.concatenate([[0], np.cumsum(k)[:-1]])
+    owner = lambda x: ((x + 1) * W - 1) // T
+    nz = k > 0
+    out[nz] = owner(off[nz] + k[nz] - 1) - owner(off[nz]) + 1
+    return out
 
 
-def counted_bytes(n, k, tsel, G, Hkv, chunk):
-    """Algorithmic bytes of one unit: n pages, k kept, tsel kept valid tokens."""
+def counted_bytes(n, k, tsel, G, Hkv, nseg):
+    """Algorithmic bytes of one unit: n pages, k kept, tsel kept valid tokens,
+    its list split into nseg attention partials."""
     return (512 * n                 # page summaries (kmin|kmax bf16)
             + 2 * 4 * G * n         # fp32 logits written and read
             + 4 * n / Hkv           # the request's page-table row, shared by its KV heads
             + 512 * tsel            # kept K and V tokens (bf16)
             + 16 * k                # kept logical/physical ids written and read
-            + 2 * math.ceil(k / chunk) * G * (D + 1) * 4   # split partials written and read
+            + 2 * nseg * G * (D + 1) * 4                   # split partials written and read
             + 2 * G * D * 2 + G * D * 4 + G * 4)           # q read twice, out, lse
 
 
-def attn_bytes(k, tsel, G, chunk):
+def attn_bytes(k, tsel, G, nseg):
     """Algorithmic bytes of the attention kernel alone for one unit."""
-    return 512 * tsel + 8 * k + G * D * 2 + math.ceil(k / chunk) * G * (D + 1) * 4
+    return 512 * tsel + 8 * k + G * D * 2 + nseg * G * (D + 1) * 4
 
 
 def kept_tokens(counts, pages, lens, Hkv, max_pages):
@@ -149,57 +161,60 @@ def source_hash(*paths):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, lens, gamma, budget_s, gpu=None):
+def _one_thread():
+    """Limit this process's BLAS / OpenMP / torch pools to one thread."""
+    import torch
+    torch.set_num_threads(1)
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:                      # pragma: no cover
+        return None
+
+
+def _oracle_unit_inputs(w, b, h, L):
+    """One unit of layer 0 generated on the host (untimed): bf16 bits of q and
+    the summaries, fp64 K, V, q, and the valid tokens per page."""
+    import oracle as O
+    from adaptive_sparse_paged_amd import inputs as I
+    k, v, q, nv = I.unit_host(w, 0, b, h, L)
+    lo, hi = O.summaries(k, nv)            # prefill-time, not timed
+    return dict(q=q, lo=lo, hi=hi, nv=nv, qf=O.bf16_bits_to_f64(q), Kf=O.bf16_bits_to_f64(k),
+                Vf=O.bf16_bits_to_f64(v))
+
+
+def _oracle_step(w, un, gamma):
+    """The timed oracle work for one unit: score, masses, cut, attention."""
+    import oracle as O
+    sel = O.select_unit(un["q"], un["lo"], un["hi"], un["nv"], w.scale, gamma)
+    O.attend_pages(un["qf"], un["Kf"], un["Vf"], un["nv"], sel["list"], w.scale)
+    return sel
+
+
+def cpu_baseline(w, lens, gamma, budget_s):
     """Time the fp64 oracle (score, masses, cut, attention) on every
     (request, KV head) unit of layer 0, on one host thread.  Each unit is
     generated once (untimed) and its oracle call repeated R times, with R
     chosen from the first unit so the timed total is about budget_s; the mean
-    per-unit time is scaled to one layer.
-
-    gpu = (counts, pages, out) of the timed run's layer 0: then every unit
-    the oracle ran is also checked, untimed, against what the GPU produced --
-    its list accepted by the coverage predicate, exact-match with the
-    oracle's list, and attention on the GPU's list within 1e-2 -- and the
-    summary is returned as a second dict (else None)."""
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:                      # pragma: no cover
-        limiter = None
-    import oracle as O
-    from adaptive_sparse_paged_amd import inputs as I
+    per-unit time is scaled to one layer."""
+    limiter = _one_thread()
     n_units = w.batch * w.kv_heads
     spent, calls, reps = 0.0, 0, None
-    chk = {"units": 0, "accepted": 0, "exact": 0, "max_abs_err": 0.0}
     t_total = time.time()
     for b in range(w.batch):
         for h in range(w.kv_heads):
-            L = int(lens[b])
-            k, v, q, nv = I.unit_host(w, 0, b, h, L)
-            lo, hi = O.summaries(k, nv)        # prefill-time, not timed
-            Kf, Vf, qf = O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v), O.bf16_bits_to_f64(q)
+            un = _oracle_unit_inputs(w, b, h, int(lens[b]))
             r = 0
             while reps is None or r < reps:
                 t0 = time.perf_counter()
-                sel = O.select_unit(q, lo, hi, nv, w.scale, gamma)
-                O.attend_pages(qf, Kf, Vf, nv, sel["list"], w.scale)
+                _oracle_step(w, un, gamma)
                 dt = time.perf_counter() - t0
                 spent += dt
                 calls += 1
                 r += 1
                 if reps is None:
                     reps = int(min(16, max(1, round(budget_s / (dt * n_units)))))
-            if gpu is not None:                # untimed: the timed run's own outputs
-                counts, pages, out = gpu
-                u = b * w.kv_heads + h
-                lst = pages[u, :int(counts[u])]
-                ok, _ = O.list_accepted(lst, sel["m"], gamma, 1e-5)
-                chk["units"] += 1
-                chk["accepted"] += int(ok)
-                chk["exact"] += int(len(lst) == sel["count"] and np.array_equal(lst, sel["list"]))
-                o_ref, _ = O.attend_pages(qf, Kf, Vf, nv, lst, w.scale)
-                o_gpu = out[b, h * w.group:(h + 1) * w.group].astype(np.float64)
-                chk["max_abs_err"] = max(chk["max_abs_err"], float(np.abs(o_gpu - o_ref).max()))
+            del un
             if time.time() - t_total > 8 * budget_s:
                 break
         if time.time() - t_total > 8 * budget_s:
@@ -208,17 +223,102 @@ def cpu_baseline(w, lens, gamma, budget_s, gpu=None):
         limiter.unregister()
     units = -(-calls // reps)
     us_layer = spent / calls * n_units * 1e6
-    base = {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
             "sample": f"{units} of {n_units} (request, KV head) units of layer 0, each run "
                       f"{reps} times: {spent:.1f} s of fp64 NumPy on one host thread, "
                       f"mean per unit scaled to one layer"}
-    if gpu is None:
-        return base, None
+
+
+def _pool_worker(w, lens, gamma, units, reps, barrier, results):
+    """One oracle process of the multi-core baseline: generate its units
+    (untimed), wait for every process, then run the oracle on its units reps
+    times and report the elapsed time."""
+    _one_thread()
+    prepared = [_oracle_unit_inputs(w, b, h, int(lens[b])) for b, h in units]
+    barrier.wait()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for un in prepared:
+            _oracle_step(w, un, gamma)
+    results.put(time.perf_counter() - t0)
+
+
+def host_cores():
+    """Host cores this process may run on, at most 16 (one GPU's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:                 # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_pool(w, lens, gamma, budget_s, procs):
+    """The same oracle on every unit of layer 0, spread over `procs` processes
+    (one thread each, units dealt round robin), all starting together once
+    their inputs are generated; one layer's time is the slowest process's
+    elapsed time over reps repetitions of its units, divided by reps.  reps
+    is set so that the run takes about budget_s.  Processes are forked, so
+    this must run before the process touches the GPU."""
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    procs = max(1, min(procs, len(units)))
+    share = [units[i::procs] for i in range(procs)]
+    # one calibration unit on this thread sets the repetition count
+    limiter = _one_thread()
+    un = _oracle_unit_inputs(w, *units[0], int(lens[units[0][0]]))
+    t0 = time.perf_counter()
+    _oracle_step(w, un, gamma)
+    per_unit = time.perf_counter() - t0
+    del un
+    if limiter is not None:
+        limiter.unregister()
+    per_rep = per_unit * max(len(x) for x in share)
+    reps = int(min(64, max(1, round(budget_s / per_rep))))
+    barrier = ctx.Barrier(procs)
+    results = ctx.Queue()
+    ps = [ctx.Process(target=_pool_worker, args=(w, lens, gamma, share[i], reps, barrier,
+                                                 results)) for i in range(procs)]
+    for p in ps:
+        p.start()
+    times = [results.get() for _ in ps]
+    for p in ps:
+        p.join()
+    layer_s = max(times) / reps
+    return {"value": round(layer_s * 1e6, 1), "unit": "us/layer", "cores": procs,
+            "kind": "oracle",
+            "sample": f"all {len(units)} (request, KV head) units of layer 0 over {procs} "
+                      f"processes (one thread each), {reps} repetitions: slowest process "
+                      f"{max(times):.1f} s, per repetition = one layer"}
+
+
+def oracle_check(w, lens, gamma, gpu):
+    """Untimed check of what the timed run produced for layer 0, unit by
+    unit against the oracle: gpu = (counts, pages, out).  Lists accepted by
+    the coverage predicate, lists equal to the oracle's, and the max-abs
+    error of attention on the GPU's own list."""
+    import oracle as O
+    counts, pages, out = gpu
+    chk = {"units": 0, "accepted": 0, "exact": 0, "max_abs_err": 0.0}
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            un = _oracle_unit_inputs(w, b, h, int(lens[b]))
+            sel = O.select_unit(un["q"], un["lo"], un["hi"], un["nv"], w.scale, gamma)
+            u = b * w.kv_heads + h
+            lst = pages[u, :int(counts[u])]
+            ok, _ = O.list_accepted(lst, sel["m"], gamma, 1e-5)
+            chk["units"] += 1
+            chk["accepted"] += int(ok)
+            chk["exact"] += int(len(lst) == sel["count"] and np.array_equal(lst, sel["list"]))
+            o_ref, _ = O.attend_pages(un["qf"], un["Kf"], un["Vf"], un["nv"], lst, w.scale)
+            o_gpu = out[b, h * w.group:(h + 1) * w.group].astype(np.float64)
+            chk["max_abs_err"] = max(chk["max_abs_err"], float(np.abs(o_gpu - o_ref).max()))
+            del un
     chk["max_abs_err"] = float(f"{chk['max_abs_err']:.3g}")
     chk["what"] = ("layer 0 of the timed run against the fp64 oracle: lists accepted by the "
                    "coverage predicate (1e-5 relative mass), lists equal to the oracle's, "
                    "max-abs error of attention on the GPU's lists (bar 1e-2)")
-    return base, chk
+    return chk
 
 
 def host_tier_bench(args):
@@ -261,8 +361,7 @@ def host_tier_bench(args):
     pooled = name == "pooled"
     cap = B * C if pooled else C          # the same HBM either way
     cache = HbmPageCache(dims, host, cap, recency_shift=shift, pooled=pooled)
-    chunk = min(args.chunk, LM)
-    st = SparseDecodeStep(dims, args.gamma, chunk, scale=w.scale)
+    st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale)
     q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
     for b in range(B):
         for h in range(H):
@@ -275,7 +374,7 @@ def host_tier_bench(args):
     kv, s_page, s_head, ppages = cache.pool_args()
     spl = None
     if args.schedule == "split":
-        spl = SplitHostTierStep(dims, cache, args.gamma, chunk, scale=w.scale)
+        spl = SplitHostTierStep(dims, cache, args.gamma, args.workers, scale=w.scale)
         spl.sel_counts.copy_(counts0)
         out_s = torch.empty((B, w.q_heads, D), dtype=torch.float32, device="cuda")
         lse_s = torch.empty((B, w.q_heads), dtype=torch.float32, device="cuda")
@@ -355,7 +454,7 @@ def host_tier_bench(args):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "ctx": int(lens.max()), "kv_heads": H,
                    "q_heads": w.q_heads, "capacity_slots": C, "list_pages": LP,
-                   "drift": ex["drift"], "chunk_pages": chunk,
+                   "drift": ex["drift"], "attn_workers": st.max_parts - U,
                    "cache_policy": args.cache_policy, "list_spread": args.list_spread,
                    "list_pages_min_max": [min(sizes), max(sizes)],
                    "schedule": "split" if spl is not None else "one_pass"},
@@ -415,9 +514,10 @@ def host_tier_layers_bench(args):
     B, H = w.batch, w.kv_heads
     U = B * H
     dims = lib.make_dims(B, w.q_heads, H, MP, max_list_pages=LP)
-    chunk = min(args.chunk, LP)
-    seq = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=False)
-    pre = LayeredHostTierStep(dims, hosts, C, args.gamma, chunk, scale=w.scale, prefetch=True)
+    seq = LayeredHostTierStep(dims, hosts, C, args.gamma, args.workers, scale=w.scale,
+                              prefetch=False)
+    pre = LayeredHostTierStep(dims, hosts, C, args.gamma, args.workers, scale=w.scale,
+                              prefetch=True)
     qs = []
     for l in range(nl):
         q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
@@ -478,7 +578,8 @@ def host_tier_layers_bench(args):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "ctx": int(lens.max()), "layers": nl,
                    "kv_heads": H, "q_heads": w.q_heads, "capacity_slots": C,
-                   "list_pages": LP, "drift": ex["drift"], "chunk_pages": chunk},
+                   "list_pages": LP, "drift": ex["drift"],
+                   "attn_workers": seq.attn.max_parts - U},
         "sequential_step_us_median": round(float(np.median(seq_step)), 1),
         "sequential_resolve_fetch_us_median": round(float(np.median(seq_io)), 1),
         "sequential_attention_merge_us_median": round(float(np.median(seq_att)), 1),
@@ -495,7 +596,7 @@ def attn_launch(lib, st, dims, li, stride_page, stride_head):
     """The step's attention launch alone (sparse_decode_attn, without its merge)."""
     b = st.buf
     lib.decode_attn(dims, li.q, li.kv_pool, stride_page, stride_head, li.pool_pages, li.ctx_lens,
-                    b.sel_counts, b.sel_pages, b.sel_phys, st.scale, st.chunk_pages, b.part_o,
+                    b.sel_counts, b.sel_pages, b.sel_phys, st.scale, st.workers, b.part_o,
                     b.part_lse, st.max_parts)
 
 
@@ -518,12 +619,13 @@ def pmc_probe(args):
     lib.build_page_summaries(dims, li.kv_pool, sp_, sh_, li.pool_pages,
                              torch.arange(li.pool_pages, dtype=torch.int32, device="cuda"),
                              li.page_valid, summ)
-    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale)
+    st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale)
     st.score_select(li.q, summ, li.pool_pages, li.page_table, li.ctx_lens)
     torch.cuda.synchronize()
     c = st.buf.sel_counts.cpu().numpy()
     tsel = kept_tokens(c, st.buf.sel_pages.cpu().numpy(), lens, w.kv_heads, li.max_pages)
-    ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, st.chunk_pages) for u in range(len(c)))
+    nseg = plan_segments(c, st.max_parts - len(c), lib.ATTN_MIN_WORKER_PAGES)
+    ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, int(nseg[u])) for u in range(len(c)))
     for _ in range(3):
         attn_launch(lib, st, dims, li, sp_, sh_)
     src = torch.empty(512 * 1024 * 1024, dtype=torch.int16, device="cuda")
@@ -538,8 +640,6 @@ def pmc_probe(args):
 
 def main():
     args = parse()
-    if not args.chunk:
-        args.chunk = DEFAULT_CHUNK.get(args.workload, 256)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(requests and KV heads shard across GPUs with no communication).", file=sys.stderr)
@@ -558,10 +658,19 @@ def main():
     from adaptive_sparse_paged_amd import lib
     from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides, capture
 
-    lib.load()
     w = I.WORKLOADS[args.workload]
     layers = args.layers or w.layers
     lens = I.context_lengths(w)
+    base = None
+    if not args.no_cpu_baseline:
+        # CPU legs first: the pool forks, which must happen before any GPU use
+        procs = args.cpu_procs or host_cores()
+        print(f"# oracle baseline: 1 thread, then {procs} processes", file=sys.stderr,
+              flush=True)
+        single = cpu_baseline(w, lens, args.gamma, args.cpu_seconds)
+        base = cpu_baseline_pool(w, lens, args.gamma, args.cpu_seconds, procs)
+        base["single_core"] = single
+    lib.load()
     dev = "cuda"
     t_gen = time.time()
     L_in, summs = [], []
@@ -583,8 +692,9 @@ def main():
     max_pages = L_in[0].max_pages
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
     groups = max(1, min(args.groups, w.batch))
-    st = SparseDecodeStep(dims, args.gamma, args.chunk, scale=w.scale, device=dev, groups=groups,
-                          offsets=False)
+    st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale, device=dev,
+                          groups=groups, offsets=False)
+    workers = st.max_parts - w.batch * w.kv_heads
     outs = [torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     lses = [torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev) for _ in range(layers)]
     counts = [torch.empty_like(st.buf.sel_counts) for _ in range(layers)]
@@ -602,7 +712,8 @@ def main():
         torch.cuda.synchronize()
         c = st.buf.sel_counts.cpu().numpy()
         pg = st.buf.sel_pages.cpu().numpy()
-        sel_stats.append((c, kept_tokens(c, pg, lens, w.kv_heads, max_pages)))
+        sel_stats.append((c, kept_tokens(c, pg, lens, w.kv_heads, max_pages),
+                          plan_segments(c, workers, lib.ATTN_MIN_WORKER_PAGES)))
         if l == 0:
             layer0 = (c.copy(), pg.copy())
     graph = capture(step_fn)
@@ -624,11 +735,11 @@ def main():
     G, Hkv = w.group, w.kv_heads
     npages = np.array([I.pages_of(L) for L in lens])
     total_bytes, attn_total, kept, pages_all = 0.0, 0.0, 0, 0
-    for c, tsel in sel_stats:
+    for c, tsel, nseg in sel_stats:
         for u in range(c.shape[0]):
             n = int(npages[u // Hkv])
-            total_bytes += counted_bytes(n, int(c[u]), int(tsel[u]), G, Hkv, st.chunk_pages)
-            attn_total += attn_bytes(int(c[u]), int(tsel[u]), G, st.chunk_pages)
+            total_bytes += counted_bytes(n, int(c[u]), int(tsel[u]), G, Hkv, int(nseg[u]))
+            attn_total += attn_bytes(int(c[u]), int(tsel[u]), G, int(nseg[u]))
             kept += int(c[u])
             pages_all += n
     gbs = total_bytes / (ms_step * 1e-3) / 1e9
@@ -646,13 +757,13 @@ def main():
             attn_launch(lib, st, dims, li, stride_page, stride_head)
             a1.record(stream)
             lib.merge_splits(dims, st.buf.part_o, st.buf.part_lse, st.buf.sel_counts,
-                             st.chunk_pages, outs[l], lses[l])
+                             st.workers, outs[l], lses[l])
             marks.append((a0, a1))
     torch.cuda.synchronize()
     attn_us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / len(marks)
     attn_launch_bytes = 0.0
-    for c, tsel in sel_stats:
-        attn_launch_bytes += sum(attn_bytes(int(c[u]), int(tsel[u]), G, st.chunk_pages)
+    for c, tsel, nseg in sel_stats:
+        attn_launch_bytes += sum(attn_bytes(int(c[u]), int(tsel[u]), G, int(nseg[u]))
                                  for u in range(c.shape[0]))
     attn_launch_bytes /= layers
     attn_gbs = attn_launch_bytes / (attn_us * 1e-6) / 1e9
@@ -666,7 +777,7 @@ def main():
         # the attention kernel is compiled from attn.hip and the helpers it includes
         src_hash = source_hash(os.path.join(csrc, "attn.hip"), os.path.join(csrc, "common.h"))
         if (rec.get("source_sha256_16") == src_hash and rec.get("workload") == w.name
-                and rec.get("chunk_pages") == st.chunk_pages and rec.get("gamma") == args.gamma):
+                and rec.get("attn_workers") == workers and rec.get("gamma") == args.gamma):
             traffic = rec.get("bytes_per_launch")
 
     ceiling = read_ceiling(lib, L_in[0].kv_pool, L_in[0].pool_pages * w.kv_heads, args.steps)
@@ -690,7 +801,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": int(lens.max()),
                    "layers": layers, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": D, "page_size": PAGE, "gamma": args.gamma,
-                   "chunk_pages": st.chunk_pages, "stream_groups": groups},
+                   "attn_workers": workers, "stream_groups": groups},
         "selected_fraction": round(kept / pages_all, 4),
         "bytes_per_step": int(total_bytes),
         "roofline": {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(attn_gbs, 1),
@@ -705,11 +816,11 @@ def main():
     result["env"] = {"hip": torch.version.hip, "library": lib.version(),
                      "device": torch.cuda.get_device_name(0),
                      "sources_sha256_16": library_source_hash()}
-    if not args.no_cpu_baseline:
+    if base is not None:
         torch.cuda.synchronize()
+        result["cpu_baseline"] = base
         gpu0 = (layer0[0], layer0[1], outs[0].cpu().numpy())
-        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(
-            w, lens, args.gamma, args.cpu_seconds, gpu=gpu0)
+        result["oracle_check"] = oracle_check(w, lens, args.gamma, gpu0)
     print(json.dumps(result), flush=True)
 
 

@@ -4,9 +4,10 @@
  * One decode step, per (request, KV head) "unit": score every KV page of the
  * request with a cheap upper bound of its attention mass, keep the fewest
  * pages holding at least gamma of the estimated mass, then run exact
- * attention for the unit's GQA group over that variable-length page list,
- * split into fixed-size chunks that each workgroup finds for itself from the
- * prefix-summed list lengths, and merge the chunk partials.
+ * attention for the unit's GQA group over that variable-length page list.
+ * The attention's workgroups each take an even share of all the step's list
+ * entries, found on the device from the prefix-summed list lengths, and the
+ * per-segment partials are merged by log-sum-exp.
  *
  * Pages cited:
  *   [P1] "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
@@ -74,9 +75,9 @@ typedef struct {
   int32_t page_size;    /* P: 16 */
   int32_t max_pages;    /* row length of page_table and of the page lists */
   int32_t max_list_pages; /* 0, or a bound 1..max_pages on every page list's
-                             length: the attention and merge plan for lists
-                             no longer (entries past it are not attended), so
-                             short lists in long rows launch a small grid */
+                             length: the attention and merge clamp each
+                             list's count to it (entries past it are not
+                             attended); 0 means max_pages */
 } sparse_dims;
 
 /* Library version string (host, static storage). */
@@ -151,24 +152,22 @@ size_t sparse_select_workspace_bytes(const sparse_dims* dims);
  *   sel_counts    int32 [U]            k* of each unit (0 when L_b = 0)
  *   sel_pages     int32 [U][max_pages] kept logical pages, ascending, first k* valid
  *   sel_phys      int32 [U][max_pages] page_table[b][sel_pages[..]]
- * Optional whole-batch prefix sums (both NULL, or both given):
+ * Optional whole-batch prefix sum (NULL to skip):
  *   sel_offsets   int32 [U + 1]        exclusive prefix sum of sel_counts
- *   chunk_offsets int32 [U + 1]        exclusive prefix sum of ceil(k* / chunk_pages)
- * They are written by whichever workgroup finishes last (a device-side
- * ticket in the workspace).  The attention and merge calls do not need them:
- * they derive their chunk plan from sel_counts.
+ * It is written by whichever workgroup finishes last (a device-side ticket
+ * in the workspace).  The attention and merge calls do not need it: they
+ * derive their plan from sel_counts.
  *
  *   ws / ws_bytes  device workspace of at least sparse_select_workspace_bytes(),
- *                  needed only with the prefix sums (NULL otherwise); it must
+ *                  needed only with the prefix sum (NULL otherwise); it must
  *                  be zero-filled ONCE before its first use and is left
  *                  zero-filled by every call.  Calls sharing one workspace
  *                  must not overlap in time.
- *   gamma          in (0, 1]; chunk_pages in [1, max_pages]
+ *   gamma          in (0, 1]
  */
 sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logits,
                                      const int32_t* ctx_lens, const int32_t* page_table,
-                                     float gamma, int32_t chunk_pages, int32_t* sel_counts,
-                                     int32_t* sel_offsets, int32_t* chunk_offsets,
+                                     float gamma, int32_t* sel_counts, int32_t* sel_offsets,
                                      int32_t* sel_pages, int32_t* sel_phys, void* ws,
                                      size_t ws_bytes, void* stream);
 
@@ -177,18 +176,20 @@ sparse_status sparse_select_coverage(const sparse_dims* dims, const float* logit
  * argued against ([P1], abstract, sentence on fixed budgets): per unit keep
  * the min(k_pages, n_b) pages of highest group mass m (m as in
  * sparse_select_coverage), ties to the lower page index.  Same outputs,
- * workspace and prefix sums as sparse_select_coverage.  k_pages >= 1.
+ * workspace and prefix sum as sparse_select_coverage.  k_pages >= 1.
  */
 sparse_status sparse_select_topk(const sparse_dims* dims, const float* logits,
                                  const int32_t* ctx_lens, const int32_t* page_table,
-                                 int32_t k_pages, int32_t chunk_pages, int32_t* sel_counts,
-                                 int32_t* sel_offsets, int32_t* chunk_offsets, int32_t* sel_pages,
-                                 int32_t* sel_phys, void* ws, size_t ws_bytes, void* stream);
+                                 int32_t k_pages, int32_t* sel_counts, int32_t* sel_offsets,
+                                 int32_t* sel_pages, int32_t* sel_phys, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /*
  * sparse_append_tokens -- decode-time append of each request's new token,
- * with the refresh of its page's summary (so the step's own token is scored
- * like every other).  For request b with L_b = ctx_lens[b] tokens, the token
+ * with the refresh of its page's summary, so that the step's own token is
+ * scored like every other: the coverage rule is applied anew at every decode
+ * step over the whole context so far ([P1], abstract, coverage-rule
+ * sentence: per request, layer, KV head and step).  For request b with L_b = ctx_lens[b] tokens, the token
  * goes to logical page p = L_b / 16, slot t = L_b % 16, of physical page
  * x = page_table[b][p] (allocated by the caller): row t of the K tile and
  * column t of the channel-major V tile, for every KV head.  The summary of
@@ -205,59 +206,72 @@ sparse_status sparse_append_tokens(const sparse_dims* dims, const uint16_t* k_ne
                                    const int32_t* page_table, int32_t* ctx_lens, uint16_t* summ,
                                    void* stream);
 
-/* Upper bound on the number of chunks (= partial slots) of one step (host):
- * U * ceil(L / chunk_pages), L = max_list_pages if set, else max_pages.
- * Returns -1 for invalid dims or chunk_pages < 1. */
-int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t chunk_pages);
+/* Fewest list entries the attention gives one workgroup: a step of T
+ * entries runs on min(W, ceil(T / SPARSE_ATTN_MIN_WORKER_PAGES)) of its W
+ * workgroups (see sparse_decode_attn). */
+#define SPARSE_ATTN_MIN_WORKER_PAGES 32
+
+/* Partial slots one step of sparse_decode_attn may write (host): U + W, with
+ * U = batch * num_kv_heads and W = workers, or the current device's compute
+ * unit count when workers = 0.  Returns -1 for invalid dims, workers < 0, or
+ * workers = 0 when the current device cannot be queried. */
+int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t workers);
 
 /*
  * sparse_decode_attn -- self-planning split-K attention over the page lists
  * ([P1], abstract, sentence on self-planning attention: every block works
  * out from the per-head list lengths which part it handles, so no plan is
- * made on the host and the step stays inside the graph).
+ * made on the host and the step stays inside the graph; and the sentence on
+ * FA3/FlashInfer, which pad the lists, run unbalanced blocks or plan on the
+ * host -- the even split below does none of these).
  *
- * Unit u's list (k_u = min(sel_counts[u], L) entries, L the dims' list
- * bound) splits evenly into n_u = ceil(k_u / chunk_pages) chunks: chunk i
- * holds entries [floor(i k_u / n_u), floor((i + 1) k_u / n_u)), so sizes
- * differ by at most one page and none exceeds chunk_pages.  Workgroups are
- * numbered over every unit's first floor(k_u / chunk_pages) chunks (unit
- * order), then the last chunk of each unit that chunk_pages does not divide
- * (unit order), so units shorter than one chunk come last.  The grid has
- * max_parts workgroups, fixed at enqueue time; workgroup c derives, from
- * sel_counts alone (wave prefix sums over the per-unit chunk counts), the
- * unit and the list entries it owns, and computes exact attention of the
- * unit's G query heads over the valid tokens of those pages; workgroups past
- * the last chunk exit.  Writes, for chunk
- * i of unit u (slot c = u * ceil(L / chunk_pages) + i; L is max_list_pages,
- * or else max_pages) and head g:
- *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the chunk)
+ * The balanced plan.  Unit u contributes k_u = min(sel_counts[u], Lb)
+ * entries (Lb the dims' list bound); laid end to end in unit order they are
+ * T = sum_u k_u global positions, entry e of unit u at off_u + e with
+ * off_u = sum_{v<u} k_v.  The grid has W = workers workgroups (0: one per
+ * compute unit of the current device), fixed at enqueue time; the step uses
+ * W' = min(W, ceil(T / SPARSE_ATTN_MIN_WORKER_PAGES)) of them (0 when
+ * T = 0), and worker w < W' owns positions [floor(w T / W'),
+ * floor((w + 1) T / W')) -- the same number of pages, to within one, for
+ * every worker whatever the list lengths.  Each workgroup derives T, W' and
+ * its units from sel_counts alone (wave prefix sums), then, for every unit
+ * u its range touches, computes exact attention of u's G query heads over
+ * the valid tokens of the pages at those positions and writes, in slot
+ * c = u + w, for head g:
+ *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the segment)
  *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
- * Slots past a unit's last chunk are left as they were.
+ * (lse = -inf and o = 0 for a segment with no valid token).  Slots that no
+ * (unit, worker) pair of this step uses are left as they were.
  * K/V are read from the pool at sel_phys (physical ids or cache slots).
  *
  *   part_o   fp32 [max_parts][G][128];  part_lse fp32 [max_parts][G]
- *   max_parts must equal sparse_decode_max_parts(dims, chunk_pages)
+ *   max_parts must equal sparse_decode_max_parts(dims, workers)
+ *   workers  0 .. 2^20
  */
 sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
                                  int64_t stride_page, int64_t stride_head, int64_t pool_pages,
                                  const int32_t* ctx_lens, const int32_t* sel_counts,
                                  const int32_t* sel_pages, const int32_t* sel_phys, float scale,
-                                 int32_t chunk_pages, float* part_o, float* part_lse,
+                                 int32_t workers, float* part_o, float* part_lse,
                                  int64_t max_parts, void* stream);
 
 /*
- * sparse_merge_splits -- log-sum-exp merge of the chunk partials of each unit:
- *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) * o_c
- * (the identity that makes the split over chunks exact).  Unit u's chunks
- * are the slots u * ceil(L / chunk_pages) + [0, ceil(k_u / chunk_pages)),
- * k_u = min(sel_counts[u], L), as sparse_decode_attn wrote them (same
- * chunk_pages and dims); other slots are not read as values.
+ * sparse_merge_splits -- log-sum-exp merge of each unit's segment partials:
+ *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) * o_c,
+ * the identity that makes exact the split of one page list over several
+ * workgroups ([P1], abstract, sentence on self-planning attention: a list
+ * is shared among the blocks that plan their own part of it).  Unit u's
+ * partials are the slots u + w for the workers w from the owner of its first
+ * position (off_u) to the owner of its last (off_u + k_u - 1) under the
+ * plan of sparse_decode_attn, found from sel_counts alone; workers and dims
+ * must be those of the sparse_decode_attn call that wrote them.  Other slots
+ * are not read as values.
  *   out      fp32 [B][Hq][128];  out_lse fp32 [B][Hq]
  * A unit with no kept page gets o = 0 and lse = -inf.
  */
 sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                   const float* part_lse, const int32_t* sel_counts,
-                                  int32_t chunk_pages, float* out, float* out_lse, void* stream);
+                                  int32_t workers, float* out, float* out_lse, void* stream);
 
 /* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
  * list of placed misses handed from the resolve kernel to the fetch kernel. */

@@ -23,7 +23,6 @@ from .sparse_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     f64_to_bf16_bits,
     summaries,
-    summaries_pool,
     bound,
     page_logits,
     head_mass,
@@ -36,7 +35,6 @@ from .sparse_oracle import (  # noqa: F401
     merge_partials,
     dense_unit,
     list_accepted,
-    unit_pages,
 )
 from .lru import (LRUState, pooled_unit, resolve_pooled_step, resolve_step,  # noqa: F401
                   textbook_bucketed_trace, textbook_lru_trace)

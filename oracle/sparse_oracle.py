@@ -26,8 +26,28 @@ What the pages fix and what is read into them:
   its definition).
 
 Functions whose agreement with the pages' own (unprinted) estimator cannot be
-checked are marked "parity unpinned" below; every other function is pinned by
-the CPU tests against closed forms, brute force or library routines.
+checked are marked "parity unpinned" below (that agreement only: each is still
+pinned to the mathematics).  Every function is pinned by a CPU test in
+tests/test_oracle_pins.py against something other than itself:
+
+  bf16_bits_to_f64, f64_to_bf16_bits  all 65536 patterns; ties to even; torch's rounding
+  summaries                           brute-force loops with tails and signed zeros
+  bound                               dominates the true max logit; loops; q >= 0 / q <= 0
+                                      and identical-key closed forms
+  page_logits, head_mass, group_mass  sum to one; equal the exact dense page masses when
+                                      every token of a page shares its key; the
+                                      hand-derived worked example (tests/golden)
+  coverage_cut                        brute force over all subsets; monotone and nested in
+                                      gamma; n = 1, ties, gamma = 1; tests/golden fixtures
+  topk_cut                            brute force; agrees with the coverage cut at k = k*
+  select_unit                         the worked example's masses and cuts from bf16 bits
+  attend_tokens, attend_pages         brute-force loops; scipy logsumexp; one token,
+                                      equal keys, page permutation; worked example
+  dense_unit                          gamma = 1 against brute-force dense attention
+  merge_partials                      any partition of the tokens merges to the whole
+  list_accepted                       accepts exact lists, rejects planted defects
+  (oracle/lru.py)                     a textbook OrderedDict LRU, an explicit bucket model
+                                      and per-request caches without pool pressure
 """
 
 import numpy as np
@@ -96,20 +116,6 @@ def summaries(k_pages_bits, n_valid):
     kmin = np.take_along_axis(k, imin[:, None, :], axis=1)[:, 0, :]
     kmax = np.take_along_axis(k, imax[:, None, :], axis=1)[:, 0, :]
     return kmin.astype(np.uint16), kmax.astype(np.uint16)
-
-
-def summaries_pool(k_pool_tiles, n_valid_per_page):
-    """Summaries of a whole pool: k_pool_tiles [Ppool][Hkv][P][D] (token-major
-    K tiles), n_valid_per_page [Ppool] -> [Ppool][Hkv][2][D] (kmin then kmax)."""
-    k = np.asarray(k_pool_tiles)
-    Pp, H, P, D = k.shape
-    out = np.empty((Pp, H, 2, D), dtype=np.uint16)
-    nv = np.asarray(n_valid_per_page).reshape(Pp)
-    for h in range(H):
-        lo, hi = summaries(k[:, h], nv)
-        out[:, h, 0] = lo
-        out[:, h, 1] = hi
-    return out
 
 
 # ----------------------------------------------------------------------------
@@ -317,24 +323,3 @@ def list_accepted(A, m, gamma, eps=1e-5):
     if not ((1 - gamma) * (1 - eps) * (S - ma) < gamma * (1 + eps) * (R + ma)):
         return False, "not minimal"
     return True, "ok"
-
-
-# ----------------------------------------------------------------------------
-# Reading a unit out of the documented pool layout
-# ----------------------------------------------------------------------------
-
-def unit_pages(kv_pool_bits, phys_pages, h):
-    """K and V tiles of one KV head for the listed physical pages, as float64.
-
-    Pool layout (the library's documented format): kv_pool_bits
-    [Ppool][Hkv][2][P*D] bf16 bits; slot 0 holds the K tile token-major
-    [P][D], slot 1 holds the V tile channel-major [D][P].  Returns
-    K [n][P][D] and V [n][P][D], both token-major.
-    """
-    pool = np.asarray(kv_pool_bits)
-    Pp, H, two, PD = pool.shape
-    D = PD // PAGE
-    phys = np.asarray(phys_pages, dtype=np.int64)
-    k = bf16_bits_to_f64(pool[phys, h, 0]).reshape(-1, PAGE, D)
-    v = bf16_bits_to_f64(pool[phys, h, 1]).reshape(-1, D, PAGE).transpose(0, 2, 1)
-    return k, np.ascontiguousarray(v)

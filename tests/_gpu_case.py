@@ -12,6 +12,8 @@ from adaptive_sparse_paged_amd import inputs as I
 from adaptive_sparse_paged_amd import lib
 from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides
 
+from _oracle_pool import score_tolerance
+
 ATTN_TOL = 1e-2      # max-abs on outputs (bf16 K/V, fp32 accumulation)
 LIST_EPS = 1e-5      # relative mass perturbation under which a list is accepted
 
@@ -40,9 +42,10 @@ class GpuLayer:
         lib.build_page_summaries(self.dims, self.li.kv_pool, self.stride_page, self.stride_head,
                                  P, pages, self.li.page_valid, self.summ)
 
-    def step(self, gamma, chunk_pages):
-        st = SparseDecodeStep(self.dims, gamma, chunk_pages, scale=self.w.scale)
-        return st
+    def step(self, gamma, workers=0):
+        """A step over this layer's shape; workers = the attention's grid
+        (0: one workgroup per compute unit)."""
+        return SparseDecodeStep(self.dims, gamma, workers, scale=self.w.scale)
 
     def run(self, st):
         li = self.li
@@ -78,9 +81,7 @@ def check_unit(layer, st, b, h, gamma, full=True, attn_on_oracle=None):
     sel = O.select_unit(un["q"], un["kmin"], un["kmax"], un["nv"], w.scale, gamma)
     x_gpu = st.buf.logits[b, h, :, :n].double().cpu().numpy()
     qf = O.bf16_bits_to_f64(un["q"])
-    mag = np.abs(qf)[:, None, :] * np.maximum(np.abs(O.bf16_bits_to_f64(un["kmin"])),
-                                              np.abs(O.bf16_bits_to_f64(un["kmax"])))[None]
-    tol = w.scale * 300 * 2.0 ** -24 * mag.sum(-1) + 1e-6
+    tol = score_tolerance(un["q"], un["kmin"], un["kmax"], w.scale)
     err = np.abs(x_gpu - sel["x"])
     res["score_err"] = float(err.max())
     assert np.all(err <= tol), f"score error {err.max()} above bound"
@@ -108,8 +109,8 @@ def check_unit(layer, st, b, h, gamma, full=True, attn_on_oracle=None):
 
 
 def feed_lists(st, layer, lists):
-    """Write host page lists {u: logical pages} into the step's buffers and the
-    chunk plan they imply (exclusive prefix sums of ceil(count/chunk))."""
+    """Write host page lists {u: logical pages} into the step's buffers (and
+    the exclusive prefix sum of their lengths)."""
     w = layer.w
     U = w.batch * w.kv_heads
     MP = layer.dims.max_pages
@@ -122,11 +123,8 @@ def feed_lists(st, layer, lists):
         counts[u] = len(lst)
         pages[u, :len(lst)] = lst
         phys[u, :len(lst)] = table[b, lst]
-    chunks = -(-counts // st.chunk_pages)
-    offs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     soff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     st.buf.sel_pages.copy_(torch.from_numpy(pages))
     st.buf.sel_phys.copy_(torch.from_numpy(phys))
     st.buf.sel_counts.copy_(torch.from_numpy(counts.astype(np.int32)))
-    st.buf.chunk_offsets.copy_(torch.from_numpy(offs))
     st.buf.sel_offsets.copy_(torch.from_numpy(soff))

@@ -60,15 +60,19 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 
 def test_max_parts_and_workspace(L):
     d = _dims()
-    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 4
-    assert L.sparse_decode_max_parts(ctypes.byref(d), 5) == 4 * 13
-    assert L.sparse_decode_max_parts(ctypes.byref(d), 0) == -1
+    # U + W partial slots: 4 units, W workers
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 + 16
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 5) == 4 + 5
+    assert L.sparse_decode_max_parts(ctypes.byref(d), -1) == -1
+    # 0 = one worker per compute unit of the current device (-1 with no device)
+    r0 = L.sparse_decode_max_parts(ctypes.byref(d), 0)
+    assert r0 == -1 or r0 > 4
     assert L.sparse_select_workspace_bytes(ctypes.byref(d)) >= 4
-    # a bound on the list lengths plans a smaller grid
+    # a bound on the list lengths clamps the lists, not the grid
     d.max_list_pages = 20
-    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 2
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 + 16
     d.max_list_pages = 64
-    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 * 4
+    assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 + 16
     for bad in (-1, 65):
         d.max_list_pages = bad
         assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == -1
@@ -81,6 +85,9 @@ def test_max_parts_and_workspace(L):
     (dict(page_size=32), lib.ERR_UNSUPPORTED),
     (dict(q_heads=7), lib.ERR_INVALID),
     (dict(q_heads=64, kv_heads=2), lib.ERR_UNSUPPORTED),
+    (dict(q_heads=6, kv_heads=2), lib.ERR_UNSUPPORTED),     # G = 3: not a power of two
+    (dict(q_heads=20, kv_heads=4), lib.ERR_UNSUPPORTED),    # G = 5
+    (dict(q_heads=24, kv_heads=2), lib.ERR_UNSUPPORTED),    # G = 12
     (dict(max_pages=40000), lib.ERR_UNSUPPORTED),
     (dict(batch=0), lib.ERR_INVALID),
 ])
@@ -95,26 +102,26 @@ def test_null_and_value_checks(L):
     assert L.sparse_score_pages(None, FAKE, FAKE, 10, FAKE, FAKE, 0.1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_score_pages(ctypes.byref(d), None, FAKE, 10, FAKE, FAKE, 0.1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_score_pages(ctypes.byref(d), FAKE, FAKE, 10, FAKE, FAKE, float("nan"), FAKE, None) == lib.ERR_INVALID
-    sel = lambda gamma, chunk, ws, wsb: L.sparse_select_coverage(
-        ctypes.byref(d), FAKE, FAKE, FAKE, gamma, chunk, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
-    assert sel(0.0, 8, FAKE, 256) == lib.ERR_INVALID
-    assert sel(1.5, 8, FAKE, 256) == lib.ERR_INVALID
-    assert sel(float("nan"), 8, FAKE, 256) == lib.ERR_INVALID
-    assert sel(0.99, 0, FAKE, 256) == lib.ERR_INVALID
-    assert sel(0.99, 65, FAKE, 256) == lib.ERR_INVALID
-    assert sel(0.99, 8, None, 256) == lib.ERR_WORKSPACE
-    assert sel(0.99, 8, FAKE, 1) == lib.ERR_WORKSPACE
-    attn = lambda kvp, sp_, sh, mp: L.sparse_decode_attn(
-        ctypes.byref(d), FAKE, kvp, sp_, sh, 100, FAKE, FAKE, FAKE, FAKE, 0.1, 16, FAKE,
+    sel = lambda gamma, ws, wsb, offs=FAKE: L.sparse_select_coverage(
+        ctypes.byref(d), FAKE, FAKE, FAKE, gamma, FAKE, offs, FAKE, FAKE, ws, wsb, None)
+    assert sel(0.0, FAKE, 256) == lib.ERR_INVALID
+    assert sel(1.5, FAKE, 256) == lib.ERR_INVALID
+    assert sel(float("nan"), FAKE, 256) == lib.ERR_INVALID
+    assert sel(0.99, None, 256) == lib.ERR_WORKSPACE              # prefix sum without workspace
+    assert sel(0.99, FAKE, 1) == lib.ERR_WORKSPACE
+    assert L.sparse_select_coverage(ctypes.byref(d), FAKE, FAKE, FAKE, 0.9, None, None, FAKE,
+                                    FAKE, None, 0, None) == lib.ERR_INVALID   # no counts
+    attn = lambda kvp, sp_, sh, mp, workers=16: L.sparse_decode_attn(
+        ctypes.byref(d), FAKE, kvp, sp_, sh, 100, FAKE, FAKE, FAKE, FAKE, 0.1, workers, FAKE,
         FAKE, mp, None)
-    assert attn(FAKE, 8192, 4096, 15) == lib.ERR_INVALID          # wrong max_parts
-    assert attn(ctypes.c_void_p(0x10002), 8192, 4096, 16) == lib.ERR_INVALID  # misaligned pool
-    assert attn(FAKE, 8191, 4096, 16) == lib.ERR_INVALID          # stride not 16-byte
-    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == lib.ERR_INVALID
-    # the prefix sums are optional, but both or neither
-    assert L.sparse_select_coverage(ctypes.byref(d), FAKE, FAKE, FAKE, 0.9, 8, FAKE, FAKE, None,
-                                    FAKE, FAKE, FAKE, 256, None) == lib.ERR_INVALID
-    assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 8, FAKE, None, None,
+    assert attn(FAKE, 8192, 4096, 19) == lib.ERR_INVALID          # wrong max_parts (U + 16 = 20)
+    assert attn(FAKE, 8192, 4096, 20, workers=-1) == lib.ERR_INVALID
+    assert attn(FAKE, 8192, 4096, 20, workers=(1 << 20) + 1) == lib.ERR_INVALID
+    assert attn(ctypes.c_void_p(0x10002), 8192, 4096, 20) == lib.ERR_INVALID  # misaligned pool
+    assert attn(FAKE, 8191, 4096, 20) == lib.ERR_INVALID          # stride not 16-byte
+    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, None, 16, FAKE, FAKE, None) == lib.ERR_INVALID
+    assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None,
                                 FAKE, FAKE, None, 0, None) == lib.ERR_INVALID
     assert L.sparse_append_tokens(ctypes.byref(d), None, FAKE, FAKE, 8192, 4096, 100, FAKE,
                                   FAKE, FAKE, None) == lib.ERR_INVALID
@@ -180,8 +187,13 @@ def test_missing_library_fails_loudly(tmp_path):
             lib._lib = saved
 
 
-def test_read_blocks_grid_constant_matches_header():
-    """The binding sizes xor_out from its own copy of the header's grid."""
+def test_binding_constants_match_header():
+    """The binding's copies of the header's constants: the read probe's grid
+    (it sizes xor_out) and the attention plan's fewest pages per worker (the
+    bench's partial count follows it)."""
     with open(HEADER) as f:
-        m = re.search(r"#define SPARSE_READ_BLOCKS_GROUPS (\d+)", f.read())
+        text = f.read()
+    m = re.search(r"#define SPARSE_READ_BLOCKS_GROUPS (\d+)", text)
     assert m and int(m.group(1)) == lib.READ_BLOCKS_GROUPS
+    m = re.search(r"#define SPARSE_ATTN_MIN_WORKER_PAGES (\d+)", text)
+    assert m and int(m.group(1)) == lib.ATTN_MIN_WORKER_PAGES

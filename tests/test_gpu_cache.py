@@ -20,7 +20,7 @@ from _gpu_case import feed_lists, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=None,
+def _case(w, C, list_pages, steps, drift, workers=8, check_all_slots=True, lists=None,
           shift=0, pooled=False):
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
@@ -37,7 +37,7 @@ def _case(w, C, list_pages, steps, drift, chunk=8, check_all_slots=True, lists=N
         pool_state = O.LRUState(C, B * space)
     else:
         states = [O.LRUState(C, space) for _ in range(B)]
-    st = SparseDecodeStep(dims, 0.99, chunk, scale=w.scale)
+    st = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
     layer = types.SimpleNamespace(w=w, dims=dims, li=li)
     sp_, sh_ = canonical_strides(H)
     out_stats = []
@@ -139,14 +139,14 @@ def test_cache_resolver_random_lists_and_ties(gpu_lib):
             for h in range(H):
                 lists[t, b, h] = np.sort(rng.choice(n if t % 3 else 30, size=L, replace=False))
     say("[cache] jumping lists, 3 requests x 3 KV heads, 40 slots")
-    stats = _case(w, C=40, list_pages=L, steps=steps, drift=0.0, chunk=5, lists=lists)
+    stats = _case(w, C=40, list_pages=L, steps=steps, drift=0.0, workers=5, lists=lists)
     assert sum(r["evictions"] for r in stats) > 0
 
 
 def test_cache_overflow_flagged(gpu_lib):
     w = I.custom_workload("cache_ovf", 2, 8, 2, ("fixed", 1600), index=122)
     say("[cache] overflow: 2 heads x 20 pages into 30 slots")
-    stats = _case(w, C=30, list_pages=20, steps=2, drift=0.1, chunk=4)
+    stats = _case(w, C=30, list_pages=20, steps=2, drift=0.1, workers=4)
     assert all(r["overflow"] == 1 for r in stats)
 
 
@@ -156,7 +156,7 @@ def test_cache_pool_overflow_flagged(gpu_lib):
     request that shares the boundary) is flagged, as in the oracle."""
     w = I.custom_workload("cache_povf", 3, 8, 2, ("fixed", 1600), index=126)
     say("[cache] pooled overflow: 3 requests x 2 heads x 20 pages into 100 slots")
-    stats = _case(w, C=100, list_pages=20, steps=2, drift=0.1, chunk=4, pooled=True)
+    stats = _case(w, C=100, list_pages=20, steps=2, drift=0.1, workers=4, pooled=True)
     flags = [r["overflow"] for r in stats]
     assert flags[:3] == [0, 0, 1]
 
@@ -170,7 +170,7 @@ def test_cache_resolver_host_tier_shape(gpu_lib):
     ex = base.extra
     say("[cache] host-tier shape: 2 x 524288 tokens, 4096 slots, 448-page lists")
     stats = _case(w, C=ex["capacity"], list_pages=ex["list_pages"], steps=4, drift=ex["drift"],
-                  chunk=128, check_all_slots=False)
+                  workers=128, check_all_slots=False)
     assert stats[-1]["misses"] > 0 and stats[-1]["hits"] > 0
 
 
@@ -182,7 +182,7 @@ def test_cache_pool_host_tier_scale(gpu_lib):
     base = I.WORKLOADS["host_tier_512k"]
     w = I.custom_workload("pool_scale", 8, 32, 8, ("fixed", 131072), alpha=base.alpha, index=127)
     say("[cache] pooled at scale: 8 x 131072 tokens, 32768 shared slots, 448-page lists")
-    stats = _case(w, C=8 * 4096, list_pages=448, steps=4, drift=0.1, chunk=128,
+    stats = _case(w, C=8 * 4096, list_pages=448, steps=4, drift=0.1, workers=128,
                   check_all_slots=False, pooled=True, shift=1)
     assert sum(r["misses"] for r in stats[-8:]) > 0 and sum(r["hits"] for r in stats[-8:]) > 0
 
@@ -275,7 +275,7 @@ def test_cache_pool_shared_by_requests(gpu_lib, shift):
                                    replace=False)
                 cur[b][h] = np.concatenate([keep, fresh])
     say(f"[cache] pooled, shift {shift}: 3 requests with lists of {sizes} pages, 100 slots")
-    stats = _case(w, C=100, list_pages=0, steps=steps, drift=0.0, chunk=5,
+    stats = _case(w, C=100, list_pages=0, steps=steps, drift=0.0, workers=5,
                   lists=_ragged(lists, sizes), shift=shift, pooled=True)
     assert sum(r["evictions"] for r in stats) > 0
 

@@ -1,11 +1,11 @@
-"""More than 512 (request, KV head) units in one step: the attention's chunk
-plan reads the list lengths in segments of 512 units, and numbers every
-unit's full chunks before the partial ones, so with U > 512 a workgroup's
-chunk can lie in a later segment of either numbering pass.  Checked against
-the fp64 oracle on every unit: the whole step (scores, lists accepted by the
-coverage predicate, attention on the GPU's own lists) and the attention +
-merge on random caller-supplied lists (empty, one page, all pages, subsets)
-with small chunks, so that chunks of both passes span several segments."""
+"""More than 512 (request, KV head) units in one step: the attention's plan
+reads the list lengths in segments of 512 units, so with U > 512 a
+workgroup's first unit, and a merge workgroup's unit, can lie in a later
+segment.  Checked against the fp64 oracle on every unit: the whole step
+(scores, lists accepted by the coverage predicate, attention on the GPU's
+own lists) and the attention + merge on random caller-supplied lists (empty,
+one page, all pages, subsets) over a few workgroups, so that each one's
+slice crosses many units and segment boundaries."""
 
 import functools
 
@@ -50,13 +50,13 @@ def test_step_over_576_units(gpu_lib):
             r = check_unit(layer, st, b, h, 0.95)
             exact += int(r["exact"])
             worst = max(worst, r["attn_err"])
-    say(f"  576 units, chunk 3: exact lists {exact}/576, max attn err {worst:.2e}")
+    say(f"  576 units, 3 workers: exact lists {exact}/576, max attn err {worst:.2e}")
 
 
-@pytest.mark.parametrize("chunk", [1, 2, 5])
-def test_attention_on_random_lists_over_576_units(gpu_lib, chunk):
+@pytest.mark.parametrize("workers", [1, 2, 5, 0])
+def test_attention_on_random_lists_over_576_units(gpu_lib, workers):
     layer, units = _layer()
-    rng = np.random.default_rng(1000 + chunk)
+    rng = np.random.default_rng(1000 + workers)
     lists = {}
     for (b, h), un in units.items():
         n = un["n"]
@@ -65,15 +65,13 @@ def test_attention_on_random_lists_over_576_units(gpu_lib, chunk):
         lists[b * W.kv_heads + h] = np.sort(rng.choice(n, size=size, replace=False))
     li = layer.li
     dims = lib.make_dims(W.batch, W.q_heads, W.kv_heads, li.max_pages)
-    stp = SparseDecodeStep(dims, 0.9, chunk, scale=W.scale)
+    stp = SparseDecodeStep(dims, 0.9, workers, scale=W.scale)
     stp.buf.out.fill_(3.0)
     stp.buf.out_lse.fill_(3.0)
     feed_lists(stp, layer, lists)
     stp.attend(li.q, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages, li.ctx_lens)
     torch.cuda.synchronize()
     counts = np.array([len(lists[u]) for u in range(len(lists))])
-    full = int((counts // chunk).sum())
-    partial = int((counts % chunk != 0).sum())
     G = W.group
     worst = 0.0
     out = stp.buf.out.double().cpu().numpy()
@@ -91,5 +89,5 @@ def test_attention_on_random_lists_over_576_units(gpu_lib, chunk):
         worst = max(worst, float(np.abs(o - o_ref).max()))
         assert np.abs(lse - lse_ref).max() < 1e-3, u
     assert worst <= ATTN_TOL
-    say(f"  chunk {chunk}: {full} full + {partial} partial chunks over 576 units, "
+    say(f"  workers {workers}: {int(counts.sum())} list entries over 576 units, "
         f"max err {worst:.1e}")

@@ -1,8 +1,10 @@
 """Property test of the attention over caller-supplied page lists: for
 randomly drawn ragged batches of lists (empty, single-page, full and
-arbitrary subsets), chunk sizes and list bounds, the GPU's attention + merge
+arbitrary subsets), attention grids (1 workgroup up to more workgroups than
+pages, and the device default) and list bounds, the GPU's attention + merge
 matches exact fp64 attention over the same pages (1e-2 max-abs), and units
-with empty lists give o = 0 and lse = -inf."""
+with empty lists give o = 0 and lse = -inf.  Run on a GQA group of 4 and on
+one of 16."""
 
 import functools
 
@@ -21,11 +23,14 @@ from _gpu_case import ATTN_TOL, GpuLayer, feed_lists, say
 
 pytestmark = pytest.mark.gpu
 
-W = I.custom_workload("prop", 4, 8, 2, ("uniform", 17, 3000), alpha=("uniform", 1, 6), index=114)
+W4 = I.custom_workload("prop", 4, 8, 2, ("uniform", 17, 3000), alpha=("uniform", 1, 6),
+                       index=114)
+W16 = I.custom_workload("prop16", 3, 32, 2, ("uniform", 17, 70000), alpha=("uniform", 1, 6),
+                        index=117)
 
 
-@functools.lru_cache(maxsize=1)
-def _layer():
+@functools.lru_cache(maxsize=2)
+def _layer(W):
     layer = GpuLayer(W)
     units = {}
     for b in range(W.batch):
@@ -36,12 +41,25 @@ def _layer():
     return layer, units
 
 
-@settings(max_examples=12, deadline=None, derandomize=True,
-          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
-@given(data=st.data(), chunk=st.sampled_from([1, 3, 8, 32, 64]),
+SETTINGS = dict(deadline=None, derandomize=True,
+                suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+
+
+@settings(max_examples=12, **SETTINGS)
+@given(data=st.data(), workers=st.sampled_from([1, 3, 8, 32, 64, 0, 5000]),
        bounded=st.booleans())
-def test_attention_on_random_ragged_lists(gpu_lib, data, chunk, bounded):
-    layer, units = _layer()
+def test_attention_on_random_ragged_lists(gpu_lib, data, workers, bounded):
+    _check_random_lists(W4, data, workers, bounded)
+
+
+@settings(max_examples=5, **SETTINGS)
+@given(data=st.data(), workers=st.sampled_from([1, 7, 0]), bounded=st.booleans())
+def test_attention_on_random_ragged_lists_g16(gpu_lib, data, workers, bounded):
+    _check_random_lists(W16, data, workers, bounded)
+
+
+def _check_random_lists(W, data, workers, bounded):
+    layer, units = _layer(W)
     lists = {}
     for (b, h), un in units.items():
         n = un["n"]
@@ -54,7 +72,7 @@ def test_attention_on_random_ragged_lists(gpu_lib, data, chunk, bounded):
     bound = max(1, longest) if bounded else 0
     li = layer.li
     dims = lib.make_dims(W.batch, W.q_heads, W.kv_heads, li.max_pages, max_list_pages=bound)
-    stp = SparseDecodeStep(dims, 0.9, chunk, scale=W.scale)
+    stp = SparseDecodeStep(dims, 0.9, workers, scale=W.scale)
     stp.buf.out.fill_(3.0)
     stp.buf.out_lse.fill_(3.0)
     feed_lists(stp, layer, lists)
@@ -74,5 +92,5 @@ def test_attention_on_random_ragged_lists(gpu_lib, data, chunk, bounded):
         worst = max(worst, float(np.abs(o - o_ref).max()))
         assert np.abs(lse - lse_ref).max() < 1e-3, u
     assert worst <= ATTN_TOL
-    say(f"  chunk {chunk} bound {bound}: sizes {sorted(len(x) for x in lists.values())}, "
-        f"max err {worst:.1e}")
+    say(f"  G {W.group} workers {workers} bound {bound}: "
+        f"sizes {sorted(len(x) for x in lists.values())}, max err {worst:.1e}")

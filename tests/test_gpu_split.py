@@ -23,7 +23,7 @@ from _gpu_case import ATTN_TOL, feed_lists, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, C, LP, steps, drift, pooled=False, shift=0, chunk=8, graph_from=None):
+def _run(w, C, LP, steps, drift, pooled=False, shift=0, workers=8, graph_from=None):
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
     host, MP = I.build_host_pool(w, 0, lens=lens)
@@ -32,8 +32,8 @@ def _run(w, C, LP, steps, drift, pooled=False, shift=0, chunk=8, graph_from=None
     U = B * H
     ref_cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
     spl_cache = HbmPageCache(dims, host, C, recency_shift=shift, pooled=pooled)
-    ref = SparseDecodeStep(dims, 0.99, chunk, scale=w.scale)
-    spl = SplitHostTierStep(dims, spl_cache, 0.99, chunk, scale=w.scale)
+    ref = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
+    spl = SplitHostTierStep(dims, spl_cache, 0.99, workers, scale=w.scale)
     layer = types.SimpleNamespace(w=w, dims=dims, li=li)
     lists = I.drift_lists(w, min(I.pages_of(L) for L in lens), LP, steps, drift)
     out = torch.empty((B, w.q_heads, 128), dtype=torch.float32, device="cuda")
@@ -111,5 +111,5 @@ def test_split_cold_step_all_misses(gpu_lib):
     (lse -inf), and the result is the miss pass alone."""
     w = I.custom_workload("split_cold", 3, 16, 4, ("fixed", 2000), index=125)
     say("[split] cold start, B=3 Hkv=4, 256 slots, lists of 40")
-    misses, worst = _run(w, 256, 40, 2, 0.5, chunk=16)
+    misses, worst = _run(w, 256, 40, 2, 0.5, workers=16)
     assert misses > 0

@@ -112,9 +112,8 @@ def test_topk_select_matches_oracle(gpu_lib):
     cov_pages = b_.sel_pages.cpu().numpy().copy()
     exact = total = 0
     for k in (1, 7, 50, 10000):
-        lib.select_topk(layer.dims, b_.logits, li.ctx_lens, li.page_table, k, st.chunk_pages,
-                        b_.sel_counts, b_.sel_offsets, b_.chunk_offsets, b_.sel_pages,
-                        b_.sel_phys, b_.ws)
+        lib.select_topk(layer.dims, b_.logits, li.ctx_lens, li.page_table, k, b_.sel_counts,
+                        b_.sel_offsets, b_.sel_pages, b_.sel_phys, b_.ws)
         torch.cuda.synchronize()
         counts = b_.sel_counts.cpu().numpy()
         for (b, h), sel in oracle.items():
@@ -136,8 +135,7 @@ def test_topk_select_matches_oracle(gpu_lib):
     for u in range(len(ks)):
         b, h = divmod(u, w.kv_heads)
         lib.select_topk(layer.dims, b_.logits, li.ctx_lens, li.page_table, int(ks[u]),
-                        st.chunk_pages, b_.sel_counts, b_.sel_offsets, b_.chunk_offsets,
-                        b_.sel_pages, b_.sel_phys, b_.ws)
+                        b_.sel_counts, b_.sel_offsets, b_.sel_pages, b_.sel_phys, b_.ws)
         torch.cuda.synchronize()
         got = b_.sel_pages[u, :ks[u]].cpu().numpy()
         assert np.array_equal(got, cov_pages[u, :ks[u]])

@@ -31,7 +31,7 @@ def test_stream_slices_regenerate():
         assert torch.equal(I.normal_bf16(key, s, c), full[s:s + c])
 
 
-def test_unit_pages_regenerate_and_queries_deterministic():
+def test_unit_tiles_regenerate_and_queries_deterministic():
     w = I.WORKLOADS["serving_b64"]
     lens = I.context_lengths(w)
     assert lens.min() >= 4096 and lens.max() <= 131072 and (lens % 16 != 0).any()

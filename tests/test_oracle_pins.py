@@ -180,6 +180,22 @@ def test_golden_worked_example_masses_cuts_attention():
     assert np.allclose(lse, np.log(ex["subset_013"]["lse_of"]), atol=1e-13)
 
 
+def test_select_unit_on_the_worked_example():
+    """select_unit (bound, page logits, masses, cut in one call, from bf16
+    bits) gives the hand-derived masses and cuts of the worked example."""
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
+    s = math.log(2.0)
+    q = np.array(ex["q"], dtype=np.float64)
+    nv = np.array([p["valid"] for p in ex["pages"]])
+    key = np.array([p["key"] for p in ex["pages"]], dtype=np.float64)
+    expect = np.array(ex["mass_num"]) / ex["mass_den"]
+    for g_str, lst in ex["cuts"].items():
+        sel = O.select_unit(_bits(q), _bits(key), _bits(key), nv, s, float(g_str))
+        assert sel["list"].tolist() == lst and sel["count"] == len(lst)
+        assert np.allclose(sel["m"], expect, rtol=1e-13, atol=0)
+
+
 # ---------------------------------------------------------------- the cut
 
 def test_golden_dyadic_cuts():
