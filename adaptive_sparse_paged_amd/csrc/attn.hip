@@ -327,6 +327,42 @@ extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t work
   return (int64_t)dims->batch * dims->num_kv_heads + wmax;
 }
 
+namespace sp {
+
+sparse_status check_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
+                         int64_t stride_page, int64_t stride_head, int64_t pool_pages,
+                         const int32_t* ctx_lens, const int32_t* sel_counts,
+                         const int32_t* sel_pages, const int32_t* sel_phys, float scale,
+                         int32_t workers, int& wmax) {
+  sparse_status st = check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if ((st = check_pool(kv, stride_page, stride_head, pool_pages)) != SPARSE_OK) return st;
+  if (!q || !ctx_lens || !sel_counts || !sel_pages || !sel_phys) return SPARSE_ERR_INVALID;
+  if (!aligned(q, 16) || !isfinite(scale)) return SPARSE_ERR_INVALID;
+  if (workers < 0 || workers > kMaxWorkers) return SPARSE_ERR_INVALID;
+  if ((int64_t)dims->batch * dims->num_kv_heads * dims->max_pages > INT32_MAX)
+    return SPARSE_ERR_UNSUPPORTED;
+  wmax = resolve_workers(workers);
+  return wmax < 1 ? SPARSE_ERR_HIP : SPARSE_OK;
+}
+
+void enqueue_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
+                  int64_t stride_page, int64_t stride_head, int64_t pool_pages,
+                  const int32_t* ctx_lens, const int32_t* sel_counts, const int32_t* sel_pages,
+                  const int32_t* sel_phys, float scale, int wmax, float* part_o, float* part_lse,
+                  hipStream_t stream) {
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  const size_t lds = sizeof(float) * (size_t)kAttnWaves * group * (kD + 2);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)wmax), dim3(256), lds, stream, q, kv,
+                     stride_page, stride_head, pool_pages, ctx_lens, sel_counts, sel_pages,
+                     sel_phys, scale_log2, hkv, group, dims->max_pages, list_cap(dims), U, wmax,
+                     part_o, part_lse);
+}
+
+}  // namespace sp
+
 extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q,
                                             const uint16_t* kv, int64_t stride_page,
                                             int64_t stride_head, int64_t pool_pages,
@@ -334,25 +370,13 @@ extern "C" sparse_status sparse_decode_attn(const sparse_dims* dims, const uint1
                                             const int32_t* sel_pages, const int32_t* sel_phys,
                                             float scale, int32_t workers, float* part_o,
                                             float* part_lse, int64_t max_parts, void* stream) {
-  sparse_status st = sp::check_dims(dims);
+  int wmax = 0;
+  sparse_status st = sp::check_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
+                                    sel_counts, sel_pages, sel_phys, scale, workers, wmax);
   if (st != SPARSE_OK) return st;
-  if ((st = sp::check_pool(kv, stride_page, stride_head, pool_pages)) != SPARSE_OK) return st;
-  if (!q || !ctx_lens || !sel_counts || !sel_pages || !sel_phys || !part_o || !part_lse)
-    return SPARSE_ERR_INVALID;
-  if (!sp::aligned(q, 16) || !sp::aligned(part_o, 16) || !isfinite(scale))
-    return SPARSE_ERR_INVALID;
-  if (workers < 0 || workers > sp::kMaxWorkers) return SPARSE_ERR_INVALID;
-  const int wmax = sp::resolve_workers(workers);
-  if (wmax < 1) return SPARSE_ERR_HIP;
-  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
-  const int U = dims->batch * hkv;
-  if (max_parts != (int64_t)U + wmax) return SPARSE_ERR_INVALID;
-  if ((int64_t)U * dims->max_pages > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
-  const size_t lds = sizeof(float) * (size_t)sp::kAttnWaves * group * (sp::kD + 2);
-  const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(sp::attn_kernel, dim3((unsigned)wmax), dim3(256), lds, (hipStream_t)stream,
-                     q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
-                     sel_pages, sel_phys, scale_log2, hkv, group, dims->max_pages,
-                     sp::list_cap(dims), U, wmax, part_o, part_lse);
+  if (!part_o || !part_lse || !sp::aligned(part_o, 16)) return SPARSE_ERR_INVALID;
+  if (max_parts != (int64_t)dims->batch * dims->num_kv_heads + wmax) return SPARSE_ERR_INVALID;
+  sp::enqueue_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
+                   sel_pages, sel_phys, scale, wmax, part_o, part_lse, (hipStream_t)stream);
   return sp::launch_status();
 }

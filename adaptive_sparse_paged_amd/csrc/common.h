@@ -291,6 +291,23 @@ inline int resolve_workers(int workers) {
   return n;
 }
 
+// Shared by the attention entry points (attn.hip, attn_merge.hip): host-side
+// checks of the attention's arguments (sets wmax, the resolved grid), and the
+// attention and merge launches without checks.
+sparse_status check_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
+                         int64_t stride_page, int64_t stride_head, int64_t pool_pages,
+                         const int32_t* ctx_lens, const int32_t* sel_counts,
+                         const int32_t* sel_pages, const int32_t* sel_phys, float scale,
+                         int32_t workers, int& wmax);
+void enqueue_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv,
+                  int64_t stride_page, int64_t stride_head, int64_t pool_pages,
+                  const int32_t* ctx_lens, const int32_t* sel_counts, const int32_t* sel_pages,
+                  const int32_t* sel_phys, float scale, int wmax, float* part_o, float* part_lse,
+                  hipStream_t stream);
+void enqueue_merge(const sparse_dims* dims, const float* part_o, const float* part_lse,
+                   const int32_t* sel_counts, int wmax, float* out, float* out_lse,
+                   hipStream_t stream);
+
 inline sparse_status launch_status() {
   return hipGetLastError() == hipSuccess ? SPARSE_OK : SPARSE_ERR_HIP;
 }

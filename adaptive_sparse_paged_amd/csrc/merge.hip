@@ -94,6 +94,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 
 }  // namespace sp
 
+namespace sp {
+
+void enqueue_merge(const sparse_dims* dims, const float* part_o, const float* part_lse,
+                   const int32_t* sel_counts, int wmax, float* out, float* out_lse,
+                   hipStream_t stream) {
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  hipLaunchKernelGGL(merge_kernel, dim3(U, group), dim3(kMergeThreads), 0, stream, part_o,
+                     part_lse, sel_counts, list_cap(dims), U, wmax, hkv, group, out, out_lse);
+}
+
+}  // namespace sp
+
 extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                              const float* part_lse, const int32_t* sel_counts,
                                              int32_t workers, float* out, float* out_lse,
@@ -106,11 +119,7 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
   if (workers < 0 || workers > sp::kMaxWorkers) return SPARSE_ERR_INVALID;
   const int wmax = sp::resolve_workers(workers);
   if (wmax < 1) return SPARSE_ERR_HIP;
-  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
-  const int U = dims->batch * hkv;
-  hipLaunchKernelGGL(sp::merge_kernel, dim3(U, group), dim3(sp::kMergeThreads), 0,
-                     (hipStream_t)stream, part_o, part_lse, sel_counts, sp::list_cap(dims), U,
-                     wmax, hkv, group, out, out_lse);
+  sp::enqueue_merge(dims, part_o, part_lse, sel_counts, wmax, out, out_lse, (hipStream_t)stream);
   return sp::launch_status();
 }
 

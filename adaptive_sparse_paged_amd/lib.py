@@ -37,6 +37,7 @@ EXPORTS = (
     "sparse_hbm_cache_fetch",
     "sparse_split_misses",
     "sparse_lse_combine",
+    "sparse_decode_attn_merge",
 )
 
 
@@ -106,6 +107,8 @@ _SIGS = {
     "sparse_hbm_cache_fetch": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "sparse_split_misses": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
+    "sparse_decode_attn_merge": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
+                                        _P, _P, _I64, _P, _P, _P]),
 }
 
 _lib = None
@@ -201,6 +204,17 @@ def decode_attn(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel
         ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
         _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, workers,
         _ptr(part_o), _ptr(part_lse), max_parts, _stream(stream)))
+
+
+def decode_attn_merge(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
+                      sel_pages, sel_phys, scale, workers, part_o, part_lse, max_parts, out,
+                      out_lse, stream=None):
+    """decode_attn then merge_splits in one call (the partials in part_o / part_lse)."""
+    _dev(q, kv, ctx_lens, sel_counts, sel_pages, sel_phys, part_o, part_lse, out, out_lse)
+    _check("sparse_decode_attn_merge", load().sparse_decode_attn_merge(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
+        _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, workers,
+        _ptr(part_o), _ptr(part_lse), max_parts, _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
 def merge_splits(dims, part_o, part_lse, sel_counts, workers, out, out_lse, stream=None):

@@ -151,11 +151,9 @@ class SparseDecodeStep:
         out_lse = b.out_lse if out_lse is None else out_lse
         sp = b.sel_pages if sel_pages is None else sel_pages
         sx = b.sel_phys if sel_phys is None else sel_phys
-        lib.decode_attn(d, q, kv, stride_page, stride_head, pool_pages, ctx_lens, b.sel_counts,
-                        sp, sx, self.scale, self.workers, b.part_o, b.part_lse,
-                        self.max_parts, stream)
-        lib.merge_splits(d, b.part_o, b.part_lse, b.sel_counts, self.workers, out, out_lse,
-                         stream)
+        lib.decode_attn_merge(d, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
+                              b.sel_counts, sp, sx, self.scale, self.workers, b.part_o,
+                              b.part_lse, self.max_parts, out, out_lse, stream)
         return out, out_lse
 
     def run(self, q, summ, kv, stride_page, stride_head, pool_pages, page_table, ctx_lens,

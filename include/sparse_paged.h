@@ -273,6 +273,25 @@ sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                   const float* part_lse, const int32_t* sel_counts,
                                   int32_t workers, float* out, float* out_lse, void* stream);
 
+/*
+ * sparse_decode_attn_merge -- sparse_decode_attn followed by
+ * sparse_merge_splits on the same stream, in one call: attention of every
+ * unit's G query heads over its page list ([P1], abstract, sentence on
+ * self-planning attention), the per-segment partials passing through the
+ * caller's part_o / part_lse (same layout, size and max_parts rule as
+ * sparse_decode_attn), the merged result in out / out_lse (as
+ * sparse_merge_splits).  Same kernels, so the outputs are bitwise those of
+ * the two calls.  Errors as the two calls; nothing is enqueued on error.
+ */
+sparse_status sparse_decode_attn_merge(const sparse_dims* dims, const uint16_t* q,
+                                       const uint16_t* kv, int64_t stride_page,
+                                       int64_t stride_head, int64_t pool_pages,
+                                       const int32_t* ctx_lens, const int32_t* sel_counts,
+                                       const int32_t* sel_pages, const int32_t* sel_phys,
+                                       float scale, int32_t workers, float* part_o,
+                                       float* part_lse, int64_t max_parts, float* out,
+                                       float* out_lse, void* stream);
+
 /* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
  * list of placed misses handed from the resolve kernel to the fetch kernel. */
 size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);

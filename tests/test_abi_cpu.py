@@ -119,6 +119,13 @@ def test_null_and_value_checks(L):
     assert attn(FAKE, 8192, 4096, 20, workers=(1 << 20) + 1) == lib.ERR_INVALID
     assert attn(ctypes.c_void_p(0x10002), 8192, 4096, 20) == lib.ERR_INVALID  # misaligned pool
     assert attn(FAKE, 8191, 4096, 20) == lib.ERR_INVALID          # stride not 16-byte
+    am = lambda mp, out=FAKE, workers=16: L.sparse_decode_attn_merge(
+        ctypes.byref(d), FAKE, FAKE, 8192, 4096, 100, FAKE, FAKE, FAKE, FAKE, 0.1, workers, FAKE,
+        FAKE, mp, out, FAKE, None)
+    assert am(19) == lib.ERR_INVALID                              # wrong max_parts
+    assert am(20, out=None) == lib.ERR_INVALID
+    assert am(20, out=ctypes.c_void_p(0x10004)) == lib.ERR_INVALID   # out not 16-byte aligned
+    assert am(20, workers=-3) == lib.ERR_INVALID
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, None, 16, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None,

@@ -362,3 +362,28 @@ def test_concentrated_query_end_to_end(gpu_lib):
             f"max attn err {max(s['attn_err'] for s in stats):.2e}")
         assert all(s["exact"] for s in stats)
         assert 1 <= min(counts) and max(counts) <= 3
+
+
+def test_attn_merge_in_one_call_equals_two_calls(gpu_lib):
+    """sparse_decode_attn_merge runs the same kernels as sparse_decode_attn
+    followed by sparse_merge_splits: bitwise the same outputs."""
+    w = I.custom_workload("one_call", 3, 8, 2, ("uniform", 20, 9000), alpha=("uniform", 1, 6),
+                          index=119)
+    layer = GpuLayer(w)
+    li = layer.li
+    for workers in (1, 7, 0):
+        st = layer.step(0.9, workers)
+        st.score_select(li.q, layer.summ, li.pool_pages, li.page_table, li.ctx_lens)
+        st.attend(li.q, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages,
+                  li.ctx_lens)                      # the one-call path
+        torch.cuda.synchronize()
+        one = (st.buf.out.clone(), st.buf.out_lse.clone())
+        out2, lse2 = torch.empty_like(one[0]), torch.empty_like(one[1])
+        lib.decode_attn(layer.dims, li.q, li.kv_pool, layer.stride_page, layer.stride_head,
+                        li.pool_pages, li.ctx_lens, st.buf.sel_counts, st.buf.sel_pages,
+                        st.buf.sel_phys, st.scale, workers, st.buf.part_o, st.buf.part_lse,
+                        st.max_parts)
+        lib.merge_splits(layer.dims, st.buf.part_o, st.buf.part_lse, st.buf.sel_counts, workers,
+                         out2, lse2)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], out2) and torch.equal(one[1], lse2), workers
