@@ -38,6 +38,7 @@ EXPORTS = (
     "sparse_split_misses",
     "sparse_lse_combine",
     "sparse_decode_attn_merge",
+    "sparse_decode_attn_merge_noalloc",
 )
 
 
@@ -109,6 +110,8 @@ _SIGS = {
     "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_decode_attn_merge": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
                                         _P, _P, _I64, _P, _P, _P]),
+    "sparse_decode_attn_merge_noalloc": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F,
+                                                _I32, _P, _P, _P]),
 }
 
 _lib = None
@@ -215,6 +218,21 @@ def decode_attn_merge(dims, q, kv, stride_page, stride_head, pool_pages, ctx_len
         ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
         _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, workers,
         _ptr(part_o), _ptr(part_lse), max_parts, _ptr(out), _ptr(out_lse), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # SPARSE_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attn_merge_noalloc(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
+                              sel_counts, sel_pages, sel_phys, scale, workers, out, out_lse,
+                              stream=None):
+    """decode_attn_merge with the partials in the library's own device array
+    (no allocation; steps up to NOALLOC_SCRATCH_BYTES of partials)."""
+    _dev(q, kv, ctx_lens, sel_counts, sel_pages, sel_phys, out, out_lse)
+    _check("sparse_decode_attn_merge_noalloc", load().sparse_decode_attn_merge_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), stride_page, stride_head, pool_pages,
+        _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), scale, workers,
+        _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
 def merge_splits(dims, part_o, part_lse, sel_counts, workers, out, out_lse, stream=None):

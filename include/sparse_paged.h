@@ -292,6 +292,38 @@ sparse_status sparse_decode_attn_merge(const sparse_dims* dims, const uint16_t* 
                                        float* part_lse, int64_t max_parts, float* out,
                                        float* out_lse, void* stream);
 
+/*
+ * sparse_decode_attn_merge_noalloc -- sparse_decode_attn_merge for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same outputs, bitwise, but the partials live in a library-owned device
+ * array of SPARSE_NOALLOC_SCRATCH_BYTES per GPU (a static __device__ array,
+ * held until the process ends), so the caller passes only inputs and outputs
+ * and the call allocates nothing.
+ *
+ * Limit: (U + W) * G * 129 * 4 bytes <= SPARSE_NOALLOC_SCRATCH_BYTES, with
+ * U = batch * num_kv_heads, W the resolved workers (see sparse_decode_attn);
+ * larger steps return SPARSE_ERR_WORKSPACE (use sparse_decode_attn_merge
+ * with a caller workspace).  16 MiB holds e.g. 7800 units at G = 4 and
+ * W = 256.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams) race and give wrong
+ * outputs; calls ordered on one stream are safe.  Nothing in the array needs
+ * clearing: a call reads only partials it wrote itself.  The first call made
+ * with a device current resolves that device's array address (a host
+ * query, no allocation); make it once before capturing a graph.  Errors as
+ * sparse_decode_attn_merge; SPARSE_ERR_HIP if the address cannot be resolved.
+ */
+#define SPARSE_NOALLOC_SCRATCH_BYTES (16u << 20)
+sparse_status sparse_decode_attn_merge_noalloc(const sparse_dims* dims, const uint16_t* q,
+                                               const uint16_t* kv, int64_t stride_page,
+                                               int64_t stride_head, int64_t pool_pages,
+                                               const int32_t* ctx_lens,
+                                               const int32_t* sel_counts,
+                                               const int32_t* sel_pages,
+                                               const int32_t* sel_phys, float scale,
+                                               int32_t workers, float* out, float* out_lse,
+                                               void* stream);
+
 /* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
  * list of placed misses handed from the resolve kernel to the fetch kernel. */
 size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);

@@ -126,6 +126,12 @@ def test_null_and_value_checks(L):
     assert am(20, out=None) == lib.ERR_INVALID
     assert am(20, out=ctypes.c_void_p(0x10004)) == lib.ERR_INVALID   # out not 16-byte aligned
     assert am(20, workers=-3) == lib.ERR_INVALID
+    na = lambda dd, out=FAKE: L.sparse_decode_attn_merge_noalloc(
+        ctypes.byref(dd), FAKE, FAKE, 8192, 4096, 100, FAKE, FAKE, FAKE, FAKE, 0.1, 16, out,
+        FAKE, None)
+    assert na(d, out=None) == lib.ERR_INVALID
+    # partials beyond the library's device array: (16384 + 16) * 4 * 129 * 4 bytes > 16 MiB
+    assert na(_dims(batch=2048, q_heads=32, kv_heads=8)) == lib.ERR_WORKSPACE
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, None, 16, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None,
@@ -204,3 +210,5 @@ def test_binding_constants_match_header():
     assert m and int(m.group(1)) == lib.READ_BLOCKS_GROUPS
     m = re.search(r"#define SPARSE_ATTN_MIN_WORKER_PAGES (\d+)", text)
     assert m and int(m.group(1)) == lib.ATTN_MIN_WORKER_PAGES
+    m = re.search(r"#define SPARSE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_SCRATCH_BYTES
