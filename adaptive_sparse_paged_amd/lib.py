@@ -39,9 +39,6 @@ EXPORTS = (
     "sparse_lse_combine",
     "sparse_decode_attn_merge",
     "sparse_decode_attn_merge_noalloc",
-    "sparse_coop_workspace_bytes",
-    "sparse_select_coverage_coop",
-    "sparse_score_select_coverage",
 )
 
 
@@ -115,11 +112,6 @@ _SIGS = {
                                         _P, _P, _I64, _P, _P, _P]),
     "sparse_decode_attn_merge_noalloc": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F,
                                                 _I32, _P, _P, _P]),
-    "sparse_coop_workspace_bytes": (ctypes.c_size_t, [_D]),
-    "sparse_select_coverage_coop": (_I32, [_D, _P, _P, _P, _F, _P, _P, _P, _P, ctypes.c_size_t,
-                                           _P]),
-    "sparse_score_select_coverage": (_I32, [_D, _P, _P, _I64, _P, _P, _F, _F, _P, _P, _P, _P,
-                                            ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -200,40 +192,6 @@ def select_coverage(dims, logits, ctx_lens, page_table, gamma, sel_counts, sel_o
 
 
 ATTN_MIN_WORKER_PAGES = 32   # SPARSE_ATTN_MIN_WORKER_PAGES
-
-
-def coop_workspace_bytes(dims):
-    return int(load().sparse_coop_workspace_bytes(ctypes.byref(dims)))
-
-
-def select_coverage_coop(dims, logits, ctx_lens, page_table, gamma, sel_counts, sel_pages,
-                         sel_phys, ws, stream=None):
-    """The coverage cut with several workgroups per unit.  Returns False
-    (nothing enqueued) when the shape does not suit it."""
-    _dev(logits, ctx_lens, page_table, sel_counts, sel_pages, sel_phys, ws)
-    code = load().sparse_select_coverage_coop(
-        ctypes.byref(dims), _ptr(logits), _ptr(ctx_lens), _ptr(page_table), gamma,
-        _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream))
-    if code == ERR_UNSUPPORTED:
-        return False
-    _check("sparse_select_coverage_coop", code)
-    return True
-
-
-def score_select_coverage(dims, q, summ, pool_pages, page_table, ctx_lens, scale, gamma,
-                          sel_counts, sel_pages, sel_phys, ws, stream=None):
-    """Scoring and the coverage cut in one cooperative kernel.  Returns False
-    (nothing enqueued) when the shape does not suit it."""
-    _dev(q, summ, page_table, ctx_lens, sel_counts, sel_pages, sel_phys, ws)
-    code = load().sparse_score_select_coverage(
-        ctypes.byref(dims), _ptr(q), _ptr(summ), pool_pages, _ptr(page_table), _ptr(ctx_lens),
-        scale, gamma, _ptr(sel_counts), _ptr(sel_pages), _ptr(sel_phys), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream))
-    if code == ERR_UNSUPPORTED:
-        return False
-    _check("sparse_score_select_coverage", code)
-    return True
 
 
 def decode_max_parts(dims, workers=0):

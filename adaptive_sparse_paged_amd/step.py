@@ -55,25 +55,10 @@ class SparseDecodeStep:
     run beside it, so the default is one group.
     """
 
-    SELECT_MODES = ("single", "coop", "fused")
-
     def __init__(self, dims, gamma, workers=0, scale=None, device="cuda", groups=1,
-                 offsets=True, select="single"):
+                 offsets=True):
         """offsets: also write the whole-batch prefix sum (sel_offsets) in the
-        selection; the attention does not need it.
-
-        select: "single" -- sparse_score_pages, then one selection workgroup
-        per unit (sparse_select_coverage); "coop" -- sparse_score_pages, then
-        several cooperating workgroups per unit (sparse_select_coverage_coop);
-        "fused" -- scoring and selection in one cooperative kernel
-        (sparse_score_select_coverage; the logits buffer is not written).
-        "coop" and "fused" fall back to "single" for shapes they do not
-        take, and need offsets=False (they write no prefix sum)."""
-        if select not in self.SELECT_MODES:
-            raise ValueError(f"select must be one of {self.SELECT_MODES}")
-        if select != "single" and offsets:
-            raise ValueError("the cooperative selections write no prefix sum: use offsets=False")
-        self.select = select
+        selection; the attention does not need it."""
         self.dims = dims
         self.offsets = bool(offsets)
         self.gamma = float(gamma)
@@ -97,14 +82,8 @@ class SparseDecodeStep:
             out=torch.empty((B, Hq, HEAD_DIM), **f32),
             out_lse=torch.empty((B, Hq), **f32),
         )
-        self.coop_ws = None
-        if select != "single":
-            self.coop_ws = torch.zeros(lib.coop_workspace_bytes(dims), dtype=torch.uint8,
-                                       device=device)
         self.groups = []
         if groups > 1:
-            if select != "single":
-                raise ValueError("stream groups use the single selection")
             self._make_groups(int(groups), device)
 
     def _make_groups(self, ngroups, device):
@@ -159,15 +138,7 @@ class SparseDecodeStep:
 
     def score_select(self, q, summ, pool_pages, page_table, ctx_lens, stream=None):
         d, b = self.dims, self.buf
-        if self.select == "fused" and lib.score_select_coverage(
-                d, q, summ, pool_pages, page_table, ctx_lens, self.scale, self.gamma,
-                b.sel_counts, b.sel_pages, b.sel_phys, self.coop_ws, stream):
-            return
         lib.score_pages(d, q, summ, pool_pages, page_table, ctx_lens, self.scale, b.logits, stream)
-        if self.select == "coop" and lib.select_coverage_coop(
-                d, b.logits, ctx_lens, page_table, self.gamma, b.sel_counts, b.sel_pages,
-                b.sel_phys, self.coop_ws, stream):
-            return
         on = self.offsets
         lib.select_coverage(d, b.logits, ctx_lens, page_table, self.gamma, b.sel_counts,
                             b.sel_offsets if on else None, b.sel_pages, b.sel_phys,

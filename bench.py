@@ -46,9 +46,6 @@ def parse():
     ap.add_argument("--workers", type=int, default=0,
                     help="attention workgroups (default 0: one per compute unit); the step's "
                          "list entries are split evenly over them on the device")
-    ap.add_argument("--select", default="single", choices=("single", "coop", "fused"),
-                    help="selection: one workgroup per unit, several cooperating workgroups "
-                         "per unit, or scoring and selection in one cooperative kernel")
     ap.add_argument("--groups", type=int, default=1,
                     help="request groups pipelined on separate streams")
     ap.add_argument("--layers", type=int, default=0, help="override the workload's layer count")
@@ -696,7 +693,7 @@ def main():
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, max_pages)
     groups = max(1, min(args.groups, w.batch))
     st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale, device=dev,
-                          groups=groups, offsets=False, select=args.select)
+                          groups=groups, offsets=False)
     workers = st.max_parts - w.batch * w.kv_heads
     outs = [torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     lses = [torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev) for _ in range(layers)]
@@ -733,9 +730,6 @@ def main():
     ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
     per_replay = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     p10, p50, p90 = (float(np.percentile(per_replay, x)) for x in (10, 50, 90))
-
-    if st.coop_ws is not None and int(st.coop_ws[:4].view(torch.int32)[0].item()) != 0:
-        raise RuntimeError("a cooperative selection's wait timed out: outputs invalid")
 
     # bytes moved per step
     G, Hkv = w.group, w.kv_heads
@@ -807,7 +801,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": int(lens.max()),
                    "layers": layers, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": D, "page_size": PAGE, "gamma": args.gamma,
-                   "attn_workers": workers, "stream_groups": groups, "select": args.select},
+                   "attn_workers": workers, "stream_groups": groups},
         "selected_fraction": round(kept / pages_all, 4),
         "bytes_per_step": int(total_bytes),
         "roofline": {"kernel": "attn_kernel", "bound": "hbm", "achieved": round(attn_gbs, 1),

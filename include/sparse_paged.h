@@ -185,48 +185,6 @@ sparse_status sparse_select_topk(const sparse_dims* dims, const float* logits,
                                  size_t ws_bytes, void* stream);
 
 /*
- * The coverage rule with several workgroups per unit, for steps with few
- * long rows (a few requests x KV heads, thousands of pages each), where one
- * workgroup per unit leaves most of the chip idle ([P1], abstract,
- * coverage-rule sentence; the sentence on adaptive budgets costing
- * selection time).  K <= 8 workgroups share a unit's row (up to 2048 pages
- * each); they agree on the unit's normalisers, key range, radix histograms
- * and list offsets through the workspace with device-scope atomics.  The
- * outputs are those of sparse_select_coverage (counts and ascending lists
- * with physical ids; no prefix sum), with the same masses up to the
- * summation order of each head's normaliser.
- *
- * sparse_select_coverage_coop -- from the logits of sparse_score_pages.
- * sparse_score_select_coverage -- each workgroup also scores its pages from
- *   the summaries (as sparse_score_pages, same arguments), so the logits
- *   never go to memory: the scoring and the cut in one kernel.
- *
- *   ws / ws_bytes  device workspace of sparse_coop_workspace_bytes(dims)
- *                  bytes, 16-byte aligned, zero-filled ONCE before its first
- *                  use (every call leaves it zeroed).  Its first 32-bit word
- *                  stays 0 unless a wait between the workgroups timed out
- *                  (~100 ms; the outputs are then invalid).  Calls sharing
- *                  one workspace must not overlap in time.
- * Every workgroup of the grid must be resident at once; the call returns
- * SPARSE_ERR_UNSUPPORTED, enqueueing nothing, when the shape does not allow
- * it on the current device or gains nothing from it (max_pages < 1024, rows
- * longer than 8 x 2048 pages), and the caller uses the one-workgroup path.
- * Other work running beside the call on the same device only delays it.
- */
-size_t sparse_coop_workspace_bytes(const sparse_dims* dims);
-sparse_status sparse_select_coverage_coop(const sparse_dims* dims, const float* logits,
-                                          const int32_t* ctx_lens, const int32_t* page_table,
-                                          float gamma, int32_t* sel_counts, int32_t* sel_pages,
-                                          int32_t* sel_phys, void* ws, size_t ws_bytes,
-                                          void* stream);
-sparse_status sparse_score_select_coverage(const sparse_dims* dims, const uint16_t* q,
-                                           const uint16_t* summ, int64_t pool_pages,
-                                           const int32_t* page_table, const int32_t* ctx_lens,
-                                           float scale, float gamma, int32_t* sel_counts,
-                                           int32_t* sel_pages, int32_t* sel_phys, void* ws,
-                                           size_t ws_bytes, void* stream);
-
-/*
  * sparse_append_tokens -- decode-time append of each request's new token,
  * with the refresh of its page's summary, so that the step's own token is
  * scored like every other: the coverage rule is applied anew at every decode
