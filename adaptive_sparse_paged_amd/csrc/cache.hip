@@ -37,28 +37,37 @@ struct MissRec {
   int32_t slot;
 };
 
-__global__ __launch_bounds__(kResThreads) void resolve_kernel(
-    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
-    int max_pages, int C, int recency_shift, const int32_t* __restrict__ step_counter,
-    int32_t* __restrict__ slot_tag,
-    int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
-    int32_t* __restrict__ sel_phys, int32_t* __restrict__ hit_phys, int32_t* __restrict__ stats,
-    MissRec* __restrict__ misses, int32_t* __restrict__ miss_count) {
+// Per-request ticket word of the resolve: bits [0, 22) misses, [22, 44) hits
+// counted by the hit-pass workgroups, [44, 64) workgroups done.  A request
+// has at most 64 * 32768 = 2^21 list entries, so the counts never carry.
+constexpr int kTkHitShift = 22;
+constexpr int kTkDoneShift = 44;
+constexpr unsigned long long kTkCountMask = (1ull << kTkHitShift) - 1ull;
+
+// Misses of request b, placed by its last workgroup (the kernel below):
+// requested-slot marks, victims, available slots, then the misses in
+// ascending unit id take them.  M (>= 1) and H are the request's miss and hit
+// totals from the ticket.  With miss lists, each unit's placed misses are also
+// written in list order (a unit's misses are a contiguous run of the
+// request's misses, which go head by head).
+__device__ void resolve_place(int b, const int32_t* __restrict__ sel_counts,
+                              const int32_t* __restrict__ sel_pages, int hkv, int max_pages,
+                              int C, int recency_shift, int step, int32_t* __restrict__ tags,
+                              int32_t* __restrict__ stamps, int32_t* __restrict__ umap,
+                              int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats,
+                              MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
+                              uint32_t M, uint32_t H, int32_t* __restrict__ miss_counts,
+                              int32_t* __restrict__ miss_pages, int32_t* __restrict__ miss_phys) {
   __shared__ uint8_t req[kMaxSlots];       // slot holds a unit requested this step
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
   __shared__ SelectScratch sel;
   __shared__ uint32_t scan32[kResThreads / 64];
-  __shared__ unsigned long long scan64[kResThreads / 64];
   __shared__ int32_t head_off[kMaxKvHeads + 1];
-
+  __shared__ uint32_t head_miss[kMaxKvHeads];     // misses per head, then their prefix
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int step = *step_counter;
-  int32_t* tags = slot_tag + (int64_t)b * C;
-  int32_t* stamps = slot_stamp + (int64_t)b * C;
-  int32_t* umap = unit_slot + (int64_t)b * hkv * max_pages;
 
   for (int s = tid; s < C; s += kResThreads) req[s] = 0;
+  if (tid < hkv) head_miss[tid] = 0u;
   if (tid == 0) {
     int acc = 0;
     for (int h = 0; h < hkv; ++h) {
@@ -70,26 +79,23 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   __syncthreads();
   const int E = head_off[hkv];
 
-  // ---- pass 1: hits (stamp, mark, slot id) and the number of misses ------
-  // Elements e = tid + 1024 k, up to 8 per thread per batch, loads issued
-  // together; only the totals are needed here (ranks come in pass 2).
-  uint32_t M = 0u, H = 0u;
+  // ---- the requested slots (units resident before this step) and each
+  // head's miss count; the other workgroups only stamped them, and never
+  // change the unit map, so it still holds the state before this step
   {
     constexpr int kBatch = 8;
-    uint32_t m_local = 0u, h_local = 0u;
     for (int base = 0; base < E; base += kBatch * kResThreads) {
-      int64_t li[kBatch];
-      int v[kBatch], s[kBatch];
+      int hh[kBatch], v[kBatch], s[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const int e = base + k * kResThreads + tid;
-        li[k] = -1;
+        hh[k] = -1;
         v[k] = -1;
         if (e < E) {
           int h = 0;
           while (e >= head_off[h + 1]) ++h;
-          li[k] = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
-          const int p = sel_pages[li[k]];
+          hh[k] = h;
+          const int p = sel_pages[(int64_t)(b * hkv + h) * max_pages + (e - head_off[h])];
           if (p >= 0 && p < max_pages) v[k] = h * max_pages + p;
         }
       }
@@ -97,38 +103,19 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       for (int k = 0; k < kBatch; ++k) s[k] = (v[k] >= 0) ? umap[v[k]] : -2;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        if (li[k] < 0) continue;
-        int sk = s[k];
-        if (sk >= C) sk = -2;                // corrupt state: never index past the cache
-        if (hit_phys) hit_phys[li[k]] = (sk >= 0) ? b * C + sk : -1;
-        if (sk >= 0) {
-          ++h_local;
-          req[sk] = 1;
-          stamps[sk] = step;
-          sel_phys[li[k]] = b * C + sk;
-        } else if (sk == -1) {
-          ++m_local;
-        } else {
-          sel_phys[li[k]] = -1;              // page id out of range: an empty page
-        }
+        if (s[k] >= 0 && s[k] < C) req[s[k]] = 1;
+        if (s[k] == -1) atomicAdd(&head_miss[hh[k]], 1u);
       }
     }
-    unsigned long long tot;
-    block_excl_scan<unsigned long long, kResThreads>(
-        ((unsigned long long)h_local << 32) | m_local, scan64, tot);
-    M = (uint32_t)tot;
-    H = (uint32_t)(tot >> 32);
   }
-  // (block_excl_scan ends with a barrier: every req mark is visible here)
-  if (M == 0u) {                 // every requested unit is resident: nothing to place
-    if (tid == 0) {
-      stats[b * 4 + 0] = (int32_t)H;
-      stats[b * 4 + 1] = 0;
-      stats[b * 4 + 2] = 0;
-      stats[b * 4 + 3] = 0;
-      miss_count[b] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0u;
+    for (int h = 0; h < hkv; ++h) {
+      const uint32_t m = head_miss[h];
+      head_miss[h] = acc;            // misses of the heads before h
+      acc += m;
     }
-    return;
   }
 
   // ---- free slots and victim candidates ----------------------------------
@@ -149,9 +136,10 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
 
   // ---- r least recently used candidates: radix select on the keys -------
   // key = (stamp >> shift) * 2^32 + unit; keys are distinct, so exactly r
-  // keys are <= kappa
+  // keys are <= kappa.  (A requested slot's stamp may be rewritten by another
+  // workgroup meanwhile; requested slots are never candidates.)
   unsigned long long kappa = 0ull;
-  bool take_all = (r == NC);
+  const bool take_all = (r == NC);
   if (r > 0u && !take_all) {
     kappa = select_rth_key<kResThreads>(
         C, r,
@@ -192,19 +180,18 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   const uint32_t placed = min(M, A);
   __syncthreads();
 
-  // ---- pass 2: misses in ascending unit id take avail[0..placed) ----------
+  // ---- misses in ascending unit id take avail[0..placed) ------------------
   uint32_t ev_local = 0u, mbase = 0u;
   for (int base = 0; base < E; base += kResThreads) {
     const int e = base + tid;
     uint32_t miss = 0u;
-    int v = -1;
+    int v = -1, h = 0, p = -1;
     int64_t li = 0;
     if (e < E) {
-      int h = 0;
       while (e >= head_off[h + 1]) ++h;
       const int i = e - head_off[h];
       li = (int64_t)(b * hkv + h) * max_pages + i;
-      const int p = sel_pages[li];
+      p = sel_pages[li];
       if (p >= 0 && p < max_pages) {
         v = h * max_pages + p;
         miss = (umap[v] == -1) ? 1u : 0u;
@@ -225,6 +212,11 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
         umap[v] = s;
         sel_phys[li] = b * C + s;
         misses[(int64_t)b * C + mr] = MissRec{v, s};
+        if (miss_counts) {
+          const int64_t j = (int64_t)(b * hkv + h) * max_pages + (mr - head_miss[h]);
+          miss_pages[j] = p;
+          miss_phys[j] = b * C + s;
+        }
       } else {
         sel_phys[li] = -1;
       }
@@ -233,6 +225,13 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   }
   uint32_t evictions;
   block_excl_scan<uint32_t, kResThreads>(ev_local, scan32, evictions);
+  if (miss_counts && tid < hkv) {
+    // placed misses of head tid: its run of the request's misses, cut at
+    // `placed` (the misses left without a slot are the last ones)
+    const uint32_t lo = head_miss[tid];
+    const uint32_t hi = (tid + 1 < hkv) ? head_miss[tid + 1] : M;
+    miss_counts[b * hkv + tid] = (int32_t)(min(hi, placed) - min(lo, placed));
+  }
   if (tid == 0) {
     stats[b * 4 + 0] = (int32_t)H;
     stats[b * 4 + 1] = (int32_t)M;
@@ -240,6 +239,94 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     stats[b * 4 + 3] = (M > placed) ? 1 : 0;
     miss_count[b] = (int32_t)placed;
   }
+}
+
+// Workgroup (b, h, c) of the grid: list entries c * 1024 + tid,
+// + nchunk * 1024, ... of unit (b, h).  Every workgroup stamps its hits and
+// writes their slot ids; the request's last workgroup to finish (ticket)
+// places the misses, or with none only writes the statistics.  With every
+// access a hit, a step is one pass of parallel lookups: the list entries and
+// the list length are loaded together, then the unit map.
+__global__ __launch_bounds__(kResThreads) void resolve_kernel(
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
+    int max_pages, int C, int nchunk, int recency_shift,
+    const int32_t* __restrict__ step_counter, int32_t* __restrict__ slot_tag,
+    int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
+    int32_t* __restrict__ sel_phys, int32_t* __restrict__ hit_phys, int32_t* __restrict__ stats,
+    MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
+    unsigned long long* __restrict__ tickets, int32_t* __restrict__ miss_counts,
+    int32_t* __restrict__ miss_pages, int32_t* __restrict__ miss_phys) {
+  __shared__ unsigned long long scan64[kResThreads / 64];
+  __shared__ unsigned long long s_tk;
+  const int tid = threadIdx.x;
+  const int per_req = hkv * nchunk;
+  const int b = blockIdx.x / per_req;
+  const int hc = blockIdx.x - b * per_req;
+  const int h = hc / nchunk, c = hc - (hc / nchunk) * nchunk;
+  const int u = b * hkv + h;
+  const int64_t row = (int64_t)u * max_pages;
+  int32_t* stamps = slot_stamp + (int64_t)b * C;
+  const int32_t* umap = unit_slot + (int64_t)b * hkv * max_pages;
+
+  // the first chunk's entries are loaded before the length is known: an
+  // index past the row re-reads its last entry, and the entry is used only
+  // if it lies inside the list
+  int i = c * kResThreads + tid;
+  int p = sel_pages[row + min(i, max_pages - 1)];
+  const int n = min(max(sel_counts[u], 0), max_pages);
+  const int step = *step_counter;
+  uint32_t m_local = 0u, h_local = 0u;
+  for (;;) {
+    const bool in = i < n;
+    const int v = (in && p >= 0 && p < max_pages) ? h * max_pages + p : -1;
+    int s = umap[max(v, 0)];                 // unit 0's entry stands in when unused
+    asm volatile("" : "+v"(s));              // keep the load ahead of the tests
+    if (in) {
+      int sk = (v >= 0) ? s : -2;
+      if (sk >= C) sk = -2;                  // corrupt state: never index past the cache
+      if (hit_phys) hit_phys[row + i] = (sk >= 0) ? b * C + sk : -1;
+      if (sk >= 0) {
+        ++h_local;
+        stamps[sk] = step;
+        sel_phys[row + i] = b * C + sk;
+      } else if (sk == -1) {
+        ++m_local;                           // placed by the request's last workgroup
+      } else {
+        sel_phys[row + i] = -1;              // page id out of range: an empty page
+      }
+    }
+    i += nchunk * kResThreads;
+    if (i - tid >= n) break;                 // (uniform across the workgroup)
+    p = sel_pages[row + min(i, max_pages - 1)];
+  }
+  unsigned long long tot;
+  block_excl_scan<unsigned long long, kResThreads>(
+      ((unsigned long long)h_local << kTkHitShift) | m_local, scan64, tot);
+  if (tid == 0) {
+    const unsigned long long mine = tot | (1ull << kTkDoneShift);
+    const unsigned long long old = atomicAdd(tickets + b, mine);
+    s_tk = old + mine;
+  }
+  __syncthreads();
+  const unsigned long long tk = s_tk;
+  if ((int)(tk >> kTkDoneShift) != per_req) return;   // not the request's last workgroup
+  const uint32_t M = (uint32_t)(tk & kTkCountMask);
+  const uint32_t H = (uint32_t)((tk >> kTkHitShift) & kTkCountMask);
+  if (tid == 0) __hip_atomic_store(tickets + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (M == 0u) {                 // every requested unit is resident: nothing to place
+    if (miss_counts && tid < hkv) miss_counts[b * hkv + tid] = 0;
+    if (tid == 0) {
+      stats[b * 4 + 0] = (int32_t)H;
+      stats[b * 4 + 1] = 0;
+      stats[b * 4 + 2] = 0;
+      stats[b * 4 + 3] = 0;
+      miss_count[b] = 0;
+    }
+    return;
+  }
+  resolve_place(b, sel_counts, sel_pages, hkv, max_pages, C, recency_shift, step,
+                slot_tag + (int64_t)b * C, stamps, unit_slot + (int64_t)b * hkv * max_pages,
+                sel_phys, stats, misses, miss_count, M, H, miss_counts, miss_pages, miss_phys);
 }
 
 // The fetch runs in a few whole compute units that it keeps to itself: each
@@ -658,12 +745,16 @@ __global__ __launch_bounds__(kSplitThreads) void split_misses_kernel(
 
 extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity) {
   if (sp::check_dims(dims) != SPARSE_OK || capacity < 1) return 0;
-  return (size_t)dims->batch * ((size_t)capacity * sizeof(sp::MissRec) + sizeof(int32_t)) + 256;
+  return (size_t)dims->batch * (sizeof(unsigned long long) +
+                                (size_t)capacity * sizeof(sp::MissRec) + sizeof(int32_t)) +
+         256;
 }
 
 namespace {
 
-// Per-request workspace: miss records [B][C], then the per-request counts.
+// Per-request workspace: the resolve's ticket words [B] (zero before the
+// first call; every call leaves them zero), miss records [B][C], then the
+// per-request counts.
 // Pooled workspace (S rounded up to whole blocks of 1024 slots, nblk of
 // them): marks [S], compacted candidate keys [S] and their blocks [S],
 // avail [S], miss records [S], the selection state, two running totals, per
@@ -705,26 +796,49 @@ sparse_status check_pool_args(const uint16_t* host_kv, const uint16_t* cache_kv)
 // units from the attention that may run beside the fetch.
 constexpr int kFetchWaves = 256;
 
-// Per-request workspace views: miss records [B][C], then the per-request counts.
+// Per-request workspace views (layout above sparse_cache_workspace_bytes).
 struct PerRequestWs {
+  unsigned long long* tickets;
   sp::MissRec* misses;
   int32_t* miss_count;
 };
 PerRequestWs per_request_ws(int B, int32_t capacity, void* ws) {
-  sp::MissRec* misses = static_cast<sp::MissRec*>(ws);
-  return {misses, reinterpret_cast<int32_t*>(misses + (size_t)B * capacity)};
+  unsigned long long* tickets = static_cast<unsigned long long*>(ws);
+  sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(tickets + B);
+  return {tickets, misses, reinterpret_cast<int32_t*>(misses + (size_t)B * capacity)};
+}
+
+// Optional per-unit lists of the misses placed this step (split schedule).
+struct MissLists {
+  int32_t* counts;
+  int32_t* pages;
+  int32_t* phys;
+};
+
+// Hit-pass workgroups per (request, KV head): enough 1024-entry chunks for
+// the longest list the dims allow, but no more than about 512 workgroups in
+// all (longer lists loop).
+int resolve_chunks(const sparse_dims* dims) {
+  const int want = (sp::list_cap(dims) + sp::kResThreads - 1) / sp::kResThreads;
+  const int64_t units = (int64_t)dims->batch * dims->num_kv_heads;
+  const int lim = (int)std::max<int64_t>(1, 512 / units);
+  return std::max(1, std::min(want, lim));
 }
 
 sparse_status resolve_per_request(const sparse_dims* dims, int shift, const int32_t* sel_counts,
                                   const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag,
                                   int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
                                   int32_t* sel_phys, int32_t* hit_phys, int32_t* stats, void* ws,
-                                  hipStream_t s) {
+                                  MissLists ml, hipStream_t s) {
   const int B = dims->batch, hkv = dims->num_kv_heads;
   const PerRequestWs w = per_request_ws(B, capacity, ws);
-  hipLaunchKernelGGL(sp::resolve_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
-                     sel_pages, hkv, dims->max_pages, capacity, shift, step_counter, slot_tag,
-                     slot_stamp, unit_slot, sel_phys, hit_phys, stats, w.misses, w.miss_count);
+  const int nchunk = resolve_chunks(dims);
+  const int64_t groups = (int64_t)B * hkv * nchunk;
+  if (groups > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(sp::resolve_kernel, dim3((unsigned)groups), dim3(sp::kResThreads), 0, s,
+                     sel_counts, sel_pages, hkv, dims->max_pages, capacity, nchunk, shift,
+                     step_counter, slot_tag, slot_stamp, unit_slot, sel_phys, hit_phys, stats,
+                     w.misses, w.miss_count, w.tickets, ml.counts, ml.pages, ml.phys);
   return sp::launch_status();
 }
 
@@ -781,7 +895,7 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
                              const int32_t* sel_pages, int32_t S, int32_t* slot_tag,
                              int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
                              int32_t* sel_phys, int32_t* hit_phys, int32_t* stats, void* ws,
-                             hipStream_t s) {
+                             MissLists ml, hipStream_t s) {
   const int B = dims->batch, hkv = dims->num_kv_heads, MP = dims->max_pages;
   const PooledWs w = pooled_ws(B, S, ws);
   hipLaunchKernelGGL(sp::pool_mark_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
@@ -800,6 +914,12 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
   hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,
                      stats, w.counts, w.moff, w.avail, w.placed, w.misses);
+  if (ml.counts) {
+    if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+    hipLaunchKernelGGL(sp::split_misses_kernel, dim3(B * hkv), dim3(sp::kSplitThreads), 0, s,
+                       sel_counts, sel_pages, sel_phys, hit_phys, MP, ml.counts, ml.pages,
+                       ml.phys);
+  }
   return sp::launch_status();
 }
 
@@ -856,13 +976,14 @@ sparse_status resolve_any(const sparse_dims* dims, const sparse_cache_policy* po
                           const int32_t* sel_counts, const int32_t* sel_pages, int32_t capacity,
                           int32_t* slot_tag, int32_t* slot_stamp, int32_t* unit_slot,
                           int32_t* step_counter, int32_t* sel_phys, int32_t* hit_phys,
-                          int32_t* stats, void* ws, hipStream_t s) {
+                          int32_t* stats, void* ws, MissLists ml, hipStream_t s) {
   if (policy->pooled)
     return resolve_pooled(dims, policy->recency_shift, sel_counts, sel_pages, capacity, slot_tag,
-                          slot_stamp, unit_slot, step_counter, sel_phys, hit_phys, stats, ws, s);
+                          slot_stamp, unit_slot, step_counter, sel_phys, hit_phys, stats, ws, ml,
+                          s);
   return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, capacity,
                              slot_tag, slot_stamp, unit_slot, step_counter, sel_phys, hit_phys,
-                             stats, ws, s);
+                             stats, ws, ml, s);
 }
 
 sparse_status fetch_any(const sparse_dims* dims, const sparse_cache_policy* policy,
@@ -886,7 +1007,8 @@ extern "C" sparse_status sparse_hbm_cache_resolve_policy(
   if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if ((st = resolve_any(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
-                        unit_slot, step_counter, sel_phys, nullptr, stats, ws, s)) != SPARSE_OK)
+                        unit_slot, step_counter, sel_phys, nullptr, stats, ws,
+                        MissLists{nullptr, nullptr, nullptr}, s)) != SPARSE_OK)
     return st;
   return fetch_any(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, s);
 }
@@ -895,14 +1017,18 @@ extern "C" sparse_status sparse_hbm_cache_resolve_split(
     const sparse_dims* dims, const sparse_cache_policy* policy, const int32_t* sel_counts,
     const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag, int32_t* slot_stamp,
     int32_t* unit_slot, int32_t* step_counter, int32_t* sel_phys, int32_t* hit_phys,
-    int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    int32_t* stats, int32_t* miss_counts, int32_t* miss_pages, int32_t* miss_phys, void* ws,
+    size_t ws_bytes, void* stream) {
   sparse_status st = check_resolve_args(dims, sel_counts, sel_pages, capacity, slot_tag,
                                         slot_stamp, unit_slot, step_counter, sel_phys, stats);
   if (st != SPARSE_OK) return st;
   if (!hit_phys) return SPARSE_ERR_INVALID;
+  const bool any = miss_counts || miss_pages || miss_phys;
+  if (any && !(miss_counts && miss_pages && miss_phys)) return SPARSE_ERR_INVALID;
   if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
   return resolve_any(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
-                     unit_slot, step_counter, sel_phys, hit_phys, stats, ws, (hipStream_t)stream);
+                     unit_slot, step_counter, sel_phys, hit_phys, stats, ws,
+                     MissLists{miss_counts, miss_pages, miss_phys}, (hipStream_t)stream);
 }
 
 extern "C" sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims,

@@ -9,23 +9,14 @@ namespace sp {
 constexpr int kMergeThreads = 256;
 constexpr int kMergeSlots = kMergeThreads / 32;   // segments read side by side
 
-// One 256-thread workgroup per (unit, query head).  The unit's partials are
-// those of the workers its list entries fall to under the balanced plan: the
-// slots u + w for w from the owner of its first entry to the owner of its
-// last, found from the list lengths alone (one round of loads of the
-// lengths, then one of the partials).  Thread t reads channel quad t % 32 of
-// segments t / 32, t / 32 + 8, ... (each segment's 128 floats are one
-// coalesced 512-byte read by 32 threads), keeping an online (max, sum,
-// weighted sum); the 8 segment slots are then combined through LDS.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ sel_counts, int cap, int U, int wmax, int hkv, int group,
-    float* __restrict__ out, float* __restrict__ out_lse) {
-  __shared__ floatx4 s_acc[kMergeSlots][32];
-  __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
-  const int u = blockIdx.x, g = blockIdx.y;
-  const int b = u / hkv, h = u - (u / hkv) * hkv;
-  const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
+// Merge segments of a unit under one plan: slot c0 + i for i < nseg.
+struct MergeRun {
+  int64_t c0;
+  int nseg;
+};
+
+__device__ __forceinline__ MergeRun merge_run(const int32_t* __restrict__ sel_counts, int U,
+                                              int cap, int wmax, int u) {
   int off, len, total;
   plan_unit(sel_counts, U, cap, u, off, len, total);
   off = __builtin_amdgcn_readfirstlane(off);
@@ -37,23 +28,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     w_lo = plan_owner(off, W, total);
     nseg = plan_owner(off + len - 1, W, total) - w_lo + 1;
   }
-  const int64_t c0 = (int64_t)u + w_lo;   // segment i of the unit is slot c0 + i
+  return MergeRun{(int64_t)u + w_lo, nseg};   // segment i of the unit is slot c0 + i
+}
+
+// One 256-thread workgroup per (unit, query head).  The unit's partials are
+// those of the workers its list entries fall to under the balanced plan: the
+// slots u + w for w from the owner of its first entry to the owner of its
+// last, found from the list lengths alone (one round of loads of the
+// lengths, then one of the partials).  Thread t reads channel quad t % 32 of
+// segments t / 32, t / 32 + 8, ... (each segment's 128 floats are one
+// coalesced 512-byte read by 32 threads), keeping an online (max, sum,
+// weighted sum); the 8 segment slots are then combined through LDS.  With
+// kPair, the unit's segments under a second plan (lists sel_counts_b,
+// partials part_o_b / part_lse_b, the same worker count) follow its
+// segments under the first: attention over the union of two disjoint lists.
+template <bool kPair>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ sel_counts, const float* __restrict__ part_o_b,
+    const float* __restrict__ part_lse_b, const int32_t* __restrict__ sel_counts_b, int cap,
+    int U, int wmax, int hkv, int group, float* __restrict__ out,
+    float* __restrict__ out_lse) {
+  __shared__ floatx4 s_acc[kMergeSlots][32];
+  __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
+  const int u = blockIdx.x, g = blockIdx.y;
+  const int b = u / hkv, h = u - (u / hkv) * hkv;
+  const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
+  const MergeRun ra = merge_run(sel_counts, U, cap, wmax, u);
+  MergeRun rb{0, 0};
+  if (kPair) rb = merge_run(sel_counts_b, U, cap, wmax, u);
+  const int nall = ra.nseg + rb.nseg;
 
   float m = -INFINITY, s = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = slot; i < nseg; i += 2 * kMergeSlots) {
+  for (int i = slot; i < nall; i += 2 * kMergeSlots) {
     // Both slots' loads are issued before any is used; an index past the
     // unit's segments is clamped to its last one (read, then discarded).  The
     // empty asm statements keep the compiler from moving a load under a test,
     // where it would become a branch that waits for it.
     const int i1 = i + kMergeSlots;
-    const int64_t r0 = (c0 + i) * group + g;
-    const int64_t r1 = (c0 + min(i1, nseg - 1)) * group + g;
-    float l0 = part_lse[r0], l1 = part_lse[r1];
-    floatx4 o0 = *reinterpret_cast<const floatx4*>(part_o + r0 * kD + 4 * quad);
-    floatx4 o1 = *reinterpret_cast<const floatx4*>(part_o + r1 * kD + 4 * quad);
+    const int j1 = min(i1, nall - 1);
+    const bool b0 = kPair && i >= ra.nseg, b1 = kPair && j1 >= ra.nseg;
+    const int64_t r0 = (b0 ? rb.c0 + (i - ra.nseg) : ra.c0 + i) * group + g;
+    const int64_t r1 = (b1 ? rb.c0 + (j1 - ra.nseg) : ra.c0 + j1) * group + g;
+    float l0 = (b0 ? part_lse_b : part_lse)[r0], l1 = (b1 ? part_lse_b : part_lse)[r1];
+    floatx4 o0 = *reinterpret_cast<const floatx4*>((b0 ? part_o_b : part_o) + r0 * kD + 4 * quad);
+    floatx4 o1 = *reinterpret_cast<const floatx4*>((b1 ? part_o_b : part_o) + r1 * kD + 4 * quad);
     asm volatile("" : "+v"(l0), "+v"(l1), "+v"(o0), "+v"(o1));
-    if (i1 >= nseg) l1 = -INFINITY;
+    if (i1 >= nall) l1 = -INFINITY;
     const float mn = fmaxf(m, fmaxf(l0, l1));
     if (mn == -INFINITY) continue;
     const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
@@ -101,25 +123,58 @@ void enqueue_merge(const sparse_dims* dims, const float* part_o, const float* pa
                    hipStream_t stream) {
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
-  hipLaunchKernelGGL(merge_kernel, dim3(U, group), dim3(kMergeThreads), 0, stream, part_o,
-                     part_lse, sel_counts, list_cap(dims), U, wmax, hkv, group, out, out_lse);
+  hipLaunchKernelGGL(merge_kernel<false>, dim3(U, group), dim3(kMergeThreads), 0, stream, part_o,
+                     part_lse, sel_counts, nullptr, nullptr, nullptr, list_cap(dims), U, wmax,
+                     hkv, group, out, out_lse);
 }
 
 }  // namespace sp
 
-extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
-                                             const float* part_lse, const int32_t* sel_counts,
-                                             int32_t workers, float* out, float* out_lse,
-                                             void* stream) {
+namespace {
+
+sparse_status check_merge(const sparse_dims* dims, const float* part_o, const float* part_lse,
+                          const int32_t* sel_counts, int32_t workers, const float* out,
+                          const float* out_lse, int& wmax) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!part_o || !part_lse || !sel_counts || !out || !out_lse)
     return SPARSE_ERR_INVALID;
   if (!sp::aligned(part_o, 16) || !sp::aligned(out, 16)) return SPARSE_ERR_INVALID;
   if (workers < 0 || workers > sp::kMaxWorkers) return SPARSE_ERR_INVALID;
-  const int wmax = sp::resolve_workers(workers);
-  if (wmax < 1) return SPARSE_ERR_HIP;
+  wmax = sp::resolve_workers(workers);
+  return wmax < 1 ? SPARSE_ERR_HIP : SPARSE_OK;
+}
+
+}  // namespace
+
+extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
+                                             const float* part_lse, const int32_t* sel_counts,
+                                             int32_t workers, float* out, float* out_lse,
+                                             void* stream) {
+  int wmax = 0;
+  const sparse_status st =
+      check_merge(dims, part_o, part_lse, sel_counts, workers, out, out_lse, wmax);
+  if (st != SPARSE_OK) return st;
   sp::enqueue_merge(dims, part_o, part_lse, sel_counts, wmax, out, out_lse, (hipStream_t)stream);
+  return sp::launch_status();
+}
+
+extern "C" sparse_status sparse_merge_splits_pair(
+    const sparse_dims* dims, const float* part_o_a, const float* part_lse_a,
+    const int32_t* sel_counts_a, const float* part_o_b, const float* part_lse_b,
+    const int32_t* sel_counts_b, int32_t workers, float* out, float* out_lse, void* stream) {
+  int wmax = 0;
+  sparse_status st =
+      check_merge(dims, part_o_a, part_lse_a, sel_counts_a, workers, out, out_lse, wmax);
+  if (st != SPARSE_OK) return st;
+  if (!part_o_b || !part_lse_b || !sel_counts_b || !sp::aligned(part_o_b, 16))
+    return SPARSE_ERR_INVALID;
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  hipLaunchKernelGGL(sp::merge_kernel<true>, dim3(U, group), dim3(sp::kMergeThreads), 0,
+                     (hipStream_t)stream, part_o_a, part_lse_a, sel_counts_a, part_o_b,
+                     part_lse_b, sel_counts_b, sp::list_cap(dims), U, wmax, hkv, group, out,
+                     out_lse);
   return sp::launch_status();
 }
 

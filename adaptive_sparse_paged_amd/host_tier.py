@@ -16,12 +16,55 @@ from .step import SparseDecodeStep
 UNIT_ELEMS = 2 * 16 * 128   # K tile + V tile of one (page, KV head)
 
 
+def _hip():
+    # the HIP runtime torch loaded (one copy per process, by its soname)
+    return ctypes.CDLL("libamdhip64.so.7")
+
+
+_HIP_EVENT_DISABLE_TIMING = 0x2
+_HIP_EVENT_RELEASE_TO_DEVICE = 0x40000000
+
+
+class DeviceEvent:
+    """A HIP event that orders work between two streams of one device.
+    Recorded with a device-scope release: a default event's record writes
+    back and invalidates the caches for the host's sake, which cost about
+    7 us of GPU time per record or wait in the host tier's steps.  Neither
+    stream's work is read by the host through it.  Works under graph capture
+    (record and wait become graph edges)."""
+
+    def __init__(self):
+        self._hip = _hip()
+        self._ev = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(
+            ctypes.byref(self._ev),
+            ctypes.c_uint(_HIP_EVENT_DISABLE_TIMING | _HIP_EVENT_RELEASE_TO_DEVICE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self._hip.hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def wait(self, stream):
+        """Make `stream` wait for the last record."""
+        rc = self._hip.hipStreamWaitEvent(ctypes.c_void_p(stream.cuda_stream), self._ev,
+                                          ctypes.c_uint(0))
+        if rc != 0:
+            raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
+
+    def __del__(self):
+        if getattr(self, "_ev", None) and self._ev.value:
+            self._hip.hipEventDestroy(self._ev)
+
+
 def device_view_ok(host):
     """Check that pinned host memory is addressable by the GPU at its own
     address (unified addressing); raises otherwise."""
     if not host.is_pinned():
         raise ValueError("host KV must be pinned host memory")
-    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip = _hip()
     dptr = ctypes.c_void_p()
     rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(host.data_ptr()), 0)
     if rc != 0 or dptr.value != host.data_ptr():
@@ -64,14 +107,16 @@ class HbmPageCache:
                                      self.slot_stamp, self.unit_slot, self.step_counter,
                                      sel_phys, self.stats, self.ws, stream)
 
-    def resolve_split(self, sel_counts, sel_pages, sel_phys, hit_phys, stream=None):
+    def resolve_split(self, sel_counts, sel_pages, sel_phys, hit_phys, miss_lists=None,
+                      stream=None):
         """The resolve alone (no copy): sel_phys as resolve() writes it, and
         hit_phys -- the slot of every entry that was resident before this
-        step, -1 for the others.  fetch() must follow."""
+        step, -1 for the others; with miss_lists = (counts, pages, phys), also
+        each unit's placed misses as a list.  fetch() must follow."""
         lib.hbm_cache_resolve_split(self.dims, self.policy, sel_counts, sel_pages, self.capacity,
                                     self.slot_tag, self.slot_stamp, self.unit_slot,
                                     self.step_counter, sel_phys, hit_phys, self.stats, self.ws,
-                                    stream)
+                                    miss_lists, stream)
 
     def fetch(self, stream=None):
         """Copy the misses placed by the last resolve_split; advances the step."""
@@ -89,13 +134,20 @@ class SplitHostTierStep:
     the hits are final once the resolve has run; attention over a partition
     of a list, merged by log-sum-exp, is attention over the whole list.
 
-    Current stream: resolve (no copy) -> fetch -> attention over the miss
-    lists -> combine.  Second stream, after the resolve: the miss lists
-    (sparse_split_misses) -> attention over the lists with hit_phys, which
-    skips the misses.  Cache state, statistics and slot ids equal those of
-    HbmPageCache.resolve; outputs equal the one-pass attention up to the
-    order of the log-sum-exp merge.  The step joins the second stream before
-    it returns, so it can be captured whole."""
+    Current stream: resolve (no copy; it also writes each unit's placed
+    misses as a list) -> fetch -> attention over the miss lists -> wait for
+    the second stream -> one merge of both sets of partials into out.
+    Second stream, after the resolve: attention over the lists with
+    hit_phys, which skips the misses.  The fetch goes first on the stream of
+    the resolve, so it is dispatched before the hit attention and gets its
+    compute units at once (dispatched after it, it waited for attention
+    workgroups to leave and took 7% longer).  With every access a hit the
+    fetch and the miss attention have nothing to do and run beside the hit
+    attention, so the step is the one-pass step with the fetch off its path.
+    Cache state, statistics and slot ids equal those of HbmPageCache.resolve;
+    outputs equal the one-pass attention up to the order of the log-sum-exp
+    merge.  The step joins the second stream before it returns, so it can be
+    captured whole."""
 
     def __init__(self, dims, cache, gamma, workers=0, scale=None, device="cuda"):
         self.dims, self.cache = dims, cache
@@ -104,16 +156,9 @@ class SplitHostTierStep:
         self.miss = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
         self.hit_phys = torch.zeros_like(self.hits.buf.sel_phys)
-        B, Hq = dims.batch, dims.num_q_heads
-        f32 = dict(dtype=torch.float32, device=device)
-        self.out_hit = torch.empty((B, Hq, 128), **f32)
-        self.lse_hit = torch.empty((B, Hq), **f32)
-        self.out_miss = torch.empty((B, Hq, 128), **f32)
-        self.lse_miss = torch.empty((B, Hq), **f32)
         self.side = torch.cuda.Stream(device=device)
-        self.resolved = torch.cuda.Event()
-        self.split_done = torch.cuda.Event()
-        self.hits_done = torch.cuda.Event()
+        self.resolved = DeviceEvent()
+        self.hits_done = DeviceEvent()
 
     @property
     def sel_counts(self):
@@ -130,27 +175,23 @@ class SplitHostTierStep:
     def run(self, q, ctx_lens, out, out_lse):
         """One step on the lists in sel_counts / sel_pages."""
         cur = torch.cuda.current_stream()
-        hb, mb = self.hits.buf, self.miss.buf
+        h, m = self.hits, self.miss
+        hb, mb = h.buf, m.buf
         kv, sp_, sh_, pp = self.cache.pool_args()
-        self.cache.resolve_split(hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys)
+        self.cache.resolve_split(hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys,
+                                 miss_lists=(mb.sel_counts, mb.sel_pages, mb.sel_phys))
         self.resolved.record(cur)
-        # The fetch is enqueued before any second-stream work, so a slow
-        # host-side launch there (the first use of the stream) cannot hold it
-        # back; the second stream waits for the resolve only.
         self.cache.fetch()
-        self.side.wait_event(self.resolved)
-        with torch.cuda.stream(self.side):
-            lib.split_misses(self.dims, hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys,
-                             mb.sel_counts, mb.sel_pages, mb.sel_phys, self.side)
-            self.split_done.record(self.side)
-            self.hits.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_hit, self.lse_hit,
-                             stream=self.side, sel_phys=self.hit_phys)
-            self.hits_done.record(self.side)
-        cur.wait_event(self.split_done)
-        self.miss.attend(q, kv, sp_, sh_, pp, ctx_lens, self.out_miss, self.lse_miss)
-        cur.wait_event(self.hits_done)
-        lib.lse_combine(self.dims, self.out_hit, self.lse_hit, self.out_miss, self.lse_miss, out,
-                        out_lse)
+        lib.decode_attn(self.dims, q, kv, sp_, sh_, pp, ctx_lens, mb.sel_counts, mb.sel_pages,
+                        mb.sel_phys, m.scale, m.workers, mb.part_o, mb.part_lse, m.max_parts)
+        self.resolved.wait(self.side)
+        lib.decode_attn(self.dims, q, kv, sp_, sh_, pp, ctx_lens, hb.sel_counts, hb.sel_pages,
+                        self.hit_phys, h.scale, h.workers, hb.part_o, hb.part_lse, h.max_parts,
+                        stream=self.side)
+        self.hits_done.record(self.side)
+        self.hits_done.wait(cur)
+        lib.merge_splits_pair(self.dims, hb.part_o, hb.part_lse, hb.sel_counts, mb.part_o,
+                              mb.part_lse, mb.sel_counts, m.workers, out, out_lse)
         return out, out_lse
 
 
@@ -181,7 +222,8 @@ class LayeredHostTierStep:
         # per-layer slot lists: layer l+1's resolve writes while layer l attends
         self.sel_phys = [torch.zeros_like(self.attn.buf.sel_phys) for _ in host_pools]
         self.io = torch.cuda.Stream(device=device)
-        self.ready = [torch.cuda.Event() for _ in host_pools]
+        self.start = DeviceEvent()
+        self.ready = [DeviceEvent() for _ in host_pools]
 
     @property
     def sel_counts(self):
@@ -204,13 +246,14 @@ class LayeredHostTierStep:
                           sel_phys=self.sel_phys[l])
             return
         cur = torch.cuda.current_stream()
-        self.io.wait_stream(cur)
+        self.start.record(cur)
+        self.start.wait(self.io)
         for l, cache in enumerate(self.caches):
             cache.resolve(counts, pages, self.sel_phys[l], stream=self.io)
             self.ready[l].record(self.io)
+        # waiting for the last layer's event joins the second stream
         for l, cache in enumerate(self.caches):
-            cur.wait_event(self.ready[l])
+            self.ready[l].wait(cur)
             kv, sp, sh, pp = cache.pool_args()
             st.attend(qs[l], kv, sp, sh, pp, ctx_lens, outs[l], lses[l],
                       sel_phys=self.sel_phys[l])
-        cur.wait_stream(self.io)

@@ -26,6 +26,7 @@ EXPORTS = (
     "sparse_decode_max_parts",
     "sparse_decode_attn",
     "sparse_merge_splits",
+    "sparse_merge_splits_pair",
     "sparse_cache_workspace_bytes",
     "sparse_hbm_cache_resolve",
     "sparse_select_topk",
@@ -93,6 +94,7 @@ _SIGS = {
     "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
                                   _P, _P, _I64, _P]),
     "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P]),
+    "sparse_merge_splits_pair": (_I32, [_D, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
     "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
@@ -104,7 +106,7 @@ _SIGS = {
                                                _P, _P, ctypes.c_size_t, _P]),
     "sparse_read_blocks": (_I32, [_P, _I64, _P, _I64, _P, _P]),
     "sparse_hbm_cache_resolve_split": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
-                                              _P, _P, ctypes.c_size_t, _P]),
+                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_hbm_cache_fetch": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "sparse_split_misses": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
@@ -242,6 +244,16 @@ def merge_splits(dims, part_o, part_lse, sel_counts, workers, out, out_lse, stre
         _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
+def merge_splits_pair(dims, part_o_a, part_lse_a, sel_counts_a, part_o_b, part_lse_b,
+                      sel_counts_b, workers, out, out_lse, stream=None):
+    """One merge over the partials of two disjoint sets of lists."""
+    _dev(part_o_a, part_lse_a, sel_counts_a, part_o_b, part_lse_b, sel_counts_b, out, out_lse)
+    _check("sparse_merge_splits_pair", load().sparse_merge_splits_pair(
+        ctypes.byref(dims), _ptr(part_o_a), _ptr(part_lse_a), _ptr(sel_counts_a),
+        _ptr(part_o_b), _ptr(part_lse_b), _ptr(sel_counts_b), workers, _ptr(out), _ptr(out_lse),
+        _stream(stream)))
+
+
 def cache_workspace_bytes(dims, capacity):
     return int(load().sparse_cache_workspace_bytes(ctypes.byref(dims), capacity))
 
@@ -317,13 +329,21 @@ def read_blocks(pool, pool_blocks, order, xor_out, stream=None):
 
 
 def hbm_cache_resolve_split(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
-                            unit_slot, step_counter, sel_phys, hit_phys, stats, ws, stream=None):
+                            unit_slot, step_counter, sel_phys, hit_phys, stats, ws,
+                            miss_lists=None, stream=None):
+    """miss_lists: None, or (miss_counts, miss_pages, miss_phys) to receive each
+    unit's placed misses."""
     _dev(sel_counts, sel_pages, slot_tag, slot_stamp, unit_slot, step_counter, sel_phys,
          hit_phys, stats, ws)
+    mc = mp = mph = None
+    if miss_lists is not None:
+        mc, mp, mph = miss_lists
+        _dev(mc, mp, mph)
     _check("sparse_hbm_cache_resolve_split", load().sparse_hbm_cache_resolve_split(
         ctypes.byref(dims), ctypes.byref(policy), _ptr(sel_counts), _ptr(sel_pages), capacity,
         _ptr(slot_tag), _ptr(slot_stamp), _ptr(unit_slot), _ptr(step_counter), _ptr(sel_phys),
-        _ptr(hit_phys), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(hit_phys), _ptr(stats), _ptr(mc), _ptr(mp), _ptr(mph), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def hbm_cache_fetch(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, stream=None):

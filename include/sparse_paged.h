@@ -274,6 +274,23 @@ sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
                                   int32_t workers, float* out, float* out_lse, void* stream);
 
 /*
+ * sparse_merge_splits_pair -- the merge of sparse_merge_splits over two
+ * disjoint sets of lists of the same rows: unit u's segments under the plan
+ * of lists a (sel_counts_a, partials part_o_a / part_lse_a) and under the plan
+ * of lists b, all merged by the same identity into one result -- attention
+ * over the union of the two lists ([P1], abstract, sentence on
+ * self-planning attention, as sparse_merge_splits).  Both sets of partials
+ * come from sparse_decode_attn calls with these dims and this workers value.
+ * The host tier's split step merges the hits' and the misses' partials with
+ * it.  Arguments and errors as sparse_merge_splits, per set.
+ */
+sparse_status sparse_merge_splits_pair(const sparse_dims* dims, const float* part_o_a,
+                                       const float* part_lse_a, const int32_t* sel_counts_a,
+                                       const float* part_o_b, const float* part_lse_b,
+                                       const int32_t* sel_counts_b, int32_t workers, float* out,
+                                       float* out_lse, void* stream);
+
+/*
  * sparse_decode_attn_merge -- sparse_decode_attn followed by
  * sparse_merge_splits on the same stream, in one call: attention of every
  * unit's G query heads over its page list ([P1], abstract, sentence on
@@ -324,8 +341,11 @@ sparse_status sparse_decode_attn_merge_noalloc(const sparse_dims* dims, const ui
                                                int32_t workers, float* out, float* out_lse,
                                                void* stream);
 
-/* Bytes of workspace sparse_hbm_cache_resolve needs (host): the per-request
- * list of placed misses handed from the resolve kernel to the fetch kernel. */
+/* Bytes of workspace sparse_hbm_cache_resolve needs (host): a ticket word per
+ * request (the resolve's workgroups of one request count themselves in on it)
+ * and the per-request list of placed misses handed from the resolve kernel to
+ * the fetch kernel.  Zero it once before the first call; every call leaves
+ * the ticket words zero. */
 size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
 
 /*
@@ -366,8 +386,13 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
  *   sel_phys   int32 [U][max_pages] out: global slot id b * capacity + slot
  *   stats      int32 [B][4] out: hits, misses, evictions, overflow flag
  *   capacity   slots per request, 1..8192; num_kv_heads <= 64
- * Enqueues two kernels (resolve: one workgroup per request; fetch).  Calls
- * sharing cache state or a workspace must not overlap in time.
+ *   ws         see sparse_cache_workspace_bytes (zeroed once before use)
+ * Enqueues two kernels.  The resolve runs one 1024-thread workgroup per
+ * (request, KV head, chunk of up to 1024 list entries); each stamps its hits
+ * and writes their slot ids, and the last of a request's workgroups to
+ * finish places the request's misses (or, with none, writes only the
+ * statistics).  The fetch copies the placed misses.  Calls sharing cache
+ * state or a workspace must not overlap in time.
  */
 sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* sel_counts,
                                        const int32_t* sel_pages, const uint16_t* host_kv,
@@ -443,24 +468,32 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
  * the misses are still crossing PCIe (the split the resolver's placement
  * rule allows: a hit's slot is never a victim of the same step, so the hits
  * are final once the resolve has run).  One step is:
- *   sparse_hbm_cache_resolve_split   hits, victims, slots; no copy
+ *   sparse_hbm_cache_resolve_split   hits, victims, slots, and each unit's
+ *                                    placed misses as a short list; no copy
  *   sparse_hbm_cache_fetch           the misses' copies; advances the step
- *   sparse_split_misses              each unit's misses as a short list
  * then attention over (sel_counts, sel_pages, hit_phys) -- it may overlap
- * the fetch -- and attention over the miss lists after the fetch, merged by
- * sparse_lse_combine.  Cache state, statistics and sel_phys equal those of
+ * the fetch -- and, after the fetch, attention over the miss lists; both
+ * sets of partials are merged by sparse_merge_splits_pair (attention over a
+ * partition of a list, merged by log-sum-exp, is attention over the list).
+ * Cache state, statistics and sel_phys equal those of
  * sparse_hbm_cache_resolve_policy on the same inputs.
  *
  * sparse_hbm_cache_resolve_split -- the resolve of
  * sparse_hbm_cache_resolve_policy without the fetch.  Arguments as there
  * (no pools: the resolve never reads them), plus
- *   hit_phys  int32 [U][max_pages] out: for list entry i of unit u, the slot
- *             (as in sel_phys) if the unit was resident before this step,
- *             else -1; entries past sel_counts[u] are not written
+ *   hit_phys    int32 [U][max_pages] out: for list entry i of unit u, the slot
+ *               (as in sel_phys) if the unit was resident before this step,
+ *               else -1; entries past sel_counts[u] are not written
+ *   miss_counts int32 [U] out, miss_pages, miss_phys int32 [U][max_pages]
+ *               out: for each unit, the list entries placed this step (not
+ *               resident before, given a slot), in list order -- lists that
+ *               sparse_decode_attn takes as (sel_counts, sel_pages,
+ *               sel_phys); entries past miss_counts[u] are not written.  All
+ *               three NULL: not written.
  * The misses it placed are recorded in ws for the next
  * sparse_hbm_cache_fetch on the same ws, which must follow it in stream
  * order before ws is used again.  Errors as sparse_hbm_cache_resolve_policy;
- * NULL hit_phys -> INVALID.
+ * NULL hit_phys, or some but not all of the miss-list pointers -> INVALID.
  */
 sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
                                              const sparse_cache_policy* policy,
@@ -469,8 +502,9 @@ sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
                                              int32_t* slot_tag, int32_t* slot_stamp,
                                              int32_t* unit_slot, int32_t* step_counter,
                                              int32_t* sel_phys, int32_t* hit_phys,
-                                             int32_t* stats, void* ws, size_t ws_bytes,
-                                             void* stream);
+                                             int32_t* stats, int32_t* miss_counts,
+                                             int32_t* miss_pages, int32_t* miss_phys, void* ws,
+                                             size_t ws_bytes, void* stream);
 
 /*
  * sparse_hbm_cache_fetch -- copy every miss placed by the last
@@ -491,7 +525,9 @@ sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims, const sparse_cache
  *   miss_pages  int32 [U][max_pages]   their logical pages (ascending)
  *   miss_phys   int32 [U][max_pages]   their slots
  * -- lists that sparse_decode_attn takes as (sel_counts, sel_pages,
- * sel_phys).  One 256-thread workgroup per unit.
+ * sel_phys).  The same lists sparse_hbm_cache_resolve_split writes when given
+ * the miss-list outputs; this is the separate pass over sel_phys and hit_phys.
+ * One 256-thread workgroup per unit.
  */
 sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_counts,
                                   const int32_t* sel_pages, const int32_t* sel_phys,

@@ -134,6 +134,13 @@ def test_null_and_value_checks(L):
     assert na(_dims(batch=2048, q_heads=32, kv_heads=8)) == lib.ERR_WORKSPACE
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, None, 16, FAKE, FAKE, None) == lib.ERR_INVALID
+    pair = lambda b_o=FAKE, b_l=FAKE, b_c=FAKE, workers=16: L.sparse_merge_splits_pair(
+        ctypes.byref(d), FAKE, FAKE, FAKE, b_o, b_l, b_c, workers, FAKE, FAKE, None)
+    assert pair(b_o=None) == lib.ERR_INVALID
+    assert pair(b_l=None) == lib.ERR_INVALID
+    assert pair(b_c=None) == lib.ERR_INVALID
+    assert pair(b_o=ctypes.c_void_p(0x10004)) == lib.ERR_INVALID      # partials 16-byte aligned
+    assert pair(workers=-1) == lib.ERR_INVALID
     assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None,
                                 FAKE, FAKE, None, 0, None) == lib.ERR_INVALID
     assert L.sparse_append_tokens(ctypes.byref(d), None, FAKE, FAKE, 8192, 4096, 100, FAKE,
@@ -160,10 +167,15 @@ def test_null_and_value_checks(L):
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, -1, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_build_page_summaries(ctypes.byref(d), FAKE, 8192, 4096, 100, FAKE, FAKE, 0, FAKE, None) == lib.OK
     # the host tier in two halves
-    split = lambda cap, ws_bytes, hit=FAKE, pol=lib.CachePolicy(0, 0): L.sparse_hbm_cache_resolve_split(
-        ctypes.byref(d), ctypes.byref(pol), FAKE, FAKE, cap, FAKE, FAKE, FAKE, FAKE, FAKE, hit,
-        FAKE, FAKE, ws_bytes, None)
+    split = lambda cap, ws_bytes, hit=FAKE, pol=lib.CachePolicy(0, 0), ml=(None, None, None): \
+        L.sparse_hbm_cache_resolve_split(
+            ctypes.byref(d), ctypes.byref(pol), FAKE, FAKE, cap, FAKE, FAKE, FAKE, FAKE, FAKE, hit,
+            FAKE, *ml, FAKE, ws_bytes, None)
     assert split(64, 1 << 30, hit=None) == lib.ERR_INVALID
+    # the miss lists: all three or none
+    assert split(64, 1 << 30, ml=(FAKE, None, None)) == lib.ERR_INVALID
+    assert split(64, 1 << 30, ml=(FAKE, FAKE, None)) == lib.ERR_INVALID
+    assert split(64, 1 << 30, ml=(None, None, FAKE)) == lib.ERR_INVALID
     assert split(0, 1 << 30) == lib.ERR_INVALID
     assert split(9000, 1 << 30) == lib.ERR_UNSUPPORTED          # per-request slot limit
     assert split(64, 16) == lib.ERR_WORKSPACE

@@ -1,5 +1,5 @@
 """The host tier in two halves -- attention over the hits beside the fetch of
-the misses, then attention over the misses and a log-sum-exp combine --
+the misses, then attention over the misses merged into the hits' result --
 against the one-call resolve and one-pass attention on a second cache fed
 the same lists: cache state, statistics and slot ids bitwise at every step;
 hit_phys equal to the residency before the step; the miss lists equal to
@@ -16,7 +16,7 @@ import oracle as O
 from adaptive_sparse_paged_amd import inputs as I
 from adaptive_sparse_paged_amd import lib
 from adaptive_sparse_paged_amd.host_tier import HbmPageCache, SplitHostTierStep
-from adaptive_sparse_paged_amd.step import SparseDecodeStep, capture
+from adaptive_sparse_paged_amd.step import SparseDecodeStep, canonical_strides, capture
 
 from _gpu_case import ATTN_TOL, feed_lists, say
 
@@ -113,3 +113,69 @@ def test_split_cold_step_all_misses(gpu_lib):
     say("[split] cold start, B=3 Hkv=4, 256 slots, lists of 40")
     misses, worst = _run(w, 256, 40, 2, 0.5, workers=16)
     assert misses > 0
+
+
+def test_merge_pair_of_disjoint_lists(gpu_lib):
+    """sparse_merge_splits_pair on lists cut in two (alternate entries; some
+    units with one side empty, some with both): attention over part A and
+    over part B, one merge of both sets of partials, against attention +
+    merge over the whole lists (up to the order of the merge), and -- for
+    units whose part A is empty -- bitwise equal to merge_splits over part B
+    alone, and the reverse."""
+    w = I.custom_workload("merge_pair", 3, 16, 4, ("fixed", 4000), index=126)
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, li.max_pages)
+    B, H, G = w.batch, w.kv_heads, w.group
+    layer = types.SimpleNamespace(w=w, dims=dims, li=li)
+    rng = np.random.default_rng(126)
+    n = I.pages_of(int(lens.min()))
+    whole, part_a, part_b = {}, {}, {}
+    for u in range(B * H):
+        k = [0, 1, 2, 37, 180][u % 5]
+        lst = np.sort(rng.choice(n, size=k, replace=False)).astype(np.int32)
+        whole[u] = lst
+        if u % 3 == 1:                          # A empty: everything in B
+            part_a[u], part_b[u] = lst[:0], lst
+        else:                                   # B empty when the list has < 2 entries
+            part_a[u], part_b[u] = lst[0::2], lst[1::2]
+    sp_, sh_ = canonical_strides(H)
+    workers = 16
+    ref = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
+    sa = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
+    sb = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
+    feed_lists(ref, layer, whole)
+    feed_lists(sa, layer, part_a)
+    feed_lists(sb, layer, part_b)
+    args = (li.q, li.kv_pool, sp_, sh_, li.pool_pages, li.ctx_lens)
+    o_ref, l_ref = ref.attend(*args)
+    for st_ in (sa, sb):
+        b_ = st_.buf
+        lib.decode_attn(dims, *args, b_.sel_counts, b_.sel_pages, b_.sel_phys, st_.scale,
+                        workers, b_.part_o, b_.part_lse, st_.max_parts)
+    a_, b_ = sa.buf, sb.buf
+    out = torch.full_like(o_ref, float("nan"))
+    lse = torch.full_like(l_ref, float("nan"))
+    lib.merge_splits_pair(dims, a_.part_o, a_.part_lse, a_.sel_counts, b_.part_o, b_.part_lse,
+                          b_.sel_counts, workers, out, lse)
+    o_a, l_a = torch.empty_like(out), torch.empty_like(lse)
+    o_b, l_b = torch.empty_like(out), torch.empty_like(lse)
+    lib.merge_splits(dims, a_.part_o, a_.part_lse, a_.sel_counts, workers, o_a, l_a)
+    lib.merge_splits(dims, b_.part_o, b_.part_lse, b_.sel_counts, workers, o_b, l_b)
+    torch.cuda.synchronize()
+    d = float((out - o_ref).abs().max())
+    say(f"  max |pair merge - whole| {d:.1e}")
+    fin = torch.isfinite(l_ref)
+    assert torch.equal(fin, torch.isfinite(lse)) and bool(torch.isneginf(lse[~fin]).all())
+    assert d <= 1e-5 and float((lse[fin] - l_ref[fin]).abs().max()) <= 1e-5
+    for u in range(B * H):
+        b, h = divmod(u, H)
+        rows = slice(h * G, (h + 1) * G)
+        if len(whole[u]) == 0:
+            assert bool((out[b, rows] == 0).all()) and bool(torch.isinf(lse[b, rows]).all())
+        elif len(part_a[u]) == 0:
+            assert torch.equal(out[b, rows], o_b[b, rows]), u
+            assert torch.equal(lse[b, rows], l_b[b, rows]), u
+        elif len(part_b[u]) == 0:
+            assert torch.equal(out[b, rows], o_a[b, rows]), u
+            assert torch.equal(lse[b, rows], l_a[b, rows]), u
