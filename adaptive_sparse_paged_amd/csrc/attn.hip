@@ -27,6 +27,7 @@
 // the merge finds a unit's partials from the same lengths.
 
 #include "common.h"
+#include "fetch.h"
 
 namespace sp {
 
@@ -265,14 +266,16 @@ __device__ __forceinline__ void seg_end(float m_run, float l_run, const floatx4 
   __syncthreads();   // the LDS is reused by the workgroup's next segment
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
+// Worker w of the balanced plan: its slice of the step's list entries, one
+// unit segment at a time.  Uses the launch's dynamic LDS: [waves][group][128]
+// O, then [waves][group] m and l.
+__device__ __forceinline__ void attn_worker(
+    int w, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
     int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_phys, float scale_log2, int hkv, int group, int max_pages,
     int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  extern __shared__ float smem[];  // [waves][group][128] O, then [waves][group] m and l
-  const int w = blockIdx.x;
+  extern __shared__ float smem[];
   int x, e, u, off, len;
   {
     PlanSeg first;
@@ -318,6 +321,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t stride_page,
+    int64_t stride_head, int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_phys, float scale_log2, int hkv, int group, int max_pages,
+    int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  attn_worker(blockIdx.x, q, kv, stride_page, stride_head, pool_pages, ctx_lens, sel_counts,
+              sel_pages, sel_phys, scale_log2, hkv, group, max_pages, cap, U, wmax, part_o,
+              part_lse);
+}
+
+// The host tier's fetch and the attention over the hits in one launch.  The
+// first nfetch workgroups copy the step's placed misses into their slots
+// (4 waves each); the others are the attention's workers over lists whose
+// misses read as empty pages (hit_phys), so no worker reads a slot being
+// written.  Every workgroup holds 96 KiB of LDS (dynamic, the attention
+// workers use the first part of it), so a compute unit runs one
+// of them at a time: a copying wave, whose host reads take microseconds,
+// never shares its unit's memory pipeline with attention waves.  The copying
+// workgroups come first in the grid and are placed first; attention workers
+// beyond the free units start as units free up.  With nothing to copy, the
+// copying workgroups exit at once and the launch is the attention alone.
+constexpr size_t kFetchAttnLds = 96 * 1024;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void fetch_attn_kernel(
+    const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv, MissTable table,
+    int nfetch, int32_t* __restrict__ step_counter, const uint16_t* __restrict__ q,
+    int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ hit_phys, float scale_log2, int hkv, int group, int max_pages,
+    int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  if ((int)blockIdx.x < nfetch) {
+    // every resolve workgroup has read the step (the resolve ran first on
+    // this stream): advance it for the next call
+    if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
+    fetch_misses((int)blockIdx.x * kAttnWaves + (int)(threadIdx.x >> 6), nfetch * kAttnWaves,
+                 host_kv, cache_kv, hkv, max_pages, table);
+    return;
+  }
+  attn_worker((int)blockIdx.x - nfetch, q, cache_kv, kUnitElems, 0, pool_pages, ctx_lens,
+              sel_counts, sel_pages, hit_phys, scale_log2, hkv, group, max_pages, cap, U, wmax,
+              part_o, part_lse);
+}
+
 }  // namespace sp
 
 extern "C" int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t workers) {
@@ -359,6 +406,24 @@ void enqueue_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv
                      stride_page, stride_head, pool_pages, ctx_lens, sel_counts, sel_pages,
                      sel_phys, scale_log2, hkv, group, dims->max_pages, list_cap(dims), U, wmax,
                      part_o, part_lse);
+}
+
+// Copying workgroups of fetch_attn_kernel: 64 of 4 waves, the 256 waves that
+// keep the PCIe link busy (the copy waits on the link, not on the waves).
+constexpr int kFetchAttnGroups = SPARSE_FETCH_ATTN_COPY_GROUPS;
+
+void enqueue_fetch_attn(const sparse_dims* dims, const uint16_t* host_kv, uint16_t* cache_kv,
+                        int64_t pool_slots, const MissTable& t, int32_t* step_counter,
+                        const uint16_t* q, const int32_t* ctx_lens, const int32_t* sel_counts,
+                        const int32_t* sel_pages, const int32_t* hit_phys, float scale, int wmax,
+                        float* part_o, float* part_lse, hipStream_t stream) {
+  const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
+  const int U = dims->batch * hkv;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(fetch_attn_kernel, dim3((unsigned)(kFetchAttnGroups + wmax)), dim3(256),
+                     kFetchAttnLds, stream, host_kv, cache_kv, t, kFetchAttnGroups, step_counter, q, pool_slots,
+                     ctx_lens, sel_counts, sel_pages, hit_phys, scale_log2, hkv, group,
+                     dims->max_pages, list_cap(dims), U, wmax, part_o, part_lse);
 }
 
 }  // namespace sp

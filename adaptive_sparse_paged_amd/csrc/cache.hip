@@ -23,19 +23,14 @@
 #include <algorithm>
 
 #include "common.h"
+#include "fetch.h"
 #include "lru_select.h"
 
 namespace sp {
 
 constexpr int kResThreads = 1024;
 constexpr int kMaxSlots = 8192;
-constexpr int kUnitElems = 2 * kTile;   // K tile + V tile
 constexpr int kMaxKvHeads = 64;
-
-struct MissRec {
-  int32_t unit;
-  int32_t slot;
-};
 
 // Per-request ticket word of the resolve: bits [0, 22) misses, [22, 44) hits
 // counted by the hit-pass workgroups, [44, 64) workgroups done.  A request
@@ -353,7 +348,6 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_kernel(
   // this stream): advance it for the next call
   if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
   const int w = blockIdx.x * kFetchWavesPerGroup + (threadIdx.x >> 6);
-  const int lane = lane_id();
   if (w >= waves_per_req * B) return;
   const int b = w % B;
   const int cnt = miss_count[b];
@@ -361,18 +355,8 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_kernel(
     cu_reserve[threadIdx.x] = 0u;
     asm volatile("" ::"v"(cu_reserve[threadIdx.x ^ 1u]));
   }
-  for (int i = w / B; i < cnt; i += waves_per_req) {
-    const MissRec m = misses[(int64_t)b * C + i];
-    const int h = m.unit / max_pages, p = m.unit - (m.unit / max_pages) * max_pages;
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        host_kv + (((int64_t)b * max_pages + p) * hkv + h) * kUnitElems);
-    u32x4* dst = reinterpret_cast<u32x4*>(cache_kv + ((int64_t)b * C + m.slot) * kUnitElems);
-    u32x4 t[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t[k] = __builtin_nontemporal_load(src + k * 64 + lane);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = t[k];
-  }
+  for (int i = w / B; i < cnt; i += waves_per_req)
+    copy_request_miss(host_kv, cache_kv, hkv, max_pages, C, b, misses[(int64_t)b * C + i]);
 }
 
 
@@ -683,26 +667,12 @@ __global__ __launch_bounds__(kFetchThreads) void pool_fetch_kernel(
   // every workgroup of the earlier kernels has read the step: advance it
   if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
   const int w = blockIdx.x * kFetchWavesPerGroup + (threadIdx.x >> 6);
-  const int lane = lane_id();
   const int P = *placed_in;
   if (P < 0) {                                 // never taken; keeps the reservation
     cu_reserve[threadIdx.x] = 0u;
     asm volatile("" ::"v"(cu_reserve[threadIdx.x ^ 1u]));
   }
-  const int per_req = hkv * max_pages;       // pooled ids fit in 31 bits
-  for (int i = w; i < P; i += waves) {
-    const MissRec m = misses[i];
-    const int b = m.unit / per_req, rest = m.unit - b * per_req;
-    const int64_t h = rest / max_pages, p = rest - h * max_pages;
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        host_kv + ((b * max_pages + p) * hkv + h) * kUnitElems);
-    u32x4* dst = reinterpret_cast<u32x4*>(cache_kv + (int64_t)m.slot * kUnitElems);
-    u32x4 t[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t[k] = __builtin_nontemporal_load(src + k * 64 + lane);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = t[k];
-  }
+  for (int i = w; i < P; i += waves) copy_pooled_miss(host_kv, cache_kv, hkv, max_pages, misses[i]);
 }
 
 // One workgroup per (request, KV head) unit: the unit's list entries that
@@ -1044,6 +1014,40 @@ extern "C" sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims,
   if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
   return fetch_any(dims, policy, host_kv, cache_kv, capacity, step_counter, ws,
                    (hipStream_t)stream);
+}
+
+extern "C" sparse_status sparse_hbm_cache_fetch_attn(
+    const sparse_dims* dims, const sparse_cache_policy* policy, const uint16_t* host_kv,
+    uint16_t* cache_kv, int32_t capacity, int32_t* step_counter, void* ws, size_t ws_bytes,
+    const uint16_t* q, const int32_t* ctx_lens, const int32_t* sel_counts,
+    const int32_t* sel_pages, const int32_t* hit_phys, float scale, int32_t workers,
+    float* part_o, float* part_lse, int64_t max_parts, void* stream) {
+  sparse_status st = sp::check_dims(dims);
+  if (st != SPARSE_OK) return st;
+  if (!step_counter || capacity < 1) return SPARSE_ERR_INVALID;
+  if ((st = check_pool_args(host_kv, cache_kv)) != SPARSE_OK) return st;
+  if (dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
+  if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
+  const int B = dims->batch;
+  const int64_t slots = policy->pooled ? (int64_t)capacity : (int64_t)B * capacity;
+  int wmax = 0;
+  if ((st = sp::check_attn(dims, q, cache_kv, sp::kUnitElems, 0, slots, ctx_lens, sel_counts,
+                           sel_pages, hit_phys, scale, workers, wmax)) != SPARSE_OK)
+    return st;
+  if (!part_o || !part_lse || !sp::aligned(part_o, 16)) return SPARSE_ERR_INVALID;
+  if (max_parts != (int64_t)B * dims->num_kv_heads + wmax) return SPARSE_ERR_INVALID;
+  sp::MissTable t;
+  if (policy->pooled) {
+    const PooledWs w = pooled_ws(B, capacity, ws);
+    t = sp::MissTable{w.misses, w.placed, 1, capacity, true};
+  } else {
+    const PerRequestWs w = per_request_ws(B, capacity, ws);
+    t = sp::MissTable{w.misses, w.miss_count, B, capacity, false};
+  }
+  sp::enqueue_fetch_attn(dims, host_kv, cache_kv, slots, t, step_counter, q, ctx_lens,
+                         sel_counts, sel_pages, hit_phys, scale, wmax, part_o, part_lse,
+                         (hipStream_t)stream);
+  return sp::launch_status();
 }
 
 extern "C" sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_counts,

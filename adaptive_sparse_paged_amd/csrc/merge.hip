@@ -40,14 +40,14 @@ __device__ __forceinline__ MergeRun merge_run(const int32_t* __restrict__ sel_co
 // coalesced 512-byte read by 32 threads), keeping an online (max, sum,
 // weighted sum); the 8 segment slots are then combined through LDS.  With
 // kPair, the unit's segments under a second plan (lists sel_counts_b,
-// partials part_o_b / part_lse_b, the same worker count) follow its
-// segments under the first: attention over the union of two disjoint lists.
+// partials part_o_b / part_lse_b, wmax_b workers) follow its segments under
+// the first: attention over the union of two disjoint lists.
 template <bool kPair>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ sel_counts, const float* __restrict__ part_o_b,
     const float* __restrict__ part_lse_b, const int32_t* __restrict__ sel_counts_b, int cap,
-    int U, int wmax, int hkv, int group, float* __restrict__ out,
+    int U, int wmax, int wmax_b, int hkv, int group, float* __restrict__ out,
     float* __restrict__ out_lse) {
   __shared__ floatx4 s_acc[kMergeSlots][32];
   __shared__ float s_m[kMergeSlots], s_s[kMergeSlots];
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const int slot = threadIdx.x >> 5, quad = threadIdx.x & 31;
   const MergeRun ra = merge_run(sel_counts, U, cap, wmax, u);
   MergeRun rb{0, 0};
-  if (kPair) rb = merge_run(sel_counts_b, U, cap, wmax, u);
+  if (kPair) rb = merge_run(sel_counts_b, U, cap, wmax_b, u);
   const int nall = ra.nseg + rb.nseg;
 
   float m = -INFINITY, s = 0.f;
@@ -125,7 +125,7 @@ void enqueue_merge(const sparse_dims* dims, const float* part_o, const float* pa
   const int U = dims->batch * hkv;
   hipLaunchKernelGGL(merge_kernel<false>, dim3(U, group), dim3(kMergeThreads), 0, stream, part_o,
                      part_lse, sel_counts, nullptr, nullptr, nullptr, list_cap(dims), U, wmax,
-                     hkv, group, out, out_lse);
+                     0, hkv, group, out, out_lse);
 }
 
 }  // namespace sp
@@ -161,20 +161,21 @@ extern "C" sparse_status sparse_merge_splits(const sparse_dims* dims, const floa
 
 extern "C" sparse_status sparse_merge_splits_pair(
     const sparse_dims* dims, const float* part_o_a, const float* part_lse_a,
-    const int32_t* sel_counts_a, const float* part_o_b, const float* part_lse_b,
-    const int32_t* sel_counts_b, int32_t workers, float* out, float* out_lse, void* stream) {
-  int wmax = 0;
+    const int32_t* sel_counts_a, int32_t workers_a, const float* part_o_b,
+    const float* part_lse_b, const int32_t* sel_counts_b, int32_t workers_b, float* out,
+    float* out_lse, void* stream) {
+  int wmax_a = 0, wmax_b = 0;
   sparse_status st =
-      check_merge(dims, part_o_a, part_lse_a, sel_counts_a, workers, out, out_lse, wmax);
+      check_merge(dims, part_o_a, part_lse_a, sel_counts_a, workers_a, out, out_lse, wmax_a);
   if (st != SPARSE_OK) return st;
-  if (!part_o_b || !part_lse_b || !sel_counts_b || !sp::aligned(part_o_b, 16))
-    return SPARSE_ERR_INVALID;
+  st = check_merge(dims, part_o_b, part_lse_b, sel_counts_b, workers_b, out, out_lse, wmax_b);
+  if (st != SPARSE_OK) return st;
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
   hipLaunchKernelGGL(sp::merge_kernel<true>, dim3(U, group), dim3(sp::kMergeThreads), 0,
                      (hipStream_t)stream, part_o_a, part_lse_a, sel_counts_a, part_o_b,
-                     part_lse_b, sel_counts_b, sp::list_cap(dims), U, wmax, hkv, group, out,
-                     out_lse);
+                     part_lse_b, sel_counts_b, sp::list_cap(dims), U, wmax_a, wmax_b, hkv, group,
+                     out, out_lse);
   return sp::launch_status();
 }
 

@@ -36,6 +36,7 @@ EXPORTS = (
     "sparse_read_blocks",
     "sparse_hbm_cache_resolve_split",
     "sparse_hbm_cache_fetch",
+    "sparse_hbm_cache_fetch_attn",
     "sparse_split_misses",
     "sparse_lse_combine",
     "sparse_decode_attn_merge",
@@ -94,7 +95,7 @@ _SIGS = {
     "sparse_decode_attn": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
                                   _P, _P, _I64, _P]),
     "sparse_merge_splits": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P]),
-    "sparse_merge_splits_pair": (_I32, [_D, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "sparse_merge_splits_pair": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P, _P]),
     "sparse_cache_workspace_bytes": (ctypes.c_size_t, [_D, _I32]),
     "sparse_select_topk": (_I32, [_D, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
@@ -108,6 +109,8 @@ _SIGS = {
     "sparse_hbm_cache_resolve_split": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_hbm_cache_fetch": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "sparse_hbm_cache_fetch_attn": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P,
+                                           _P, _P, _P, _P, _F, _I32, _P, _P, _I64, _P]),
     "sparse_split_misses": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_decode_attn_merge": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
@@ -223,6 +226,7 @@ def decode_attn_merge(dims, q, kv, stride_page, stride_head, pool_pages, ctx_len
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SPARSE_NOALLOC_SCRATCH_BYTES
+FETCH_ATTN_COPY_GROUPS = 64         # SPARSE_FETCH_ATTN_COPY_GROUPS
 
 
 def decode_attn_merge_noalloc(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens,
@@ -244,14 +248,14 @@ def merge_splits(dims, part_o, part_lse, sel_counts, workers, out, out_lse, stre
         _ptr(out), _ptr(out_lse), _stream(stream)))
 
 
-def merge_splits_pair(dims, part_o_a, part_lse_a, sel_counts_a, part_o_b, part_lse_b,
-                      sel_counts_b, workers, out, out_lse, stream=None):
+def merge_splits_pair(dims, part_o_a, part_lse_a, sel_counts_a, workers_a, part_o_b, part_lse_b,
+                      sel_counts_b, workers_b, out, out_lse, stream=None):
     """One merge over the partials of two disjoint sets of lists."""
     _dev(part_o_a, part_lse_a, sel_counts_a, part_o_b, part_lse_b, sel_counts_b, out, out_lse)
     _check("sparse_merge_splits_pair", load().sparse_merge_splits_pair(
-        ctypes.byref(dims), _ptr(part_o_a), _ptr(part_lse_a), _ptr(sel_counts_a),
-        _ptr(part_o_b), _ptr(part_lse_b), _ptr(sel_counts_b), workers, _ptr(out), _ptr(out_lse),
-        _stream(stream)))
+        ctypes.byref(dims), _ptr(part_o_a), _ptr(part_lse_a), _ptr(sel_counts_a), workers_a,
+        _ptr(part_o_b), _ptr(part_lse_b), _ptr(sel_counts_b), workers_b, _ptr(out),
+        _ptr(out_lse), _stream(stream)))
 
 
 def cache_workspace_bytes(dims, capacity):
@@ -353,6 +357,22 @@ def hbm_cache_fetch(dims, policy, host_kv, cache_kv, capacity, step_counter, ws,
     _check("sparse_hbm_cache_fetch", load().sparse_hbm_cache_fetch(
         ctypes.byref(dims), ctypes.byref(policy), _ptr(host_kv), _ptr(cache_kv), capacity,
         _ptr(step_counter), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hbm_cache_fetch_attn(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, q,
+                         ctx_lens, sel_counts, sel_pages, hit_phys, scale, workers, part_o,
+                         part_lse, max_parts, stream=None):
+    """hbm_cache_fetch and decode_attn over (sel_counts, sel_pages, hit_phys) on
+    the cache pool, in one launch."""
+    _dev(cache_kv, step_counter, ws, q, ctx_lens, sel_counts, sel_pages, hit_phys, part_o,
+         part_lse)
+    if not host_kv.is_pinned():
+        raise ValueError("host_kv must be pinned host memory")
+    _check("sparse_hbm_cache_fetch_attn", load().sparse_hbm_cache_fetch_attn(
+        ctypes.byref(dims), ctypes.byref(policy), _ptr(host_kv), _ptr(cache_kv), capacity,
+        _ptr(step_counter), _ptr(ws), ws.numel() * ws.element_size(), _ptr(q), _ptr(ctx_lens),
+        _ptr(sel_counts), _ptr(sel_pages), _ptr(hit_phys), scale, workers, _ptr(part_o),
+        _ptr(part_lse), max_parts, _stream(stream)))
 
 
 def split_misses(dims, sel_counts, sel_pages, sel_phys, hit_phys, miss_counts, miss_pages,

@@ -276,19 +276,20 @@ sparse_status sparse_merge_splits(const sparse_dims* dims, const float* part_o,
 /*
  * sparse_merge_splits_pair -- the merge of sparse_merge_splits over two
  * disjoint sets of lists of the same rows: unit u's segments under the plan
- * of lists a (sel_counts_a, partials part_o_a / part_lse_a) and under the plan
- * of lists b, all merged by the same identity into one result -- attention
- * over the union of the two lists ([P1], abstract, sentence on
- * self-planning attention, as sparse_merge_splits).  Both sets of partials
- * come from sparse_decode_attn calls with these dims and this workers value.
- * The host tier's split step merges the hits' and the misses' partials with
- * it.  Arguments and errors as sparse_merge_splits, per set.
+ * of lists a (sel_counts_a, partials part_o_a / part_lse_a, written by
+ * sparse_decode_attn with workers_a) and under the plan of lists b, all
+ * merged by the same identity into one result -- attention over the union
+ * of the two lists ([P1], abstract, sentence on self-planning attention, as
+ * sparse_merge_splits).  The host tier's split step merges the hits' and the
+ * misses' partials with it.  Arguments and errors as sparse_merge_splits,
+ * per set.
  */
 sparse_status sparse_merge_splits_pair(const sparse_dims* dims, const float* part_o_a,
                                        const float* part_lse_a, const int32_t* sel_counts_a,
-                                       const float* part_o_b, const float* part_lse_b,
-                                       const int32_t* sel_counts_b, int32_t workers, float* out,
-                                       float* out_lse, void* stream);
+                                       int32_t workers_a, const float* part_o_b,
+                                       const float* part_lse_b, const int32_t* sel_counts_b,
+                                       int32_t workers_b, float* out, float* out_lse,
+                                       void* stream);
 
 /*
  * sparse_decode_attn_merge -- sparse_decode_attn followed by
@@ -472,9 +473,10 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
  *                                    placed misses as a short list; no copy
  *   sparse_hbm_cache_fetch           the misses' copies; advances the step
  * then attention over (sel_counts, sel_pages, hit_phys) -- it may overlap
- * the fetch -- and, after the fetch, attention over the miss lists; both
- * sets of partials are merged by sparse_merge_splits_pair (attention over a
- * partition of a list, merged by log-sum-exp, is attention over the list).
+ * the fetch; sparse_hbm_cache_fetch_attn runs the two in one launch -- and,
+ * after the fetch, attention over the miss lists; both sets of partials are
+ * merged by sparse_merge_splits_pair (attention over a partition of a list,
+ * merged by log-sum-exp, is attention over the list).
  * Cache state, statistics and sel_phys equal those of
  * sparse_hbm_cache_resolve_policy on the same inputs.
  *
@@ -516,6 +518,36 @@ sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims, const sparse_cache
                                      const uint16_t* host_kv, uint16_t* cache_kv,
                                      int32_t capacity, int32_t* step_counter, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/*
+ * sparse_hbm_cache_fetch_attn -- sparse_hbm_cache_fetch and the attention
+ * over the hits in one launch: the copies of the misses placed by the last
+ * sparse_hbm_cache_resolve_split on this ws, and sparse_decode_attn over
+ * (sel_counts, sel_pages, hit_phys) on the cache pool (kv = cache_kv,
+ * stride_page 4096, stride_head 0, pool_pages = B * capacity, or capacity
+ * pooled).  A hit's slot is never written by the same step, so the two run
+ * side by side in one grid: SPARSE_FETCH_ATTN_COPY_GROUPS copying
+ * workgroups first, then the attention's workers; every workgroup holds 96
+ * KiB of LDS, so a compute unit never mixes copying waves (whose host reads
+ * take microseconds) with attention waves; attention workers beyond the
+ * free units start as units free up.  With nothing to copy the copying
+ * workgroups exit at once and the launch is the attention alone.
+ * The split schedule of the host tier on one stream, with no wait between
+ * streams: resolve_split, fetch_attn, attention over the miss lists,
+ * sparse_merge_splits_pair.  Arguments: as sparse_hbm_cache_fetch, then as
+ * sparse_decode_attn (part_o / part_lse / max_parts for this workers value).
+ * Advances *step_counter.  Errors as those two calls.
+ */
+#define SPARSE_FETCH_ATTN_COPY_GROUPS 64
+sparse_status sparse_hbm_cache_fetch_attn(const sparse_dims* dims,
+                                          const sparse_cache_policy* policy,
+                                          const uint16_t* host_kv, uint16_t* cache_kv,
+                                          int32_t capacity, int32_t* step_counter, void* ws,
+                                          size_t ws_bytes, const uint16_t* q,
+                                          const int32_t* ctx_lens, const int32_t* sel_counts,
+                                          const int32_t* sel_pages, const int32_t* hit_phys,
+                                          float scale, int32_t workers, float* part_o,
+                                          float* part_lse, int64_t max_parts, void* stream);
 
 /*
  * sparse_split_misses -- for each unit u, the list entries i < sel_counts[u]

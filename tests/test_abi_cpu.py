@@ -134,13 +134,14 @@ def test_null_and_value_checks(L):
     assert na(_dims(batch=2048, q_heads=32, kv_heads=8)) == lib.ERR_WORKSPACE
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == lib.ERR_INVALID
     assert L.sparse_merge_splits(ctypes.byref(d), FAKE, FAKE, None, 16, FAKE, FAKE, None) == lib.ERR_INVALID
-    pair = lambda b_o=FAKE, b_l=FAKE, b_c=FAKE, workers=16: L.sparse_merge_splits_pair(
-        ctypes.byref(d), FAKE, FAKE, FAKE, b_o, b_l, b_c, workers, FAKE, FAKE, None)
+    pair = lambda b_o=FAKE, b_l=FAKE, b_c=FAKE, workers=16, workers_b=8: L.sparse_merge_splits_pair(
+        ctypes.byref(d), FAKE, FAKE, FAKE, workers, b_o, b_l, b_c, workers_b, FAKE, FAKE, None)
     assert pair(b_o=None) == lib.ERR_INVALID
     assert pair(b_l=None) == lib.ERR_INVALID
     assert pair(b_c=None) == lib.ERR_INVALID
     assert pair(b_o=ctypes.c_void_p(0x10004)) == lib.ERR_INVALID      # partials 16-byte aligned
     assert pair(workers=-1) == lib.ERR_INVALID
+    assert pair(workers_b=-1) == lib.ERR_INVALID
     assert L.sparse_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None,
                                 FAKE, FAKE, None, 0, None) == lib.ERR_INVALID
     assert L.sparse_append_tokens(ctypes.byref(d), None, FAKE, FAKE, 8192, 4096, 100, FAKE,
@@ -224,3 +225,5 @@ def test_binding_constants_match_header():
     assert m and int(m.group(1)) == lib.ATTN_MIN_WORKER_PAGES
     m = re.search(r"#define SPARSE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_SCRATCH_BYTES
+    m = re.search(r"#define SPARSE_FETCH_ATTN_COPY_GROUPS (\d+)", text)
+    assert m and int(m.group(1)) == lib.FETCH_ATTN_COPY_GROUPS

@@ -140,10 +140,10 @@ def test_merge_pair_of_disjoint_lists(gpu_lib):
         else:                                   # B empty when the list has < 2 entries
             part_a[u], part_b[u] = lst[0::2], lst[1::2]
     sp_, sh_ = canonical_strides(H)
-    workers = 16
+    workers, workers_b = 16, 5          # the two sets planned for different grids
     ref = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
     sa = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
-    sb = SparseDecodeStep(dims, 0.99, workers, scale=w.scale)
+    sb = SparseDecodeStep(dims, 0.99, workers_b, scale=w.scale)
     feed_lists(ref, layer, whole)
     feed_lists(sa, layer, part_a)
     feed_lists(sb, layer, part_b)
@@ -152,16 +152,16 @@ def test_merge_pair_of_disjoint_lists(gpu_lib):
     for st_ in (sa, sb):
         b_ = st_.buf
         lib.decode_attn(dims, *args, b_.sel_counts, b_.sel_pages, b_.sel_phys, st_.scale,
-                        workers, b_.part_o, b_.part_lse, st_.max_parts)
+                        st_.workers, b_.part_o, b_.part_lse, st_.max_parts)
     a_, b_ = sa.buf, sb.buf
     out = torch.full_like(o_ref, float("nan"))
     lse = torch.full_like(l_ref, float("nan"))
-    lib.merge_splits_pair(dims, a_.part_o, a_.part_lse, a_.sel_counts, b_.part_o, b_.part_lse,
-                          b_.sel_counts, workers, out, lse)
+    lib.merge_splits_pair(dims, a_.part_o, a_.part_lse, a_.sel_counts, workers, b_.part_o,
+                          b_.part_lse, b_.sel_counts, workers_b, out, lse)
     o_a, l_a = torch.empty_like(out), torch.empty_like(lse)
     o_b, l_b = torch.empty_like(out), torch.empty_like(lse)
     lib.merge_splits(dims, a_.part_o, a_.part_lse, a_.sel_counts, workers, o_a, l_a)
-    lib.merge_splits(dims, b_.part_o, b_.part_lse, b_.sel_counts, workers, o_b, l_b)
+    lib.merge_splits(dims, b_.part_o, b_.part_lse, b_.sel_counts, workers_b, o_b, l_b)
     torch.cuda.synchronize()
     d = float((out - o_ref).abs().max())
     say(f"  max |pair merge - whole| {d:.1e}")
