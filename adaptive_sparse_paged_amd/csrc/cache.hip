@@ -764,7 +764,7 @@ sparse_status check_pool_args(const uint16_t* host_kv, const uint16_t* cache_kv)
 // About 256 fetching waves in all (each has one 8 KiB unit in flight; 32
 // compute units in all) keep the PCIe link busy; more only take compute
 // units from the attention that may run beside the fetch.
-constexpr int kFetchWaves = 256;
+constexpr int kFetchWaves = SPARSE_FETCH_GROUPS * sp::kFetchWavesPerGroup;
 
 // Per-request workspace views (layout above sparse_cache_workspace_bytes).
 struct PerRequestWs {

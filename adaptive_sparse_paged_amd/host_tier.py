@@ -196,25 +196,44 @@ class LayeredHostTierStep:
 
     Each layer has its own pinned host pool and HBM cache.  With
     prefetch=False every layer runs resolve+fetch then attention+merge on the
-    current stream.  With prefetch=True the resolves (hit detection, LRU,
-    fetch) of all layers run in layer order on a second stream, each
-    recording an event, and layer l's attention waits only for layer l's
-    event -- so the PCIe fetch of layer l+1 runs under the attention of layer
-    l.  Both modes run the same kernels on the same data in the same per-layer
-    order: outputs and cache state are bitwise the same.  The step joins the
-    second stream before it returns, so it can be captured whole."""
+    current stream.  With prefetch=True:
+      - a resolve stream runs every layer's resolve (hits, LRU, placement; no
+        copy) in layer order, up front: they depend on the shared lists
+        only, so none of them waits for a fetch or runs beside an attention
+        (a resolve beside an attention slowed both about twofold);
+      - an IO stream runs the layers' fetches back to back, each after its
+        layer's resolve;
+      - the current stream runs layer l's attention + merge after layer l's
+        fetch, so the PCIe fetch of layer l+1 runs under it.
+    Given the same worker count, both modes leave the same cache state and
+    outputs bitwise the same.  With workers=0 the pipelined attention runs on
+    all compute units but FETCH_GROUPS (the next layer's fetch takes whole
+    units), so its lists split differently and outputs agree up to the
+    rounding of the merge.  The step joins the other streams before it
+    returns, so it can be captured whole."""
 
     def __init__(self, dims, host_pools, capacity, gamma, workers=0, scale=None,
                  prefetch=True, device="cuda"):
         self.dims = dims
         self.prefetch = bool(prefetch)
         self.caches = [HbmPageCache(dims, h, capacity, device) for h in host_pools]
+        if workers == 0 and self.prefetch:
+            # leave the next layer's fetch its compute units: it needs whole
+            # units, and attention workers on every unit would hold it off
+            # until the attention drains
+            cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+            workers = max(1, cus - lib.FETCH_GROUPS)
         self.attn = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
-        # per-layer slot lists: layer l+1's resolve writes while layer l attends
+        # per-layer slot lists: later layers' resolves write while layer l attends
         self.sel_phys = [torch.zeros_like(self.attn.buf.sel_phys) for _ in host_pools]
+        # the split resolve's hit slots, unused here (one buffer: the resolves
+        # run one after another)
+        self.hit_phys = torch.zeros_like(self.attn.buf.sel_phys)
+        self.rs = torch.cuda.Stream(device=device)
         self.io = torch.cuda.Stream(device=device)
         self.start = DeviceEvent()
+        self.resolved = [DeviceEvent() for _ in host_pools]
         self.ready = [DeviceEvent() for _ in host_pools]
 
     @property
@@ -239,11 +258,16 @@ class LayeredHostTierStep:
             return
         cur = torch.cuda.current_stream()
         self.start.record(cur)
-        self.start.wait(self.io)
+        self.start.wait(self.rs)
         for l, cache in enumerate(self.caches):
-            cache.resolve(counts, pages, self.sel_phys[l], stream=self.io)
+            cache.resolve_split(counts, pages, self.sel_phys[l], self.hit_phys, stream=self.rs)
+            self.resolved[l].record(self.rs)
+        for l, cache in enumerate(self.caches):
+            self.resolved[l].wait(self.io)
+            cache.fetch(stream=self.io)
             self.ready[l].record(self.io)
-        # waiting for the last layer's event joins the second stream
+        # waiting for the last layer's fetch joins both other streams (the IO
+        # stream waited for every resolve)
         for l, cache in enumerate(self.caches):
             self.ready[l].wait(cur)
             kv, sp, sh, pp = cache.pool_args()

@@ -227,6 +227,7 @@ def decode_attn_merge(dims, q, kv, stride_page, stride_head, pool_pages, ctx_len
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SPARSE_NOALLOC_SCRATCH_BYTES
 FETCH_ATTN_COPY_GROUPS = 64         # SPARSE_FETCH_ATTN_COPY_GROUPS
+FETCH_GROUPS = 32                   # SPARSE_FETCH_GROUPS
 
 
 def decode_attn_merge_noalloc(dims, q, kv, stride_page, stride_head, pool_pages, ctx_lens,

@@ -509,6 +509,16 @@ sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
                                              size_t ws_bytes, void* stream);
 
 /*
+ * The fetch kernels (of sparse_hbm_cache_resolve, _resolve_policy and
+ * sparse_hbm_cache_fetch) run SPARSE_FETCH_GROUPS workgroups of 8 waves (for
+ * up to 256 requests; one more per 8 requests beyond), each holding a whole
+ * compute unit's LDS so that no other workgroup shares its unit.  A caller
+ * that runs attention on another stream while a fetch is in flight can size
+ * the attention (sparse_decode_attn's workers) to leave that many units free.
+ */
+#define SPARSE_FETCH_GROUPS 32
+
+/*
  * sparse_hbm_cache_fetch -- copy every miss placed by the last
  * sparse_hbm_cache_resolve_split on this ws from host_kv into its slot of
  * cache_kv (device-initiated reads of pinned host memory), and advance

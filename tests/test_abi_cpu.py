@@ -227,3 +227,5 @@ def test_binding_constants_match_header():
     assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_SCRATCH_BYTES
     m = re.search(r"#define SPARSE_FETCH_ATTN_COPY_GROUPS (\d+)", text)
     assert m and int(m.group(1)) == lib.FETCH_ATTN_COPY_GROUPS
+    m = re.search(r"#define SPARSE_FETCH_GROUPS (\d+)", text)
+    assert m and int(m.group(1)) == lib.FETCH_GROUPS
