@@ -61,7 +61,9 @@ struct MissTable {
 };
 
 // Wave fw of FW copies the misses whose position in the concatenation of
-// the requests' miss lists is fw, fw + FW, ...
+// the requests' miss lists is fw, fw + FW, ...  The per-request counts are
+// read 64 at a time in one vector load (lane i: request b0 + i), so with
+// nothing to copy a wave leaves after one round trip.
 __device__ __forceinline__ void fetch_misses(int fw, int FW, const uint16_t* __restrict__ host_kv,
                                              uint16_t* __restrict__ cache_kv, int hkv,
                                              int max_pages, const MissTable& t) {
@@ -71,14 +73,24 @@ __device__ __forceinline__ void fetch_misses(int fw, int FW, const uint16_t* __r
                                                       t.misses[i]);
     return;
   }
-  int base = 0;                              // misses of the requests before b
-  for (int b = 0; b < t.B; ++b) {
-    const int cnt = t.counts[b];
-    const int i0 = ((fw - base) % FW + FW) % FW;
-    for (int i = i0; i < cnt; i += FW)
-      copy_request_miss(host_kv, cache_kv, hkv, max_pages, t.C, b,
-                        t.misses[(int64_t)b * t.C + i]);
-    base = (int)(((int64_t)base + cnt) % FW);
+  const int lane = lane_id();
+  int base = 0;                              // misses of the requests before b0, mod FW
+  for (int b0 = 0; b0 < t.B; b0 += 64) {
+    const int cnt = (b0 + lane < t.B) ? max(t.counts[b0 + lane], 0) : 0;
+    const int incl = wave_incl_scan(cnt);
+    unsigned long long busy = __ballot(cnt > 0);
+    while (busy) {                           // the requests of this block with misses
+      const int j = __ffsll((long long)busy) - 1;
+      busy &= busy - 1;
+      const int cb = __builtin_amdgcn_readlane(cnt, j);
+      const int pre = __builtin_amdgcn_readlane(incl, j) - cb;     // before b0 + j in block
+      const int bb = (int)(((int64_t)base + pre) % FW);
+      const int b = b0 + j;
+      for (int i = ((fw - bb) % FW + FW) % FW; i < cb; i += FW)
+        copy_request_miss(host_kv, cache_kv, hkv, max_pages, t.C, b,
+                          t.misses[(int64_t)b * t.C + i]);
+    }
+    base = (int)(((int64_t)base + __builtin_amdgcn_readlane(incl, 63)) % FW);
   }
 }
 
