@@ -45,7 +45,7 @@ constexpr unsigned long long kTkCountMask = (1ull << kTkHitShift) - 1ull;
 // totals from the ticket.  With miss lists, each unit's placed misses are also
 // written in list order (a unit's misses are a contiguous run of the
 // request's misses, which go head by head).
-__device__ void resolve_place(int b, const int32_t* __restrict__ sel_counts,
+__device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
                               const int32_t* __restrict__ sel_pages, int hkv, int max_pages,
                               int C, int recency_shift, int step, int32_t* __restrict__ tags,
                               int32_t* __restrict__ stamps, int32_t* __restrict__ umap,
@@ -234,6 +234,7 @@ __device__ void resolve_place(int b, const int32_t* __restrict__ sel_counts,
     stats[b * 4 + 3] = (M > placed) ? 1 : 0;
     miss_count[b] = (int32_t)placed;
   }
+  return placed;
 }
 
 // Workgroup (b, h, c) of the grid: list entries c * 1024 + tid,
@@ -242,15 +243,23 @@ __device__ void resolve_place(int b, const int32_t* __restrict__ sel_counts,
 // places the misses, or with none only writes the statistics.  With every
 // access a hit, a step is one pass of parallel lookups: the list entries and
 // the list length are loaded together, then the unit map.
+//
+// kFetch: the resolve of the one-pass call.  Each request's last workgroup
+// then copies the request's placed misses itself (its 16 waves, from pinned
+// host memory into the slots), and the last workgroup of the whole grid
+// (a second ticket) advances the step counter -- every workgroup has read
+// the step by then.  One launch instead of resolve + fetch.
+template <bool kFetch>
 __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
-    int max_pages, int C, int nchunk, int recency_shift,
-    const int32_t* __restrict__ step_counter, int32_t* __restrict__ slot_tag,
-    int32_t* __restrict__ slot_stamp, int32_t* __restrict__ unit_slot,
-    int32_t* __restrict__ sel_phys, int32_t* __restrict__ hit_phys, int32_t* __restrict__ stats,
-    MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
-    unsigned long long* __restrict__ tickets, int32_t* __restrict__ miss_counts,
-    int32_t* __restrict__ miss_pages, int32_t* __restrict__ miss_phys) {
+    int max_pages, int C, int nchunk, int recency_shift, int32_t* __restrict__ step_counter,
+    int32_t* __restrict__ slot_tag, int32_t* __restrict__ slot_stamp,
+    int32_t* __restrict__ unit_slot, int32_t* __restrict__ sel_phys,
+    int32_t* __restrict__ hit_phys, int32_t* __restrict__ stats, MissRec* __restrict__ misses,
+    int32_t* __restrict__ miss_count, unsigned long long* __restrict__ tickets,
+    int32_t* __restrict__ miss_counts, int32_t* __restrict__ miss_pages,
+    int32_t* __restrict__ miss_phys, const uint16_t* __restrict__ host_kv,
+    uint16_t* __restrict__ cache_kv, uint32_t* __restrict__ grid_ticket) {
   __shared__ unsigned long long scan64[kResThreads / 64];
   __shared__ unsigned long long s_tk;
   const int tid = threadIdx.x;
@@ -294,6 +303,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     if (i - tid >= n) break;                 // (uniform across the workgroup)
     p = sel_pages[row + min(i, max_pages - 1)];
   }
+  // every thread holds the step before the block's first barrier, so the
+  // grid ticket below (taken after it) follows every read of the step
+  asm volatile("" ::"v"(step));
   unsigned long long tot;
   block_excl_scan<unsigned long long, kResThreads>(
       ((unsigned long long)h_local << kTkHitShift) | m_local, scan64, tot);
@@ -304,24 +316,39 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   }
   __syncthreads();
   const unsigned long long tk = s_tk;
-  if ((int)(tk >> kTkDoneShift) != per_req) return;   // not the request's last workgroup
-  const uint32_t M = (uint32_t)(tk & kTkCountMask);
-  const uint32_t H = (uint32_t)((tk >> kTkHitShift) & kTkCountMask);
-  if (tid == 0) __hip_atomic_store(tickets + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (M == 0u) {                 // every requested unit is resident: nothing to place
-    if (miss_counts && tid < hkv) miss_counts[b * hkv + tid] = 0;
-    if (tid == 0) {
-      stats[b * 4 + 0] = (int32_t)H;
-      stats[b * 4 + 1] = 0;
-      stats[b * 4 + 2] = 0;
-      stats[b * 4 + 3] = 0;
-      miss_count[b] = 0;
+  if ((int)(tk >> kTkDoneShift) == per_req) {           // the request's last workgroup
+    const uint32_t M = (uint32_t)(tk & kTkCountMask);
+    const uint32_t H = (uint32_t)((tk >> kTkHitShift) & kTkCountMask);
+    if (tid == 0) __hip_atomic_store(tickets + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (M == 0u) {               // every requested unit is resident: nothing to place
+      if (miss_counts && tid < hkv) miss_counts[b * hkv + tid] = 0;
+      if (tid == 0) {
+        stats[b * 4 + 0] = (int32_t)H;
+        stats[b * 4 + 1] = 0;
+        stats[b * 4 + 2] = 0;
+        stats[b * 4 + 3] = 0;
+        miss_count[b] = 0;
+      }
+    } else {
+      const uint32_t placed = resolve_place(
+          b, sel_counts, sel_pages, hkv, max_pages, C, recency_shift, step,
+          slot_tag + (int64_t)b * C, stamps, unit_slot + (int64_t)b * hkv * max_pages, sel_phys,
+          stats, misses, miss_count, M, H, miss_counts, miss_pages, miss_phys);
+      if (kFetch) {
+        __syncthreads();         // the miss records written above, visible to every wave
+        for (int k = tid >> 6; k < (int)placed; k += kResThreads / 64)
+          copy_request_miss(host_kv, cache_kv, hkv, max_pages, C, b,
+                            misses[(int64_t)b * C + k]);
+      }
     }
-    return;
   }
-  resolve_place(b, sel_counts, sel_pages, hkv, max_pages, C, recency_shift, step,
-                slot_tag + (int64_t)b * C, stamps, unit_slot + (int64_t)b * hkv * max_pages,
-                sel_phys, stats, misses, miss_count, M, H, miss_counts, miss_pages, miss_phys);
+  if (kFetch && tid == 0) {
+    const uint32_t t = atomicAdd(grid_ticket, 1u);
+    if (t == gridDim.x - 1u) {   // the grid's last workgroup: advance the step
+      *step_counter = step + 1;
+      __hip_atomic_store(grid_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // The fetch runs in a few whole compute units that it keeps to itself: each
@@ -717,14 +744,15 @@ extern "C" size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t 
   if (sp::check_dims(dims) != SPARSE_OK || capacity < 1) return 0;
   return (size_t)dims->batch * (sizeof(unsigned long long) +
                                 (size_t)capacity * sizeof(sp::MissRec) + sizeof(int32_t)) +
-         256;
+         sizeof(uint32_t) + 256;
 }
 
 namespace {
 
 // Per-request workspace: the resolve's ticket words [B] (zero before the
-// first call; every call leaves them zero), miss records [B][C], then the
-// per-request counts.
+// first call; every call leaves them zero), miss records [B][C], the
+// per-request counts [B], then the one-pass resolve's grid ticket (zero
+// before the first call, left zero).
 // Pooled workspace (S rounded up to whole blocks of 1024 slots, nblk of
 // them): marks [S], compacted candidate keys [S] and their blocks [S],
 // avail [S], miss records [S], the selection state, two running totals, per
@@ -771,11 +799,13 @@ struct PerRequestWs {
   unsigned long long* tickets;
   sp::MissRec* misses;
   int32_t* miss_count;
+  uint32_t* grid_ticket;
 };
 PerRequestWs per_request_ws(int B, int32_t capacity, void* ws) {
   unsigned long long* tickets = static_cast<unsigned long long*>(ws);
   sp::MissRec* misses = reinterpret_cast<sp::MissRec*>(tickets + B);
-  return {tickets, misses, reinterpret_cast<int32_t*>(misses + (size_t)B * capacity)};
+  int32_t* counts = reinterpret_cast<int32_t*>(misses + (size_t)B * capacity);
+  return {tickets, misses, counts, reinterpret_cast<uint32_t*>(counts + B)};
 }
 
 // Optional per-unit lists of the misses placed this step (split schedule).
@@ -795,20 +825,32 @@ int resolve_chunks(const sparse_dims* dims) {
   return std::max(1, std::min(want, lim));
 }
 
+// host_kv and cache_kv given: the one-pass resolve, which also copies the
+// misses and advances the step (resolve_kernel<true>); else the resolve
+// alone, for a fetch that follows.
 sparse_status resolve_per_request(const sparse_dims* dims, int shift, const int32_t* sel_counts,
                                   const int32_t* sel_pages, int32_t capacity, int32_t* slot_tag,
                                   int32_t* slot_stamp, int32_t* unit_slot, int32_t* step_counter,
                                   int32_t* sel_phys, int32_t* hit_phys, int32_t* stats, void* ws,
-                                  MissLists ml, hipStream_t s) {
+                                  MissLists ml, const uint16_t* host_kv, uint16_t* cache_kv,
+                                  hipStream_t s) {
   const int B = dims->batch, hkv = dims->num_kv_heads;
   const PerRequestWs w = per_request_ws(B, capacity, ws);
   const int nchunk = resolve_chunks(dims);
   const int64_t groups = (int64_t)B * hkv * nchunk;
   if (groups > INT32_MAX) return SPARSE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(sp::resolve_kernel, dim3((unsigned)groups), dim3(sp::kResThreads), 0, s,
-                     sel_counts, sel_pages, hkv, dims->max_pages, capacity, nchunk, shift,
-                     step_counter, slot_tag, slot_stamp, unit_slot, sel_phys, hit_phys, stats,
-                     w.misses, w.miss_count, w.tickets, ml.counts, ml.pages, ml.phys);
+  if (host_kv)
+    hipLaunchKernelGGL(sp::resolve_kernel<true>, dim3((unsigned)groups), dim3(sp::kResThreads), 0,
+                       s, sel_counts, sel_pages, hkv, dims->max_pages, capacity, nchunk, shift,
+                       step_counter, slot_tag, slot_stamp, unit_slot, sel_phys, hit_phys, stats,
+                       w.misses, w.miss_count, w.tickets, ml.counts, ml.pages, ml.phys, host_kv,
+                       cache_kv, w.grid_ticket);
+  else
+    hipLaunchKernelGGL(sp::resolve_kernel<false>, dim3((unsigned)groups), dim3(sp::kResThreads),
+                       0, s, sel_counts, sel_pages, hkv, dims->max_pages, capacity, nchunk, shift,
+                       step_counter, slot_tag, slot_stamp, unit_slot, sel_phys, hit_phys, stats,
+                       w.misses, w.miss_count, w.tickets, ml.counts, ml.pages, ml.phys, nullptr,
+                       nullptr, w.grid_ticket);
   return sp::launch_status();
 }
 
@@ -953,7 +995,7 @@ sparse_status resolve_any(const sparse_dims* dims, const sparse_cache_policy* po
                           s);
   return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, capacity,
                              slot_tag, slot_stamp, unit_slot, step_counter, sel_phys, hit_phys,
-                             stats, ws, ml, s);
+                             stats, ws, ml, nullptr, nullptr, s);
 }
 
 sparse_status fetch_any(const sparse_dims* dims, const sparse_cache_policy* policy,
@@ -976,6 +1018,11 @@ extern "C" sparse_status sparse_hbm_cache_resolve_policy(
   if ((st = check_pool_args(host_kv, cache_kv)) != SPARSE_OK) return st;
   if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (!policy->pooled)          // one launch: the resolve copies its requests' misses itself
+    return resolve_per_request(dims, policy->recency_shift, sel_counts, sel_pages, capacity,
+                               slot_tag, slot_stamp, unit_slot, step_counter, sel_phys, nullptr,
+                               stats, ws, MissLists{nullptr, nullptr, nullptr}, host_kv,
+                               cache_kv, s);
   if ((st = resolve_any(dims, policy, sel_counts, sel_pages, capacity, slot_tag, slot_stamp,
                         unit_slot, step_counter, sel_phys, nullptr, stats, ws,
                         MissLists{nullptr, nullptr, nullptr}, s)) != SPARSE_OK)

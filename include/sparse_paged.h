@@ -343,10 +343,10 @@ sparse_status sparse_decode_attn_merge_noalloc(const sparse_dims* dims, const ui
                                                void* stream);
 
 /* Bytes of workspace sparse_hbm_cache_resolve needs (host): a ticket word per
- * request (the resolve's workgroups of one request count themselves in on it)
- * and the per-request list of placed misses handed from the resolve kernel to
- * the fetch kernel.  Zero it once before the first call; every call leaves
- * the ticket words zero. */
+ * request (the resolve's workgroups of one request count themselves in on
+ * it), the per-request list of placed misses (kept for a separate fetch, see
+ * sparse_hbm_cache_fetch) and a ticket for the whole grid.  Zero it once
+ * before the first call; every call leaves the tickets zero. */
 size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
 
 /*
@@ -388,12 +388,12 @@ size_t sparse_cache_workspace_bytes(const sparse_dims* dims, int32_t capacity);
  *   stats      int32 [B][4] out: hits, misses, evictions, overflow flag
  *   capacity   slots per request, 1..8192; num_kv_heads <= 64
  *   ws         see sparse_cache_workspace_bytes (zeroed once before use)
- * Enqueues two kernels.  The resolve runs one 1024-thread workgroup per
- * (request, KV head, chunk of up to 1024 list entries); each stamps its hits
- * and writes their slot ids, and the last of a request's workgroups to
- * finish places the request's misses (or, with none, writes only the
- * statistics).  The fetch copies the placed misses.  Calls sharing cache
- * state or a workspace must not overlap in time.
+ * Enqueues one kernel: one 1024-thread workgroup per (request, KV head,
+ * chunk of up to 1024 list entries); each stamps its hits and writes their
+ * slot ids, and the last of a request's workgroups to finish places the
+ * request's misses and copies them into their slots (or, with none, writes
+ * only the statistics); the grid's last workgroup advances the step.  Calls
+ * sharing cache state or a workspace must not overlap in time.
  */
 sparse_status sparse_hbm_cache_resolve(const sparse_dims* dims, const int32_t* sel_counts,
                                        const int32_t* sel_pages, const uint16_t* host_kv,
@@ -509,8 +509,8 @@ sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
                                              size_t ws_bytes, void* stream);
 
 /*
- * The fetch kernels (of sparse_hbm_cache_resolve, _resolve_policy and
- * sparse_hbm_cache_fetch) run SPARSE_FETCH_GROUPS workgroups of 8 waves (for
+ * The fetch kernels (of sparse_hbm_cache_fetch, and of the pooled
+ * sparse_hbm_cache_resolve_policy) run SPARSE_FETCH_GROUPS workgroups of 8 waves (for
  * up to 256 requests; one more per 8 requests beyond), each holding a whole
  * compute unit's LDS so that no other workgroup shares its unit.  A caller
  * that runs attention on another stream while a fetch is in flight can size
