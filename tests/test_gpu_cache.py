@@ -118,6 +118,19 @@ def _case(w, C, list_pages, steps, drift, workers=8, check_all_slots=True, lists
     return out_stats
 
 
+def test_cache_resolver_repeated_lists_all_hit(gpu_lib):
+    """Drifting steps, then the same lists again: every access hits, the
+    resolve places nothing and copies nothing, stamps move to the new step
+    and the step counter still advances once per call."""
+    w = I.custom_workload("cache_rep", 3, 8, 2, ("fixed", 3200), index=128)
+    base = I.drift_lists(w, I.pages_of(3200), 20, 4, 0.3)
+    lists = np.concatenate([base, base[-1:], base[-1:], base[-1:]])
+    say("[cache] 4 drifting steps then 3 all-hit steps, B=3 Hkv=2, 64 slots")
+    stats = _case(w, C=64, list_pages=20, steps=lists.shape[0], drift=0.0, lists=lists)
+    assert all(r["misses"] == 0 for r in stats[-9:])
+    assert sum(r["misses"] for r in stats[:12]) > 0
+
+
 def test_cache_resolver_small_drift(gpu_lib):
     w = I.custom_workload("cache_small", 2, 8, 2, ("fixed", 3200), index=120)
     say("[cache] small: B=2 Hkv=2 200 pages, 48 slots, lists of 20, drift 20%, 14 steps")

@@ -23,7 +23,10 @@ from _gpu_case import ATTN_TOL, feed_lists, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, C, LP, steps, drift, pooled=False, shift=0, workers=8, graph_from=None):
+def _run(w, C, LP, steps, drift, pooled=False, shift=0, workers=8, graph_from=None,
+         hit_steps=0):
+    """hit_steps: that many more steps on the last lists again, where every
+    access hits (the copying workgroups find nothing to copy)."""
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
     host, MP = I.build_host_pool(w, 0, lens=lens)
@@ -36,6 +39,9 @@ def _run(w, C, LP, steps, drift, pooled=False, shift=0, workers=8, graph_from=No
     spl = SplitHostTierStep(dims, spl_cache, 0.99, workers, scale=w.scale)
     layer = types.SimpleNamespace(w=w, dims=dims, li=li)
     lists = I.drift_lists(w, min(I.pages_of(L) for L in lens), LP, steps, drift)
+    if hit_steps:
+        lists = np.concatenate([lists] + [lists[-1:]] * hit_steps)
+        steps += hit_steps
     out = torch.empty((B, w.q_heads, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, w.q_heads), dtype=torch.float32, device="cuda")
     graph, misses_total, worst = None, 0, 0.0
@@ -58,6 +64,8 @@ def _run(w, C, LP, steps, drift, pooled=False, shift=0, workers=8, graph_from=No
             assert torch.equal(getattr(ref_cache, name), getattr(spl_cache, name)), (t, name)
         assert int(spl_cache.stats[:, 3].sum()) == 0, "case sized to never overflow"
         misses_total += int(spl_cache.stats[:, 1].sum())
+        if hit_steps and t >= steps - hit_steps:
+            assert int(spl_cache.stats[:, 1].sum()) == 0, (t, "an all-hit step missed")
         counts = ref.buf.sel_counts.cpu().numpy()
         pages = ref.buf.sel_pages.cpu().numpy()
         phys = ref.buf.sel_phys.cpu().numpy()
@@ -103,6 +111,22 @@ def test_split_host_tier_matches_one_pass(gpu_lib, pooled, shift):
     C = 2 * 64 if pooled else 64
     misses, worst = _run(w, C, 24, 10, 0.25, pooled=pooled, shift=shift, graph_from=5)
     say(f"  10 steps (graph from step 5), {misses} misses, max |split - one pass| {worst:.1e}")
+    assert misses > 0
+
+
+@pytest.mark.parametrize("pooled", [False, True], ids=["exact", "pooled"])
+def test_split_many_requests_then_all_hits(gpu_lib, pooled):
+    """70 requests (the copying waves read the per-request miss counts 64 at
+    a time: two blocks), lists of 12 pages drifting 50%, then two steps on
+    the same lists where every access hits: nothing to copy, the one-pass
+    resolve places nothing.  Against the one-pass step as above, eagerly and
+    (from step 3) replayed from a graph."""
+    w = I.custom_workload("split_many", 70, 8, 2, ("fixed", 1600), index=127)
+    say(f"[split] 70 requests x 2 KV heads, 48 slots each, lists of 12, 4 drifting steps "
+        f"then 2 all-hit steps, pooled={pooled}")
+    C = 70 * 48 if pooled else 48
+    misses, worst = _run(w, C, 12, 4, 0.5, pooled=pooled, workers=32, graph_from=3,
+                         hit_steps=2)
     assert misses > 0
 
 
