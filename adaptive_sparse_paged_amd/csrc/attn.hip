@@ -290,14 +290,18 @@ __device__ __forceinline__ void attn_worker(
   off = __builtin_amdgcn_readfirstlane(off);
   len = __builtin_amdgcn_readfirstlane(len);
   if (u < 0) return;                   // (x < T always lies in some unit)
+  // Unit u's entries are its positions past the first kPlanUnitCost; the
+  // worker's first unit always gives it some (its range is longer than that).
+  constexpr int C = kPlanUnitCost;
   Seg cur;
-  seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, x - off,
-            min(e, off + len) - off);
+  seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, max(x - off - C, 0),
+            min(e, off + len) - off - C);
   // Segment by segment.  After the first, the next unit is u + 1 (its length
   // loaded at the segment's start), skipping empty lists.  x < e <= T, so a
   // later unit holds position x whenever the loop goes on; the u < U - 1
-  // test only guards against lengths changed under the kernel.  (Issuing the
-  // next segment's loads before this one's epilogue gains nothing: the
+  // test only guards against lengths changed under the kernel.  A range that
+  // ends within a unit's first C positions gives no entries there.  (Issuing
+  // the next segment's loads before this one's epilogue gains nothing: the
   // epilogue's workgroup barrier waits for every load still in flight.)
   while (true) {
     const int next_raw = sel_counts[min(u + 1, U - 1)];
@@ -306,18 +310,18 @@ __device__ __forceinline__ void attn_worker(
     seg_pages(cur, kv, stride_page, stride_head, pool_pages, sel_pages, sel_phys, scale_log2,
               group, max_pages, m_run, l_run, o);
     seg_end(m_run, l_run, o, group, (int64_t)cur.u + w, smem, part_o, part_lse);
-    x = off + cur.i1;
+    x = off + C + cur.i1;
     if (x >= e) break;
     off += len;
     ++u;
-    len = min(max(next_raw, 0), cap);
+    len = plan_positions(next_raw, cap);
     while (len == 0 && u < U - 1) {
       ++u;
-      len = min(max(sel_counts[u], 0), cap);
+      len = plan_positions(sel_counts[u], cap);
     }
-    if (len == 0) break;
-    seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, x - off,
-              min(e, off + len) - off);
+    if (len == 0 || e - off <= C) break;
+    seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, 0,
+              min(e, off + len) - off - C);
   }
 }
 

@@ -93,24 +93,37 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 }
 
 // ---- the balanced plan, derived on the device from the list lengths -------
-// The step's T = sum_u k_u list entries (k_u = min(count_u, cap), cap the
-// dims' list bound) are laid end to end in unit order: entry e of unit u sits
-// at global position off_u + e, off_u = sum_{v<u} k_v.  W workers share them
-// evenly: worker w owns positions [floor(w T / W), floor((w + 1) T / W)),
-// crossing unit boundaries where they fall, and writes one partial per unit
-// it touches, in slot u + w (unit and worker indices both grow along the
-// positions, so the slots of distinct (unit, worker) pairs differ and every
-// slot is below U + W).  W is the grid size the caller gave, cut to
-// ceil(T / kMinWorkerPages) so short steps do not spread a few pages over
-// hundreds of workgroups; every worker then owns at least one entry.
+// Every unit with a nonempty list (k_u = min(count_u, cap) entries, cap the
+// dims' list bound) takes c = kPlanUnitCost + k_u positions: c positions that
+// stand for the fixed cost of starting a unit's segment, then its entries.
+// The units are laid end to end in unit order: entry e of unit u sits at
+// global position off_u + c + e, off_u the sum of the positions of the units
+// before it; T is the total.  W workers share the positions evenly: worker w
+// owns [floor(w T / W), floor((w + 1) T / W)), crossing unit boundaries where
+// they fall, and writes one partial per unit whose entries its range meets,
+// in slot u + w (unit and worker indices both grow along the positions, so
+// the slots of distinct (unit, worker) pairs differ and every slot is below
+// U + W).  A worker whose range crosses into a unit therefore gets c fewer
+// entries for the segment it starts there.  W is the grid size the caller
+// gave, cut to ceil(T / kMinWorkerPages) so short steps do not spread a few
+// pages over hundreds of workgroups; every worker's range is then at least
+// 16 positions, more than c, so its first unit always gives it entries.
 // Everything here is computed by each wave from sel_counts alone: no host
-// plan and no precomputed offsets.
+// plan and no precomputed offsets.  The functions below work in positions;
+// the attention and the merge turn them into entries.
 constexpr int kPlanVU = 8;                  // units per lane in one scan segment
 constexpr int kPlanSeg = 64 * kPlanVU;      // units per scan segment
 constexpr int kMinWorkerPages = SPARSE_ATTN_MIN_WORKER_PAGES;
+constexpr int kPlanUnitCost = SPARSE_ATTN_UNIT_COST_PAGES;
+static_assert(kPlanUnitCost < kMinWorkerPages / 2, "a worker's first unit must give it entries");
 
-// List lengths of units base .. base + kPlanVU - 1, clamped to [0, cap]
-// (0 past the last unit).  The loads are unconditional -- an index past the
+// Positions a unit of `raw` list entries takes in the plan.
+__device__ __forceinline__ int plan_positions(int raw, int cap) {
+  const int k = min(max(raw, 0), cap);
+  return k > 0 ? k + kPlanUnitCost : 0;
+}
+
+// Plan positions of units base .. base + kPlanVU - 1 (0 past the last unit).  The loads are unconditional -- an index past the
 // last unit re-reads unit U-1 -- and all are issued before any is used.  The
 // empty asm statement pins each loaded value in a register; without it the
 // compiler moves each load under the `idx < U` test, and a load under a
@@ -124,7 +137,7 @@ __device__ __forceinline__ void plan_counts8(const int32_t* __restrict__ counts,
 #pragma unroll
   for (int v = 0; v < kPlanVU; ++v) {
     asm volatile("" : "+v"(raw[v]));
-    k[v] = (base + v < U) ? min(max(raw[v], 0), cap) : 0;
+    k[v] = (base + v < U) ? plan_positions(raw[v], cap) : 0;
   }
 }
 
@@ -171,7 +184,7 @@ __device__ __forceinline__ bool plan_seg_find(const PlanSeg& P, int seg, int bef
   return true;
 }
 
-// T, the step's total list entries.  `first` receives segment 0 (units
+// T, the step's total positions.  `first` receives segment 0 (units
 // 0 .. 511), which is all of them when U <= 512.
 __device__ __forceinline__ int plan_total(const int32_t* __restrict__ counts, int U, int cap,
                                           PlanSeg& first) {
@@ -202,7 +215,7 @@ __device__ __forceinline__ void plan_find(const int32_t* __restrict__ counts, in
   }
 }
 
-// Unit u's first global position, its length and T (wave-uniform).
+// Unit u's first global position, its positions and T (wave-uniform).
 __device__ __forceinline__ void plan_unit(const int32_t* __restrict__ counts, int U, int cap,
                                           int u, int& off, int& len, int& total) {
   total = 0;
@@ -225,13 +238,13 @@ __device__ __forceinline__ void plan_unit(const int32_t* __restrict__ counts, in
   }
 }
 
-// Workers the plan uses for T entries with a grid of wmax workgroups.
+// Workers the plan uses for T positions with a grid of wmax workgroups.
 __device__ __forceinline__ int plan_workers(int total, int wmax) {
   if (total <= 0) return 0;
   return min(wmax, (total + kMinWorkerPages - 1) / kMinWorkerPages);
 }
 
-// First position owned by worker w (of W over T entries).
+// First position owned by worker w (of W over T positions).
 __device__ __forceinline__ int plan_start(int w, int W, int total) {
   return (int)(((int64_t)w * total) / W);
 }

@@ -23,9 +23,9 @@ __device__ __forceinline__ MergeRun merge_run(const int32_t* __restrict__ sel_co
   len = __builtin_amdgcn_readfirstlane(len);
   total = __builtin_amdgcn_readfirstlane(total);
   int w_lo = 0, nseg = 0;
-  if (len > 0) {
+  if (len > 0) {                 // its entries: positions off + C .. off + len - 1
     const int W = plan_workers(total, wmax);
-    w_lo = plan_owner(off, W, total);
+    w_lo = plan_owner(off + kPlanUnitCost, W, total);
     nseg = plan_owner(off + len - 1, W, total) - w_lo + 1;
   }
   return MergeRun{(int64_t)u + w_lo, nseg};   // segment i of the unit is slot c0 + i
@@ -33,8 +33,8 @@ __device__ __forceinline__ MergeRun merge_run(const int32_t* __restrict__ sel_co
 
 // One 256-thread workgroup per (unit, query head).  The unit's partials are
 // those of the workers its list entries fall to under the balanced plan: the
-// slots u + w for w from the owner of its first entry to the owner of its
-// last, found from the list lengths alone (one round of loads of the
+// slots u + w for w from the owner of its first entry's position to the owner
+// of its last, found from the list lengths alone (one round of loads of the
 // lengths, then one of the partials).  Thread t reads channel quad t % 32 of
 // segments t / 32, t / 32 + 8, ... (each segment's 128 floats are one
 // coalesced 512-byte read by 32 threads), keeping an online (max, sum,

@@ -197,6 +197,7 @@ def select_coverage(dims, logits, ctx_lens, page_table, gamma, sel_counts, sel_o
 
 
 ATTN_MIN_WORKER_PAGES = 32   # SPARSE_ATTN_MIN_WORKER_PAGES
+ATTN_UNIT_COST_PAGES = 12    # SPARSE_ATTN_UNIT_COST_PAGES
 
 
 def decode_max_parts(dims, workers=0):

@@ -66,24 +66,27 @@ def parse():
     return ap.parse_args()
 
 
-def plan_segments(counts, workers, min_pages, cap=None):
+def plan_segments(counts, workers, min_pages, unit_cost, cap=None):
     """Partials each unit's list is split into by the attention's balanced
-    plan (the formulas of sparse_decode_attn in include/sparse_paged.h): the
-    lists laid end to end, T entries over W' = min(workers, ceil(T /
-    min_pages)) workers, worker w owning [floor(w T / W'), floor((w+1) T / W')).
-    Returns int64 [U]: the number of workers each unit's entries fall to."""
+    plan (the formulas of sparse_decode_attn in include/sparse_paged.h): a
+    unit of k > 0 entries takes unit_cost + k positions (its entries are the
+    last k), the units laid end to end, T positions over W' = min(workers,
+    ceil(T / min_pages)) workers, worker w owning [floor(w T / W'),
+    floor((w+1) T / W')).  Returns int64 [U]: the number of workers each
+    unit's entries fall to."""
     k = np.asarray(counts, dtype=np.int64).clip(min=0)
     if cap is not None:
         k = np.minimum(k, cap)
-    T = int(k.sum())
+    p = np.where(k > 0, k + int(unit_cost), 0)
+    T = int(p.sum())
     out = np.zeros(k.shape[0], dtype=np.int64)
     if T == 0:
         return out
     W = min(int(workers), -(-T // int(min_pages)))
-    off = np.concatenate([[0], np.cumsum(k)[:-1]])
+    off = np.concatenate([[0], np.cumsum(p)[:-1]])
     owner = lambda x: ((x + 1) * W - 1) // T
     nz = k > 0
-    out[nz] = owner(off[nz] + k[nz] - 1) - owner(off[nz]) + 1
+    out[nz] = owner(off[nz] + p[nz] - 1) - owner(off[nz] + int(unit_cost)) + 1
     return out
 
 
@@ -707,7 +710,8 @@ def pmc_probe(args):
     torch.cuda.synchronize()
     c = st.buf.sel_counts.cpu().numpy()
     tsel = kept_tokens(c, st.buf.sel_pages.cpu().numpy(), lens, w.kv_heads, li.max_pages)
-    nseg = plan_segments(c, st.max_parts - len(c), lib.ATTN_MIN_WORKER_PAGES)
+    nseg = plan_segments(c, st.max_parts - len(c), lib.ATTN_MIN_WORKER_PAGES,
+                         lib.ATTN_UNIT_COST_PAGES)
     ab = sum(attn_bytes(int(c[u]), int(tsel[u]), w.group, int(nseg[u])) for u in range(len(c)))
     for _ in range(3):
         attn_launch(lib, st, dims, li, sp_, sh_)
@@ -796,7 +800,8 @@ def main():
         c = st.buf.sel_counts.cpu().numpy()
         pg = st.buf.sel_pages.cpu().numpy()
         sel_stats.append((c, kept_tokens(c, pg, lens, w.kv_heads, max_pages),
-                          plan_segments(c, workers, lib.ATTN_MIN_WORKER_PAGES)))
+                          plan_segments(c, workers, lib.ATTN_MIN_WORKER_PAGES,
+                                        lib.ATTN_UNIT_COST_PAGES)))
         if l == 0:
             layer0 = (c.copy(), pg.copy())
     graph = capture(step_fn)

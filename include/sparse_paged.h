@@ -206,10 +206,13 @@ sparse_status sparse_append_tokens(const sparse_dims* dims, const uint16_t* k_ne
                                    const int32_t* page_table, int32_t* ctx_lens, uint16_t* summ,
                                    void* stream);
 
-/* Fewest list entries the attention gives one workgroup: a step of T
- * entries runs on min(W, ceil(T / SPARSE_ATTN_MIN_WORKER_PAGES)) of its W
+/* Fewest plan positions the attention gives one workgroup: a step of T
+ * positions runs on min(W, ceil(T / SPARSE_ATTN_MIN_WORKER_PAGES)) of its W
  * workgroups (see sparse_decode_attn). */
 #define SPARSE_ATTN_MIN_WORKER_PAGES 32
+/* Positions the attention's plan charges a unit on top of its entries: the
+ * fixed cost, in pages, of starting a unit's segment (see sparse_decode_attn). */
+#define SPARSE_ATTN_UNIT_COST_PAGES 12
 
 /* Partial slots one step of sparse_decode_attn may write (host): U + W, with
  * U = batch * num_kv_heads and W = workers, or the current device's compute
@@ -225,19 +228,22 @@ int64_t sparse_decode_max_parts(const sparse_dims* dims, int32_t workers);
  * FA3/FlashInfer, which pad the lists, run unbalanced blocks or plan on the
  * host -- the even split below does none of these).
  *
- * The balanced plan.  Unit u contributes k_u = min(sel_counts[u], Lb)
- * entries (Lb the dims' list bound); laid end to end in unit order they are
- * T = sum_u k_u global positions, entry e of unit u at off_u + e with
- * off_u = sum_{v<u} k_v.  The grid has W = workers workgroups (0: one per
- * compute unit of the current device), fixed at enqueue time; the step uses
- * W' = min(W, ceil(T / SPARSE_ATTN_MIN_WORKER_PAGES)) of them (0 when
- * T = 0), and worker w < W' owns positions [floor(w T / W'),
- * floor((w + 1) T / W')) -- the same number of pages, to within one, for
- * every worker whatever the list lengths.  Each workgroup derives T, W' and
- * its units from sel_counts alone (wave prefix sums), then, for every unit
- * u its range touches, computes exact attention of u's G query heads over
- * the valid tokens of the pages at those positions and writes, in slot
- * c = u + w, for head g:
+ * The balanced plan.  Unit u has k_u = min(sel_counts[u], Lb) entries (Lb
+ * the dims' list bound); a unit with k_u > 0 takes p_u = C + k_u positions,
+ * C = SPARSE_ATTN_UNIT_COST_PAGES positions standing for the fixed cost of
+ * starting a unit's segment, then one per entry.  Laid end to end in unit
+ * order they are T = sum_u p_u global positions, entry e of unit u at
+ * off_u + C + e with off_u = sum_{v<u} p_v.  The grid has W = workers
+ * workgroups (0: one per compute unit of the current device), fixed at
+ * enqueue time; the step uses W' = min(W, ceil(T /
+ * SPARSE_ATTN_MIN_WORKER_PAGES)) of them (0 when T = 0), and worker w < W'
+ * owns positions [floor(w T / W'), floor((w + 1) T / W')) -- the same work,
+ * to within one page, for every worker whatever the list lengths (a worker
+ * that starts a second unit's segment gets C fewer pages).  Each workgroup
+ * derives T, W' and its units from sel_counts alone (wave prefix sums),
+ * then, for every unit u whose entries its range meets, computes exact
+ * attention of u's G query heads over the valid tokens of the pages at those
+ * entries and writes, in slot c = u + w, for head g:
  *   part_o[c][g][:]  = sum_t softmax_t(scale * q.k_t) v_t   (normalised over the segment)
  *   part_lse[c][g]   = ln sum_t exp(scale * q.k_t)
  * (lse = -inf and o = 0 for a segment with no valid token).  Slots that no
@@ -262,8 +268,8 @@ sparse_status sparse_decode_attn(const sparse_dims* dims, const uint16_t* q, con
  * workgroups ([P1], abstract, sentence on self-planning attention: a list
  * is shared among the blocks that plan their own part of it).  Unit u's
  * partials are the slots u + w for the workers w from the owner of its first
- * position (off_u) to the owner of its last (off_u + k_u - 1) under the
- * plan of sparse_decode_attn, found from sel_counts alone; workers and dims
+ * entry's position (off_u + C) to the owner of its last (off_u + C + k_u - 1)
+ * under the plan of sparse_decode_attn, found from sel_counts alone; workers and dims
  * must be those of the sparse_decode_attn call that wrote them.  Other slots
  * are not read as values.
  *   out      fp32 [B][Hq][128];  out_lse fp32 [B][Hq]

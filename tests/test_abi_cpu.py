@@ -223,6 +223,8 @@ def test_binding_constants_match_header():
     assert m and int(m.group(1)) == lib.READ_BLOCKS_GROUPS
     m = re.search(r"#define SPARSE_ATTN_MIN_WORKER_PAGES (\d+)", text)
     assert m and int(m.group(1)) == lib.ATTN_MIN_WORKER_PAGES
+    m = re.search(r"#define SPARSE_ATTN_UNIT_COST_PAGES (\d+)", text)
+    assert m and int(m.group(1)) == lib.ATTN_UNIT_COST_PAGES
     m = re.search(r"#define SPARSE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_SCRATCH_BYTES
     m = re.search(r"#define SPARSE_FETCH_ATTN_COPY_GROUPS (\d+)", text)

@@ -53,17 +53,23 @@ def test_cpu_baselines_and_parity_report():
     assert 1 <= bench.host_cores() <= 16
 
 
-def _plan_brute(counts, workers, min_pages):
-    """Workers touching each unit, by walking every position."""
+def _plan_brute(counts, workers, min_pages, unit_cost):
+    """Workers whose range meets each unit's entries, by walking every
+    position: a nonempty unit's unit_cost leading positions (marked -1) hold
+    no entry."""
     k = np.asarray(counts, dtype=np.int64)
-    T = int(k.sum())
+    unit = []
+    for u, n in enumerate(k):
+        if n > 0:
+            unit += [-1] * unit_cost + [u] * int(n)
+    unit = np.array(unit, dtype=np.int64)
+    T = len(unit)
     if T == 0:
         return np.zeros(len(k), dtype=np.int64)
     W = min(workers, -(-T // min_pages))
     owner = np.zeros(T, dtype=np.int64)
     for w in range(W):
         owner[w * T // W:(w + 1) * T // W] = w
-    unit = np.repeat(np.arange(len(k)), k)
     return np.array([len(set(owner[unit == u])) for u in range(len(k))], dtype=np.int64)
 
 
@@ -74,12 +80,14 @@ def test_plan_segments_match_a_walk_over_positions():
         counts = rng.integers(0, 300, size=U) * (rng.random(U) < 0.8)
         workers = int(rng.integers(1, 80))
         minp = int(rng.choice([1, 7, 32]))
-        assert np.array_equal(bench.plan_segments(counts, workers, minp),
-                              _plan_brute(counts, workers, minp)), (trial, counts, workers, minp)
-    assert bench.plan_segments([0, 0], 4, 32).tolist() == [0, 0]
+        c = int(rng.choice([0, 5, 12]))
+        assert np.array_equal(bench.plan_segments(counts, workers, minp, c),
+                              _plan_brute(counts, workers, minp, c)), (trial, counts, workers,
+                                                                       minp, c)
+    assert bench.plan_segments([0, 0], 4, 32, 12).tolist() == [0, 0]
     # cap clamps every list before the plan
-    assert np.array_equal(bench.plan_segments([500, 10], 8, 1, cap=100),
-                          _plan_brute([100, 10], 8, 1))
+    assert np.array_equal(bench.plan_segments([500, 10], 8, 1, 12, cap=100),
+                          _plan_brute([100, 10], 8, 1, 12))
 
 
 def test_byte_accounting():
