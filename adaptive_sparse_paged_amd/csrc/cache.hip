@@ -44,24 +44,37 @@ constexpr unsigned long long kTkCountMask = (1ull << kTkHitShift) - 1ull;
 // ascending unit id take them.  M (>= 1) and H are the request's miss and hit
 // totals from the ticket.  With miss lists, each unit's placed misses are also
 // written in list order (a unit's misses are a contiguous run of the
-// request's misses, which go head by head).
+// request's misses, which go head by head).  The slots' tags and stamps are
+// read once into LDS: the victim search reads them several times.  (A
+// requested slot's stamp may have been rewritten by another workgroup
+// meanwhile; requested slots are never candidates, and only the stamps of
+// candidates are used.)
+constexpr int kPlaceEpt = 4;                 // list entries per thread per ranking round
+
 __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
-                              const int32_t* __restrict__ sel_pages, int hkv, int max_pages,
-                              int C, int recency_shift, int step, int32_t* __restrict__ tags,
-                              int32_t* __restrict__ stamps, int32_t* __restrict__ umap,
-                              int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats,
-                              MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
-                              uint32_t M, uint32_t H, int32_t* __restrict__ miss_counts,
-                              int32_t* __restrict__ miss_pages, int32_t* __restrict__ miss_phys) {
+                                  const int32_t* __restrict__ sel_pages, int hkv, int max_pages,
+                                  int C, int recency_shift, int step, int32_t* __restrict__ tags,
+                                  int32_t* __restrict__ stamps, int32_t* __restrict__ umap,
+                                  int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats,
+                                  MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
+                                  uint32_t M, uint32_t H, int32_t* __restrict__ miss_counts,
+                                  int32_t* __restrict__ miss_pages,
+                                  int32_t* __restrict__ miss_phys) {
   __shared__ uint8_t req[kMaxSlots];       // slot holds a unit requested this step
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
+  __shared__ int32_t s_tag[kMaxSlots];     // the slots' tags and stamps before this step
+  __shared__ int32_t s_stamp[kMaxSlots];
   __shared__ SelectScratch sel;
   __shared__ uint32_t scan32[kResThreads / 64];
   __shared__ int32_t head_off[kMaxKvHeads + 1];
   __shared__ uint32_t head_miss[kMaxKvHeads];     // misses per head, then their prefix
   const int tid = threadIdx.x;
 
-  for (int s = tid; s < C; s += kResThreads) req[s] = 0;
+  for (int s = tid; s < C; s += kResThreads) {
+    req[s] = 0;
+    s_tag[s] = tags[s];
+    s_stamp[s] = stamps[s];
+  }
   if (tid < hkv) head_miss[tid] = 0u;
   if (tid == 0) {
     int acc = 0;
@@ -119,7 +132,7 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   for (int k = 0; k < kSPT; ++k) {
     const int s = k * kResThreads + tid;
     if (s < C) {
-      const int tg = tags[s];
+      const int tg = s_tag[s];
       nfree += (tg < 0) ? 1u : 0u;
       ncand += (tg >= 0 && !req[s]) ? 1u : 0u;
     }
@@ -131,17 +144,15 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
 
   // ---- r least recently used candidates: radix select on the keys -------
   // key = (stamp >> shift) * 2^32 + unit; keys are distinct, so exactly r
-  // keys are <= kappa.  (A requested slot's stamp may be rewritten by another
-  // workgroup meanwhile; requested slots are never candidates.)
+  // keys are <= kappa
   unsigned long long kappa = 0ull;
   const bool take_all = (r == NC);
   if (r > 0u && !take_all) {
     kappa = select_rth_key<kResThreads>(
         C, r,
         [&](int s, unsigned long long& key) {
-          const int tg = tags[s];
-          const int st = stamps[s];
-          key = lru_key(st, tg, recency_shift);
+          const int tg = s_tag[s];
+          key = lru_key(s_stamp[s], tg, recency_shift);
           return tg >= 0 && !req[s];
         },
         sel);
@@ -155,10 +166,10 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   for (int k = 0; k < run; ++k) {
     const int s = s0 + k;
     if (s >= C) break;
-    const int tg = tags[s];
+    const int tg = s_tag[s];
     bool av = tg < 0;
     if (!av && r > 0u && !req[s])
-      av = take_all || lru_key(stamps[s], tg, recency_shift) <= kappa;
+      av = take_all || lru_key(s_stamp[s], tg, recency_shift) <= kappa;
     navail += av ? 1u : 0u;
   }
   uint32_t A;
@@ -166,55 +177,71 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   for (int k = 0; k < run; ++k) {
     const int s = s0 + k;
     if (s >= C) break;
-    const int tg = tags[s];
+    const int tg = s_tag[s];
     bool av = tg < 0;
     if (!av && r > 0u && !req[s])
-      av = take_all || lru_key(stamps[s], tg, recency_shift) <= kappa;
+      av = take_all || lru_key(s_stamp[s], tg, recency_shift) <= kappa;
     if (av) avail[rank++] = s;
   }
   const uint32_t placed = min(M, A);
   __syncthreads();
 
   // ---- misses in ascending unit id take avail[0..placed) ------------------
+  // Rounds of kPlaceEpt * 1024 list entries; thread t ranks the blocked run
+  // of kPlaceEpt entries starting at kPlaceEpt t, its loads issued together.
   uint32_t ev_local = 0u, mbase = 0u;
-  for (int base = 0; base < E; base += kResThreads) {
-    const int e = base + tid;
-    uint32_t miss = 0u;
-    int v = -1, h = 0, p = -1;
-    int64_t li = 0;
-    if (e < E) {
-      while (e >= head_off[h + 1]) ++h;
-      const int i = e - head_off[h];
-      li = (int64_t)(b * hkv + h) * max_pages + i;
-      p = sel_pages[li];
-      if (p >= 0 && p < max_pages) {
-        v = h * max_pages + p;
-        miss = (umap[v] == -1) ? 1u : 0u;
+  for (int base = 0; base < E; base += kPlaceEpt * kResThreads) {
+    int hh[kPlaceEpt], pp[kPlaceEpt], vv[kPlaceEpt];
+    int64_t li[kPlaceEpt];
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) {
+      const int e = base + kPlaceEpt * tid + k;
+      hh[k] = 0;
+      pp[k] = -1;
+      li[k] = -1;
+      if (e < E) {
+        int h = 0;
+        while (e >= head_off[h + 1]) ++h;
+        hh[k] = h;
+        li[k] = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
+        pp[k] = sel_pages[li[k]];
       }
     }
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) {
+      vv[k] = (pp[k] >= 0 && pp[k] < max_pages) ? hh[k] * max_pages + pp[k] : -1;
+      const bool miss = vv[k] >= 0 && umap[vv[k]] == -1;
+      if (!miss) vv[k] = -1;
+      mine += miss ? 1u : 0u;
+    }
     uint32_t tot;
-    const uint32_t mr = mbase + block_excl_scan<uint32_t, kResThreads>(miss, scan32, tot);
-    if (miss) {
+    uint32_t mr = mbase + block_excl_scan<uint32_t, kResThreads>(mine, scan32, tot);
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) {
+      if (vv[k] < 0) continue;
       if (mr < placed) {
         const int s = avail[mr];
-        const int old = tags[s];
+        const int old = s_tag[s];
         if (old >= 0) {
           if (old < hkv * max_pages) umap[old] = -1;
           ++ev_local;
         }
-        tags[s] = v;
+        tags[s] = vv[k];
         stamps[s] = step;
-        umap[v] = s;
-        sel_phys[li] = b * C + s;
-        misses[(int64_t)b * C + mr] = MissRec{v, s};
+        umap[vv[k]] = s;
+        sel_phys[li[k]] = b * C + s;
+        misses[(int64_t)b * C + mr] = MissRec{vv[k], s};
         if (miss_counts) {
+          const int h = hh[k];
           const int64_t j = (int64_t)(b * hkv + h) * max_pages + (mr - head_miss[h]);
-          miss_pages[j] = p;
+          miss_pages[j] = pp[k];
           miss_phys[j] = b * C + s;
         }
       } else {
-        sel_phys[li] = -1;
+        sel_phys[li[k]] = -1;
       }
+      ++mr;
     }
     mbase += tot;
   }
