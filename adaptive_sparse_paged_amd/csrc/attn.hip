@@ -336,35 +336,217 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
               part_lse);
 }
 
-// The host tier's fetch and the attention over the hits in one launch.  The
-// first nfetch workgroups copy the step's placed misses into their slots
-// (4 waves each); the others are the attention's workers over lists whose
-// misses read as empty pages (hit_phys), so no worker reads a slot being
-// written.  Every workgroup holds 96 KiB of LDS (dynamic, the attention
-// workers use the first part of it), so a compute unit runs one
+// A host-tier miss on its way through a copying wave: read from pinned host
+// memory as the plain copy reads it (lane l of read k holds bytes
+// 1024 k + 16 l .. + 15 of the unit: every read is 1 KiB contiguous),
+// written to its slot the same way, and staged in the wave's LDS tile to be
+// read back in load_page's fragment layout.  K rows are padded to 272 bytes
+// in LDS, so the fragment reads of 16 rows fall in distinct banks.
+struct RawUnit {
+  u32x4 t[8];
+};
+constexpr int kStageKRow = 2 * kD + 16;                   // bytes per padded K row
+constexpr int kStageBytes = kP * kStageKRow + 2 * kTile;  // padded K tile + V tile
+
+__device__ __forceinline__ void load_raw(RawUnit& r, const uint16_t* __restrict__ unit) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(unit);
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r.t[k] = __builtin_nontemporal_load(s + k * 64 + lane);
+}
+
+__device__ __forceinline__ void store_raw(const RawUnit& r, uint16_t* __restrict__ unit) {
+  u32x4* d = reinterpret_cast<u32x4*>(unit);
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k * 64 + lane] = r.t[k];
+}
+
+// Through the wave's LDS tile into f (K token (lane & 15), V^T channels).
+__device__ __forceinline__ void raw_to_frag(const RawUnit& r, char* tile, PageFrag& f) {
+  const int lane = lane_id(), row = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)          // K: token 4k + (lane >> 4), channels 8 (lane & 15) ..
+    *reinterpret_cast<u32x4*>(tile + (4 * k + j) * kStageKRow + 16 * row) = r.t[k];
+  char* vt = tile + kP * kStageKRow;
+#pragma unroll
+  for (int k = 4; k < 8; ++k) *reinterpret_cast<u32x4*>(vt + (k - 4) * 1024 + 16 * lane) = r.t[k];
+  // the wave's own LDS writes, read back by other lanes: complete them, and
+  // keep the compiler from moving the reads above them
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    f.k[s] = *reinterpret_cast<const u32x4*>(tile + row * kStageKRow + 64 * s + 16 * j);
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    f.v[m] = *reinterpret_cast<const u32x2*>(vt + (16 * m + row) * 32 + 8 * j);
+  asm volatile("" ::: "memory");     // the next unit's LDS writes stay after these reads
+}
+
+// A copying wave of the host tier's fetch: wave fw of FW is worker fw of the
+// balanced plan over the per-unit miss lists (miss_counts, miss_pages,
+// miss_phys), one worker per wave.  For each miss of its slice it reads the
+// unit from pinned host memory into registers, writes it to its slot, and
+// attends it from its LDS tile with the unit's queries (one online softmax
+// per unit segment), so the misses are attended without being read back
+// from HBM.  Uses kStageBytes of the launch's dynamic LDS per wave.
+// Each segment's normalised partial and log-sum-exp go to slot u + fw of
+// part_o / part_lse, where the merge finds them from miss_counts and FW as
+// it finds the attention's.  A miss whose page or slot is out of range is
+// neither copied nor attended.
+__device__ __forceinline__ void miss_worker(
+    int fw, int FW, const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv,
+    int64_t pool_slots, const uint16_t* __restrict__ q, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ miss_counts, const int32_t* __restrict__ miss_pages,
+    const int32_t* __restrict__ miss_phys, float scale_log2, int hkv, int group, int max_pages,
+    int cap, int U, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  int x, e, u, off, len;
+  {
+    PlanSeg first;
+    const int total = __builtin_amdgcn_readfirstlane(plan_total(miss_counts, U, cap, first));
+    const int W = plan_workers(total, FW);
+    if (fw >= W) return;               // nothing to copy, or too little for this wave
+    x = plan_start(fw, W, total);
+    e = plan_start(fw + 1, W, total);
+    plan_find(miss_counts, U, cap, first, x, u, off, len);
+  }
+  u = __builtin_amdgcn_readfirstlane(u);
+  off = __builtin_amdgcn_readfirstlane(off);
+  len = __builtin_amdgcn_readfirstlane(len);
+  if (u < 0) return;
+  constexpr int C = kPlanUnitCost;
+  const int lane = lane_id(), row = lane & 15, j = lane >> 4;
+  const bool gok = row < group;
+  extern __shared__ float smem[];
+  char* tile = reinterpret_cast<char*>(smem) + (threadIdx.x >> 6) * kStageBytes;
+  int i0 = max(x - off - C, 0);
+  while (true) {
+    const int i1 = min(e, off + len) - off - C;
+    const int b = u / hkv, h = u - b * hkv;
+    const int L = __builtin_amdgcn_readfirstlane(min(max(ctx_lens[b], 0), max_pages * kP));
+    const uint16_t* qrow =
+        q + ((int64_t)b * hkv * group + h * group + min(row, group - 1)) * kD + 8 * j;
+    bf16x8 qf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
+      qf[s] = as_bf16x8(gok ? w : u32x4{0u, 0u, 0u, 0u});
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    floatx4 o[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int32_t* lp = miss_pages + (int64_t)u * max_pages;
+    const int32_t* lx = miss_phys + (int64_t)u * max_pages;
+    // 64 ids at a time into lanes k (read with readlane), and two units in
+    // flight: the next unit's host read is issued before the current one is
+    // stored and attended, so the wave keeps the link busy while it attends.
+    // A miss out of range reads unit 0 of the pool (in bounds) and is
+    // neither stored nor attended.
+    for (int base = i0; base < i1; base += 64) {
+      const int cnt = min(64, i1 - base);
+      const int ie = min(base + lane, i1 - 1);
+      int pl = lp[ie], xl = lx[ie];
+      asm volatile("" : "+v"(pl), "+v"(xl));
+      auto src = [&](int k) {
+        const int p = __builtin_amdgcn_readlane(pl, k), x = __builtin_amdgcn_readlane(xl, k);
+        const bool ok = p >= 0 && p < max_pages && x >= 0 && x < pool_slots;
+        return host_kv + (ok ? (((int64_t)b * max_pages + p) * hkv + h) * kUnitElems : 0);
+      };
+      auto finish = [&](const RawUnit& r, int k) {
+        const int p = __builtin_amdgcn_readlane(pl, k), x = __builtin_amdgcn_readlane(xl, k);
+        if (p < 0 || p >= max_pages || x < 0 || x >= pool_slots) return;
+        store_raw(r, cache_kv + (int64_t)x * kUnitElems);
+        PageFrag f;
+        raw_to_frag(r, tile, f);
+        f.valid = max(min(kP, L - kP * p), 0);
+        attend_page(f, qf, gok, j, scale_log2, m_run, l_run, o);
+      };
+      RawUnit ra, rb;
+      load_raw(ra, src(0));
+      int k = 0;
+      for (; k + 2 < cnt; k += 2) {
+        load_raw(rb, src(k + 1));
+        finish(ra, k);
+        load_raw(ra, src(k + 2));
+        finish(rb, k + 1);
+      }
+      if (k + 1 < cnt) {
+        load_raw(rb, src(k + 1));
+        finish(ra, k);
+        finish(rb, k + 1);
+      } else {
+        finish(ra, k);
+      }
+    }
+    // the wave's partial: tokens 4j .. 4j + 3 of each page were summed in
+    // lane (g, j); lane (g, j) holds channels 16 m + 4 j .. + 3 of head g
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (gok) {
+      const int64_t r = ((int64_t)u + fw) * group + row;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        floatx4 v = o[m];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (l_run > 0.f) ? v[c] / l_run : 0.f;
+        *reinterpret_cast<floatx4*>(part_o + r * kD + 16 * m + 4 * j) = v;
+      }
+      if (j == 0)
+        part_lse[r] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    }
+    if (off + len >= e) break;         // the slice ends in this unit
+    off += len;
+    ++u;
+    len = 0;
+    while (len == 0 && u < U) {
+      len = plan_positions(miss_counts[u], cap);
+      if (len == 0) ++u;
+    }
+    if (len == 0 || e - off <= C) break;
+    i0 = 0;
+  }
+}
+
+// The host tier's fetch with its attention, and the attention over the
+// hits, in one launch.  The first nfetch workgroups are the copying waves
+// (miss_worker, 4 waves each: they copy the step's placed misses into their
+// slots and attend them); the others are the attention's workers over lists
+// whose misses read as empty pages (hit_phys), so no worker reads a slot
+// being written.  Every workgroup holds 96 KiB of LDS (dynamic, the
+// attention workers use the first part of it), so a compute unit runs one
 // of them at a time: a copying wave, whose host reads take microseconds,
 // never shares its unit's memory pipeline with attention waves.  The copying
 // workgroups come first in the grid and are placed first; attention workers
 // beyond the free units start as units free up.  With nothing to copy, the
-// copying workgroups exit at once and the launch is the attention alone.
+// copying waves exit after reading the miss counts.
 constexpr size_t kFetchAttnLds = 96 * 1024;
+// Copying workgroups: 64 of 4 waves, the 256 waves that keep the PCIe link
+// busy (the copy waits on the link, not on the waves).
+constexpr int kFetchAttnGroups = SPARSE_FETCH_ATTN_COPY_GROUPS;
+static_assert(SPARSE_FETCH_ATTN_COPY_WAVES == kFetchAttnGroups * kAttnWaves,
+              "copying waves: 4 per copying workgroup");
+static_assert(kAttnWaves * kStageBytes <= kFetchAttnLds, "copying waves' LDS tiles");
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void fetch_attn_kernel(
-    const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv, MissTable table,
+    const uint16_t* __restrict__ host_kv, uint16_t* __restrict__ cache_kv, int64_t pool_slots,
     int nfetch, int32_t* __restrict__ step_counter, const uint16_t* __restrict__ q,
-    int64_t pool_pages, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ hit_phys, float scale_log2, int hkv, int group, int max_pages,
-    int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ sel_counts,
+    const int32_t* __restrict__ sel_pages, const int32_t* __restrict__ hit_phys,
+    const int32_t* __restrict__ miss_counts, const int32_t* __restrict__ miss_pages,
+    const int32_t* __restrict__ miss_phys, float scale_log2, int hkv, int group, int max_pages,
+    int cap, int U, int wmax, float* __restrict__ part_o, float* __restrict__ part_lse,
+    float* __restrict__ miss_part_o, float* __restrict__ miss_part_lse) {
   if ((int)blockIdx.x < nfetch) {
     // every resolve workgroup has read the step (the resolve ran first on
     // this stream): advance it for the next call
     if (blockIdx.x == 0 && threadIdx.x == 0) *step_counter += 1;
-    fetch_misses((int)blockIdx.x * kAttnWaves + (int)(threadIdx.x >> 6), nfetch * kAttnWaves,
-                 host_kv, cache_kv, hkv, max_pages, table);
+    miss_worker((int)blockIdx.x * kAttnWaves + (int)(threadIdx.x >> 6), nfetch * kAttnWaves,
+                host_kv, cache_kv, pool_slots, q, ctx_lens, miss_counts, miss_pages, miss_phys,
+                scale_log2, hkv, group, max_pages, cap, U, miss_part_o, miss_part_lse);
     return;
   }
-  attn_worker((int)blockIdx.x - nfetch, q, cache_kv, kUnitElems, 0, pool_pages, ctx_lens,
+  attn_worker((int)blockIdx.x - nfetch, q, cache_kv, kUnitElems, 0, pool_slots, ctx_lens,
               sel_counts, sel_pages, hit_phys, scale_log2, hkv, group, max_pages, cap, U, wmax,
               part_o, part_lse);
 }
@@ -412,22 +594,22 @@ void enqueue_attn(const sparse_dims* dims, const uint16_t* q, const uint16_t* kv
                      part_o, part_lse);
 }
 
-// Copying workgroups of fetch_attn_kernel: 64 of 4 waves, the 256 waves that
-// keep the PCIe link busy (the copy waits on the link, not on the waves).
-constexpr int kFetchAttnGroups = SPARSE_FETCH_ATTN_COPY_GROUPS;
-
 void enqueue_fetch_attn(const sparse_dims* dims, const uint16_t* host_kv, uint16_t* cache_kv,
-                        int64_t pool_slots, const MissTable& t, int32_t* step_counter,
-                        const uint16_t* q, const int32_t* ctx_lens, const int32_t* sel_counts,
-                        const int32_t* sel_pages, const int32_t* hit_phys, float scale, int wmax,
-                        float* part_o, float* part_lse, hipStream_t stream) {
+                        int64_t pool_slots, int32_t* step_counter, const uint16_t* q,
+                        const int32_t* ctx_lens, const int32_t* sel_counts,
+                        const int32_t* sel_pages, const int32_t* hit_phys,
+                        const int32_t* miss_counts, const int32_t* miss_pages,
+                        const int32_t* miss_phys, float scale, int wmax, float* part_o,
+                        float* part_lse, float* miss_part_o, float* miss_part_lse,
+                        hipStream_t stream) {
   const int hkv = dims->num_kv_heads, group = dims->num_q_heads / hkv;
   const int U = dims->batch * hkv;
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(fetch_attn_kernel, dim3((unsigned)(kFetchAttnGroups + wmax)), dim3(256),
-                     kFetchAttnLds, stream, host_kv, cache_kv, t, kFetchAttnGroups, step_counter, q, pool_slots,
-                     ctx_lens, sel_counts, sel_pages, hit_phys, scale_log2, hkv, group,
-                     dims->max_pages, list_cap(dims), U, wmax, part_o, part_lse);
+                     kFetchAttnLds, stream, host_kv, cache_kv, pool_slots, kFetchAttnGroups,
+                     step_counter, q, ctx_lens, sel_counts, sel_pages, hit_phys, miss_counts,
+                     miss_pages, miss_phys, scale_log2, hkv, group, dims->max_pages,
+                     list_cap(dims), U, wmax, part_o, part_lse, miss_part_o, miss_part_lse);
 }
 
 }  // namespace sp

@@ -994,8 +994,9 @@ extern "C" size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
 
 namespace {
 
-sparse_status check_policy(const sparse_dims* dims, const sparse_cache_policy* policy,
-                           int32_t capacity, const void* ws, size_t ws_bytes) {
+// The policy and the capacity it allows (no workspace).
+sparse_status check_policy_args(const sparse_dims* dims, const sparse_cache_policy* policy,
+                                int32_t capacity) {
   if (!policy || policy->recency_shift < 0 || policy->recency_shift > 30 ||
       (policy->pooled != 0 && policy->pooled != 1))
     return SPARSE_ERR_INVALID;
@@ -1005,6 +1006,13 @@ sparse_status check_policy(const sparse_dims* dims, const sparse_cache_policy* p
   } else if (capacity > sp::kMaxSlots) {
     return SPARSE_ERR_UNSUPPORTED;
   }
+  return SPARSE_OK;
+}
+
+sparse_status check_policy(const sparse_dims* dims, const sparse_cache_policy* policy,
+                           int32_t capacity, const void* ws, size_t ws_bytes) {
+  const sparse_status st = check_policy_args(dims, policy, capacity);
+  if (st != SPARSE_OK) return st;
   if (!ws || ws_bytes < sparse_cache_policy_workspace_bytes(dims, policy, capacity) ||
       !sp::aligned(ws, 8))
     return SPARSE_ERR_WORKSPACE;
@@ -1092,16 +1100,16 @@ extern "C" sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims,
 
 extern "C" sparse_status sparse_hbm_cache_fetch_attn(
     const sparse_dims* dims, const sparse_cache_policy* policy, const uint16_t* host_kv,
-    uint16_t* cache_kv, int32_t capacity, int32_t* step_counter, void* ws, size_t ws_bytes,
-    const uint16_t* q, const int32_t* ctx_lens, const int32_t* sel_counts,
-    const int32_t* sel_pages, const int32_t* hit_phys, float scale, int32_t workers,
-    float* part_o, float* part_lse, int64_t max_parts, void* stream) {
+    uint16_t* cache_kv, int32_t capacity, int32_t* step_counter, const uint16_t* q,
+    const int32_t* ctx_lens, const int32_t* sel_counts, const int32_t* sel_pages,
+    const int32_t* hit_phys, const int32_t* miss_counts, const int32_t* miss_pages,
+    const int32_t* miss_phys, float scale, int32_t workers, float* part_o, float* part_lse,
+    int64_t max_parts, float* miss_part_o, float* miss_part_lse, void* stream) {
   sparse_status st = sp::check_dims(dims);
   if (st != SPARSE_OK) return st;
   if (!step_counter || capacity < 1) return SPARSE_ERR_INVALID;
   if ((st = check_pool_args(host_kv, cache_kv)) != SPARSE_OK) return st;
-  if (dims->num_kv_heads > sp::kMaxKvHeads) return SPARSE_ERR_UNSUPPORTED;
-  if ((st = check_policy(dims, policy, capacity, ws, ws_bytes)) != SPARSE_OK) return st;
+  if ((st = check_policy_args(dims, policy, capacity)) != SPARSE_OK) return st;
   const int B = dims->batch;
   const int64_t slots = policy->pooled ? (int64_t)capacity : (int64_t)B * capacity;
   int wmax = 0;
@@ -1110,17 +1118,12 @@ extern "C" sparse_status sparse_hbm_cache_fetch_attn(
     return st;
   if (!part_o || !part_lse || !sp::aligned(part_o, 16)) return SPARSE_ERR_INVALID;
   if (max_parts != (int64_t)B * dims->num_kv_heads + wmax) return SPARSE_ERR_INVALID;
-  sp::MissTable t;
-  if (policy->pooled) {
-    const PooledWs w = pooled_ws(B, capacity, ws);
-    t = sp::MissTable{w.misses, w.placed, 1, capacity, true};
-  } else {
-    const PerRequestWs w = per_request_ws(B, capacity, ws);
-    t = sp::MissTable{w.misses, w.miss_count, B, capacity, false};
-  }
-  sp::enqueue_fetch_attn(dims, host_kv, cache_kv, slots, t, step_counter, q, ctx_lens,
-                         sel_counts, sel_pages, hit_phys, scale, wmax, part_o, part_lse,
-                         (hipStream_t)stream);
+  if (!miss_counts || !miss_pages || !miss_phys || !miss_part_o || !miss_part_lse ||
+      !sp::aligned(miss_part_o, 16))
+    return SPARSE_ERR_INVALID;
+  sp::enqueue_fetch_attn(dims, host_kv, cache_kv, slots, step_counter, q, ctx_lens, sel_counts,
+                         sel_pages, hit_phys, miss_counts, miss_pages, miss_phys, scale, wmax,
+                         part_o, part_lse, miss_part_o, miss_part_lse, (hipStream_t)stream);
   return sp::launch_status();
 }
 

@@ -134,27 +134,27 @@ class SplitHostTierStep:
     the hits are final once the resolve has run; attention over a partition
     of a list, merged by log-sum-exp, is attention over the whole list.
 
-    One stream, four launches: the resolve (no copy; it also writes each
-    unit's placed misses as a list); the fetch and the attention over the
-    lists with hit_phys (misses read as empty pages) in one grid, side by
-    side; the attention over the miss lists; one merge of both sets of
-    partials into out.  With every access a hit the copying workgroups exit
-    at once and the miss attention has nothing to do.  Cache state,
-    statistics and slot ids equal those of HbmPageCache.resolve; outputs
-    equal the one-pass attention up to the order of the log-sum-exp merge.
-    It can be captured whole."""
+    One stream, three launches: the resolve (no copy; it also writes each
+    unit's placed misses as a list); one grid in which the copying waves
+    fetch the misses and attend them as they arrive, beside the attention's
+    workers over the lists with hit_phys (misses read as empty pages); one
+    merge of both sets of partials into out.  With every access a hit the
+    copying waves exit at once.  Cache state, statistics and slot ids equal
+    those of HbmPageCache.resolve; outputs equal the one-pass attention up to
+    the order of the log-sum-exp merge.  It can be captured whole."""
 
     def __init__(self, dims, cache, gamma, workers=0, scale=None, device="cuda"):
-        """workers: the attention grids (0 = one workgroup per compute unit).
-        The hit attention keeps every unit's worker although the copies take
+        """workers: the hit attention's grid (0 = one workgroup per compute
+        unit).  It keeps every unit's worker although the copies take
         FETCH_ATTN_COPY_GROUPS units first: with fewer workers (units minus
         the copies) the launch took 87 us instead of 78 with every access a
         hit."""
         self.dims, self.cache = dims, cache
         self.hits = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
                                      offsets=False)
-        self.miss = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
-                                     offsets=False)
+        # the miss lists, and the copying waves' partials (one worker per wave)
+        self.miss = SparseDecodeStep(dims, gamma, lib.FETCH_ATTN_COPY_WAVES, scale=scale,
+                                     device=device, offsets=False)
         self.hit_phys = torch.zeros_like(self.hits.buf.sel_phys)
 
     @property
@@ -173,17 +173,16 @@ class SplitHostTierStep:
         """One step on the lists in sel_counts / sel_pages."""
         h, m, c = self.hits, self.miss, self.cache
         hb, mb = h.buf, m.buf
-        kv, sp_, sh_, pp = c.pool_args()
         c.resolve_split(hb.sel_counts, hb.sel_pages, hb.sel_phys, self.hit_phys,
                         miss_lists=(mb.sel_counts, mb.sel_pages, mb.sel_phys))
         lib.hbm_cache_fetch_attn(self.dims, c.policy, c.host_kv, c.cache_kv, c.capacity,
-                                 c.step_counter, c.ws, q, ctx_lens, hb.sel_counts, hb.sel_pages,
-                                 self.hit_phys, h.scale, h.workers, hb.part_o, hb.part_lse,
-                                 h.max_parts)
-        lib.decode_attn(self.dims, q, kv, sp_, sh_, pp, ctx_lens, mb.sel_counts, mb.sel_pages,
-                        mb.sel_phys, m.scale, m.workers, mb.part_o, mb.part_lse, m.max_parts)
+                                 c.step_counter, q, ctx_lens, hb.sel_counts, hb.sel_pages,
+                                 self.hit_phys, mb.sel_counts, mb.sel_pages, mb.sel_phys,
+                                 h.scale, h.workers, hb.part_o, hb.part_lse, h.max_parts,
+                                 mb.part_o, mb.part_lse)
         lib.merge_splits_pair(self.dims, hb.part_o, hb.part_lse, hb.sel_counts, h.workers,
-                              mb.part_o, mb.part_lse, mb.sel_counts, m.workers, out, out_lse)
+                              mb.part_o, mb.part_lse, mb.sel_counts, lib.FETCH_ATTN_COPY_WAVES,
+                              out, out_lse)
         return out, out_lse
 
 

@@ -109,8 +109,8 @@ _SIGS = {
     "sparse_hbm_cache_resolve_split": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_hbm_cache_fetch": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
-    "sparse_hbm_cache_fetch_attn": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P,
-                                           _P, _P, _P, _P, _F, _I32, _P, _P, _I64, _P]),
+    "sparse_hbm_cache_fetch_attn": (_I32, [_D, _CP, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _F, _I32, _P, _P, _I64, _P, _P, _P]),
     "sparse_split_misses": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_lse_combine": (_I32, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_decode_attn_merge": (_I32, [_D, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _I32,
@@ -228,6 +228,7 @@ def decode_attn_merge(dims, q, kv, stride_page, stride_head, pool_pages, ctx_len
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SPARSE_NOALLOC_SCRATCH_BYTES
 FETCH_ATTN_COPY_GROUPS = 64         # SPARSE_FETCH_ATTN_COPY_GROUPS
+FETCH_ATTN_COPY_WAVES = 4 * FETCH_ATTN_COPY_GROUPS   # SPARSE_FETCH_ATTN_COPY_WAVES
 FETCH_GROUPS = 32                   # SPARSE_FETCH_GROUPS
 
 
@@ -361,20 +362,29 @@ def hbm_cache_fetch(dims, policy, host_kv, cache_kv, capacity, step_counter, ws,
         _ptr(step_counter), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def hbm_cache_fetch_attn(dims, policy, host_kv, cache_kv, capacity, step_counter, ws, q,
-                         ctx_lens, sel_counts, sel_pages, hit_phys, scale, workers, part_o,
-                         part_lse, max_parts, stream=None):
-    """hbm_cache_fetch and decode_attn over (sel_counts, sel_pages, hit_phys) on
-    the cache pool, in one launch."""
-    _dev(cache_kv, step_counter, ws, q, ctx_lens, sel_counts, sel_pages, hit_phys, part_o,
-         part_lse)
+def hbm_cache_fetch_attn(dims, policy, host_kv, cache_kv, capacity, step_counter, q, ctx_lens,
+                         sel_counts, sel_pages, hit_phys, miss_counts, miss_pages, miss_phys,
+                         scale, workers, part_o, part_lse, max_parts, miss_part_o, miss_part_lse,
+                         stream=None):
+    """The copies of the miss lists, attended in the copying waves (partials
+    miss_part_o / miss_part_lse, FETCH_ATTN_COPY_WAVES workers), and
+    decode_attn over (sel_counts, sel_pages, hit_phys) on the cache pool, in
+    one launch."""
+    _dev(cache_kv, step_counter, q, ctx_lens, sel_counts, sel_pages, hit_phys, miss_counts,
+         miss_pages, miss_phys, part_o, part_lse, miss_part_o, miss_part_lse)
     if not host_kv.is_pinned():
         raise ValueError("host_kv must be pinned host memory")
+    U = dims.batch * dims.num_kv_heads
+    G = dims.num_q_heads // dims.num_kv_heads
+    if (miss_part_o.numel() < (U + FETCH_ATTN_COPY_WAVES) * G * 128
+            or miss_part_lse.numel() < (U + FETCH_ATTN_COPY_WAVES) * G):
+        raise ValueError("miss partials hold U + FETCH_ATTN_COPY_WAVES slots")
     _check("sparse_hbm_cache_fetch_attn", load().sparse_hbm_cache_fetch_attn(
         ctypes.byref(dims), ctypes.byref(policy), _ptr(host_kv), _ptr(cache_kv), capacity,
-        _ptr(step_counter), _ptr(ws), ws.numel() * ws.element_size(), _ptr(q), _ptr(ctx_lens),
-        _ptr(sel_counts), _ptr(sel_pages), _ptr(hit_phys), scale, workers, _ptr(part_o),
-        _ptr(part_lse), max_parts, _stream(stream)))
+        _ptr(step_counter), _ptr(q), _ptr(ctx_lens), _ptr(sel_counts), _ptr(sel_pages),
+        _ptr(hit_phys), _ptr(miss_counts), _ptr(miss_pages), _ptr(miss_phys), scale, workers,
+        _ptr(part_o), _ptr(part_lse), max_parts, _ptr(miss_part_o), _ptr(miss_part_lse),
+        _stream(stream)))
 
 
 def split_misses(dims, sel_counts, sel_pages, sel_phys, hit_phys, miss_counts, miss_pages,

@@ -477,14 +477,18 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
  * are final once the resolve has run).  One step is:
  *   sparse_hbm_cache_resolve_split   hits, victims, slots, and each unit's
  *                                    placed misses as a short list; no copy
- *   sparse_hbm_cache_fetch           the misses' copies; advances the step
- * then attention over (sel_counts, sel_pages, hit_phys) -- it may overlap
- * the fetch; sparse_hbm_cache_fetch_attn runs the two in one launch -- and,
- * after the fetch, attention over the miss lists; both sets of partials are
- * merged by sparse_merge_splits_pair (attention over a partition of a list,
- * merged by log-sum-exp, is attention over the list).
- * Cache state, statistics and sel_phys equal those of
- * sparse_hbm_cache_resolve_policy on the same inputs.
+ *   sparse_hbm_cache_fetch_attn      the misses' copies, each attended in
+ *                                    the copying wave as it arrives, beside
+ *                                    attention over the hits; advances the
+ *                                    step
+ *   sparse_merge_splits_pair         both sets of partials into the output
+ *                                    (attention over a partition of a list,
+ *                                    merged by log-sum-exp, is attention
+ *                                    over the list)
+ * or, with the copy on its own (sparse_hbm_cache_fetch), attention over the
+ * hits beside it and attention over the miss lists after it.  Cache state,
+ * statistics and sel_phys equal those of sparse_hbm_cache_resolve_policy on
+ * the same inputs.
  *
  * sparse_hbm_cache_resolve_split -- the resolve of
  * sparse_hbm_cache_resolve_policy without the fetch.  Arguments as there
@@ -536,34 +540,50 @@ sparse_status sparse_hbm_cache_fetch(const sparse_dims* dims, const sparse_cache
                                      size_t ws_bytes, void* stream);
 
 /*
- * sparse_hbm_cache_fetch_attn -- sparse_hbm_cache_fetch and the attention
- * over the hits in one launch: the copies of the misses placed by the last
- * sparse_hbm_cache_resolve_split on this ws, and sparse_decode_attn over
- * (sel_counts, sel_pages, hit_phys) on the cache pool (kv = cache_kv,
- * stride_page 4096, stride_head 0, pool_pages = B * capacity, or capacity
- * pooled).  A hit's slot is never written by the same step, so the two run
- * side by side in one grid: SPARSE_FETCH_ATTN_COPY_GROUPS copying
- * workgroups first, then the attention's workers; every workgroup holds 96
- * KiB of LDS, so a compute unit never mixes copying waves (whose host reads
- * take microseconds) with attention waves; attention workers beyond the
- * free units start as units free up.  With nothing to copy the copying
- * workgroups exit at once and the launch is the attention alone.
- * The split schedule of the host tier on one stream, with no wait between
- * streams: resolve_split, fetch_attn, attention over the miss lists,
- * sparse_merge_splits_pair.  Arguments: as sparse_hbm_cache_fetch, then as
- * sparse_decode_attn (part_o / part_lse / max_parts for this workers value).
- * Advances *step_counter.  Errors as those two calls.
+ * sparse_hbm_cache_fetch_attn -- the copies of a step's placed misses with
+ * the attention over them, and the attention over its hits, in one launch.
+ *   - SPARSE_FETCH_ATTN_COPY_WAVES copying waves share the miss lists
+ *     (miss_counts, miss_pages, miss_phys as written by
+ *     sparse_hbm_cache_resolve_split) under the balanced plan of
+ *     sparse_decode_attn with one worker per wave.  Each reads its misses
+ *     from host_kv (device-initiated reads of pinned host memory), writes
+ *     them to their slots of cache_kv, and attends them from registers with
+ *     the unit's queries; its partial for unit u goes to slot u + wave of
+ *     miss_part_o / miss_part_lse.  A miss whose page is outside
+ *     0 .. max_pages - 1 or whose slot is outside the pool is skipped.
+ *   - The attention's workers run sparse_decode_attn over (sel_counts,
+ *     sel_pages, hit_phys) on the cache pool (kv = cache_kv, stride_page
+ *     4096, stride_head 0, pool_pages = B * capacity, or capacity pooled).
+ *     A hit's slot is never written by the same step, so the two run side by
+ *     side.
+ * The copying waves form SPARSE_FETCH_ATTN_COPY_GROUPS workgroups placed
+ * first in the grid; every workgroup holds 96 KiB of LDS, so a compute unit
+ * never mixes copying waves (whose host reads take microseconds) with
+ * attention waves.  With nothing to copy the copying waves exit after
+ * reading miss_counts.  sparse_merge_splits_pair(part_o, part_lse,
+ * sel_counts, workers, miss_part_o, miss_part_lse, miss_counts,
+ * SPARSE_FETCH_ATTN_COPY_WAVES) then gives the step's output.
+ * Arguments: dims, policy, host_kv, cache_kv, capacity and step_counter as
+ * sparse_hbm_cache_resolve_policy; q, ctx_lens, sel_counts, sel_pages,
+ * scale, workers, part_o, part_lse, max_parts as sparse_decode_attn with
+ * hit_phys as sel_phys;
+ *   miss_counts  int32 [U]; miss_pages, miss_phys int32 [U][max_pages]
+ *   miss_part_o  fp32 [U + SPARSE_FETCH_ATTN_COPY_WAVES][G][128] out,
+ *                16-byte aligned
+ *   miss_part_lse fp32 [U + SPARSE_FETCH_ATTN_COPY_WAVES][G] out
+ * Advances *step_counter.  Errors: as sparse_decode_attn and
+ * sparse_hbm_cache_resolve_policy (no workspace); a NULL miss list or miss
+ * partial -> INVALID.
  */
 #define SPARSE_FETCH_ATTN_COPY_GROUPS 64
-sparse_status sparse_hbm_cache_fetch_attn(const sparse_dims* dims,
-                                          const sparse_cache_policy* policy,
-                                          const uint16_t* host_kv, uint16_t* cache_kv,
-                                          int32_t capacity, int32_t* step_counter, void* ws,
-                                          size_t ws_bytes, const uint16_t* q,
-                                          const int32_t* ctx_lens, const int32_t* sel_counts,
-                                          const int32_t* sel_pages, const int32_t* hit_phys,
-                                          float scale, int32_t workers, float* part_o,
-                                          float* part_lse, int64_t max_parts, void* stream);
+#define SPARSE_FETCH_ATTN_COPY_WAVES (4 * SPARSE_FETCH_ATTN_COPY_GROUPS)
+sparse_status sparse_hbm_cache_fetch_attn(
+    const sparse_dims* dims, const sparse_cache_policy* policy, const uint16_t* host_kv,
+    uint16_t* cache_kv, int32_t capacity, int32_t* step_counter, const uint16_t* q,
+    const int32_t* ctx_lens, const int32_t* sel_counts, const int32_t* sel_pages,
+    const int32_t* hit_phys, const int32_t* miss_counts, const int32_t* miss_pages,
+    const int32_t* miss_phys, float scale, int32_t workers, float* part_o, float* part_lse,
+    int64_t max_parts, float* miss_part_o, float* miss_part_lse, void* stream);
 
 /*
  * sparse_split_misses -- for each unit u, the list entries i < sel_counts[u]

@@ -215,8 +215,9 @@ def test_missing_library_fails_loudly(tmp_path):
 
 def test_binding_constants_match_header():
     """The binding's copies of the header's constants: the read probe's grid
-    (it sizes xor_out) and the attention plan's fewest pages per worker (the
-    bench's partial count follows it)."""
+    (it sizes xor_out), the attention plan's fewest pages per worker (the
+    bench's partial count follows it) and the host tier's copying grid (it
+    sizes the copying waves' partials)."""
     with open(HEADER) as f:
         text = f.read()
     m = re.search(r"#define SPARSE_READ_BLOCKS_GROUPS (\d+)", text)
@@ -229,5 +230,8 @@ def test_binding_constants_match_header():
     assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_SCRATCH_BYTES
     m = re.search(r"#define SPARSE_FETCH_ATTN_COPY_GROUPS (\d+)", text)
     assert m and int(m.group(1)) == lib.FETCH_ATTN_COPY_GROUPS
+    m = re.search(r"#define SPARSE_FETCH_ATTN_COPY_WAVES \((\d+) \* SPARSE_FETCH_ATTN_COPY_GROUPS\)",
+                  text)
+    assert m and int(m.group(1)) * lib.FETCH_ATTN_COPY_GROUPS == lib.FETCH_ATTN_COPY_WAVES
     m = re.search(r"#define SPARSE_FETCH_GROUPS (\d+)", text)
     assert m and int(m.group(1)) == lib.FETCH_GROUPS

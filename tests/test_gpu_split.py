@@ -203,3 +203,119 @@ def test_merge_pair_of_disjoint_lists(gpu_lib):
         elif len(part_b[u]) == 0:
             assert torch.equal(out[b, rows], o_a[b, rows]), u
             assert torch.equal(lse[b, rows], l_a[b, rows]), u
+
+
+_FETCH_ATTN_CASES = {
+    # per-unit miss and hit counts; 609 plan positions: ~30 per copying wave,
+    # so slices cross units
+    "short": dict(kv_heads=4, pages=260, C=640, bad_u=6,
+                  miss_n=[0, 1, 2, 63, 64, 65, 130, 200], hit_n=[5, 0, 40, 3, 17, 0, 64, 33]),
+    # 16 units of ~1300 misses: 18816 positions, over 64 per copying wave, so
+    # a wave's slice of one unit can take its ids in two batches; one pool of
+    # slots shared by both requests
+    "long": dict(kv_heads=8, pages=1400, C=20000, pooled=True, bad_u=3,
+                 miss_n=[1400, 1337, 0, 1290, 1363, 1400, 64, 1301, 1400, 1299, 1342, 0, 1385,
+                         1400, 1317, 1350], hit_n=[0, 3, 7, 0, 1, 0, 0, 2, 0, 0, 0, 5, 0, 0, 1, 0]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_FETCH_ATTN_CASES))
+def test_fetch_attn_direct_lists(gpu_lib, case):
+    """sparse_hbm_cache_fetch_attn on hand-made lists, without a resolve:
+    miss lists of many lengths (0, 1, 64, 65, ... 1100) beside hit lists on
+    units placed in the cache beforehand; two miss entries out of range (a
+    page of -1, a slot past the pool), which must be neither copied nor
+    attended.  Every valid miss's slot then holds its host unit bitwise, the
+    slot named by the bad page keeps its old bytes, the step advances by one,
+    and the pair merge of both sets of partials equals attention + merge over
+    the union lists on the filled cache, and the oracle on two units."""
+    from adaptive_sparse_paged_amd.host_tier import UNIT_ELEMS
+    cf = _FETCH_ATTN_CASES[case]
+    w = I.custom_workload("fetch_attn_" + case, 2, 4 * cf["kv_heads"], cf["kv_heads"],
+                          ("fixed", 16 * cf["pages"] - 5), index=128)
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
+    B, H, G = w.batch, w.kv_heads, w.group
+    U, C, workers = B * H, cf["C"], 8
+    pooled = cf.get("pooled", False)
+    S = C if pooled else B * C              # slots in all
+    miss_n, hit_n = cf["miss_n"], cf["hit_n"]
+    say(f"[fetch_attn] {case}: B=2 Hkv={H}, {C} slots {'pooled' if pooled else 'per request'}, "
+        f"miss counts {miss_n}")
+    rng = np.random.default_rng(128)
+    n = I.pages_of(int(lens[0]))
+    cache = HbmPageCache(dims, host, C, pooled=pooled)
+    poison = torch.from_numpy(rng.integers(-2**15, 2**15, size=(S, UNIT_ELEMS),
+                                           dtype=np.int16)).cuda()
+    cache.cache_kv.copy_(poison)
+    i32 = np.int32
+    hc, hp, hx = np.zeros(U, i32), np.full((U, MP), -1, i32), np.full((U, MP), -1, i32)
+    mc, mp, mx = np.zeros(U, i32), np.full((U, MP), -1, i32), np.full((U, MP), -1, i32)
+    shared = list(rng.permutation(C))
+    free = [shared] * B if pooled else [list(rng.permutation(C)) for _ in range(B)]
+    for u in range(U):
+        b, h = divmod(u, H)
+        pages = rng.choice(n, size=hit_n[u] + miss_n[u], replace=False).astype(i32)
+        slots = np.array([(0 if pooled else b * C) + free[b].pop() for _ in pages], i32)
+        hc[u], mc[u] = hit_n[u], miss_n[u]
+        hp[u, :hit_n[u]], hx[u, :hit_n[u]] = pages[:hit_n[u]], slots[:hit_n[u]]
+        mp[u, :miss_n[u]], mx[u, :miss_n[u]] = pages[hit_n[u]:], slots[hit_n[u]:]
+        for p, x in zip(hp[u, :hit_n[u]], hx[u, :hit_n[u]]):      # the hits are resident
+            cache.cache_kv[x].copy_(host[b, p, h].reshape(-1).cuda())
+    bad_u = cf["bad_u"]
+    bad_page_slot = int(mx[bad_u, 70])
+    mp[bad_u, 70] = -1                    # a page of -1: skipped, its slot untouched
+    mx[bad_u, 100] = S + 5                # a slot past the pool: skipped
+    valid = (mp >= 0) & (mx >= 0) & (mx < S)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    hmax = lib.decode_max_parts(dims, workers)
+    ho, hl = torch.empty((hmax, G, 128), **f32), torch.empty((hmax, G), **f32)
+    mo = torch.empty((U + lib.FETCH_ATTN_COPY_WAVES, G, 128), **f32)
+    ml = torch.empty((U + lib.FETCH_ATTN_COPY_WAVES, G), **f32)
+    out = torch.full((B, w.q_heads, 128), float("nan"), **f32)
+    lse = torch.full((B, w.q_heads), float("nan"), **f32)
+    g_hc, g_mc = dev(hc), dev(mc)
+    lib.hbm_cache_fetch_attn(dims, cache.policy, host, cache.cache_kv, C, cache.step_counter,
+                             li.q, li.ctx_lens, g_hc, dev(hp), dev(hx), g_mc, dev(mp), dev(mx),
+                             w.scale, workers, ho, hl, hmax, mo, ml)
+    lib.merge_splits_pair(dims, ho, hl, g_hc, workers, mo, ml, g_mc, lib.FETCH_ATTN_COPY_WAVES,
+                          out, lse)
+    torch.cuda.synchronize()
+    assert int(cache.step_counter) == 1
+    got = cache.cache_kv.cpu()
+    for u in range(U):
+        b, h = divmod(u, H)
+        for i in range(miss_n[u]):
+            if valid[u, i]:
+                assert torch.equal(got[mx[u, i]], host[b, mp[u, i], h].reshape(-1)), (u, i)
+    assert torch.equal(got[bad_page_slot], poison[bad_page_slot].cpu()), "bad page copied"
+    # the union lists on the filled cache, one pass
+    uc, up, ux = np.zeros(U, i32), np.full((U, MP), -1, i32), np.full((U, MP), -1, i32)
+    for u in range(U):
+        keep = valid[u, :miss_n[u]]
+        pg = np.concatenate([hp[u, :hit_n[u]], mp[u, :miss_n[u]][keep]])
+        sl = np.concatenate([hx[u, :hit_n[u]], mx[u, :miss_n[u]][keep]])
+        uc[u] = pg.size
+        up[u, :pg.size], ux[u, :pg.size] = pg, sl
+    po, pl = torch.empty_like(ho), torch.empty_like(hl)
+    o_ref, l_ref = torch.empty_like(out), torch.empty_like(lse)
+    g_uc = dev(uc)
+    lib.decode_attn(dims, li.q, cache.cache_kv, UNIT_ELEMS, 0, S, li.ctx_lens, g_uc, dev(up),
+                    dev(ux), w.scale, workers, po, pl, hmax)
+    lib.merge_splits(dims, po, pl, g_uc, workers, o_ref, l_ref)
+    torch.cuda.synchronize()
+    d = float((out - o_ref).abs().max())
+    say(f"  max |fused - one pass| {d:.1e}")
+    fin = torch.isfinite(l_ref)
+    assert torch.equal(fin, torch.isfinite(lse)) and bool(torch.isneginf(lse[~fin]).all())
+    assert d <= 1e-5 and float((lse[fin] - l_ref[fin]).abs().max()) <= 1e-5
+    for u in (bad_u, U - 1):
+        b, h = divmod(u, H)
+        k_, v_, q_, nv = I.unit_host(w, 0, b, h, int(lens[b]))
+        o_or, _ = O.attend_pages(O.bf16_bits_to_f64(q_), O.bf16_bits_to_f64(k_),
+                                 O.bf16_bits_to_f64(v_), nv, up[u, :uc[u]], w.scale)
+        o_gpu = out[b, h * G:(h + 1) * G].double().cpu().numpy()
+        assert np.abs(o_gpu - o_or).max() <= ATTN_TOL
