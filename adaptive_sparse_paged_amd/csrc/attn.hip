@@ -118,23 +118,24 @@ __device__ __forceinline__ void attend_page(PageFrag& f, const bf16x8* qf, bool 
 
 // One unit segment of a workgroup's slice: unit u's list entries [i0, i1).
 // seg_begin issues the segment's first loads (context length, the first 64
-// list ids of each wave, q) in one round trip and returns without waiting
-// for them.  Every load is unconditional (an index past the
-// segment re-reads its last entry, a padding column of q re-reads the
-// group's last head and is zeroed when used): a load under a condition
-// becomes a branch that waits for it.
+// list ids of each wave) in one round trip and returns without waiting for
+// them.  Every load is unconditional (an index past the segment re-reads its
+// last entry): a load under a condition becomes a branch that waits for it.
 struct Seg {
   int u, b, h, L, i0, i1;
   int pl, xl;        // lane k: logical / physical id of this wave's k-th page of the batch
-  u32x4 qw[4];       // lane (g, j): q of head min(g, G - 1), channels 32 s + 8 j .. +7
 };
 
-__device__ __forceinline__ void seg_begin(Seg& S, const uint16_t* __restrict__ q,
-                                          const int32_t* __restrict__ ctx_lens,
+__device__ __forceinline__ void seg_begin(Seg& S, const int32_t* __restrict__ ctx_lens,
                                           const int32_t* __restrict__ sel_pages,
                                           const int32_t* __restrict__ sel_phys, int hkv,
-                                          int group, int max_pages, int u, int i0, int i1) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6, row = lane & 15, j = lane >> 4;
+                                          int max_pages, int u, int i0, int i1) {
+  // (lane and thread index through empty asm statements: the lane-dependent
+  // address parts are computed here rather than hoisted out of the segment
+  // loop, where they would be live, or spilled, across the page loop)
+  int lane = lane_id(), tid = threadIdx.x;
+  asm volatile("" : "+v"(lane), "+v"(tid));
+  const int wv = tid >> 6;
   S.u = u;
   S.b = u / hkv;
   S.h = u - S.b * hkv;
@@ -145,17 +146,16 @@ __device__ __forceinline__ void seg_begin(Seg& S, const uint16_t* __restrict__ q
   const int ie = min(i0 + wv + kAttnWaves * lane, i1 - 1);
   S.pl = sel_pages[rowoff + ie];
   S.xl = sel_phys[rowoff + ie];
-  const uint16_t* qrow =
-      q + ((int64_t)S.b * hkv * group + S.h * group + min(row, group - 1)) * kD + 8 * j;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) S.qw[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
 }
 
 // The segment's pages: each wave takes list entries i0 + wv + 4k and runs an
 // online softmax over them (m_run, l_run, o).  The ids are read 64 at a time
 // into lanes k and broadcast with readlane, so no KV load waits on a list
 // load; each batch's ids are loaded while the previous batch is attended.
-__device__ __forceinline__ void seg_pages(Seg& S, const uint16_t* __restrict__ kv,
+// The unit's queries are loaded here, beside the first page (their round
+// trip overlaps the page's), so no register carries them between segments.
+__device__ __forceinline__ void seg_pages(Seg& S, const uint16_t* __restrict__ q, int hkv,
+                                          const uint16_t* __restrict__ kv,
                                           int64_t stride_page, int64_t stride_head,
                                           int64_t pool_pages,
                                           const int32_t* __restrict__ sel_pages,
@@ -169,14 +169,14 @@ __device__ __forceinline__ void seg_pages(Seg& S, const uint16_t* __restrict__ k
   const int32_t* lx = sel_phys + (int64_t)S.u * max_pages;
   int pl = S.pl, xl = S.xl;
   asm volatile("" : "+v"(pl), "+v"(xl));
-  // B operand of QK: q of head g = row (zero for padding columns).
+  // B operand of QK: q of head g = row.  A padding column (g >= group)
+  // re-reads the group's last head; its logits and weights are masked in
+  // attend_page, so it is not zeroed (a select here would wait for the load).
+  const uint16_t* qrow =
+      q + ((int64_t)S.b * hkv * group + h * group + min(row, group - 1)) * kD + 8 * j;
   bf16x8 qf[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 w = S.qw[s];
-    asm volatile("" : "+v"(w));
-    qf[s] = as_bf16x8(gok ? w : u32x4{0u, 0u, 0u, 0u});
-  }
+  for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * s));
   m_run = -INFINITY;
   l_run = 0.f;
 #pragma unroll
@@ -218,13 +218,25 @@ __device__ __forceinline__ void seg_pages(Seg& S, const uint16_t* __restrict__ k
   }
 }
 
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() is a
+// fence over all memory, which waits for every global load the wave has in
+// flight; this one lets the next segment's loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Merge the 4 waves' (max, sum, O) in LDS into one normalised partial and
-// its log-sum-exp per head, written to `slot`.  All 256 threads call it.
-__device__ __forceinline__ void seg_end(float m_run, float l_run, const floatx4 (&o)[8],
-                                        int group, int64_t slot, float* smem,
-                                        float* __restrict__ part_o,
-                                        float* __restrict__ part_lse) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6, g = lane & 15, j = lane >> 4;
+// its log-sum-exp per head, written to `slot`, in two calls made by all 256
+// threads: seg_stage puts each wave's (max, sum, O) in LDS (after it the
+// accumulators are free), seg_combine merges them.  Loads issued between
+// the two stay in flight through seg_combine's barriers.
+__device__ __forceinline__ void seg_stage(float m_run, float l_run, const floatx4 (&o)[8],
+                                          int group, float* smem) {
+  int lane = lane_id(), tid = threadIdx.x;       // (not hoisted: as in seg_begin)
+  asm volatile("" : "+v"(lane), "+v"(tid));
+  const int wv = tid >> 6, g = lane & 15, j = lane >> 4;
   const bool gok = g < group;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -241,9 +253,22 @@ __device__ __forceinline__ void seg_end(float m_run, float l_run, const floatx4 
       sl[wv * group + g] = l_run;
     }
   }
-  __syncthreads();
+}
+
+__device__ __forceinline__ void seg_combine(int group, int64_t slot, const float* smem,
+                                            float* __restrict__ part_o,
+                                            float* __restrict__ part_lse) {
+  const float* so = smem;
+  const float* sm = smem + kAttnWaves * group * kD;
+  const float* sl = sm + kAttnWaves * group;
+  lds_barrier();
   const float ln2 = 0.6931471805599453f;
-  for (int idx = threadIdx.x; idx < group * kD; idx += 256) {
+  // (the thread index passes through an empty asm statement so that the
+  // addresses below are computed here, not hoisted out of the segment loop
+  // and kept live, or spilled, across the page loop)
+  int t0 = threadIdx.x;
+  asm volatile("" : "+v"(t0));
+  for (int idx = t0; idx < group * kD; idx += 256) {
     const int gg = idx / kD, d = idx - (idx / kD) * kD;
     float M = -INFINITY;
 #pragma unroll
@@ -263,7 +288,7 @@ __device__ __forceinline__ void seg_end(float m_run, float l_run, const floatx4 
     part_o[r * kD + d] = (den > 0.f) ? num / den : 0.f;
     if (d == 0) part_lse[r] = (den > 0.f) ? (M + log2f(den)) * ln2 : -INFINITY;
   }
-  __syncthreads();   // the LDS is reused by the workgroup's next segment
+  lds_barrier();     // the LDS is reused by the workgroup's next segment
 }
 
 // Worker w of the balanced plan: its slice of the step's list entries, one
@@ -294,34 +319,39 @@ __device__ __forceinline__ void attn_worker(
   // worker's first unit always gives it some (its range is longer than that).
   constexpr int C = kPlanUnitCost;
   Seg cur;
-  seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, max(x - off - C, 0),
+  seg_begin(cur, ctx_lens, sel_pages, sel_phys, hkv, max_pages, u, max(x - off - C, 0),
             min(e, off + len) - off - C);
   // Segment by segment.  After the first, the next unit is u + 1 (its length
   // loaded at the segment's start), skipping empty lists.  x < e <= T, so a
   // later unit holds position x whenever the loop goes on; the u < U - 1
   // test only guards against lengths changed under the kernel.  A range that
-  // ends within a unit's first C positions gives no entries there.  (Issuing
-  // the next segment's loads before this one's epilogue gains nothing: the
-  // epilogue's workgroup barrier waits for every load still in flight.)
+  // ends within a unit's first C positions gives no entries there.  The next
+  // segment's first loads are issued before this one's epilogue, whose
+  // barriers order LDS only, so they are in flight while it runs.
   while (true) {
     const int next_raw = sel_counts[min(u + 1, U - 1)];
     float m_run, l_run;
     floatx4 o[8];
-    seg_pages(cur, kv, stride_page, stride_head, pool_pages, sel_pages, sel_phys, scale_log2,
-              group, max_pages, m_run, l_run, o);
-    seg_end(m_run, l_run, o, group, (int64_t)cur.u + w, smem, part_o, part_lse);
-    x = off + C + cur.i1;
-    if (x >= e) break;
-    off += len;
-    ++u;
-    len = plan_positions(next_raw, cap);
-    while (len == 0 && u < U - 1) {
+    seg_pages(cur, q, hkv, kv, stride_page, stride_head, pool_pages, sel_pages, sel_phys,
+              scale_log2, group, max_pages, m_run, l_run, o);
+    const int64_t slot = (int64_t)cur.u + w;
+    bool more = off + C + cur.i1 < e;
+    if (more) {
+      off += len;
       ++u;
-      len = plan_positions(sel_counts[u], cap);
+      len = plan_positions(next_raw, cap);
+      while (len == 0 && u < U - 1) {
+        ++u;
+        len = plan_positions(sel_counts[u], cap);
+      }
+      more = len > 0 && e - off > C;
     }
-    if (len == 0 || e - off <= C) break;
-    seg_begin(cur, q, ctx_lens, sel_pages, sel_phys, hkv, group, max_pages, u, 0,
-              min(e, off + len) - off - C);
+    seg_stage(m_run, l_run, o, group, smem);
+    if (more)
+      seg_begin(cur, ctx_lens, sel_pages, sel_phys, hkv, max_pages, u, 0,
+                min(e, off + len) - off - C);
+    seg_combine(group, slot, smem, part_o, part_lse);
+    if (!more) break;
   }
 }
 
