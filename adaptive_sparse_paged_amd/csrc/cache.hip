@@ -49,17 +49,46 @@ constexpr unsigned long long kTkCountMask = (1ull << kTkHitShift) - 1ull;
 // requested slot's stamp may have been rewritten by another workgroup
 // meanwhile; requested slots are never candidates, and only the stamps of
 // candidates are used.)
+// head_off[h] = the first entry of head h when a request's lists are laid
+// end to end in head order, head_off[hkv] = the request's entry count.
+// Wave 0 reads the hkv counts at once and scans them; then a barrier.
+__device__ __forceinline__ void request_heads(const int32_t* __restrict__ sel_counts, int b,
+                                              int hkv, int max_pages, int32_t* head_off) {
+  const int t = threadIdx.x;
+  if (t < 64) {                              // hkv <= kMaxKvHeads = 64
+    int c = sel_counts[b * hkv + min(t, hkv - 1)];
+    c = (t < hkv) ? min(max(c, 0), max_pages) : 0;
+    const int incl = wave_incl_scan(c);
+    if (t < hkv) head_off[t] = incl - c;
+    if (t == hkv - 1) head_off[hkv] = incl;
+  }
+  __syncthreads();
+}
+
+// The head of each entry ee[k] (0 <= ee[k] < head_off[hkv]): how many heads
+// after the first start at or before it.  Broadcast reads of the offsets,
+// instead of a chain of dependent reads per entry.
+template <int K>
+__device__ __forceinline__ void entry_heads(const int (&ee)[K], int (&hh)[K],
+                                            const int32_t* head_off, int hkv) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) hh[k] = 0;
+  for (int h2 = 1; h2 < hkv; ++h2) {
+    const int o = head_off[h2];
+#pragma unroll
+    for (int k = 0; k < K; ++k) hh[k] += (ee[k] >= o) ? 1 : 0;
+  }
+}
+
 constexpr int kPlaceEpt = 4;                 // list entries per thread per ranking round
 
-__device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
-                                  const int32_t* __restrict__ sel_pages, int hkv, int max_pages,
-                                  int C, int recency_shift, int step, int32_t* __restrict__ tags,
-                                  int32_t* __restrict__ stamps, int32_t* __restrict__ umap,
-                                  int32_t* __restrict__ sel_phys, int32_t* __restrict__ stats,
-                                  MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
-                                  uint32_t M, uint32_t H, int32_t* __restrict__ miss_counts,
-                                  int32_t* __restrict__ miss_pages,
-                                  int32_t* __restrict__ miss_phys) {
+__device__ __forceinline__ uint32_t resolve_place(
+    int b, const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages,
+    int hkv, int max_pages, int C, int recency_shift, int step, int32_t* __restrict__ tags,
+    int32_t* __restrict__ stamps, int32_t* __restrict__ umap, int32_t* __restrict__ sel_phys,
+    int32_t* __restrict__ stats, MissRec* __restrict__ misses, int32_t* __restrict__ miss_count,
+    uint32_t M, uint32_t H, int32_t* __restrict__ miss_counts, int32_t* __restrict__ miss_pages,
+    int32_t* __restrict__ miss_phys) {
   __shared__ uint8_t req[kMaxSlots];       // slot holds a unit requested this step
   __shared__ int32_t avail[kMaxSlots];     // available slots, ascending
   __shared__ int32_t s_tag[kMaxSlots];     // the slots' tags and stamps before this step
@@ -69,22 +98,35 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   __shared__ int32_t head_off[kMaxKvHeads + 1];
   __shared__ uint32_t head_miss[kMaxKvHeads];     // misses per head, then their prefix
   const int tid = threadIdx.x;
+  constexpr int kSPT = kMaxSlots / kResThreads;   // slots per thread, strided
 
-  for (int s = tid; s < C; s += kResThreads) {
-    req[s] = 0;
-    s_tag[s] = tags[s];
-    s_stamp[s] = stamps[s];
+  // Every global read below is issued in batches: a thread's loads of one
+  // batch go out together (indices clamped in range, values pinned by empty
+  // asm statements so that no load moves under a test), and only then are
+  // any of them used.  A load under a per-lane condition, or one behind a
+  // data-dependent loop, becomes its own round trip.
+  {
+    int tg[kSPT], st[kSPT];
+#pragma unroll
+    for (int k = 0; k < kSPT; ++k) {
+      const int sl = min(k * kResThreads + tid, C - 1);
+      tg[k] = tags[sl];
+      st[k] = stamps[sl];
+    }
+#pragma unroll
+    for (int k = 0; k < kSPT; ++k) asm volatile("" : "+v"(tg[k]), "+v"(st[k]));
+#pragma unroll
+    for (int k = 0; k < kSPT; ++k) {
+      const int sl = k * kResThreads + tid;
+      if (sl < C) {
+        req[sl] = 0;
+        s_tag[sl] = tg[k];
+        s_stamp[sl] = st[k];
+      }
+    }
   }
   if (tid < hkv) head_miss[tid] = 0u;
-  if (tid == 0) {
-    int acc = 0;
-    for (int h = 0; h < hkv; ++h) {
-      head_off[h] = acc;
-      acc += min(max(sel_counts[b * hkv + h], 0), max_pages);
-    }
-    head_off[hkv] = acc;
-  }
-  __syncthreads();
+  request_heads(sel_counts, b, hkv, max_pages, head_off);
   const int E = head_off[hkv];
 
   // ---- the requested slots (units resident before this step) and each
@@ -93,26 +135,33 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   {
     constexpr int kBatch = 8;
     for (int base = 0; base < E; base += kBatch * kResThreads) {
-      int hh[kBatch], v[kBatch], s[kBatch];
+      int hh[kBatch], pg[kBatch], v[kBatch], sm[kBatch];
+      int64_t li[kBatch];
+      int ee[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) ee[k] = min(base + k * kResThreads + tid, E - 1);
+      entry_heads(ee, hh, head_off, hkv);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        li[k] = (int64_t)(b * hkv + hh[k]) * max_pages + (ee[k] - head_off[hh[k]]);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) pg[k] = sel_pages[li[k]];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) asm volatile("" : "+v"(pg[k]));
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        const int e = base + k * kResThreads + tid;
-        hh[k] = -1;
-        v[k] = -1;
-        if (e < E) {
-          int h = 0;
-          while (e >= head_off[h + 1]) ++h;
-          hh[k] = h;
-          const int p = sel_pages[(int64_t)(b * hkv + h) * max_pages + (e - head_off[h])];
-          if (p >= 0 && p < max_pages) v[k] = h * max_pages + p;
-        }
+        const bool in = base + k * kResThreads + tid < E;
+        v[k] = (in && pg[k] >= 0 && pg[k] < max_pages) ? hh[k] * max_pages + pg[k] : -1;
       }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) s[k] = (v[k] >= 0) ? umap[v[k]] : -2;
+      for (int k = 0; k < kBatch; ++k) sm[k] = umap[max(v[k], 0)];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) asm volatile("" : "+v"(sm[k]));
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        if (s[k] >= 0 && s[k] < C) req[s[k]] = 1;
-        if (s[k] == -1) atomicAdd(&head_miss[hh[k]], 1u);
+        if (v[k] < 0) continue;
+        if (sm[k] >= 0 && sm[k] < C) req[sm[k]] = 1;
+        if (sm[k] == -1) atomicAdd(&head_miss[hh[k]], 1u);
       }
     }
   }
@@ -127,7 +176,6 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   }
 
   // ---- free slots and victim candidates ----------------------------------
-  constexpr int kSPT = kMaxSlots / kResThreads;   // slots per thread, strided
   uint32_t nfree = 0u, ncand = 0u;
   for (int k = 0; k < kSPT; ++k) {
     const int s = k * kResThreads + tid;
@@ -143,8 +191,9 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   const uint32_t r = (M > F) ? min(M - F, NC) : 0u;   // victims to take
 
   // ---- r least recently used candidates: radix select on the keys -------
-  // key = (stamp >> shift) * 2^32 + unit; keys are distinct, so exactly r
-  // keys are <= kappa
+  // key = (stamp >> shift) * 2^tag_bits + unit; keys are distinct, so
+  // exactly r keys are <= kappa
+  const int tag_bits = unit_tag_bits((long long)hkv * max_pages);
   unsigned long long kappa = 0ull;
   const bool take_all = (r == NC);
   if (r > 0u && !take_all) {
@@ -152,7 +201,7 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
         C, r,
         [&](int s, unsigned long long& key) {
           const int tg = s_tag[s];
-          key = lru_key(s_stamp[s], tg, recency_shift);
+          key = lru_key(s_stamp[s], tg, recency_shift, tag_bits);
           return tg >= 0 && !req[s];
         },
         sel);
@@ -169,7 +218,7 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
     const int tg = s_tag[s];
     bool av = tg < 0;
     if (!av && r > 0u && !req[s])
-      av = take_all || lru_key(s_stamp[s], tg, recency_shift) <= kappa;
+      av = take_all || lru_key(s_stamp[s], tg, recency_shift, tag_bits) <= kappa;
     navail += av ? 1u : 0u;
   }
   uint32_t A;
@@ -180,7 +229,7 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
     const int tg = s_tag[s];
     bool av = tg < 0;
     if (!av && r > 0u && !req[s])
-      av = take_all || lru_key(s_stamp[s], tg, recency_shift) <= kappa;
+      av = take_all || lru_key(s_stamp[s], tg, recency_shift, tag_bits) <= kappa;
     if (av) avail[rank++] = s;
   }
   const uint32_t placed = min(M, A);
@@ -193,25 +242,31 @@ __device__ uint32_t resolve_place(int b, const int32_t* __restrict__ sel_counts,
   for (int base = 0; base < E; base += kPlaceEpt * kResThreads) {
     int hh[kPlaceEpt], pp[kPlaceEpt], vv[kPlaceEpt];
     int64_t li[kPlaceEpt];
+    int ee[kPlaceEpt];
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) ee[k] = min(base + kPlaceEpt * tid + k, E - 1);
+    entry_heads(ee, hh, head_off, hkv);
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k)
+      li[k] = (int64_t)(b * hkv + hh[k]) * max_pages + (ee[k] - head_off[hh[k]]);
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) pp[k] = sel_pages[li[k]];
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) asm volatile("" : "+v"(pp[k]));
 #pragma unroll
     for (int k = 0; k < kPlaceEpt; ++k) {
-      const int e = base + kPlaceEpt * tid + k;
-      hh[k] = 0;
-      pp[k] = -1;
-      li[k] = -1;
-      if (e < E) {
-        int h = 0;
-        while (e >= head_off[h + 1]) ++h;
-        hh[k] = h;
-        li[k] = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
-        pp[k] = sel_pages[li[k]];
-      }
+      const bool in = base + kPlaceEpt * tid + k < E;
+      vv[k] = (in && pp[k] >= 0 && pp[k] < max_pages) ? hh[k] * max_pages + pp[k] : -1;
     }
+    int sm[kPlaceEpt];
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) sm[k] = umap[max(vv[k], 0)];
+#pragma unroll
+    for (int k = 0; k < kPlaceEpt; ++k) asm volatile("" : "+v"(sm[k]));
     uint32_t mine = 0u;
 #pragma unroll
     for (int k = 0; k < kPlaceEpt; ++k) {
-      vv[k] = (pp[k] >= 0 && pp[k] < max_pages) ? hh[k] * max_pages + pp[k] : -1;
-      const bool miss = vv[k] >= 0 && umap[vv[k]] == -1;
+      const bool miss = vv[k] >= 0 && sm[k] == -1;
       if (!miss) vv[k] = -1;
       mine += miss ? 1u : 0u;
     }
@@ -435,19 +490,6 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_kernel(
 //   pool_fetch_kernel  copies every placed miss from pinned host memory.
 constexpr int kMaxPoolSlots = 1 << 22;
 
-__device__ __forceinline__ void request_heads(const int32_t* __restrict__ sel_counts, int b,
-                                              int hkv, int max_pages, int32_t* head_off) {
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int h = 0; h < hkv; ++h) {
-      head_off[h] = acc;
-      acc += min(max(sel_counts[b * hkv + h], 0), max_pages);
-    }
-    head_off[hkv] = acc;
-  }
-  __syncthreads();
-}
-
 __global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
     const int32_t* __restrict__ sel_counts, const int32_t* __restrict__ sel_pages, int hkv,
     int max_pages, int S, const int32_t* __restrict__ step_counter,
@@ -460,27 +502,47 @@ __global__ __launch_bounds__(kResThreads) void pool_mark_kernel(
   const int step = *step_counter;
   request_heads(sel_counts, b, hkv, max_pages, head_off);
   const int E = head_off[hkv];
+  // kMarkEpt entries per thread per round, their loads issued together
+  constexpr int kMarkEpt = 4;
   uint32_t m_local = 0u, h_local = 0u;
-  for (int e = tid; e < E; e += kResThreads) {
-    int h = 0;
-    while (e >= head_off[h + 1]) ++h;
-    const int64_t li = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
-    const int p = sel_pages[li];
-    int sk = -2;
-    if (p >= 0 && p < max_pages) {
-      sk = unit_slot[(int64_t)(b * hkv + h) * max_pages + p];
-      if (sk >= S) sk = -2;                  // corrupt state: never index past the pool
+  for (int base = 0; base < E; base += kMarkEpt * kResThreads) {
+    int ee[kMarkEpt], hh[kMarkEpt], pg[kMarkEpt], sk[kMarkEpt];
+    int64_t li[kMarkEpt], v[kMarkEpt];
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) ee[k] = min(base + k * kResThreads + tid, E - 1);
+    entry_heads(ee, hh, head_off, hkv);
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) {
+      li[k] = (int64_t)(b * hkv + hh[k]) * max_pages + (ee[k] - head_off[hh[k]]);
+      pg[k] = sel_pages[li[k]];
     }
-    if (hit_phys) hit_phys[li] = (sk >= 0) ? sk : -1;
-    if (sk >= 0) {
-      ++h_local;
-      req[sk] = 1;
-      slot_stamp[sk] = step;
-      sel_phys[li] = sk;
-    } else if (sk == -1) {
-      ++m_local;
-    } else {
-      sel_phys[li] = -1;                     // page id out of range: an empty page
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) asm volatile("" : "+v"(pg[k]));
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) {
+      const bool in = base + k * kResThreads + tid < E;
+      v[k] = (in && pg[k] >= 0 && pg[k] < max_pages)
+                 ? (int64_t)(b * hkv + hh[k]) * max_pages + pg[k] : -1;
+      sk[k] = unit_slot[max(v[k], (int64_t)0)];   // unit 0's entry stands in when unused
+    }
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) asm volatile("" : "+v"(sk[k]));
+#pragma unroll
+    for (int k = 0; k < kMarkEpt; ++k) {
+      if (base + k * kResThreads + tid >= E) continue;
+      int s_ = (v[k] >= 0) ? sk[k] : -2;
+      if (s_ >= S) s_ = -2;                  // corrupt state: never index past the pool
+      if (hit_phys) hit_phys[li[k]] = (s_ >= 0) ? s_ : -1;
+      if (s_ >= 0) {
+        ++h_local;
+        req[s_] = 1;
+        slot_stamp[s_] = step;
+        sel_phys[li[k]] = s_;
+      } else if (s_ == -1) {
+        ++m_local;
+      } else {
+        sel_phys[li[k]] = -1;                // page id out of range: an empty page
+      }
     }
   }
   unsigned long long tot;
@@ -505,7 +567,7 @@ struct PoolSel {
 };
 
 __global__ __launch_bounds__(kPoolBlkThreads) void pool_scan_kernel(
-    int S, int recency_shift, const int32_t* __restrict__ slot_tag,
+    int S, int recency_shift, int tag_bits, const int32_t* __restrict__ slot_tag,
     const int32_t* __restrict__ slot_stamp, const uint8_t* __restrict__ req,
     unsigned long long* __restrict__ ckeys, int32_t* __restrict__ cblk,
     int32_t* __restrict__ blk_free, uint32_t* __restrict__ totals) {
@@ -545,7 +607,7 @@ __global__ __launch_bounds__(kPoolBlkThreads) void pool_scan_kernel(
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     if (cd[k]) {
-      ckeys[at] = lru_key(st[k], tg[k], recency_shift);
+      ckeys[at] = lru_key(st[k], tg[k], recency_shift, tag_bits);
       cblk[at] = blk;
       ++at;
     }
@@ -613,7 +675,7 @@ __global__ __launch_bounds__(kResThreads) void pool_select_kernel(
 }
 
 __global__ __launch_bounds__(kPoolBlkThreads) void pool_avail_kernel(
-    int S, int recency_shift, const int32_t* __restrict__ slot_tag,
+    int S, int recency_shift, int tag_bits, const int32_t* __restrict__ slot_tag,
     const int32_t* __restrict__ slot_stamp, uint8_t* __restrict__ req,
     const PoolSel* __restrict__ sel_in, const int32_t* __restrict__ blk_off,
     int32_t* __restrict__ avail, int32_t* __restrict__ placed_out) {
@@ -633,7 +695,7 @@ __global__ __launch_bounds__(kPoolBlkThreads) void pool_avail_kernel(
       const int st = slot_stamp[sk];
       if (tg < 0) av[k] = true;
       else if (sl.r > 0u && !rq)
-        av[k] = sl.take_all || lru_key(st, tg, recency_shift) <= sl.kappa;
+        av[k] = sl.take_all || lru_key(st, tg, recency_shift, tag_bits) <= sl.kappa;
       req[sk] = 0;                             // marks are read only here: clear them
     }
     n += av[k] ? 1u : 0u;
@@ -665,23 +727,42 @@ __global__ __launch_bounds__(kResThreads) void pool_place_kernel(
   const int64_t n_units = (int64_t)gridDim.x * hkv * max_pages;
   uint32_t ev_local = 0u, mbase = 0u;
   if (Mb > 0u) {
-    for (int base = 0; base < E; base += kResThreads) {
-      const int e = base + tid;
-      uint32_t miss = 0u;
-      int64_t v = -1, li = 0;
-      if (e < E) {
-        int h = 0;
-        while (e >= head_off[h + 1]) ++h;
-        li = (int64_t)(b * hkv + h) * max_pages + (e - head_off[h]);
-        const int p = sel_pages[li];
-        if (p >= 0 && p < max_pages) {
-          v = (int64_t)(b * hkv + h) * max_pages + p;
-          miss = (unit_slot[v] == -1) ? 1u : 0u;
-        }
+    // rounds of kPlaceEpt * 1024 entries; thread t ranks the blocked run of
+    // kPlaceEpt entries from kPlaceEpt t, its loads issued together
+    for (int base = 0; base < E; base += kPlaceEpt * kResThreads) {
+      int ee[kPlaceEpt], hh[kPlaceEpt], pp[kPlaceEpt], sm[kPlaceEpt];
+      int64_t li[kPlaceEpt], vv[kPlaceEpt];
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) ee[k] = min(base + kPlaceEpt * tid + k, E - 1);
+      entry_heads(ee, hh, head_off, hkv);
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) {
+        li[k] = (int64_t)(b * hkv + hh[k]) * max_pages + (ee[k] - head_off[hh[k]]);
+        pp[k] = sel_pages[li[k]];
+      }
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) asm volatile("" : "+v"(pp[k]));
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) {
+        const bool in = base + kPlaceEpt * tid + k < E;
+        vv[k] = (in && pp[k] >= 0 && pp[k] < max_pages)
+                    ? (int64_t)(b * hkv + hh[k]) * max_pages + pp[k] : -1;
+        sm[k] = unit_slot[max(vv[k], (int64_t)0)];
+      }
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) asm volatile("" : "+v"(sm[k]));
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) {
+        const bool miss = vv[k] >= 0 && sm[k] == -1;
+        if (!miss) vv[k] = -1;
+        mine += miss ? 1u : 0u;
       }
       uint32_t tot;
-      const uint32_t mr = off + mbase + block_excl_scan<uint32_t, kResThreads>(miss, scan32, tot);
-      if (miss) {
+      uint32_t mr = off + mbase + block_excl_scan<uint32_t, kResThreads>(mine, scan32, tot);
+#pragma unroll
+      for (int k = 0; k < kPlaceEpt; ++k) {
+        if (vv[k] < 0) continue;
         if (mr < P) {
           const int sl = avail[mr];
           const int old = slot_tag[sl];
@@ -689,14 +770,15 @@ __global__ __launch_bounds__(kResThreads) void pool_place_kernel(
             if (old < n_units) unit_slot[old] = -1;
             ++ev_local;
           }
-          slot_tag[sl] = (int32_t)v;
+          slot_tag[sl] = (int32_t)vv[k];
           slot_stamp[sl] = step;
-          unit_slot[v] = sl;
-          sel_phys[li] = sl;
-          misses[mr] = MissRec{(int32_t)v, sl};
+          unit_slot[vv[k]] = sl;
+          sel_phys[li[k]] = sl;
+          misses[mr] = MissRec{(int32_t)vv[k], sl};
         } else {
-          sel_phys[li] = -1;
+          sel_phys[li[k]] = -1;
         }
+        ++mr;
       }
       mbase += tot;
     }
@@ -941,14 +1023,18 @@ sparse_status resolve_pooled(const sparse_dims* dims, int shift, const int32_t* 
                      sel_pages, hkv, MP, S, step_counter, slot_stamp, unit_slot, sel_phys,
                      hit_phys, w.req, w.counts);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
+  // pooled unit ids: (b * Hkv + h) * max_pages + p
+  const int tag_bits = sp::unit_tag_bits((long long)B * hkv * MP);
   hipLaunchKernelGGL(sp::pool_scan_kernel, dim3(w.nblk), dim3(sp::kPoolBlkThreads), 0, s, S,
-                     shift, slot_tag, slot_stamp, w.req, w.ckeys, w.cblk, w.blk_free, w.totals);
+                     shift, tag_bits, slot_tag, slot_stamp, w.req, w.ckeys, w.cblk, w.blk_free,
+                     w.totals);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_select_kernel, dim3(1), dim3(sp::kResThreads), 0, s, B, w.nblk,
                      w.counts, w.moff, w.ckeys, w.cblk, w.blk_free, w.totals, w.blk_off, w.psel);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_avail_kernel, dim3(w.nblk), dim3(sp::kPoolBlkThreads), 0, s, S,
-                     shift, slot_tag, slot_stamp, w.req, w.psel, w.blk_off, w.avail, w.placed);
+                     shift, tag_bits, slot_tag, slot_stamp, w.req, w.psel, w.blk_off, w.avail,
+                     w.placed);
   if (hipGetLastError() != hipSuccess) return SPARSE_ERR_HIP;
   hipLaunchKernelGGL(sp::pool_place_kernel, dim3(B), dim3(sp::kResThreads), 0, s, sel_counts,
                      sel_pages, hkv, MP, step_counter, slot_tag, slot_stamp, unit_slot, sel_phys,

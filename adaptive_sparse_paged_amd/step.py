@@ -121,9 +121,11 @@ class SparseDecodeStep:
             with torch.cuda.stream(s):
                 lib.score_pages(dg, q[b0:b1], summ, pool_pages, page_table[b0:b1],
                                 ctx_lens[b0:b1], self.scale, b.logits[b0:b1], s)
+                on = self.offsets
                 lib.select_coverage(dg, b.logits[b0:b1], ctx_lens[b0:b1], page_table[b0:b1],
-                                    self.gamma, b.sel_counts[u0:u1], gr["sel_offsets"],
-                                    b.sel_pages[u0:u1], b.sel_phys[u0:u1], gr["ws"], s)
+                                    self.gamma, b.sel_counts[u0:u1],
+                                    gr["sel_offsets"] if on else None, b.sel_pages[u0:u1],
+                                    b.sel_phys[u0:u1], gr["ws"] if on else None, s)
                 gr["selected"].record(s)
                 lib.decode_attn(dg, q[b0:b1], kv, stride_page, stride_head, pool_pages,
                                 ctx_lens[b0:b1], b.sel_counts[u0:u1], b.sel_pages[u0:u1],

@@ -252,19 +252,21 @@ def test_deterministic(gpu_lib):
     assert torch.equal(a[2], st.buf.logits)
 
 
-def test_grouped_streams_match_single_stream(gpu_lib):
+@pytest.mark.parametrize("offsets", [True, False], ids=["offsets", "no_offsets"])
+def test_grouped_streams_match_single_stream(gpu_lib, offsets):
     """Request groups on separate streams (selection of one group under the
     attention of another) give bitwise the same lists, and the same outputs
     up to the order of the log-sum-exp merge (each group's attention splits
-    its own lists over the workgroups), eagerly and replayed from a graph."""
+    its own lists over the workgroups), eagerly and replayed from a graph;
+    with and without the per-group prefix sums of the counts."""
     w = I.custom_workload("groups", 5, 8, 2, ("uniform", 300, 9000), alpha=("uniform", 1, 6),
                           index=111)
-    say("[groups] 5 requests in 3 stream groups")
+    say(f"[groups] 5 requests in 3 stream groups, offsets={offsets}")
     layer = GpuLayer(w)
     li = layer.li
     ref = layer.step(0.97, 16)
     layer.run(ref)
-    grp = SparseDecodeStep(layer.dims, 0.97, 16, scale=w.scale, groups=3)
+    grp = SparseDecodeStep(layer.dims, 0.97, 16, scale=w.scale, groups=3, offsets=offsets)
     args = (li.q, layer.summ, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages,
             li.page_table, li.ctx_lens)
     grp.run(*args)
