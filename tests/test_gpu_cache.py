@@ -302,3 +302,19 @@ def _ragged(lists, sizes):
             for h in range(H):
                 out[t, b, h] = lists[t, b, h, :sizes[b]]
     return out
+
+
+@pytest.mark.timeout(300)
+def test_cache_resolver_host_tier_full(gpu_lib):
+    """The host-tier workload itself: all 16 requests of 524288 tokens, 4096
+    slots each, 448-page lists drifting 10%, 256 attention workers (the
+    benchmarked shape), 6 steps from cold -- every request's LRU state,
+    statistics and slot ids against the oracle at every step, every resident
+    slot's bytes, and attention through the cache bit-identical to attention
+    over the HBM pool."""
+    w = I.WORKLOADS["host_tier_512k"]
+    ex = w.extra
+    say("[cache] host_tier_512k in full: 16 x 524288 tokens, 4096 slots, 448-page lists")
+    stats = _case(w, C=ex["capacity"], list_pages=ex["list_pages"], steps=6, drift=ex["drift"],
+                  workers=256)
+    assert sum(r["evictions"] for r in stats[-16:]) > 0 and sum(r["hits"] for r in stats[-16:]) > 0

@@ -319,3 +319,19 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
                                  O.bf16_bits_to_f64(v_), nv, up[u, :uc[u]], w.scale)
         o_gpu = out[b, h * G:(h + 1) * G].double().cpu().numpy()
         assert np.abs(o_gpu - o_or).max() <= ATTN_TOL
+
+
+@pytest.mark.timeout(300)
+def test_split_host_tier_full(gpu_lib):
+    """The split schedule at the benchmarked host-tier shape (16 requests of
+    524288 tokens, 4096 slots each, 448-page lists drifting 10%, 256
+    attention workers, the copying waves' plan over ~5750 misses per step):
+    5 steps from cold, the last two replayed from a graph, then one step where
+    every access hits, against the one-pass step as above."""
+    w = I.WORKLOADS["host_tier_512k"]
+    ex = w.extra
+    say("[split] host_tier_512k in full: 16 x 524288 tokens, 4096 slots, 448-page lists")
+    misses, worst = _run(w, ex["capacity"], ex["list_pages"], 5, ex["drift"], workers=256,
+                         graph_from=3, hit_steps=1)
+    say(f"  {misses} misses, max |split - one pass| {worst:.1e}")
+    assert misses > 0
