@@ -187,6 +187,23 @@ def test_null_and_value_checks(L):
     assert fetch(None, FAKE, 1 << 30) == lib.ERR_INVALID
     assert fetch(FAKE, ctypes.c_void_p(0x10002), 1 << 30) == lib.ERR_INVALID
     assert fetch(FAKE, FAKE, 16) == lib.ERR_WORKSPACE
+    # the fetch with its attention beside the attention over the hits
+    fa = lambda host=FAKE, cap=64, step=FAKE, pol=lib.CachePolicy(0, 0), ml=(FAKE, FAKE, FAKE), \
+        mp=20, mo=FAKE, mlse=FAKE: L.sparse_hbm_cache_fetch_attn(
+            ctypes.byref(d), ctypes.byref(pol), host, FAKE, cap, step, FAKE, FAKE, FAKE, FAKE,
+            FAKE, *ml, 0.1, 16, FAKE, FAKE, mp, mo, mlse, None)
+    assert fa(host=None) == lib.ERR_INVALID
+    assert fa(cap=0) == lib.ERR_INVALID
+    assert fa(cap=9000) == lib.ERR_UNSUPPORTED                   # per-request slot limit
+    assert fa(step=None) == lib.ERR_INVALID
+    assert fa(pol=lib.CachePolicy(0, 3)) == lib.ERR_INVALID
+    assert fa(mp=19) == lib.ERR_INVALID                          # hits' partials: U + 16 = 20
+    assert fa(ml=(None, FAKE, FAKE)) == lib.ERR_INVALID
+    assert fa(ml=(FAKE, None, FAKE)) == lib.ERR_INVALID
+    assert fa(ml=(FAKE, FAKE, None)) == lib.ERR_INVALID
+    assert fa(mo=None) == lib.ERR_INVALID
+    assert fa(mlse=None) == lib.ERR_INVALID
+    assert fa(mo=ctypes.c_void_p(0x10004)) == lib.ERR_INVALID    # 16-byte aligned partials
     assert L.sparse_split_misses(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                                  None) == lib.ERR_INVALID
     assert L.sparse_lse_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
