@@ -388,8 +388,8 @@ def host_tier_bench(args):
     host memory (32 GiB), a 4096-slot HBM cache per request, page lists of 448
     pages per (request, KV head) drifting 10% per step over 64 steps, each
     step timed with HIP events.  Schedule "split" (default): resolve, then the
-    fetch of the misses beside attention over the hits, then attention over
-    the misses merged into the hits' result.  Schedule "one_pass": resolve
+    fetch of the misses (attended by the waves that copy them) beside
+    attention over the hits, then one merge of both.  Schedule "one_pass": resolve
     and fetch, then attention + merge over whole lists, with the two phases
     timed apart.  Either way, then steps with every access a hit (no host
     IO), timed on the device: the one-pass resolve against its attention +
