@@ -213,6 +213,11 @@ _FETCH_ATTN_CASES = {
     # 16 units of ~1300 misses: 18816 positions, over 64 per copying wave, so
     # a wave's slice of one unit can take its ids in two batches; one pool of
     # slots shared by both requests
+    # all 16 MFMA columns live (G = 16), and one (G = 1)
+    "short_g16": dict(kv_heads=2, group=16, pages=260, C=640, bad_u=3,
+                      miss_n=[0, 65, 130, 200], hit_n=[7, 0, 64, 33]),
+    "short_g1": dict(kv_heads=4, group=1, pages=260, C=640, bad_u=6,
+                     miss_n=[1, 0, 63, 64, 65, 17, 130, 2], hit_n=[5, 9, 0, 3, 17, 0, 64, 33]),
     "long": dict(kv_heads=8, pages=1400, C=20000, pooled=True, bad_u=3,
                  miss_n=[1400, 1337, 0, 1290, 1363, 1400, 64, 1301, 1400, 1299, 1342, 0, 1385,
                          1400, 1317, 1350], hit_n=[0, 3, 7, 0, 1, 0, 0, 2, 0, 0, 0, 5, 0, 0, 1, 0]),
@@ -231,7 +236,7 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
     the union lists on the filled cache, and the oracle on two units."""
     from adaptive_sparse_paged_amd.host_tier import UNIT_ELEMS
     cf = _FETCH_ATTN_CASES[case]
-    w = I.custom_workload("fetch_attn_" + case, 2, 4 * cf["kv_heads"], cf["kv_heads"],
+    w = I.custom_workload("fetch_attn_" + case, 2, cf.get("group", 4) * cf["kv_heads"], cf["kv_heads"],
                           ("fixed", 16 * cf["pages"] - 5), index=128)
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
