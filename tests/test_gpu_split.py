@@ -224,33 +224,26 @@ _FETCH_ATTN_CASES = {
 }
 
 
-@pytest.mark.parametrize("case", sorted(_FETCH_ATTN_CASES))
-def test_fetch_attn_direct_lists(gpu_lib, case):
-    """sparse_hbm_cache_fetch_attn on hand-made lists, without a resolve:
-    miss lists of many lengths (0, 1, 64, 65, ... 1100) beside hit lists on
-    units placed in the cache beforehand; two miss entries out of range (a
-    page of -1, a slot past the pool), which must be neither copied nor
-    attended.  Every valid miss's slot then holds its host unit bitwise, the
-    slot named by the bad page keeps its old bytes, the step advances by one,
-    and the pair merge of both sets of partials equals attention + merge over
-    the union lists on the filled cache, and the oracle on two units."""
+def _fetch_attn_check(w, C, pooled, miss_n, hit_n, bad_u=None, workers=8, seed=128):
+    """One sparse_hbm_cache_fetch_attn call on hand-made lists: per unit u,
+    hit_n[u] pages already resident in the cache and miss_n[u] pages to copy
+    and attend, distinct pages of the request's context and distinct slots
+    (per request, or of the pool).  With bad_u, two of that unit's miss
+    entries are out of range (a page of -1, a slot past the pool) and must be
+    neither copied nor attended.  Checks: every valid miss's slot holds its
+    host unit bitwise, the bad page's slot keeps its old bytes, the step
+    advances by one, and the pair merge of both sets of partials equals
+    attention + merge over the union lists on the filled cache (and the
+    oracle on two units)."""
     from adaptive_sparse_paged_amd.host_tier import UNIT_ELEMS
-    cf = _FETCH_ATTN_CASES[case]
-    w = I.custom_workload("fetch_attn_" + case, 2, cf.get("group", 4) * cf["kv_heads"], cf["kv_heads"],
-                          ("fixed", 16 * cf["pages"] - 5), index=128)
     lens = I.context_lengths(w)
     li = I.build_layer(w, 0, "cuda", lens=lens)
     host, MP = I.build_host_pool(w, 0, lens=lens)
     dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
     B, H, G = w.batch, w.kv_heads, w.group
-    U, C, workers = B * H, cf["C"], 8
-    pooled = cf.get("pooled", False)
+    U = B * H
     S = C if pooled else B * C              # slots in all
-    miss_n, hit_n = cf["miss_n"], cf["hit_n"]
-    say(f"[fetch_attn] {case}: B=2 Hkv={H}, {C} slots {'pooled' if pooled else 'per request'}, "
-        f"miss counts {miss_n}")
-    rng = np.random.default_rng(128)
-    n = I.pages_of(int(lens[0]))
+    rng = np.random.default_rng(seed)
     cache = HbmPageCache(dims, host, C, pooled=pooled)
     poison = torch.from_numpy(rng.integers(-2**15, 2**15, size=(S, UNIT_ELEMS),
                                            dtype=np.int16)).cuda()
@@ -262,6 +255,7 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
     free = [shared] * B if pooled else [list(rng.permutation(C)) for _ in range(B)]
     for u in range(U):
         b, h = divmod(u, H)
+        n = I.pages_of(int(lens[b]))
         pages = rng.choice(n, size=hit_n[u] + miss_n[u], replace=False).astype(i32)
         slots = np.array([(0 if pooled else b * C) + free[b].pop() for _ in pages], i32)
         hc[u], mc[u] = hit_n[u], miss_n[u]
@@ -269,10 +263,11 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
         mp[u, :miss_n[u]], mx[u, :miss_n[u]] = pages[hit_n[u]:], slots[hit_n[u]:]
         for p, x in zip(hp[u, :hit_n[u]], hx[u, :hit_n[u]]):      # the hits are resident
             cache.cache_kv[x].copy_(host[b, p, h].reshape(-1).cuda())
-    bad_u = cf["bad_u"]
-    bad_page_slot = int(mx[bad_u, 70])
-    mp[bad_u, 70] = -1                    # a page of -1: skipped, its slot untouched
-    mx[bad_u, 100] = S + 5                # a slot past the pool: skipped
+    bad_page_slot = None
+    if bad_u is not None:
+        bad_page_slot = int(mx[bad_u, 70])
+        mp[bad_u, 70] = -1                # a page of -1: skipped, its slot untouched
+        mx[bad_u, 100] = S + 5            # a slot past the pool: skipped
     valid = (mp >= 0) & (mx >= 0) & (mx < S)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -296,7 +291,8 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
         for i in range(miss_n[u]):
             if valid[u, i]:
                 assert torch.equal(got[mx[u, i]], host[b, mp[u, i], h].reshape(-1)), (u, i)
-    assert torch.equal(got[bad_page_slot], poison[bad_page_slot].cpu()), "bad page copied"
+    if bad_page_slot is not None:
+        assert torch.equal(got[bad_page_slot], poison[bad_page_slot].cpu()), "bad page copied"
     # the union lists on the filled cache, one pass
     uc, up, ux = np.zeros(U, i32), np.full((U, MP), -1, i32), np.full((U, MP), -1, i32)
     for u in range(U):
@@ -313,17 +309,65 @@ def test_fetch_attn_direct_lists(gpu_lib, case):
     lib.merge_splits(dims, po, pl, g_uc, workers, o_ref, l_ref)
     torch.cuda.synchronize()
     d = float((out - o_ref).abs().max())
-    say(f"  max |fused - one pass| {d:.1e}")
     fin = torch.isfinite(l_ref)
     assert torch.equal(fin, torch.isfinite(lse)) and bool(torch.isneginf(lse[~fin]).all())
     assert d <= 1e-5 and float((lse[fin] - l_ref[fin]).abs().max()) <= 1e-5
-    for u in (bad_u, U - 1):
+    nonempty = [u for u in range(U) if uc[u] > 0]
+    for u in ([bad_u] if bad_u is not None else []) + nonempty[-1:]:
         b, h = divmod(u, H)
         k_, v_, q_, nv = I.unit_host(w, 0, b, h, int(lens[b]))
         o_or, _ = O.attend_pages(O.bf16_bits_to_f64(q_), O.bf16_bits_to_f64(k_),
                                  O.bf16_bits_to_f64(v_), nv, up[u, :uc[u]], w.scale)
         o_gpu = out[b, h * G:(h + 1) * G].double().cpu().numpy()
         assert np.abs(o_gpu - o_or).max() <= ATTN_TOL
+    return d
+
+
+@pytest.mark.parametrize("case", sorted(_FETCH_ATTN_CASES))
+def test_fetch_attn_direct_lists(gpu_lib, case):
+    """sparse_hbm_cache_fetch_attn on hand-made lists, without a resolve:
+    miss lists of many lengths (0, 1, 64, 65, ... 1400) beside hit lists on
+    units placed in the cache beforehand, at G = 1, 4 and 16, per-request
+    and pooled slots, with two bad miss entries (see _fetch_attn_check)."""
+    cf = _FETCH_ATTN_CASES[case]
+    w = I.custom_workload("fetch_attn_" + case, 2, cf.get("group", 4) * cf["kv_heads"],
+                          cf["kv_heads"], ("fixed", 16 * cf["pages"] - 5), index=128)
+    say(f"[fetch_attn] {case}: B=2 Hkv={w.kv_heads} G={w.group}, {cf['C']} slots "
+        f"{'pooled' if cf.get('pooled') else 'per request'}, miss counts {cf['miss_n']}")
+    d = _fetch_attn_check(w, cf["C"], cf.get("pooled", False), cf["miss_n"], cf["hit_n"],
+                          bad_u=cf["bad_u"])
+    say(f"  max |fused - one pass| {d:.1e}")
+
+
+def test_fetch_attn_random_lists(gpu_lib):
+    """A seeded sweep of the same check: batch 1-4, 1-4 KV heads, every
+    supported G, ragged contexts, per-request or pooled slots, miss and hit
+    counts drawn per unit from 0 to 300 (some units empty), 1-16 attention
+    workers."""
+    rng = np.random.default_rng(2024)
+    for case in range(8):
+        B = int(rng.integers(1, 5))
+        H = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        pooled = bool(rng.integers(0, 2))
+        w = I.custom_workload(f"fetch_attn_rand{case}", B, G * H, H, ("uniform", 2000, 9000),
+                              index=200 + case)
+        lens = I.context_lengths(w)
+        miss_n, hit_n = [], []
+        for u in range(B * H):
+            n = I.pages_of(int(lens[u // H]))
+            m = int(rng.integers(0, min(300, n) + 1)) if rng.random() > 0.2 else 0
+            k = int(rng.integers(0, min(300, n - m) + 1)) if rng.random() > 0.2 else 0
+            miss_n.append(m)
+            hit_n.append(k)
+        per_req = [sum(miss_n[b * H:(b + 1) * H]) + sum(hit_n[b * H:(b + 1) * H])
+                   for b in range(B)]
+        C = max(sum(per_req), 1) if pooled else max(max(per_req), 1)
+        workers = int(rng.integers(1, 17))
+        say(f"[fetch_attn] random case {case}: B={B} Hkv={H} G={G} "
+            f"{'pooled' if pooled else 'per request'} C={C} workers={workers} "
+            f"misses {sum(miss_n)} hits {sum(hit_n)}")
+        _fetch_attn_check(w, C, pooled, miss_n, hit_n, workers=workers, seed=300 + case)
 
 
 @pytest.mark.timeout(300)
