@@ -389,3 +389,57 @@ def test_attn_merge_in_one_call_equals_two_calls(gpu_lib):
                          out2, lse2)
         torch.cuda.synchronize()
         assert torch.equal(one[0], out2) and torch.equal(one[1], lse2), workers
+
+
+def test_out_of_range_ids_inside_lists(gpu_lib):
+    """Physical ids outside the pool in the middle of otherwise valid lists
+    (-1, a negative id, exactly pool_pages, far past it), and one unit whose
+    every entry is out of range: each such entry reads as an empty page, so
+    the outputs equal attention over the same lists with those entries
+    removed, and nothing is NaN."""
+    w = I.custom_workload("bad_ids", 3, 16, 4, ("uniform", 3000, 9000), index=117)
+    say("[edge] out-of-range physical ids inside lists")
+    layer = GpuLayer(w)
+    li = layer.li
+    H = w.kv_heads
+    U = w.batch * H
+    rng = np.random.default_rng(117)
+    lens = li.ctx_lens.cpu().numpy()
+    lists = {}
+    for u in range(U):
+        n = I.pages_of(int(lens[u // H]))
+        lists[u] = np.sort(rng.choice(n, size=int(rng.integers(1, min(n, 150) + 1)),
+                                      replace=False)).astype(np.int32)
+    bad_vals = [-1, -12345, int(li.pool_pages), int(li.pool_pages) + 100000]
+    st = layer.step(0.99, 12)
+    ref = layer.step(0.99, 12)
+    feed_lists(st, layer, lists)
+    phys = st.buf.sel_phys.cpu().numpy()
+    keep = {}
+    for u in range(U):
+        k = len(lists[u])
+        if u == U - 2:
+            bad = np.arange(k)                       # every entry out of range
+        else:
+            bad = rng.choice(k, size=min(k, int(rng.integers(0, 6))), replace=False)
+        for i in bad:
+            phys[u, i] = bad_vals[int(rng.integers(0, len(bad_vals)))]
+        mask = np.ones(k, bool)
+        mask[bad] = False
+        keep[u] = lists[u][mask]
+    st.buf.sel_phys.copy_(torch.from_numpy(phys))
+    args = (li.q, li.kv_pool, layer.stride_page, layer.stride_head, li.pool_pages, li.ctx_lens)
+    o, l = st.attend(*args)
+    o, l = o.clone(), l.clone()
+    feed_lists(ref, layer, keep)
+    o_ref, l_ref = ref.attend(*args)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(l).any()
+    fin = torch.isfinite(l_ref)
+    assert torch.equal(fin, torch.isfinite(l))
+    assert float((o - o_ref).abs().max()) <= 1e-5
+    assert float((l[fin] - l_ref[fin]).abs().max()) <= 1e-5
+    b, h = divmod(U - 2, H)
+    G = w.group
+    assert torch.all(o[b, h * G:(h + 1) * G] == 0)
+    assert torch.all(torch.isneginf(l[b, h * G:(h + 1) * G]))
