@@ -151,10 +151,10 @@ class SplitHostTierStep:
         hit."""
         self.dims, self.cache = dims, cache
         self.hits = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
-                                     offsets=False)
+                                     offsets=False, scoring=False)
         # the miss lists, and the copying waves' partials (one worker per wave)
         self.miss = SparseDecodeStep(dims, gamma, lib.FETCH_ATTN_COPY_WAVES, scale=scale,
-                                     device=device, offsets=False)
+                                     device=device, offsets=False, scoring=False)
         self.hit_phys = torch.zeros_like(self.hits.buf.sel_phys)
 
     @property
@@ -223,7 +223,7 @@ class LayeredHostTierStep:
             cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
             workers = max(1, cus - lib.FETCH_GROUPS)
         self.attn = SparseDecodeStep(dims, gamma, workers, scale=scale, device=device,
-                                     offsets=False)
+                                     offsets=False, scoring=False)
         # per-layer slot lists: later layers' resolves write while layer l attends
         self.sel_phys = [torch.zeros_like(self.attn.buf.sel_phys) for _ in host_pools]
         # the split resolve's hit slots, unused here (one buffer: the resolves

@@ -56,9 +56,11 @@ class SparseDecodeStep:
     """
 
     def __init__(self, dims, gamma, workers=0, scale=None, device="cuda", groups=1,
-                 offsets=True):
+                 offsets=True, scoring=True):
         """offsets: also write the whole-batch prefix sum (sel_offsets) in the
-        selection; the attention does not need it."""
+        selection; the attention does not need it.  scoring=False: attention
+        over lists the caller writes (sel_counts / sel_pages / sel_phys) only,
+        so no logits buffer or selection workspace is allocated."""
         self.dims = dims
         self.offsets = bool(offsets)
         self.gamma = float(gamma)
@@ -70,13 +72,15 @@ class SparseDecodeStep:
         self.max_parts = lib.decode_max_parts(dims, self.workers)
         i32 = dict(dtype=torch.int32, device=device)
         f32 = dict(dtype=torch.float32, device=device)
+        self.scoring = bool(scoring)
         self.buf = StepBuffers(
-            logits=torch.empty((B, Hkv, G, MP), **f32),
+            logits=torch.empty((B, Hkv, G, MP) if scoring else (0,), **f32),
             sel_counts=torch.zeros(U, **i32),
             sel_offsets=torch.zeros(U + 1, **i32),
             sel_pages=torch.zeros((U, MP), **i32),
             sel_phys=torch.zeros((U, MP), **i32),
-            ws=torch.zeros(lib.select_workspace_bytes(dims), dtype=torch.uint8, device=device),
+            ws=torch.zeros(lib.select_workspace_bytes(dims) if scoring else 0, dtype=torch.uint8,
+                           device=device),
             part_o=torch.empty((self.max_parts, G, HEAD_DIM), **f32),
             part_lse=torch.empty((self.max_parts, G), **f32),
             out=torch.empty((B, Hq, HEAD_DIM), **f32),
@@ -84,6 +88,8 @@ class SparseDecodeStep:
         )
         self.groups = []
         if groups > 1:
+            if not scoring:
+                raise ValueError("request groups score and select: scoring=False has none")
             self._make_groups(int(groups), device)
 
     def _make_groups(self, ngroups, device):
@@ -139,6 +145,8 @@ class SparseDecodeStep:
         return out, out_lse
 
     def score_select(self, q, summ, pool_pages, page_table, ctx_lens, stream=None):
+        if not self.scoring:
+            raise ValueError("this step was made with scoring=False")
         d, b = self.dims, self.buf
         lib.score_pages(d, q, summ, pool_pages, page_table, ctx_lens, self.scale, b.logits, stream)
         on = self.offsets
