@@ -425,7 +425,7 @@ def host_tier_bench(args):
     pooled = name == "pooled"
     cap = B * C if pooled else C          # the same HBM either way
     cache = HbmPageCache(dims, host, cap, recency_shift=shift, pooled=pooled)
-    st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale)
+    st = SparseDecodeStep(dims, args.gamma, args.workers, scale=w.scale, scoring=False)
     q = torch.empty((B, w.q_heads, D), dtype=torch.int16)
     for b in range(B):
         for h in range(H):
