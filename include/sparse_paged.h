@@ -595,7 +595,8 @@ sparse_status sparse_hbm_cache_fetch_attn(
  * -- lists that sparse_decode_attn takes as (sel_counts, sel_pages,
  * sel_phys).  The same lists sparse_hbm_cache_resolve_split writes when given
  * the miss-list outputs; this is the separate pass over sel_phys and hit_phys.
- * One 256-thread workgroup per unit.
+ * Each sel_counts[u] is clamped to [0, max_pages]; entries past a unit's
+ * miss count are left as they were.  One 256-thread workgroup per unit.
  */
 sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_counts,
                                   const int32_t* sel_pages, const int32_t* sel_phys,
