@@ -68,6 +68,11 @@ def test_max_parts_and_workspace(L):
     r0 = L.sparse_decode_max_parts(ctypes.byref(d), 0)
     assert r0 == -1 or r0 > 4
     assert L.sparse_select_workspace_bytes(ctypes.byref(d)) >= 4
+    # the exact per-request cache's workspace is the {0, 0} policy's
+    for cap in (1, 64, 4096):
+        plain = lib.cache_workspace_bytes(d, cap)
+        assert plain > 0
+        assert plain == lib.cache_policy_workspace_bytes(d, lib.CachePolicy(0, 0), cap)
     # a bound on the list lengths clamps the lists, not the grid
     d.max_list_pages = 20
     assert L.sparse_decode_max_parts(ctypes.byref(d), 16) == 4 + 16

@@ -318,3 +318,36 @@ def test_cache_resolver_host_tier_full(gpu_lib):
     stats = _case(w, C=ex["capacity"], list_pages=ex["list_pages"], steps=6, drift=ex["drift"],
                   workers=256)
     assert sum(r["evictions"] for r in stats[-16:]) > 0 and sum(r["hits"] for r in stats[-16:]) > 0
+
+
+def test_plain_resolve_entry_equals_exact_policy(gpu_lib):
+    """sparse_hbm_cache_resolve (no policy argument) is the exact per-request
+    LRU: bitwise the same state, statistics, slot ids and slot bytes as
+    sparse_hbm_cache_resolve_policy with {0, 0}, step after step."""
+    w = I.custom_workload("cache_plain", 2, 8, 2, ("fixed", 1600), index=143)
+    say("plain resolve entry: 2 requests, 64 slots, 8 steps")
+    lens = I.context_lengths(w)
+    li = I.build_layer(w, 0, "cuda", lens=lens)
+    host, MP = I.build_host_pool(w, 0, lens=lens)
+    dims = lib.make_dims(w.batch, w.q_heads, w.kv_heads, MP)
+    C = 64
+    a = HbmPageCache(dims, host, C)
+    b = HbmPageCache(dims, host, C)
+    lists = I.drift_lists(w, min(I.pages_of(L) for L in lens), 40, 8, 0.25)
+    B, H = w.batch, w.kv_heads
+    st = SparseDecodeStep(dims, 0.99, 8, scale=w.scale)
+    layer = types.SimpleNamespace(w=w, dims=dims, li=li)
+    for t in range(lists.shape[0]):
+        feed_lists(st, layer, {q * H + h: lists[t, q, h] for q in range(B) for h in range(H)})
+        phys_b = torch.empty_like(st.buf.sel_phys)
+        a.resolve(st.buf.sel_counts, st.buf.sel_pages, st.buf.sel_phys)
+        lib.hbm_cache_resolve(dims, st.buf.sel_counts, st.buf.sel_pages, b.host_kv, b.cache_kv,
+                              b.capacity, b.slot_tag, b.slot_stamp, b.unit_slot, b.step_counter,
+                              phys_b, b.stats, b.ws)
+        torch.cuda.synchronize()
+        for name in ("slot_tag", "slot_stamp", "unit_slot", "stats", "step_counter", "cache_kv"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (t, name)
+        U = B * H
+        for u in range(U):
+            n = int(st.buf.sel_counts[u].item())
+            assert torch.equal(st.buf.sel_phys[u, :n], phys_b[u, :n]), (t, u, "slot ids")
