@@ -132,7 +132,8 @@ sparse_status sparse_score_pages(const sparse_dims* dims, const uint16_t* q, con
                                  const int32_t* ctx_lens, float scale, float* logits,
                                  void* stream);
 
-/* Bytes of workspace sparse_select_coverage needs (host). */
+/* Bytes of workspace sparse_select_coverage needs (host; a helper of the
+ * coverage rule, [P1], abstract, coverage-rule sentence). */
 size_t sparse_select_workspace_bytes(const sparse_dims* dims);
 
 /*
@@ -214,7 +215,8 @@ sparse_status sparse_append_tokens(const sparse_dims* dims, const uint16_t* k_ne
  * fixed cost, in pages, of starting a unit's segment (see sparse_decode_attn). */
 #define SPARSE_ATTN_UNIT_COST_PAGES 12
 
-/* Partial slots one step of sparse_decode_attn may write (host): U + W, with
+/* Partial slots one step of sparse_decode_attn may write (host; a helper of
+ * [P1]'s self-planning attention, abstract, self-planning sentence): U + W, with
  * U = batch * num_kv_heads and W = workers, or the current device's compute
  * unit count when workers = 0.  Returns -1 for invalid dims, workers < 0, or
  * workers = 0 when the current device cannot be queried. */
@@ -348,7 +350,8 @@ sparse_status sparse_decode_attn_merge_noalloc(const sparse_dims* dims, const ui
                                                int32_t workers, float* out, float* out_lse,
                                                void* stream);
 
-/* Bytes of workspace sparse_hbm_cache_resolve needs (host): a ticket word per
+/* Bytes of workspace sparse_hbm_cache_resolve needs (host; the resolver of
+ * [P2], abstract, sentence on the fused in-graph resolver): a ticket word per
  * request (the resolve's workgroups of one request count themselves in on
  * it), the per-request list of placed misses (kept for a separate fetch, see
  * sparse_hbm_cache_fetch) and a ticket for the whole grid.  Zero it once
@@ -440,7 +443,8 @@ size_t sparse_cache_policy_workspace_bytes(const sparse_dims* dims,
 
 /*
  * sparse_hbm_cache_resolve_policy -- sparse_hbm_cache_resolve under a
- * replacement policy (see sparse_cache_policy).  Arguments as
+ * replacement policy (see sparse_cache_policy: [P3], abstract, technique
+ * (2), bucketed LRU and per-request budgets sized dynamically).  Arguments as
  * sparse_hbm_cache_resolve, except when policy->pooled = 1:
  *   capacity   slots of the pool, 1 .. 2^22 (B * Hkv * max_pages < 2^31)
  *   cache_kv   bf16 [capacity][2][2048] device (stride_page 4096, stride_head
@@ -474,7 +478,11 @@ sparse_status sparse_hbm_cache_resolve_policy(const sparse_dims* dims,
  * The host tier in two halves, so that attention over the hits can run while
  * the misses are still crossing PCIe (the split the resolver's placement
  * rule allows: a hit's slot is never a victim of the same step, so the hits
- * are final once the resolve has run).  One step is:
+ * are final once the resolve has run).  The resolver is [P2]'s (abstract:
+ * hit detection, LRU replacement and host-to-device fetches inside the
+ * decode graph; only KV placement changes, so outputs do not), and the
+ * merge is the split-and-merge identity of [P1]'s self-planning attention
+ * (abstract, self-planning sentence).  One step is:
  *   sparse_hbm_cache_resolve_split   hits, victims, slots, and each unit's
  *                                    placed misses as a short list; no copy
  *   sparse_hbm_cache_fetch_attn      the misses' copies, each attended in
@@ -529,7 +537,8 @@ sparse_status sparse_hbm_cache_resolve_split(const sparse_dims* dims,
 #define SPARSE_FETCH_GROUPS 32
 
 /*
- * sparse_hbm_cache_fetch -- copy every miss placed by the last
+ * sparse_hbm_cache_fetch -- the host-to-device fetch of [P2]'s resolver
+ * (abstract, fused-resolver sentence) on its own: copy every miss placed by the last
  * sparse_hbm_cache_resolve_split on this ws from host_kv into its slot of
  * cache_kv (device-initiated reads of pinned host memory), and advance
  * *step_counter.  Arguments as sparse_hbm_cache_resolve_policy.
@@ -586,7 +595,8 @@ sparse_status sparse_hbm_cache_fetch_attn(
     int64_t max_parts, float* miss_part_o, float* miss_part_lse, void* stream);
 
 /*
- * sparse_split_misses -- for each unit u, the list entries i < sel_counts[u]
+ * sparse_split_misses -- a helper of the split host tier above ([P2],
+ * abstract): for each unit u, the list entries i < sel_counts[u]
  * with hit_phys < 0 and sel_phys >= 0 (placed this step, not resident
  * before), in list order, as
  *   miss_counts int32 [U]              their number
@@ -605,7 +615,8 @@ sparse_status sparse_split_misses(const sparse_dims* dims, const int32_t* sel_co
 
 /*
  * sparse_lse_combine -- two attention results over disjoint token sets of
- * the same rows, combined by the identity of sparse_merge_splits:
+ * the same rows, combined by the identity of sparse_merge_splits (the merge
+ * behind [P1]'s self-planning attention, abstract, self-planning sentence):
  *   lse = ln(exp(lse_a) + exp(lse_b)),
  *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b
  * (a side with lse = -inf contributes nothing; both -inf gives out = 0 and
