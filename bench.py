@@ -205,8 +205,10 @@ def library_source_hash():
     return source_hash(*files)
 
 
-# attn.hip and the headers it includes, in this order
-ATTN_SOURCES = ("attn.hip", "common.h", "fetch.h")
+# attn.hip and the headers it includes (the C ABI header holds constants the
+# kernel uses), in this order, relative to the repository root
+ATTN_SOURCES = ("adaptive_sparse_paged_amd/csrc/attn.hip", "adaptive_sparse_paged_amd/csrc/common.h",
+                "adaptive_sparse_paged_amd/csrc/fetch.h", "include/sparse_paged.h")
 
 
 def source_hash(*paths):
@@ -861,9 +863,8 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as f:
             rec = json.load(f)
-        csrc = os.path.join(ROOT, "adaptive_sparse_paged_amd", "csrc")
         # the attention kernel is compiled from attn.hip and the headers it includes
-        src_hash = source_hash(*(os.path.join(csrc, f) for f in ATTN_SOURCES))
+        src_hash = source_hash(*(os.path.join(ROOT, f) for f in ATTN_SOURCES))
         if (rec.get("source_sha256_16") == src_hash and rec.get("workload") == w.name
                 and rec.get("attn_workers") == workers and rec.get("gamma") == args.gamma):
             traffic = rec.get("bytes_per_launch")
