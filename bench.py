@@ -820,6 +820,19 @@ def main():
     ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
     per_replay = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     p10, p50, p90 = (float(np.percentile(per_replay, x)) for x in (10, 50, 90))
+    # The device's own time per step: the GPU first runs a wait long enough
+    # for the host to enqueue every replay, so these events time the device
+    # alone.  A step shorter than the host's launch of its graph (the tiny
+    # workload) is otherwise timed at the host's launch rate.
+    torch.cuda.synchronize()
+    torch.cuda._sleep(ALLHIT_HOST_LEAD_CYCLES)
+    dv = [TimingEvent() for _ in range(2)]
+    dv[0].record()
+    for i in range(args.steps):
+        graph.replay()
+    dv[1].record()
+    torch.cuda.synchronize()
+    device_ms_step = dv[0].elapsed_time(dv[1]) / args.steps
 
     # bytes moved per step
     G, Hkv = w.group, w.kv_heads
@@ -883,6 +896,7 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "us_per_layer": round(ms_step * 1e3 / layers, 2),
         "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
+        "device_ms_per_step": round(device_ms_step, 4),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
